@@ -1,0 +1,155 @@
+/*
+ * submconv.h -- C ABI of the MI355X (gfx950) submanifold 3x3x3 sparse convolution library.
+ *
+ * The operation is SubMConv3d: a 3x3x3 convolution whose output sites are exactly its input
+ * sites (stride 1, no padding).  Every sparse convolution the TRELLIS.2-lineage models
+ * construct is this op (lato.2_mrp_mlx README, "The scope, once measured"; pixal3d_mrp_mlx
+ * working notes, "Measured facts"), with kernel size 3 and the k = 1 case (lato.2_mrp_mlx
+ * README, "Status").
+ *
+ * Two pieces:
+ *   1. an indice map per coordinate set: for every active voxel i and each of the 27 offsets
+ *      d in {-1,0,1}^3, the row of the active voxel at coord_i + d, or -1.  It is built once
+ *      and reused by every convolution on the same coordinates, the way the pages cache it
+ *      per coordinate set like spconv's indice_key (lato.2_mrp_mlx README, header summary);
+ *   2. the convolution
+ *          out[i, o] = bias[o] + sum_{k : nbr[i,k] >= 0} sum_c W[o, dz+1, dy+1, dx+1, c] * f[nbr[i,k], c]
+ *      with W in the KRSC layout [Cout, kz, ky, kx, Cin] (lato.2_mrp_mlx README, header
+ *      summary) and the cross-correlation orientation f[c + d] (lato.2_mrp_mlx README,
+ *      "Correctness", which notes that the mirrored c - d reading is silent when wrong).
+ *
+ * Conventions shared by every entry point
+ *   - Tap index k = 9*(dz+1) + 3*(dy+1) + (dx+1) for d = (dz, dy, dx); the centre tap is 13.
+ *     This is the KRSC flatten order, so W viewed as [Cout, 27, Cin] holds tap k at [:, k, :].
+ *   - Coordinates are int32 rows (b, z, y, x); z pairs with kz, y with ky, x with kx.
+ *     Neighbours never cross different b.
+ *   - Array arguments are DEVICE pointers (hipMalloc'd or from any device allocator), row-major
+ *     and contiguous, aligned at least to their element size.  16-byte aligned bases with
+ *     16-byte-multiple row sizes take the vectorised kernels; anything else takes a slower
+ *     element-wise path with identical results.
+ *   - Scalars and out-parameters named in the signatures as host values are HOST pointers.
+ *   - All device work is enqueued on `stream` (0 = the null stream).  Nothing throws across the
+ *     ABI: every call returns an int status (subm_status_t); on error out-parameters are left
+ *     as documented and subm_last_error() gives a thread-local message.
+ *   - The library keeps a device memory pool per GPU (stream-ordered allocations whose release
+ *     threshold is raised so freed memory is reused, not returned to the driver).
+ */
+#ifndef SUBMCONV_H
+#define SUBMCONV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque handle of one indice map (one per coordinate set). */
+typedef struct submconv_map* submconv_map_t;
+
+typedef enum {
+  SUBM_F32 = 0,  /* float32 storage */
+  SUBM_F16 = 1,  /* IEEE binary16 storage */
+  SUBM_BF16 = 2  /* bfloat16 storage */
+} subm_dtype_t;
+
+typedef enum {
+  SUBM_OK = 0,
+  SUBM_ERR_INVALID_ARG = 1,      /* null pointer, negative size, bad enum, aliasing, ... */
+  SUBM_ERR_DUPLICATE_COORD = 2,  /* two rows share (b, z, y, x) */
+  SUBM_ERR_COORD_RANGE = 3,      /* b outside [0, 65534] or a z/y/x extent above 65534 */
+  SUBM_ERR_SHAPE_MISMATCH = 4,   /* n differs from the map's voxel count */
+  SUBM_ERR_UNSUPPORTED = 5,      /* ksize or dtype the library does not implement */
+  SUBM_ERR_OUT_OF_MEMORY = 6,    /* device allocation failed */
+  SUBM_ERR_HIP = 7               /* any other HIP runtime error (message in subm_last_error) */
+} subm_status_t;
+
+#define SUBM_TAPS 27
+#define SUBM_MAX_BATCH 65535       /* b must lie in [0, SUBM_MAX_BATCH) */
+#define SUBM_MAX_EXTENT 65534      /* max - min of each of z, y, x must not exceed this */
+
+/*
+ * sparse_indice_map_build -- build the indice map (rulebook) of one coordinate set.
+ *   coords   device int32 [n, 4], rows (b, z, y, x).  Borrowed for the duration of the call
+ *            (stream-ordered); the map keeps no reference to it.  Any row order; rows must be
+ *            distinct.
+ *   n        number of rows, 0 <= n <= 2^31 - 1.  n == 0 yields a valid empty map, no launch.
+ *   stream   stream on which the build runs.
+ *   out_map  host pointer; receives the new handle.  Set to NULL first, left NULL on error.
+ * The map stores nbr[n, 27] (int32, row = ORIGINAL input row of the neighbour, -1 if absent),
+ * the total pair count (entries >= 0, centre included) and the per-tap pair counts.
+ * The call synchronises `stream` once, to read the duplicate / range flags and the counts.
+ * Errors: SUBM_ERR_INVALID_ARG, SUBM_ERR_DUPLICATE_COORD, SUBM_ERR_COORD_RANGE,
+ *         SUBM_ERR_OUT_OF_MEMORY, SUBM_ERR_HIP.
+ * Source: lato.2_mrp_mlx README, header summary (indice map with 27 lookups per voxel,
+ * cached per coordinate set) and "Correctness" (batch isolation, isolated voxels).
+ */
+int sparse_indice_map_build(const int32_t* coords, int64_t n, hipStream_t stream,
+                            submconv_map_t* out_map);
+
+/*
+ * sparse_indice_map_free -- release a map.  NULL is accepted (returns SUBM_OK).  No work that
+ * uses the map may still be in flight on any stream, as for freeing any device buffer.
+ */
+int sparse_indice_map_free(submconv_map_t map);
+
+/*
+ * sparse_indice_map_info -- host scalars of a built map: voxel count and total pair count
+ * (number of nbr entries >= 0, centre tap included).  Either out pointer may be NULL.
+ * Source: lato.2_mrp_mlx README, "Correctness" (indice-map hit rates are tested).
+ */
+int sparse_indice_map_info(submconv_map_t map, int64_t* n, int64_t* pairs);
+
+/*
+ * sparse_indice_map_offset_counts -- host int64[27]: pairs per tap k (hit count of each
+ * offset).  counts must point to 27 host int64 values.
+ */
+int sparse_indice_map_offset_counts(submconv_map_t map, int64_t* counts);
+
+/*
+ * sparse_indice_map_copy_nbr -- copy the rulebook into caller memory.
+ *   nbr     device int32 [n, 27] in input row order; nbr[i, k] is the input row of the active
+ *           voxel at coord_i + offset(k), or -1.  Independent of any internal ordering.
+ *   stream  stream on which the copy is enqueued (asynchronous).
+ */
+int sparse_indice_map_copy_nbr(submconv_map_t map, int32_t* nbr, hipStream_t stream);
+
+/*
+ * subm_conv3d_forward -- out = SubMConv3d(feats) on the map's coordinate set.
+ *   map      built map of the coordinate set; may be NULL only when ksize == 1.
+ *   n        number of rows of feats / out; must equal the map's voxel count when map != NULL.
+ *   ksize    3 (27 taps through the map) or 1 (per-voxel linear map; the map is not read).
+ *   cin,cout channel counts, >= 1.
+ *   dtype    storage dtype shared by feats, weight, bias and out.  Products are accumulated in
+ *            float32; the bias is added in float32; the result is rounded once to the storage
+ *            dtype, to nearest even.
+ *   feats    device [n, cin].
+ *   weight   device KRSC [cout, ksize, ksize, ksize, cin].  The library never guesses a layout;
+ *            a torch Conv3d weight [cout, cin, kz, ky, kx] must be permuted by the caller
+ *            (lato.2_mrp_mlx README, header summary: rank alone does not tell the layouts apart).
+ *   bias     device [cout], or NULL for no bias.
+ *   out      device [n, cout]; must not be the same pointer as feats (partial overlap is
+ *            undefined).  Fully overwritten.
+ *   stream   stream on which the kernel is enqueued.  Never synchronises; validation is on the
+ *            host only.  n == 0 returns SUBM_OK with no launch.
+ * Row i of out is written only from rows of feats that are neighbours of i, so the result does
+ * not depend on launch order and is bitwise reproducible run to run (no float atomics).
+ * Errors: SUBM_ERR_INVALID_ARG, SUBM_ERR_SHAPE_MISMATCH, SUBM_ERR_UNSUPPORTED, SUBM_ERR_HIP.
+ * Source: lato.2_mrp_mlx README, header summary and "Correctness"; trellis_sparse_mrp_mlx
+ * commit log, "Extracted from lato.2_mrp_mlx" commit (the 128^3 / 128-channel timing).
+ */
+int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int cin, int cout,
+                        int dtype, const void* feats, const void* weight, const void* bias,
+                        void* out, hipStream_t stream);
+
+/* Static string naming a status code ("SUBM_OK", ...); "unknown status" otherwise. */
+const char* subm_status_string(int status);
+
+/* Thread-local detail of the last error on this thread (empty string if none). */
+const char* subm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SUBMCONV_H */

@@ -1,0 +1,223 @@
+"""ctypes binding of libsubmconv.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls.  Tensors are
+device tensors; PyTorch supplies their memory (data_ptr) and the current HIP
+stream.  No arithmetic of the method happens in Python, and there is no
+fallback: when the shared library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsubmconv.so")
+
+SUBM_F32, SUBM_F16, SUBM_BF16 = 0, 1, 2
+_DTYPE_CODES = {torch.float32: SUBM_F32, torch.float16: SUBM_F16, torch.bfloat16: SUBM_BF16}
+TAPS = 27
+
+# Exported C symbols (kept equal to the declarations in include/submconv.h).
+C_FUNCTIONS = (
+    "sparse_indice_map_build",
+    "sparse_indice_map_free",
+    "sparse_indice_map_info",
+    "sparse_indice_map_offset_counts",
+    "sparse_indice_map_copy_nbr",
+    "subm_conv3d_forward",
+    "subm_status_string",
+    "subm_last_error",
+)
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+class SubmError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, func: str, status: int, name: str, detail: str):
+        super().__init__(f"{func} failed: {name} ({status}): {detail}")
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load (once) and return the shared library.  Raises if it has not been built."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(
+                f"HIP library not found at {p}; build it with "
+                "`python -m submanifold_sparse_convolution_amd.build` (there is no CPU fallback)")
+        lib = ctypes.CDLL(p)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.sparse_indice_map_build.argtypes = [vp, i64, vp, ctypes.POINTER(vp)]
+        lib.sparse_indice_map_free.argtypes = [vp]
+        lib.sparse_indice_map_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        lib.sparse_indice_map_offset_counts.argtypes = [vp, ctypes.POINTER(i64)]
+        lib.sparse_indice_map_copy_nbr.argtypes = [vp, vp, vp]
+        lib.subm_conv3d_forward.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp]
+        for name in C_FUNCTIONS[:6]:
+            getattr(lib, name).restype = ci
+        lib.subm_status_string.argtypes = [ci]
+        lib.subm_status_string.restype = ctypes.c_char_p
+        lib.subm_last_error.argtypes = []
+        lib.subm_last_error.restype = ctypes.c_char_p
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _check(lib, func: str, status: int) -> None:
+    if status != 0:
+        name = lib.subm_status_string(status).decode()
+        detail = lib.subm_last_error().decode()
+        raise SubmError(func, status, name, detail)
+
+
+def _stream_ptr(stream, device) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _device_tensor(t: torch.Tensor, what: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+class IndiceMap:
+    """Owner of one built indice map (submconv_map_t) for one coordinate set."""
+
+    def __init__(self, handle: int, device: torch.device):
+        self._handle = handle
+        self.device = device
+        n = ctypes.c_int64()
+        pairs = ctypes.c_int64()
+        lib = load_library()
+        _check(lib, "sparse_indice_map_info", lib.sparse_indice_map_info(handle, ctypes.byref(n), ctypes.byref(pairs)))
+        self.n = n.value
+        self.pairs = pairs.value
+
+    @property
+    def handle(self) -> int:
+        if self._handle is None:
+            raise ValueError("indice map already freed")
+        return self._handle
+
+    def free(self) -> None:
+        """Release the map.  No work using it may still be in flight."""
+        if self._handle is not None:
+            lib = load_library()
+            h, self._handle = self._handle, None
+            _check(lib, "sparse_indice_map_free", lib.sparse_indice_map_free(h))
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.free()
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def sparse_indice_map_build(coords: torch.Tensor, stream=None) -> IndiceMap:
+    """Build the indice map of int32 device coordinates [N, 4] = (b, z, y, x)."""
+    _device_tensor(coords, "coords")
+    if coords.dtype != torch.int32 or coords.dim() != 2 or coords.shape[1] != 4:
+        raise ValueError("coords must be int32 [N, 4]")
+    lib = load_library()
+    out = ctypes.c_void_p()
+    with torch.cuda.device(coords.device):
+        st = lib.sparse_indice_map_build(coords.data_ptr(), coords.shape[0], _stream_ptr(stream, coords.device),
+                                         ctypes.byref(out))
+    _check(lib, "sparse_indice_map_build", st)
+    return IndiceMap(out.value, coords.device)
+
+
+def sparse_indice_map_free(m: IndiceMap) -> None:
+    m.free()
+
+
+def sparse_indice_map_info(m: IndiceMap) -> tuple[int, int]:
+    """(voxel count, pair count) of a built map."""
+    lib = load_library()
+    n = ctypes.c_int64()
+    pairs = ctypes.c_int64()
+    _check(lib, "sparse_indice_map_info", lib.sparse_indice_map_info(m.handle, ctypes.byref(n), ctypes.byref(pairs)))
+    return n.value, pairs.value
+
+
+def sparse_indice_map_offset_counts(m: IndiceMap) -> list[int]:
+    """Pairs per tap k (27 values)."""
+    lib = load_library()
+    arr = (ctypes.c_int64 * TAPS)()
+    _check(lib, "sparse_indice_map_offset_counts", lib.sparse_indice_map_offset_counts(m.handle, arr))
+    return list(arr)
+
+
+def sparse_indice_map_copy_nbr(m: IndiceMap, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The rulebook nbr [N, 27] int32 (input row of the neighbour, or -1) as a device tensor."""
+    if out is None:
+        out = torch.empty((m.n, TAPS), dtype=torch.int32, device=m.device)
+    _device_tensor(out, "out")
+    if out.dtype != torch.int32 or tuple(out.shape) != (m.n, TAPS):
+        raise ValueError("out must be int32 [N, 27]")
+    lib = load_library()
+    with torch.cuda.device(out.device):
+        st = lib.sparse_indice_map_copy_nbr(m.handle, out.data_ptr(), _stream_ptr(stream, out.device))
+    _check(lib, "sparse_indice_map_copy_nbr", st)
+    return out
+
+
+def subm_conv3d_forward(m: IndiceMap | None, feats: torch.Tensor, weight: torch.Tensor,
+                        bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """SubMConv3d forward: feats [N, Cin], KRSC weight [Cout, k, k, k, Cin] (k = 3 or 1), bias [Cout]."""
+    _device_tensor(feats, "feats")
+    _device_tensor(weight, "weight")
+    if feats.dim() != 2 or weight.dim() != 5:
+        raise ValueError("feats must be [N, Cin] and weight KRSC [Cout, k, k, k, Cin]")
+    k = weight.shape[1]
+    if weight.shape[2] != k or weight.shape[3] != k:
+        raise ValueError("weight spatial dims must be equal (KRSC [Cout, k, k, k, Cin])")
+    if weight.shape[4] != feats.shape[1]:
+        raise ValueError("weight Cin does not match feats")
+    if feats.dtype not in _DTYPE_CODES or weight.dtype != feats.dtype:
+        raise ValueError("feats and weight must share one of float32 / float16 / bfloat16")
+    n, cin, cout = feats.shape[0], feats.shape[1], weight.shape[0]
+    bias_ptr = None
+    if bias is not None:
+        _device_tensor(bias, "bias")
+        if bias.dtype != feats.dtype or tuple(bias.shape) != (cout,):
+            raise ValueError("bias must be [Cout] in the feats dtype")
+        bias_ptr = bias.data_ptr()
+    if out is None:
+        out = torch.empty((n, cout), dtype=feats.dtype, device=feats.device)
+    _device_tensor(out, "out")
+    if out.dtype != feats.dtype or tuple(out.shape) != (n, cout):
+        raise ValueError("out must be [N, Cout] in the feats dtype")
+    lib = load_library()
+    handle = None if m is None else m.handle
+    with torch.cuda.device(feats.device):
+        st = lib.subm_conv3d_forward(handle, n, k, cin, cout, _DTYPE_CODES[feats.dtype], feats.data_ptr(),
+                                     weight.data_ptr(), bias_ptr, out.data_ptr(), _stream_ptr(stream, feats.device))
+    _check(lib, "subm_conv3d_forward", st)
+    return out

@@ -1,0 +1,257 @@
+// C ABI entry points: argument validation, status codes, device memory, the map handle.
+// Every check that does not need the GPU runs before any HIP call, so invalid arguments are
+// rejected identically on a machine without a GPU.
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+
+#include "internal.h"
+
+namespace submconv {
+
+namespace {
+thread_local std::string g_last_error;
+
+int fail(const Status& s) {
+  g_last_error = s.msg;
+  return s.code;
+}
+int fail(int code, const char* msg) {
+  g_last_error = msg;
+  return code;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mu;
+bool g_pool_ready[kMaxDevices] = {};
+
+// Keep freed blocks in the device's default pool (no release back to the driver at every
+// synchronisation), so repeated builds and frees cost no driver allocations after warm-up.
+Status ensure_pool(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return make_status(SUBM_ERR_HIP, "device ordinal out of range");
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if (g_pool_ready[dev]) return Status{};
+  hipMemPool_t pool;
+  SUBM_HIP_TRY(hipDeviceGetDefaultMemPool(&pool, dev));
+  uint64_t threshold = UINT64_MAX;
+  SUBM_HIP_TRY(hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold));
+  g_pool_ready[dev] = true;
+  return Status{};
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+Status make_status(int code, std::string msg) {
+  Status s;
+  s.code = code;
+  s.msg = std::move(msg);
+  return s;
+}
+
+Status hip_status(hipError_t e, const char* what) {
+  const int code = (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) ? SUBM_ERR_OUT_OF_MEMORY : SUBM_ERR_HIP;
+  return make_status(code, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+Status device_alloc(void** ptr, size_t bytes, hipStream_t stream) {
+  int dev = 0;
+  SUBM_HIP_TRY(hipGetDevice(&dev));
+  Status s = ensure_pool(dev);
+  if (!s.ok()) return s;
+  *ptr = nullptr;
+  SUBM_HIP_TRY(hipMallocAsync(ptr, bytes, stream));
+  return Status{};
+}
+
+void device_free(void* ptr, hipStream_t stream) {
+  if (ptr != nullptr) (void)hipFreeAsync(ptr, stream);
+}
+
+}  // namespace submconv
+
+using namespace submconv;
+
+extern "C" const char* subm_status_string(int status) {
+  switch (status) {
+    case SUBM_OK: return "SUBM_OK";
+    case SUBM_ERR_INVALID_ARG: return "SUBM_ERR_INVALID_ARG";
+    case SUBM_ERR_DUPLICATE_COORD: return "SUBM_ERR_DUPLICATE_COORD";
+    case SUBM_ERR_COORD_RANGE: return "SUBM_ERR_COORD_RANGE";
+    case SUBM_ERR_SHAPE_MISMATCH: return "SUBM_ERR_SHAPE_MISMATCH";
+    case SUBM_ERR_UNSUPPORTED: return "SUBM_ERR_UNSUPPORTED";
+    case SUBM_ERR_OUT_OF_MEMORY: return "SUBM_ERR_OUT_OF_MEMORY";
+    case SUBM_ERR_HIP: return "SUBM_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char* subm_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int sparse_indice_map_build(const int32_t* coords, int64_t n, hipStream_t stream,
+                                       submconv_map_t* out_map) {
+  g_last_error.clear();
+  if (out_map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "out_map is NULL");
+  *out_map = nullptr;
+  if (n < 0) return fail(SUBM_ERR_INVALID_ARG, "n is negative");
+  if (n > INT32_MAX) return fail(SUBM_ERR_INVALID_ARG, "n exceeds 2^31 - 1 (rows are int32)");
+  if (n > 0 && coords == nullptr) return fail(SUBM_ERR_INVALID_ARG, "coords is NULL");
+  if ((reinterpret_cast<uintptr_t>(coords) & 3u) != 0) return fail(SUBM_ERR_INVALID_ARG, "coords is not 4-byte aligned");
+
+  submconv_map* m = new (std::nothrow) submconv_map;
+  if (m == nullptr) return fail(SUBM_ERR_OUT_OF_MEMORY, "host allocation of the map handle failed");
+  if (hipGetDevice(&m->d.device) != hipSuccess) {
+    delete m;
+    return fail(SUBM_ERR_HIP, "hipGetDevice failed");
+  }
+  m->d.n = n;
+  if (n == 0) {
+    *out_map = m;
+    return SUBM_OK;
+  }
+
+  const int64_t slots = map_table_slots(n);
+  const int pblocks = map_partial_blocks(n);
+  const size_t table_bytes = round_up((size_t)slots * 16, 256);
+  const size_t partial_bytes = round_up((size_t)pblocks * 27 * sizeof(uint32_t), 256);
+  const size_t tmp_bytes = table_bytes + partial_bytes + sizeof(BuildStats);
+
+  void* tmp = nullptr;
+  void* nbr = nullptr;
+  Status s = device_alloc(&tmp, tmp_bytes, stream);
+  if (s.ok()) s = device_alloc(&nbr, (size_t)n * 27 * sizeof(int32_t), stream);
+  if (!s.ok()) {
+    device_free(tmp, stream);
+    device_free(nbr, stream);
+    delete m;
+    return fail(s);
+  }
+  unsigned char* base = static_cast<unsigned char*>(tmp);
+  uint32_t* partials = reinterpret_cast<uint32_t*>(base + table_bytes);
+  BuildStats* dstats = reinterpret_cast<BuildStats*>(base + table_bytes + partial_bytes);
+
+  BuildStats st;
+  hipError_t e = launch_map_build(coords, n, base, slots, partials, pblocks, static_cast<int32_t*>(nbr), dstats, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(&st, dstats, sizeof(st), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  device_free(tmp, stream);
+  if (e != hipSuccess) {
+    device_free(nbr, stream);
+    delete m;
+    return fail(hip_status(e, "indice map build"));
+  }
+
+  int code = SUBM_OK;
+  std::string msg;
+  if (st.flags & kFlagBatchRange) {
+    code = SUBM_ERR_COORD_RANGE;
+    msg = "batch index outside [0, 65534]";
+  } else if (st.flags & kFlagDuplicate) {
+    code = SUBM_ERR_DUPLICATE_COORD;
+    msg = "two rows share the same (b, z, y, x)";
+  } else if (st.flags & kFlagProbeOverflow) {
+    code = SUBM_ERR_HIP;
+    msg = "internal error: hash table full";
+  } else {
+    static const char* axis[4] = {"b", "z", "y", "x"};
+    for (int a = 1; a < 4; ++a) {
+      if ((int64_t)st.mx[a] - (int64_t)st.mn[a] > SUBM_MAX_EXTENT) {
+        code = SUBM_ERR_COORD_RANGE;
+        msg = std::string("extent of ") + axis[a] + " (max - min) exceeds 65534";
+        break;
+      }
+    }
+  }
+  if (code != SUBM_OK) {
+    device_free(nbr, stream);
+    delete m;
+    return fail(code, msg.c_str());
+  }
+  m->d.nbr = static_cast<int32_t*>(nbr);
+  m->d.pairs = (int64_t)st.pairs;
+  for (int k = 0; k < 27; ++k) m->d.per_tap[k] = (int64_t)st.per_tap[k];
+  *out_map = m;
+  return SUBM_OK;
+}
+
+extern "C" int sparse_indice_map_free(submconv_map_t map) {
+  g_last_error.clear();
+  if (map == nullptr) return SUBM_OK;
+  if (map->d.nbr != nullptr) {
+    DeviceGuard guard(map->d.device);
+    device_free(map->d.nbr, nullptr);
+  }
+  delete map;
+  return SUBM_OK;
+}
+
+extern "C" int sparse_indice_map_info(submconv_map_t map, int64_t* n, int64_t* pairs) {
+  g_last_error.clear();
+  if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
+  if (n != nullptr) *n = map->d.n;
+  if (pairs != nullptr) *pairs = map->d.pairs;
+  return SUBM_OK;
+}
+
+extern "C" int sparse_indice_map_offset_counts(submconv_map_t map, int64_t* counts) {
+  g_last_error.clear();
+  if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
+  if (counts == nullptr) return fail(SUBM_ERR_INVALID_ARG, "counts is NULL");
+  std::memcpy(counts, map->d.per_tap, sizeof(map->d.per_tap));
+  return SUBM_OK;
+}
+
+extern "C" int sparse_indice_map_copy_nbr(submconv_map_t map, int32_t* nbr, hipStream_t stream) {
+  g_last_error.clear();
+  if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
+  if (map->d.n == 0) return SUBM_OK;
+  if (nbr == nullptr) return fail(SUBM_ERR_INVALID_ARG, "nbr is NULL");
+  hipError_t e = hipMemcpyAsync(nbr, map->d.nbr, (size_t)map->d.n * 27 * sizeof(int32_t), hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return fail(hip_status(e, "copy of nbr"));
+  return SUBM_OK;
+}
+
+extern "C" int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int cin, int cout, int dtype,
+                                   const void* feats, const void* weight, const void* bias, void* out,
+                                   hipStream_t stream) {
+  g_last_error.clear();
+  if (ksize != 1 && ksize != 3) return fail(SUBM_ERR_UNSUPPORTED, "ksize must be 1 or 3");
+  if (dtype != SUBM_F32 && dtype != SUBM_F16 && dtype != SUBM_BF16) return fail(SUBM_ERR_UNSUPPORTED, "dtype must be SUBM_F32, SUBM_F16 or SUBM_BF16");
+  if (n < 0) return fail(SUBM_ERR_INVALID_ARG, "n is negative");
+  if (cin < 1 || cout < 1) return fail(SUBM_ERR_INVALID_ARG, "cin and cout must be >= 1");
+  if (cin > (1 << 24) || cout > (1 << 24)) return fail(SUBM_ERR_INVALID_ARG, "cin / cout above 2^24");
+  if (ksize == 3 && map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL but ksize == 3");
+  if (map != nullptr && map->d.n != n) return fail(SUBM_ERR_SHAPE_MISMATCH, "n differs from the map's voxel count");
+  if (n > INT32_MAX) return fail(SUBM_ERR_INVALID_ARG, "n exceeds 2^31 - 1");
+  if (n == 0) return SUBM_OK;
+  if (feats == nullptr || weight == nullptr || out == nullptr) return fail(SUBM_ERR_INVALID_ARG, "feats, weight or out is NULL");
+  if (out == feats) return fail(SUBM_ERR_INVALID_ARG, "out must not alias feats");
+  const uintptr_t elem = dtype == SUBM_F32 ? 4 : 2;
+  if ((reinterpret_cast<uintptr_t>(feats) | reinterpret_cast<uintptr_t>(weight) | reinterpret_cast<uintptr_t>(out) |
+       reinterpret_cast<uintptr_t>(bias)) % elem != 0)
+    return fail(SUBM_ERR_INVALID_ARG, "a pointer is not aligned to the element size");
+  if (map != nullptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(hip_status(e, "hipGetDevice"));
+    if (dev != map->d.device) return fail(SUBM_ERR_INVALID_ARG, "the map was built on another device");
+  }
+  hipError_t e = launch_subm_conv(map == nullptr ? nullptr : &map->d, n, ksize, cin, cout, dtype, feats, weight, bias, out, stream);
+  if (e != hipSuccess) return fail(hip_status(e, "subm_conv3d_forward launch"));
+  return SUBM_OK;
+}

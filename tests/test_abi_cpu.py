@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad arguments on the host.
+
+No compute call is made: every case here fails validation before any HIP call,
+so it runs identically on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import submanifold_sparse_convolution_amd as sc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "submconv.h")
+
+OK, INVALID, DUP, RANGE, SHAPE, UNSUPPORTED, OOM, HIP = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sc.load_library()
+
+
+def test_header_declares_the_binding_functions():
+    assert declared_functions() == sorted(sc.C_FUNCTIONS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    names = ["SUBM_OK", "SUBM_ERR_INVALID_ARG", "SUBM_ERR_DUPLICATE_COORD", "SUBM_ERR_COORD_RANGE",
+             "SUBM_ERR_SHAPE_MISMATCH", "SUBM_ERR_UNSUPPORTED", "SUBM_ERR_OUT_OF_MEMORY", "SUBM_ERR_HIP"]
+    for code, name in enumerate(names):
+        assert lib.subm_status_string(code).decode() == name
+    assert lib.subm_status_string(99).decode() == "unknown status"
+
+
+def test_build_rejects_bad_arguments(lib):
+    out = ctypes.c_void_p(12345)
+    assert lib.sparse_indice_map_build(None, 4, None, None) == INVALID
+    assert lib.sparse_indice_map_build(None, -1, None, ctypes.byref(out)) == INVALID
+    assert out.value is None  # *out_map is cleared first
+    assert lib.sparse_indice_map_build(None, 5, None, ctypes.byref(out)) == INVALID
+    assert b"coords" in lib.subm_last_error()
+    assert lib.sparse_indice_map_build(ctypes.c_void_p(16), 2 ** 31, None, ctypes.byref(out)) == INVALID
+    assert lib.sparse_indice_map_build(ctypes.c_void_p(18), 5, None, ctypes.byref(out)) == INVALID  # misaligned
+
+
+def test_map_accessors_reject_null(lib):
+    assert lib.sparse_indice_map_free(None) == OK
+    n = ctypes.c_int64()
+    assert lib.sparse_indice_map_info(None, ctypes.byref(n), None) == INVALID
+    assert lib.sparse_indice_map_offset_counts(None, (ctypes.c_int64 * 27)()) == INVALID
+    assert lib.sparse_indice_map_copy_nbr(None, ctypes.c_void_p(256), None) == INVALID
+
+
+def fwd(lib, m=None, n=10, k=1, cin=4, cout=4, dtype=0, f=256, w=512, b=None, o=1024):
+    return lib.subm_conv3d_forward(m, n, k, cin, cout, dtype, f, w, b, o, None)
+
+
+def test_forward_rejects_bad_arguments(lib):
+    assert fwd(lib, k=2) == UNSUPPORTED
+    assert fwd(lib, dtype=3) == UNSUPPORTED
+    assert fwd(lib, dtype=-1) == UNSUPPORTED
+    assert fwd(lib, n=-1) == INVALID
+    assert fwd(lib, cin=0) == INVALID
+    assert fwd(lib, cout=0) == INVALID
+    assert fwd(lib, k=3) == INVALID  # k=3 needs a map
+    assert b"map" in lib.subm_last_error()
+    assert fwd(lib, f=None) == INVALID
+    assert fwd(lib, w=None) == INVALID
+    assert fwd(lib, o=None) == INVALID
+    assert fwd(lib, o=256) == INVALID  # out aliases feats
+    assert b"alias" in lib.subm_last_error()
+    assert fwd(lib, f=258) == INVALID  # fp32 pointer not 4-byte aligned
+    assert fwd(lib, dtype=2, f=257) == INVALID  # bf16 pointer not 2-byte aligned
+    assert fwd(lib, n=2 ** 31) == INVALID
+
+
+def test_forward_empty_input_is_a_no_op(lib):
+    # n == 0 with k == 1 and no map returns before touching the device.
+    assert fwd(lib, n=0, f=None, w=None, o=None) == OK
+
+
+def test_python_binding_validates_before_calling(lib):
+    import torch
+    with pytest.raises(ValueError):
+        sc.sparse_indice_map_build(torch.zeros((4, 4), dtype=torch.int32))  # CPU tensor

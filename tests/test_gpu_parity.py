@@ -1,0 +1,334 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Rulebook: bit-exact.  Features: normwise relative error max|y - ref| / max|ref|
+against the float64 oracle on the same rounded inputs, at most 1e-5 for fp32
+storage and 1e-2 for fp16 / bf16 storage (fp32 accumulation, one rounding to
+the storage dtype at the end: the rounding alone contributes up to 2^-9 for
+bf16 and 2^-11 for fp16).
+
+Small configurations are compared in full.  At the full multi-million-voxel
+sizes (the launch configuration the benchmark times) the rulebook is still
+compared in full, and the features on sampled rows (first and last tiles plus
+random rows) that the oracle computes one by one.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import submanifold_sparse_convolution_amd as sc
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2}
+TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    sc.load_library()
+
+
+@functools.lru_cache(maxsize=None)
+def coords_of(key):
+    return synth.coords_for(key)
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_nbr(key):
+    return oracle.rulebook_sorted(coords_of(key))
+
+
+def to_dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def as64(t):
+    return t.double().cpu().numpy()
+
+
+def gpu_nbr(m):
+    out = sc.sparse_indice_map_copy_nbr(m)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def forward(m, f, w, b):
+    out = sc.subm_conv3d_forward(m, to_dev(f), to_dev(w), to_dev(b))
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def check(out, ref, dtype, what=""):
+    err = oracle.normwise_rel_error(as64(out), ref)
+    print(f"  {what} normwise err {err:.3e} (tol {TOL[dtype]:g})", flush=True)
+    assert err <= TOL[dtype], f"{what}: error {err:.3e} above {TOL[dtype]}"
+
+
+def sample_rows(n, tile=128, count=4096, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([np.arange(min(n, 2 * tile)), np.arange(max(0, n - 2 * tile), n),
+                           rng.integers(0, n, count)])
+    return np.unique(rows)
+
+
+# ----------------------------------------------------------------- rulebook, all configs
+
+@pytest.mark.parametrize("key", ["1", "2a", "3a", "3b", "4", "5"])
+def test_rulebook_bit_exact(key):
+    coords = coords_of(key)
+    want = oracle_nbr(key)
+    if key == "1":
+        assert np.array_equal(want, oracle.rulebook(coords))
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        got = gpu_nbr(m)
+        assert m.n == len(coords)
+        assert np.array_equal(got, want)
+        assert m.pairs == int((want >= 0).sum())
+        assert sc.sparse_indice_map_offset_counts(m) == (want >= 0).sum(axis=0).tolist()
+    print(f"  config {key}: N={len(coords)} pairs={int((want >= 0).sum())}", flush=True)
+
+
+# ----------------------------------------------------------------- convolution, all configs
+
+def cfg_tensors(key, layer, cin=None, cout=None):
+    c = synth.config(key)
+    cin = cin or c.cin
+    cout = cout or c.cout
+    n = len(coords_of(key))
+    f = synth.feats_for(c.number, layer, n, cin, c.dtype)
+    w = synth.weight_for(c.number, layer, c.ksize, cin, cout, c.dtype)
+    b = synth.bias_for(c.number, layer, cout, c.dtype)
+    return f, w, b
+
+
+def test_config1_tiny_fp32_full():
+    coords = coords_of("1")
+    f, w, b = cfg_tensors("1", 0)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        out = forward(m, f, w, b)
+    check(out, oracle.conv3(coords, as64(f), as64(w), as64(b)), "f32", "config 1")
+
+
+def test_config2_fp16_k3_and_k1_full():
+    coords = coords_of("2a")
+    f3, w3, b3 = cfg_tensors("2a", 0)
+    f1, w1, b1 = cfg_tensors("2b", 1)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        out3 = forward(m, f3, w3, b3)
+        out1 = forward(m, f1, w1, b1)
+    out1_nomap = forward(None, f1, w1, b1)
+    check(out3, oracle.conv3_rulebook(oracle_nbr("2a"), as64(f3), as64(w3), as64(b3)), "f16", "config 2a k3")
+    ref1 = oracle.conv1(as64(f1), as64(w1), as64(b1))
+    check(out1, ref1, "f16", "config 2b k1")
+    assert torch.equal(out1, out1_nomap)
+
+
+def test_config3a_shell_bf16_full():
+    coords = coords_of("3a")
+    f, w, b = cfg_tensors("3a", 0)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        out = forward(m, f, w, b)
+    check(out, oracle.conv3_rulebook(oracle_nbr("3a"), as64(f), as64(w), as64(b)), "bf16", "config 3a")
+    # spot-check the sampled-row path against the dictionary oracle as well
+    rows = sample_rows(len(coords), count=256)
+    check(out[rows], oracle.conv3(coords, as64(f), as64(w), as64(b), rows=rows), "bf16", "config 3a (dict rows)")
+
+
+def test_config3b_dense_bf16_sampled():
+    coords = coords_of("3b")
+    f, w, b = cfg_tensors("3b", 0)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        out = forward(m, f, w, b)
+    rows = sample_rows(len(coords))
+    check(out[rows], oracle.conv3_rulebook(oracle_nbr("3b"), as64(f), as64(w), as64(b), rows=rows), "bf16", "config 3b")
+
+
+def test_config4_four_layers_shared_map_sampled():
+    key = "4"
+    c = synth.config(key)
+    coords = coords_of(key)
+    f = synth.feats_for(c.number, 0, len(coords), c.cin, c.dtype)
+    rows = sample_rows(len(coords))
+    fd = f.to(DEV)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        for layer in range(c.layers):
+            w = synth.weight_for(c.number, layer, 3, c.cin, c.cout, c.dtype)
+            b = synth.bias_for(c.number, layer, c.cout, c.dtype)
+            out = sc.subm_conv3d_forward(m, fd, w.to(DEV), b.to(DEV))
+            torch.cuda.synchronize()
+            ref = oracle.conv3_rulebook(oracle_nbr(key), as64(f), as64(w), as64(b), rows=rows)
+            check(out.cpu()[rows], ref, c.dtype, f"config 4 layer {layer}")
+
+
+def test_config5_eight_chained_layers_sampled():
+    key = "5"
+    c = synth.config(key)
+    coords = coords_of(key)
+    x = synth.feats_for(c.number, 0, len(coords), c.cin, c.dtype).to(DEV)
+    rows = sample_rows(len(coords), count=2048)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        for layer in range(c.layers):
+            w = synth.weight_for(c.number, layer, 3, c.cin, c.cout, c.dtype)
+            b = synth.bias_for(c.number, layer, c.cout, c.dtype)
+            y = sc.subm_conv3d_forward(m, x, w.to(DEV), b.to(DEV))
+            torch.cuda.synchronize()
+            # The oracle consumes the GPU's stored input of this layer (same rounded values).
+            ref = oracle.conv3_rulebook(oracle_nbr(key), as64(x), as64(w), as64(b), rows=rows)
+            check(y.cpu()[rows], ref, c.dtype, f"config 5 layer {layer}")
+            x = y
+
+
+# ----------------------------------------------------------------- edge cases
+
+def small_case(dtype, cin, cout, key="1", seed=0, ksize=3):
+    coords = coords_of(key)
+    rng = np.random.default_rng(seed)
+    n = len(coords)
+    f = synth.round_to(rng.standard_normal((n, cin)), dtype)
+    w = synth.round_to(rng.standard_normal((cout, ksize, ksize, ksize, cin)) / np.sqrt(ksize ** 3 * cin), dtype)
+    b = synth.round_to(rng.standard_normal(cout) * 0.3, dtype)
+    return coords, f, w, b
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("cin,cout", [(3, 5), (16, 1), (8, 17), (24, 33), (64, 65), (32, 129), (200, 160), (136, 40)])
+def test_channel_shapes_and_tails(dtype, cin, cout):
+    coords, f, w, b = small_case(dtype, cin, cout)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        out = forward(m, f, w, b)
+    check(out, oracle.conv3(coords, as64(f), as64(w), as64(b)), dtype, f"{dtype} {cin}->{cout}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("cin,cout", [(3, 5), (64, 64), (128, 128), (40, 200)])
+def test_k1_matches_linear(dtype, cin, cout):
+    coords, f, w, b = small_case(dtype, cin, cout, key="2a", ksize=1)
+    out = forward(None, f, w, b)
+    check(out, oracle.conv1(as64(f), as64(w), as64(b)), dtype, f"k1 {dtype} {cin}->{cout}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_misaligned_pointers_take_the_elementwise_path(dtype):
+    coords, f, w, b = small_case(dtype, 16, 16)
+    n = len(coords)
+    big = torch.empty(n * 16 + 1, dtype=TDT[dtype], device=DEV)
+    fd = big[1:].view(n, 16)
+    fd.copy_(f.to(DEV))
+    obig = torch.empty(n * 16 + 1, dtype=TDT[dtype], device=DEV)
+    od = obig[1:].view(n, 16)
+    assert fd.data_ptr() % 16 != 0 and od.data_ptr() % 16 != 0
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        sc.subm_conv3d_forward(m, fd, w.to(DEV), b.to(DEV), out=od)
+        aligned = sc.subm_conv3d_forward(m, f.to(DEV), w.to(DEV), b.to(DEV))
+    torch.cuda.synchronize()
+    check(od.cpu(), oracle.conv3(coords, as64(f), as64(w), as64(b)), dtype, "misaligned")
+    assert torch.equal(od.cpu(), aligned.cpu())
+
+
+def test_no_bias():
+    coords, f, w, _ = small_case("bf16", 32, 32)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        out = forward(m, f, w, None)
+    check(out, oracle.conv3(coords, as64(f), as64(w), None), "bf16", "no bias")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_identity_kernel_is_bit_exact(dtype):
+    coords, f, _, _ = small_case(dtype, 64, 64, key="2a")
+    w = torch.zeros((64, 3, 3, 3, 64), dtype=TDT[dtype])
+    w[:, 1, 1, 1, :] = torch.eye(64, dtype=TDT[dtype])
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        out = forward(m, f, w, None)
+    assert torch.equal(out, f)
+
+
+def test_deterministic_bitwise():
+    coords, f, w, b = small_case("bf16", 128, 128, key="2a")
+    cd = torch.from_numpy(coords).to(DEV)
+    with sc.sparse_indice_map_build(cd) as m1, sc.sparse_indice_map_build(cd) as m2:
+        assert np.array_equal(gpu_nbr(m1), gpu_nbr(m2))
+        a = forward(m1, f, w, b)
+        bb = forward(m2, f, w, b)
+    assert torch.equal(a, bb)
+
+
+def test_empty_input():
+    c = torch.zeros((0, 4), dtype=torch.int32, device=DEV)
+    with sc.sparse_indice_map_build(c) as m:
+        assert (m.n, m.pairs) == (0, 0)
+        assert sc.sparse_indice_map_copy_nbr(m).shape == (0, 27)
+        f = torch.zeros((0, 8), dtype=torch.bfloat16, device=DEV)
+        w = torch.zeros((4, 3, 3, 3, 8), dtype=torch.bfloat16, device=DEV)
+        out = sc.subm_conv3d_forward(m, f, w)
+        assert out.shape == (0, 4)
+
+
+def test_single_voxel_sees_only_centre():
+    coords = np.array([[3, -7, 100, 2]], dtype=np.int32)
+    rng = np.random.default_rng(4)
+    f = torch.from_numpy(rng.standard_normal((1, 5)).astype(np.float32))
+    w = torch.from_numpy(rng.standard_normal((6, 3, 3, 3, 5)).astype(np.float32))
+    b = torch.from_numpy(rng.standard_normal(6).astype(np.float32))
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        assert gpu_nbr(m).tolist() == [[-1] * 13 + [0] + [-1] * 13]
+        out = forward(m, f, w, b)
+    check(out, oracle.conv3(coords, as64(f), as64(w), as64(b)), "f32", "single voxel")
+
+
+def test_shuffled_rows_and_batch_isolation():
+    base = coords_of("2a")
+    rng = np.random.default_rng(8)
+    two = np.concatenate([base, base * np.array([0, 1, 1, 1], np.int32) + np.array([1, 0, 0, 0], np.int32)])
+    perm = rng.permutation(len(two))
+    coords = two[perm]
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        assert np.array_equal(gpu_nbr(m), oracle.rulebook_sorted(coords))
+        f = synth.round_to(rng.standard_normal((len(coords), 16)), "f32")
+        w = synth.round_to(rng.standard_normal((8, 3, 3, 3, 16)) * 0.05, "f32")
+        out = forward(m, f, w, None)
+    check(out, oracle.conv3_rulebook(oracle.rulebook_sorted(coords), as64(f), as64(w)), "f32", "shuffled 2-batch")
+
+
+def test_translation_to_large_and_negative_coordinates():
+    base = coords_of("1")
+    for shift in ([0, -2 ** 31, 5, -7], [0, 2 ** 31 - 20, -2 ** 31, 2 ** 31 - 18], [65533, 0, 0, 0]):
+        moved = (base.astype(np.int64) + np.array(shift, np.int64)).astype(np.int32)
+        with sc.sparse_indice_map_build(torch.from_numpy(moved).to(DEV)) as m:
+            assert np.array_equal(gpu_nbr(m), oracle_nbr("1")), shift
+
+
+def test_extent_limits():
+    ok = np.array([[0, 0, 0, 0], [0, 0, 0, 1], [0, 65534, 0, 0], [0, 65533, 0, 0]], dtype=np.int32)
+    with sc.sparse_indice_map_build(torch.from_numpy(ok).to(DEV)) as m:
+        assert np.array_equal(gpu_nbr(m), oracle.rulebook(ok))
+    for bad in ([[0, 0, 0, 0], [0, 65535, 0, 0]], [[0, 0, -40000, 0], [0, 0, 30000, 0]],
+                [[-1, 0, 0, 0]], [[65535, 0, 0, 0]]):
+        with pytest.raises(sc.SubmError) as e:
+            sc.sparse_indice_map_build(torch.tensor(bad, dtype=torch.int32, device=DEV))
+        assert e.value.name == "SUBM_ERR_COORD_RANGE"
+
+
+def test_duplicates_rejected():
+    coords = np.concatenate([coords_of("1"), coords_of("1")[17:18]])
+    with pytest.raises(sc.SubmError) as e:
+        sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV))
+    assert e.value.name == "SUBM_ERR_DUPLICATE_COORD"
+
+
+def test_shape_mismatch_and_alias_rejected():
+    coords, f, w, b = small_case("bf16", 16, 16)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        fd = f.to(DEV)
+        with pytest.raises(sc.SubmError) as e:
+            sc.subm_conv3d_forward(m, fd[:-1].contiguous(), w.to(DEV), b.to(DEV))
+        assert e.value.name == "SUBM_ERR_SHAPE_MISMATCH"
+        w1 = torch.zeros((16, 1, 1, 1, 16), dtype=torch.bfloat16, device=DEV)
+        with pytest.raises(sc.SubmError) as e:
+            sc.subm_conv3d_forward(None, fd, w1, out=fd)
+        assert e.value.name == "SUBM_ERR_INVALID_ARG"
