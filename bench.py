@@ -45,7 +45,21 @@ def parse():
     p.add_argument("--conv-reps", type=int, default=200, help="back-to-back launches timed for the roofline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target duration of the oracle sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run 5 plain device copies of MIB MiB (reference for hardware byte counters)")
     return p.parse_args()
+
+
+def copy_calibration(mib):
+    """Five plain device-to-device copies of a known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_copy": n * 4, "copies": 5}), flush=True)
 
 
 def layer_plan(key):
@@ -88,12 +102,17 @@ def cpu_baseline(key, coords, feats, weight, bias, nbr_pairs_per_row, cin, cout,
     n = coords.shape[0]
     rng = np.random.default_rng(12345)
     with threadpool_limits(limits=1):
-        # calibration call on a small sample, then one timed call sized to the budget
-        probe = rng.choice(n, size=min(n, 256), replace=False)
-        t0 = time.perf_counter()
-        oracle.conv3(coords, f64, w64, b64, rows=probe)
-        t_probe = time.perf_counter() - t0
-        rows_target = int(min(n, max(256, 256 * budget_s / max(t_probe, 1e-3))))
+        # Two calibration calls fit cost = fixed (dictionary build) + per_row * rows; then one
+        # timed call sized to the budget.
+        def run(k):
+            sel = rng.choice(n, size=min(n, k), replace=False)
+            t0 = time.perf_counter()
+            oracle.conv3(coords, f64, w64, b64, rows=sel)
+            return time.perf_counter() - t0
+        t_a, t_b = run(64), run(512)
+        per_row = max((t_b - t_a) / (512 - 64), 1e-7)
+        fixed = max(t_a - 64 * per_row, 0.0)
+        rows_target = int(min(n, max(256, (budget_s - fixed) / per_row)))
         rows = rng.choice(n, size=rows_target, replace=False)
         t0 = time.perf_counter()
         oracle.conv3(coords, f64, w64, b64, rows=rows)
@@ -113,6 +132,9 @@ def cpu_baseline(key, coords, feats, weight, bias, nbr_pairs_per_row, cin, cout,
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the submanifold convolution path here is a single-GPU "
               "build (see the sharding paragraph of the design notes); run with --gpus 1.", file=sys.stderr)
@@ -220,7 +242,8 @@ def main():
         achieved = bytes_launch / conv_s / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic}
-    roofline.update({"kernel": "subm_conv_kernel", "avg_launch_ms": conv_ms, "launches": len(per_layer[dom]),
+    kernel = "subm_conv_dma_kernel" if cfg.dtype in ("bf16", "f16") and cout > 16 else "subm_conv_generic_kernel"
+    roofline.update({"kernel": kernel, "avg_launch_ms": conv_ms, "launches": len(per_layer[dom]),
                      "algorithmic_flop_per_launch": flop_launch, "algorithmic_bytes_per_launch": bytes_launch})
 
     value = flops_per_step / step_s / 1e12

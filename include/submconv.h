@@ -64,15 +64,22 @@ typedef enum {
   SUBM_ERR_HIP = 7               /* any other HIP runtime error (message in subm_last_error) */
 } subm_status_t;
 
+/* Which structure a map build uses to find neighbours (see sparse_indice_map_build_ex). */
+typedef enum {
+  SUBM_MAP_AUTO = 0,  /* dense grid when the bounding box is small enough, else hash table */
+  SUBM_MAP_HASH = 1,  /* always the hash table */
+  SUBM_MAP_GRID = 2   /* dense grid when it fits the grid budget (16 cells per voxel), else hash */
+} subm_map_mode_t;
+
 #define SUBM_TAPS 27
 #define SUBM_MAX_BATCH 65535       /* b must lie in [0, SUBM_MAX_BATCH) */
 #define SUBM_MAX_EXTENT 65534      /* max - min of each of z, y, x must not exceed this */
 
 /*
  * sparse_indice_map_build -- build the indice map (rulebook) of one coordinate set.
- *   coords   device int32 [n, 4], rows (b, z, y, x).  Borrowed for the duration of the call
- *            (stream-ordered); the map keeps no reference to it.  Any row order; rows must be
- *            distinct.
+ *   coords   device int32 [n, 4], rows (b, z, y, x), 16-byte aligned.  Borrowed for the
+ *            duration of the call (stream-ordered); the map keeps no reference to it.  Any row
+ *            order; rows must be distinct.
  *   n        number of rows, 0 <= n <= 2^31 - 1.  n == 0 yields a valid empty map, no launch.
  *   stream   stream on which the build runs.
  *   out_map  host pointer; receives the new handle.  Set to NULL first, left NULL on error.
@@ -86,6 +93,20 @@ typedef enum {
  */
 int sparse_indice_map_build(const int32_t* coords, int64_t n, hipStream_t stream,
                             submconv_map_t* out_map);
+
+/*
+ * sparse_indice_map_build_ex -- sparse_indice_map_build with an explicit structure request
+ * (a subm_map_mode_t).  Both structures give the identical rulebook; the choice only changes
+ * speed and memory.  An unknown mode returns SUBM_ERR_INVALID_ARG.
+ */
+int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int mode, hipStream_t stream,
+                               submconv_map_t* out_map);
+
+/*
+ * sparse_indice_map_mode -- the structure a built map used: SUBM_MAP_HASH or SUBM_MAP_GRID
+ * (SUBM_MAP_HASH for an empty map).  *mode is a host int.
+ */
+int sparse_indice_map_mode(submconv_map_t map, int* mode);
 
 /*
  * sparse_indice_map_free -- release a map.  NULL is accepted (returns SUBM_OK).  No work that

@@ -10,11 +10,16 @@ from ._binding import (  # noqa: F401
     SUBM_BF16,
     SUBM_F16,
     SUBM_F32,
+    SUBM_MAP_AUTO,
+    SUBM_MAP_GRID,
+    SUBM_MAP_HASH,
     TAPS,
     IndiceMap,
     SubmError,
     load_library,
     sparse_indice_map_build,
+    sparse_indice_map_build_ex,
+    sparse_indice_map_mode,
     sparse_indice_map_copy_nbr,
     sparse_indice_map_free,
     sparse_indice_map_info,

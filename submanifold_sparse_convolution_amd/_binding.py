@@ -16,12 +16,15 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsubmconv.so")
 
 SUBM_F32, SUBM_F16, SUBM_BF16 = 0, 1, 2
+SUBM_MAP_AUTO, SUBM_MAP_HASH, SUBM_MAP_GRID = 0, 1, 2
 _DTYPE_CODES = {torch.float32: SUBM_F32, torch.float16: SUBM_F16, torch.bfloat16: SUBM_BF16}
 TAPS = 27
 
 # Exported C symbols (kept equal to the declarations in include/submconv.h).
 C_FUNCTIONS = (
     "sparse_indice_map_build",
+    "sparse_indice_map_build_ex",
+    "sparse_indice_map_mode",
     "sparse_indice_map_free",
     "sparse_indice_map_info",
     "sparse_indice_map_offset_counts",
@@ -59,12 +62,14 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib = ctypes.CDLL(p)
         vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.sparse_indice_map_build.argtypes = [vp, i64, vp, ctypes.POINTER(vp)]
+        lib.sparse_indice_map_build_ex.argtypes = [vp, i64, ci, vp, ctypes.POINTER(vp)]
+        lib.sparse_indice_map_mode.argtypes = [vp, ctypes.POINTER(ci)]
         lib.sparse_indice_map_free.argtypes = [vp]
         lib.sparse_indice_map_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
         lib.sparse_indice_map_offset_counts.argtypes = [vp, ctypes.POINTER(i64)]
         lib.sparse_indice_map_copy_nbr.argtypes = [vp, vp, vp]
         lib.subm_conv3d_forward.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp]
-        for name in C_FUNCTIONS[:6]:
+        for name in C_FUNCTIONS[:8]:
             getattr(lib, name).restype = ci
         lib.subm_status_string.argtypes = [ci]
         lib.subm_status_string.restype = ctypes.c_char_p
@@ -102,15 +107,23 @@ def _device_tensor(t: torch.Tensor, what: str) -> None:
 class IndiceMap:
     """Owner of one built indice map (submconv_map_t) for one coordinate set."""
 
-    def __init__(self, handle: int, device: torch.device):
+    def __init__(self, handle: int, device: torch.device, n: int):
         self._handle = handle
         self.device = device
-        n = ctypes.c_int64()
-        pairs = ctypes.c_int64()
-        lib = load_library()
-        _check(lib, "sparse_indice_map_info", lib.sparse_indice_map_info(handle, ctypes.byref(n), ctypes.byref(pairs)))
-        self.n = n.value
-        self.pairs = pairs.value
+        self.n = n
+        self._pairs = None
+
+    @property
+    def pairs(self) -> int:
+        """Total pair count (rulebook entries >= 0, centre included)."""
+        if self._pairs is None:
+            self._pairs = sparse_indice_map_info(self)[1]
+        return self._pairs
+
+    @property
+    def mode(self) -> int:
+        """SUBM_MAP_HASH or SUBM_MAP_GRID: the structure the build used."""
+        return sparse_indice_map_mode(self)
 
     @property
     def handle(self) -> int:
@@ -140,16 +153,28 @@ class IndiceMap:
 
 def sparse_indice_map_build(coords: torch.Tensor, stream=None) -> IndiceMap:
     """Build the indice map of int32 device coordinates [N, 4] = (b, z, y, x)."""
+    return sparse_indice_map_build_ex(coords, SUBM_MAP_AUTO, stream)
+
+
+def sparse_indice_map_build_ex(coords: torch.Tensor, mode: int, stream=None) -> IndiceMap:
+    """Build the indice map with an explicit structure request (SUBM_MAP_AUTO / _HASH / _GRID)."""
     _device_tensor(coords, "coords")
     if coords.dtype != torch.int32 or coords.dim() != 2 or coords.shape[1] != 4:
         raise ValueError("coords must be int32 [N, 4]")
     lib = load_library()
     out = ctypes.c_void_p()
     with torch.cuda.device(coords.device):
-        st = lib.sparse_indice_map_build(coords.data_ptr(), coords.shape[0], _stream_ptr(stream, coords.device),
-                                         ctypes.byref(out))
-    _check(lib, "sparse_indice_map_build", st)
-    return IndiceMap(out.value, coords.device)
+        st = lib.sparse_indice_map_build_ex(coords.data_ptr(), coords.shape[0], int(mode),
+                                            _stream_ptr(stream, coords.device), ctypes.byref(out))
+    _check(lib, "sparse_indice_map_build_ex", st)
+    return IndiceMap(out.value, coords.device, coords.shape[0])
+
+
+def sparse_indice_map_mode(m: IndiceMap) -> int:
+    lib = load_library()
+    mode = ctypes.c_int()
+    _check(lib, "sparse_indice_map_mode", lib.sparse_indice_map_mode(m.handle, ctypes.byref(mode)))
+    return mode.value
 
 
 def sparse_indice_map_free(m: IndiceMap) -> None:

@@ -1,23 +1,35 @@
 // Indice map (rulebook) build for submanifold 3x3x3 convolution on gfx950.
 //
 // The pages build the map from sorted coordinate keys with 27 lookups per voxel, once per
-// coordinate set (lato.2_mrp_mlx README, header summary).  Here the key set goes into an
-// open-addressing hash table in HBM instead of a sorted array: one insert per voxel and one
-// probe sequence per (voxel, tap), so no radix passes and no binary searches.  The result,
-// nbr[i, k] = input row of the voxel at coord_i + offset(k) or -1, is unique and therefore
-// identical to what any sorted-key construction gives.
+// coordinate set (lato.2_mrp_mlx README, header summary).  Here the coordinate set goes into
+// one of two direct-addressed structures in HBM instead of a sorted array, so there are no
+// radix passes and no binary searches; the result, nbr[i, k] = input row of the voxel at
+// coord_i + offset(k) or -1, is unique and therefore identical to any sorted-key construction.
 //
-// Key packing: (b, z mod 2^16, y mod 2^16, x mod 2^16) in 16-bit fields, b most significant.
-// Reducing z, y, x modulo 2^16 is injective on every coordinate and every +-1 neighbour of it
-// as long as each axis' extent (max - min) is at most 65534; the build checks that extent and
-// the batch range [0, 65534] and reports SUBM_ERR_COORD_RANGE otherwise.  The all-ones key
-// cannot occur (b <= 65534) and marks an empty slot.
+//   GRID  a dense int32 volume over the bounding box of the set with a one-cell margin on each
+//         spatial side (cell = row or -1).  Used when the box has at most kGridCellsPerVoxel
+//         cells per voxel (thin shells in small grids, dense grids).  A neighbour is one load at
+//         a fixed offset from the voxel's own cell; the margin keeps every +-1 step in bounds
+//         and inside the voxel's own batch slab.
+//   HASH  an open-addressing table (linear probing, 16-byte slots, load factor <= 1/2) keyed by
+//         (b, z mod 2^16, y mod 2^16, x mod 2^16).  Used for sparse sets in large boxes.  The
+//         modular reduction is injective on every coordinate and +-1 neighbour as long as each
+//         axis' extent (max - min) is at most 65534, which the build enforces.
+//
+// The structure is chosen on the device from the set's bounds, so the whole build needs one
+// host synchronisation (to read the error flags and counts at the end).
 //
 // Kernels, all on the caller's stream:
-//   map_clear_kernel    empty every slot; reset the statistics block
-//   map_insert_kernel   CAS each key into the table (duplicate -> flag); per-column min/max
-//   map_lookup_kernel   one thread per (voxel, tap): probe, write nbr coalesced, count hits
-//   map_reduce_kernel   sum the per-block hit counts into per-tap and total pair counts
+//   map_bounds_kernel   per-block min/max of (b, z, y, x) and the batch-range flag -> partials
+//   map_clear_kernel    every block reduces the partials (same result everywhere), picks the
+//                       structure; block 0 publishes the plan and zeroes the counters; all
+//                       blocks clear the chosen structure
+//   map_insert_kernel   GRID: CAS the row into its cell; HASH: CAS the key into the table.
+//                       A cell or key already taken by another row raises the duplicate flag.
+//   map_lookup_kernel   one thread per voxel: 27 loads (GRID) or 27 probe sequences (HASH), nine
+//                       in flight at a time; the block's rows are staged in LDS and written as
+//                       one contiguous run of nbr; per-row 27-bit hit mask; hits counted per tap
+//                       with wave ballots and added to one of 16 counter banks
 #include "internal.h"
 
 namespace submconv {
@@ -25,7 +37,8 @@ namespace {
 
 constexpr unsigned long long kEmptyKey = ~0ull;
 constexpr int kThreads = 256;
-constexpr int kMaxBlocks = 2048;
+constexpr int kMaxBoundsBlocks = 256;
+constexpr int kMaxClearBlocks = 1024;
 
 struct __align__(16) Slot {
   unsigned long long key;
@@ -33,6 +46,13 @@ struct __align__(16) Slot {
   int32_t pad;
 };
 static_assert(sizeof(Slot) == 16, "slot must be 16 bytes");
+
+struct BoundsPartial {
+  int32_t mn[4];
+  int32_t mx[4];
+  uint32_t flags;
+  uint32_t pad[3];
+};
 
 __device__ __forceinline__ unsigned long long pack_key(int32_t b, int32_t z, int32_t y, int32_t x) {
   return ((unsigned long long)(uint32_t)b << 48) | ((unsigned long long)((uint32_t)z & 0xFFFFu) << 32) |
@@ -54,26 +74,6 @@ __device__ __forceinline__ unsigned long long home_slot(unsigned long long key, 
   return __umul64hi(mix64(key), slots);
 }
 
-__global__ __launch_bounds__(kThreads) void map_clear_kernel(Slot* __restrict__ table, int64_t slots,
-                                                             BuildStats* __restrict__ st) {
-  if (blockIdx.x == 0) {
-    const int t = threadIdx.x;
-    if (t < 4) {
-      st->mn[t] = INT32_MAX;
-      st->mx[t] = INT32_MIN;
-    }
-    if (t == 0) {
-      st->flags = 0;
-      st->pad = 0;
-      st->pairs = 0;
-    }
-    if (t < 27) st->per_tap[t] = 0;
-  }
-  const Slot empty = {kEmptyKey, -1, 0};
-  for (int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x; s < slots; s += (int64_t)gridDim.x * kThreads)
-    table[s] = empty;
-}
-
 __device__ __forceinline__ int wave_min(int v) {
   for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
   return v;
@@ -82,49 +82,28 @@ __device__ __forceinline__ int wave_max(int v) {
   for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
   return v;
 }
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  for (int off = 32; off > 0; off >>= 1) v |= __shfl_xor(v, off, 64);
+  return v;
+}
 
-__global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __restrict__ coords, int64_t n,
-                                                              Slot* __restrict__ table, int64_t slots,
-                                                              BuildStats* __restrict__ st) {
+// ------------------------------------------------------------------ bounds
+__global__ __launch_bounds__(kThreads) void map_bounds_kernel(const int32_t* __restrict__ coords, int64_t n,
+                                                              BoundsPartial* __restrict__ partials) {
   int mn[4] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX};
   int mx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
   uint32_t flags = 0;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
-    const int32_t* c = coords + 4 * i;
-    const int32_t b = c[0], z = c[1], y = c[2], x = c[3];
-    mn[0] = min(mn[0], b); mx[0] = max(mx[0], b);
-    mn[1] = min(mn[1], z); mx[1] = max(mx[1], z);
-    mn[2] = min(mn[2], y); mx[2] = max(mx[2], y);
-    mn[3] = min(mn[3], x); mx[3] = max(mx[3], x);
-    if (b < 0 || b >= SUBM_MAX_BATCH) {
-      flags |= kFlagBatchRange;
-      continue;
-    }
-    const unsigned long long key = pack_key(b, z, y, x);
-    unsigned long long s = home_slot(key, (unsigned long long)slots);
-    bool placed = false;
-    for (int64_t probe = 0; probe < slots; ++probe) {
-      const unsigned long long prev = atomicCAS(&table[s].key, kEmptyKey, key);
-      if (prev == kEmptyKey) {
-        table[s].val = (int32_t)i;
-        placed = true;
-        break;
-      }
-      if (prev == key) {
-        flags |= kFlagDuplicate;
-        placed = true;
-        break;
-      }
-      s = (s + 1 == (unsigned long long)slots) ? 0 : s + 1;
-    }
-    if (!placed) flags |= kFlagProbeOverflow;
+    const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
+    mn[0] = min(mn[0], c.x); mx[0] = max(mx[0], c.x);
+    mn[1] = min(mn[1], c.y); mx[1] = max(mx[1], c.y);
+    mn[2] = min(mn[2], c.z); mx[2] = max(mx[2], c.z);
+    mn[3] = min(mn[3], c.w); mx[3] = max(mx[3], c.w);
+    if (c.x < 0 || c.x >= SUBM_MAX_BATCH) flags |= kFlagBatchRange;
   }
-  // Block reduction of min / max / flags, then one atomic per quantity per block.
   __shared__ int smn[kThreads / 64][4];
   __shared__ int smx[kThreads / 64][4];
-  __shared__ uint32_t sfl;
-  if (threadIdx.x == 0) sfl = 0;
-  __syncthreads();
+  __shared__ uint32_t sfl[kThreads / 64];
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -135,7 +114,8 @@ __global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __r
       smx[wave][a] = hi;
     }
   }
-  if (flags) atomicOr(&sfl, flags);
+  flags = wave_or(flags);
+  if (lane == 0) sfl[wave] = flags;
   __syncthreads();
   if (threadIdx.x < 4) {
     const int a = threadIdx.x;
@@ -144,95 +124,283 @@ __global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __r
       lo = min(lo, smn[w][a]);
       hi = max(hi, smx[w][a]);
     }
-    if (lo != INT32_MAX) atomicMin(&st->mn[a], lo);
-    if (hi != INT32_MIN) atomicMax(&st->mx[a], hi);
+    partials[blockIdx.x].mn[a] = lo;
+    partials[blockIdx.x].mx[a] = hi;
   }
-  if (threadIdx.x == 0 && sfl) atomicOr(&st->flags, sfl);
+  if (threadIdx.x == 0) {
+    uint32_t f = 0;
+    for (int w = 0; w < kThreads / 64; ++w) f |= sfl[w];
+    partials[blockIdx.x].flags = f;
+  }
+}
+
+// ------------------------------------------------------------------ plan + clear
+__global__ __launch_bounds__(kThreads) void map_clear_kernel(const BoundsPartial* __restrict__ partials, int nparts,
+                                                             int64_t n, int64_t grid_budget_cells, int64_t slots,
+                                                             int mode_request, void* __restrict__ table,
+                                                             MapStats* __restrict__ st) {
+  // Every block reduces the (few) partials itself, so all blocks agree on the plan without
+  // another launch.
+  __shared__ int s_mn[4], s_mx[4];
+  __shared__ uint32_t s_fl;
+  const int t = threadIdx.x;
+  {
+    int mn[4] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX};
+    int mx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
+    uint32_t fl = 0;
+    for (int p = t; p < nparts; p += kThreads) {
+      const BoundsPartial q = partials[p];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        mn[a] = min(mn[a], q.mn[a]);
+        mx[a] = max(mx[a], q.mx[a]);
+      }
+      fl |= q.flags;
+    }
+    __shared__ int rmn[kThreads / 64][4], rmx[kThreads / 64][4];
+    __shared__ uint32_t rfl[kThreads / 64];
+    const int wave = t / 64, lane = t % 64;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int lo = wave_min(mn[a]);
+      const int hi = wave_max(mx[a]);
+      if (lane == 0) {
+        rmn[wave][a] = lo;
+        rmx[wave][a] = hi;
+      }
+    }
+    fl = wave_or(fl);
+    if (lane == 0) rfl[wave] = fl;
+    __syncthreads();
+    if (t < 4) {
+      int lo = rmn[0][t], hi = rmx[0][t];
+      for (int w = 1; w < kThreads / 64; ++w) {
+        lo = min(lo, rmn[w][t]);
+        hi = max(hi, rmx[w][t]);
+      }
+      s_mn[t] = lo;
+      s_mx[t] = hi;
+    }
+    if (t == 0) {
+      uint32_t f = 0;
+      for (int w = 0; w < kThreads / 64; ++w) f |= rfl[w];
+      s_fl = f;
+    }
+    __syncthreads();
+  }
+  // Plan (identical in every block).
+  uint32_t flags = s_fl;
+  const int64_t ext_b = (int64_t)s_mx[0] - s_mn[0] + 1;
+  const int64_t ext_z = (int64_t)s_mx[1] - s_mn[1];
+  const int64_t ext_y = (int64_t)s_mx[2] - s_mn[2];
+  const int64_t ext_x = (int64_t)s_mx[3] - s_mn[3];
+  if (ext_z > SUBM_MAX_EXTENT || ext_y > SUBM_MAX_EXTENT || ext_x > SUBM_MAX_EXTENT) flags |= kFlagExtentRange;
+  int mode = kModeHash;
+  int64_t cells = 0, sx = 1, sy = 0, sz = 0, sb = 0;
+  if ((flags & (kFlagBatchRange | kFlagExtentRange)) != 0) {
+    mode = kModeNone;
+  } else {
+    const int64_t gx = ext_x + 3, gy = ext_y + 3, gz = ext_z + 3;
+    sy = gx;
+    sz = gx * gy;
+    sb = sz * gz;
+    // ext_b <= 65535 and each g <= 65537, so compare in steps to avoid overflow.
+    const bool small = sb <= grid_budget_cells && ext_b <= grid_budget_cells / sb;
+    cells = small ? sb * ext_b : 0;
+    if (mode_request == SUBM_MAP_GRID && small) mode = kModeGrid;
+    else if (mode_request == SUBM_MAP_AUTO && small) mode = kModeGrid;
+    else mode = kModeHash;
+  }
+  if (blockIdx.x == 0) {
+    if (t < 4) {
+      st->mn[t] = s_mn[t];
+      st->mx[t] = s_mx[t];
+    }
+    if (t == 0) {
+      st->flags = flags;
+      st->mode = mode;
+      st->cells = cells;
+      st->slots = slots;
+      st->sy = sy;
+      st->sz = sz;
+      st->sb = sb;
+    }
+    for (int k = t; k < kTapBanks * 27; k += kThreads) (&st->tap_counts[0][0])[k] = 0;
+  }
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  if (mode == kModeGrid) {
+    int4* g4 = static_cast<int4*>(table);
+    const int64_t n4 = (cells + 3) / 4;
+    const int4 m1 = make_int4(-1, -1, -1, -1);
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + t; i < n4; i += stride) g4[i] = m1;
+  } else if (mode == kModeHash) {
+    Slot* tab = static_cast<Slot*>(table);
+    const Slot empty = {kEmptyKey, -1, 0};
+    for (int64_t s = (int64_t)blockIdx.x * kThreads + t; s < slots; s += stride) tab[s] = empty;
+  }
+}
+
+// ------------------------------------------------------------------ insert
+__device__ __forceinline__ int64_t grid_cell(const MapStats& p, int b, int z, int y, int x) {
+  return (int64_t)(b - p.mn[0]) * p.sb + (int64_t)(z - p.mn[1] + 1) * p.sz + (int64_t)(y - p.mn[2] + 1) * p.sy +
+         (int64_t)(x - p.mn[3] + 1);
+}
+
+__global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __restrict__ coords, int64_t n,
+                                                              void* __restrict__ table, MapStats* __restrict__ st) {
+  const int mode = st->mode;
+  if (mode == kModeNone) return;
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
+  bool dup = false, overflow = false;
+  if (mode == kModeGrid) {
+    int32_t* grid = static_cast<int32_t*>(table);
+    const int64_t cell = grid_cell(*st, c.x, c.y, c.z, c.w);
+    dup = atomicCAS(&grid[cell], -1, (int32_t)i) != -1;
+  } else {
+    Slot* tab = static_cast<Slot*>(table);
+    const unsigned long long slots = (unsigned long long)st->slots;
+    const unsigned long long key = pack_key(c.x, c.y, c.z, c.w);
+    unsigned long long s = home_slot(key, slots);
+    overflow = true;
+    for (unsigned long long probe = 0; probe < slots; ++probe) {
+      const unsigned long long prev = atomicCAS(&tab[s].key, kEmptyKey, key);
+      if (prev == kEmptyKey) {
+        tab[s].val = (int32_t)i;
+        overflow = false;
+        break;
+      }
+      if (prev == key) {
+        dup = true;
+        overflow = false;
+        break;
+      }
+      s = (s + 1 == slots) ? 0 : s + 1;
+    }
+  }
+  if (dup) atomicOr(&st->flags, kFlagDuplicate);
+  if (overflow) atomicOr(&st->flags, kFlagProbeOverflow);
+}
+
+// ------------------------------------------------------------------ lookup
+// One thread per voxel: the 27 neighbours are resolved one dz-plane (9 taps) at a time with
+// all 9 loads in flight, staged in LDS, and written back as one contiguous block of rows.
+__device__ __forceinline__ int32_t probe_rest(const Slot* __restrict__ tab, unsigned long long slots,
+                                              unsigned long long key, unsigned long long s) {
+  // Continue a probe sequence after its home slot held another key.
+  for (unsigned long long probe = 1; probe < slots; ++probe) {
+    s = (s + 1 == slots) ? 0 : s + 1;
+    const Slot e = tab[s];
+    if (e.key == key) return e.val;
+    if (e.key == kEmptyKey) return -1;
+  }
+  return -1;
 }
 
 __global__ __launch_bounds__(kThreads) void map_lookup_kernel(const int32_t* __restrict__ coords, int64_t n,
-                                                              const Slot* __restrict__ table, int64_t slots,
-                                                              int32_t* __restrict__ nbr,
-                                                              uint32_t* __restrict__ partials) {
-  __shared__ uint32_t hits[27];
-  if (threadIdx.x < 27) hits[threadIdx.x] = 0;
-  __syncthreads();
-  const int64_t total = n * 27;
-  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < total; t += (int64_t)gridDim.x * kThreads) {
-    const int64_t i = t / 27;
-    const int k = (int)(t - i * 27);
-    const int32_t* c = coords + 4 * i;
-    const int32_t b = c[0];
-    // Unsigned adds: wrap-around is harmless because only the low 16 bits enter the key.
-    const int32_t z = (int32_t)((uint32_t)c[1] + (uint32_t)(k / 9 - 1));
-    const int32_t y = (int32_t)((uint32_t)c[2] + (uint32_t)((k / 3) % 3 - 1));
-    const int32_t x = (int32_t)((uint32_t)c[3] + (uint32_t)(k % 3 - 1));
-    int32_t found = -1;
-    if (b >= 0 && b < SUBM_MAX_BATCH) {
-      const unsigned long long key = pack_key(b, z, y, x);
-      unsigned long long s = home_slot(key, (unsigned long long)slots);
-      for (int64_t probe = 0; probe < slots; ++probe) {
-        const Slot e = table[s];
-        if (e.key == key) {
-          found = e.val;
-          break;
+                                                              const void* __restrict__ table,
+                                                              int32_t* __restrict__ nbr, uint32_t* __restrict__ masks,
+                                                              MapStats* __restrict__ st) {
+  __shared__ int32_t s_out[kThreads * 27];
+  __shared__ uint32_t s_cnt[27];
+  const int mode = st->mode;
+  if (mode == kModeNone) return;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  if (t < 27) s_cnt[t] = 0;
+  const int64_t i0 = (int64_t)blockIdx.x * kThreads;
+  const int64_t i = i0 + t;
+  uint32_t mask = 0;
+  if (i < n) {
+    const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
+    if (mode == kModeGrid) {
+      const int32_t* grid = static_cast<const int32_t*>(table);
+      const int64_t sy = st->sy, sz = st->sz;
+      const int64_t base = grid_cell(*st, c.x, c.y, c.z, c.w);
+#pragma unroll
+      for (int k = 0; k < 27; ++k) {
+        const int dz = k / 9 - 1, dy = (k / 3) % 3 - 1, dx = k % 3 - 1;
+        const int32_t v = grid[base + dz * sz + dy * sy + dx];
+        s_out[t * 27 + k] = v;
+        mask |= (v >= 0 ? 1u : 0u) << k;
+      }
+    } else {
+      const Slot* tab = static_cast<const Slot*>(table);
+      const unsigned long long slots = (unsigned long long)st->slots;
+#pragma unroll
+      for (int plane = 0; plane < 3; ++plane) {
+        unsigned long long key[9], home[9];
+        Slot e[9];
+#pragma unroll
+        for (int q = 0; q < 9; ++q) {
+          const int dz = plane - 1, dy = q / 3 - 1, dx = q % 3 - 1;
+          // Unsigned adds: wrap-around is harmless because only the low 16 bits enter the key.
+          key[q] = pack_key(c.x, (int32_t)((uint32_t)c.y + (uint32_t)dz), (int32_t)((uint32_t)c.z + (uint32_t)dy),
+                            (int32_t)((uint32_t)c.w + (uint32_t)dx));
+          home[q] = home_slot(key[q], slots);
         }
-        if (e.key == kEmptyKey) break;
-        s = (s + 1 == (unsigned long long)slots) ? 0 : s + 1;
+#pragma unroll
+        for (int q = 0; q < 9; ++q) e[q] = tab[home[q]];
+#pragma unroll
+        for (int q = 0; q < 9; ++q) {
+          int32_t v;
+          if (e[q].key == key[q]) v = e[q].val;
+          else if (e[q].key == kEmptyKey) v = -1;
+          else v = probe_rest(tab, slots, key[q], home[q]);
+          const int k = plane * 9 + q;
+          s_out[t * 27 + k] = v;
+          mask |= (v >= 0 ? 1u : 0u) << k;
+        }
       }
     }
-    nbr[t] = found;
-    if (found >= 0) atomicAdd(&hits[k], 1u);
+    masks[i] = mask;
   }
   __syncthreads();
-  if (threadIdx.x < 27) partials[(int64_t)blockIdx.x * 27 + threadIdx.x] = hits[threadIdx.x];
+  const int64_t rows = (n - i0) < kThreads ? (n - i0) : kThreads;
+  const int total = (int)rows * 27;
+  int32_t* dst = nbr + i0 * 27;
+  for (int e = t; e < total; e += kThreads) dst[e] = s_out[e];
+  // Per-tap hit counts: one ballot per tap and wave, 27 LDS adds per wave, 27 global adds per block.
+#pragma unroll
+  for (int k = 0; k < 27; ++k) {
+    const unsigned long long b = __ballot((mask >> k) & 1u);
+    if (lane == 0 && b) atomicAdd(&s_cnt[k], (uint32_t)__popcll(b));
+  }
+  __syncthreads();
+  if (t < 27 && s_cnt[t] != 0) atomicAdd(&st->tap_counts[blockIdx.x % kTapBanks][t], s_cnt[t]);
 }
 
-__global__ __launch_bounds__(kThreads) void map_reduce_kernel(const uint32_t* __restrict__ partials, int blocks,
-                                                              BuildStats* __restrict__ st) {
-  // 9 threads per tap, each summing every 9th block; then an LDS reduction.
-  __shared__ unsigned long long part[27][9];
-  const int t = threadIdx.x;
-  if (t < 27 * 9) {
-    const int k = t % 27, r = t / 27;
-    unsigned long long acc = 0;
-    for (int b = r; b < blocks; b += 9) acc += partials[(int64_t)b * 27 + k];
-    part[k][r] = acc;
-  }
-  __syncthreads();
-  if (t < 27) {
-    unsigned long long acc = 0;
-    for (int r = 0; r < 9; ++r) acc += part[t][r];
-    st->per_tap[t] = acc;
-    part[t][0] = acc;
-  }
-  __syncthreads();
-  if (t == 0) {
-    unsigned long long total = 0;
-    for (int k = 0; k < 27; ++k) total += part[k][0];
-    st->pairs = total;
-  }
-}
-
-int blocks_for(int64_t items) {
-  const int64_t b = (items + kThreads - 1) / kThreads;
-  return (int)(b < 1 ? 1 : (b > kMaxBlocks ? kMaxBlocks : b));
-}
+int clamp_blocks(int64_t b, int64_t cap) { return (int)(b < 1 ? 1 : (b > cap ? cap : b)); }
 
 }  // namespace
 
-int64_t map_table_slots(int64_t n) { return n * 2 < 64 ? 64 : n * 2; }
+int64_t map_hash_slots(int64_t n) { return n * 2 < 64 ? 64 : n * 2; }
+int64_t map_grid_budget_cells(int64_t n) {
+  const int64_t c = n * kGridCellsPerVoxel;
+  return c < 4096 ? 4096 : c;
+}
+int map_bounds_blocks(int64_t n) { return clamp_blocks((n + 4 * kThreads - 1) / (4 * kThreads), kMaxBoundsBlocks); }
+size_t map_table_bytes(int64_t n) {
+  const size_t hash = (size_t)map_hash_slots(n) * sizeof(Slot);
+  const size_t grid = (size_t)map_grid_budget_cells(n) * sizeof(int32_t);
+  return hash > grid ? hash : grid;
+}
+size_t map_partials_bytes(int64_t n) { return (size_t)map_bounds_blocks(n) * sizeof(BoundsPartial); }
 
-int map_partial_blocks(int64_t n) { return blocks_for(n * 27); }
-
-hipError_t launch_map_build(const int32_t* coords, int64_t n, void* table, int64_t table_slots,
-                            uint32_t* partials, int partial_blocks, int32_t* nbr, BuildStats* stats,
-                            hipStream_t stream) {
-  Slot* tab = static_cast<Slot*>(table);
-  map_clear_kernel<<<blocks_for(table_slots), kThreads, 0, stream>>>(tab, table_slots, stats);
-  map_insert_kernel<<<blocks_for(n), kThreads, 0, stream>>>(coords, n, tab, table_slots, stats);
-  map_lookup_kernel<<<partial_blocks, kThreads, 0, stream>>>(coords, n, tab, table_slots, nbr, partials);
-  map_reduce_kernel<<<1, kThreads, 0, stream>>>(partials, partial_blocks, stats);
+hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, void* table, void* partials,
+                            int32_t* nbr, uint32_t* masks, MapStats* stats, hipStream_t stream) {
+  BoundsPartial* parts = static_cast<BoundsPartial*>(partials);
+  const int nb = map_bounds_blocks(n);
+  const int64_t slots = map_hash_slots(n);
+  const int64_t budget = map_grid_budget_cells(n);
+  const int64_t clear_items = budget / 4 > slots ? budget / 4 : slots;  // 16-byte stores
+  map_bounds_kernel<<<nb, kThreads, 0, stream>>>(coords, n, parts);
+  map_clear_kernel<<<clamp_blocks((clear_items + 4 * kThreads - 1) / (4 * kThreads), kMaxClearBlocks), kThreads, 0, stream>>>(
+      parts, nb, n, budget, slots, mode_request, table, stats);
+  map_insert_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, stream>>>(coords, n, table, stats);
+  map_lookup_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, stream>>>(coords, n, table, nbr,
+                                                                                       masks, stats);
   return hipGetLastError();
 }
 

@@ -20,53 +20,64 @@ struct Status {
 Status make_status(int code, std::string msg);
 Status hip_status(hipError_t e, const char* what);
 
-#define SUBM_HIP_TRY(expr)                                       \
-  do {                                                           \
-    hipError_t _e = (expr);                                      \
+#define SUBM_HIP_TRY(expr)                                          \
+  do {                                                              \
+    hipError_t _e = (expr);                                         \
     if (_e != hipSuccess) return ::submconv::hip_status(_e, #expr); \
   } while (0)
 
-// Stream-ordered device allocation from the per-device pool (see allocator in submconv_api.hip).
+// Stream-ordered device allocation from the per-device pool (submconv_api.hip).
 Status device_alloc(void** ptr, size_t bytes, hipStream_t stream);
 void device_free(void* ptr, hipStream_t stream);
 
-// Device-side statistics written by the map build.
-struct BuildStats {
-  int32_t mn[4];                     // per-column minimum of (b, z, y, x)
-  int32_t mx[4];                     // per-column maximum
-  uint32_t flags;                    // kFlag* bits
-  uint32_t pad;
-  unsigned long long pairs;          // total nbr entries >= 0
-  unsigned long long per_tap[27];    // entries >= 0 per tap
-};
+// Device-side plan and statistics of one map build (copied to the host at its end).
+constexpr int kTapBanks = 16;               // tap hit counters are spread over banks of 27
+constexpr int64_t kGridCellsPerVoxel = 16;  // dense grid allowed up to this many cells per voxel
+constexpr int kModeNone = -1;               // coordinates out of range: nothing built
+constexpr int kModeHash = 0;
+constexpr int kModeGrid = 1;
 
 constexpr uint32_t kFlagDuplicate = 1u;
 constexpr uint32_t kFlagBatchRange = 2u;
 constexpr uint32_t kFlagProbeOverflow = 4u;
+constexpr uint32_t kFlagExtentRange = 8u;
+
+struct MapStats {
+  int32_t mn[4];       // per-column minimum of (b, z, y, x)
+  int32_t mx[4];       // per-column maximum
+  uint32_t flags;      // kFlag* bits
+  int32_t mode;        // kMode*
+  int64_t cells;       // GRID: number of cells
+  int64_t slots;       // HASH: number of slots
+  int64_t sy, sz, sb;  // GRID strides of y, z and the batch slab (x stride is 1)
+  uint32_t tap_counts[kTapBanks][27];
+};
 
 // Map handle contents.
 struct MapData {
   int device = 0;
+  int mode = kModeHash;
   int64_t n = 0;
   int64_t pairs = 0;
   int64_t per_tap[27] = {};
-  int32_t* nbr = nullptr;   // device [n, 27], input row order
+  int32_t* nbr = nullptr;     // device [n, 27], input row order
+  uint32_t* masks = nullptr;  // device [n]: bit k set when nbr[i, k] >= 0 (same allocation as nbr)
 };
 
-// Launchers (indice_map.hip).  All enqueue on `stream`; none synchronises.
-// Builds nbr[n,27] and fills *stats (device).  `table_slots` is the hash capacity, `table`
-// a device buffer of table_slots 16-byte slots, `partials` a device buffer of
-// map_partial_count() * 27 uint32 for per-block pair counts.
-int64_t map_table_slots(int64_t n);
-int map_partial_blocks(int64_t n);
-hipError_t launch_map_build(const int32_t* coords, int64_t n, void* table, int64_t table_slots,
-                            uint32_t* partials, int partial_blocks, int32_t* nbr,
-                            BuildStats* stats, hipStream_t stream);
+// Map build (indice_map.hip).  Enqueues on `stream`; does not synchronise.  `table` holds
+// map_table_bytes(n), `partials` map_partials_bytes(n), `stats` one MapStats (all device).
+int64_t map_hash_slots(int64_t n);
+int64_t map_grid_budget_cells(int64_t n);
+int map_bounds_blocks(int64_t n);
+size_t map_table_bytes(int64_t n);
+size_t map_partials_bytes(int64_t n);
+hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, void* table, void* partials,
+                            int32_t* nbr, uint32_t* masks, MapStats* stats, hipStream_t stream);
 
 // Convolution launcher (conv.hip).  Arguments already validated by the caller.
-hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, int cout,
-                            int dtype, const void* feats, const void* weight, const void* bias,
-                            void* out, hipStream_t stream);
+hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, int cout, int dtype,
+                            const void* feats, const void* weight, const void* bias, void* out,
+                            hipStream_t stream);
 
 }  // namespace submconv
 

@@ -103,15 +103,34 @@ extern "C" const char* subm_status_string(int status) {
 
 extern "C" const char* subm_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int sparse_indice_map_build(const int32_t* coords, int64_t n, hipStream_t stream,
-                                       submconv_map_t* out_map) {
+namespace {
+
+// Per-thread pinned host buffer that receives the build statistics (one per device; a thread
+// runs one build at a time).  Pinned memory lets the device-to-host copy be a plain DMA.
+MapStats* pinned_stats(int dev) {
+  thread_local MapStats* bufs[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (bufs[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipHostMalloc(&p, sizeof(MapStats), hipHostMallocDefault) != hipSuccess) return nullptr;
+    bufs[dev] = static_cast<MapStats*>(p);
+  }
+  return bufs[dev];
+}
+
+}  // namespace
+
+extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int mode, hipStream_t stream,
+                                          submconv_map_t* out_map) {
   g_last_error.clear();
   if (out_map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "out_map is NULL");
   *out_map = nullptr;
+  if (mode != SUBM_MAP_AUTO && mode != SUBM_MAP_HASH && mode != SUBM_MAP_GRID)
+    return fail(SUBM_ERR_INVALID_ARG, "mode must be SUBM_MAP_AUTO, SUBM_MAP_HASH or SUBM_MAP_GRID");
   if (n < 0) return fail(SUBM_ERR_INVALID_ARG, "n is negative");
   if (n > INT32_MAX) return fail(SUBM_ERR_INVALID_ARG, "n exceeds 2^31 - 1 (rows are int32)");
   if (n > 0 && coords == nullptr) return fail(SUBM_ERR_INVALID_ARG, "coords is NULL");
-  if ((reinterpret_cast<uintptr_t>(coords) & 3u) != 0) return fail(SUBM_ERR_INVALID_ARG, "coords is not 4-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(coords) & 15u) != 0) return fail(SUBM_ERR_INVALID_ARG, "coords is not 16-byte aligned");
 
   submconv_map* m = new (std::nothrow) submconv_map;
   if (m == nullptr) return fail(SUBM_ERR_OUT_OF_MEMORY, "host allocation of the map handle failed");
@@ -120,21 +139,25 @@ extern "C" int sparse_indice_map_build(const int32_t* coords, int64_t n, hipStre
     return fail(SUBM_ERR_HIP, "hipGetDevice failed");
   }
   m->d.n = n;
+  m->d.mode = kModeHash;
   if (n == 0) {
     *out_map = m;
     return SUBM_OK;
   }
+  MapStats* host = pinned_stats(m->d.device);
+  if (host == nullptr) {
+    delete m;
+    return fail(SUBM_ERR_OUT_OF_MEMORY, "pinned host buffer for the build statistics");
+  }
 
-  const int64_t slots = map_table_slots(n);
-  const int pblocks = map_partial_blocks(n);
-  const size_t table_bytes = round_up((size_t)slots * 16, 256);
-  const size_t partial_bytes = round_up((size_t)pblocks * 27 * sizeof(uint32_t), 256);
-  const size_t tmp_bytes = table_bytes + partial_bytes + sizeof(BuildStats);
+  const size_t table_bytes = round_up(map_table_bytes(n), 256);
+  const size_t partial_bytes = round_up(map_partials_bytes(n), 256);
+  const size_t tmp_bytes = table_bytes + partial_bytes + sizeof(MapStats);
 
   void* tmp = nullptr;
   void* nbr = nullptr;
   Status s = device_alloc(&tmp, tmp_bytes, stream);
-  if (s.ok()) s = device_alloc(&nbr, (size_t)n * 27 * sizeof(int32_t), stream);
+  if (s.ok()) s = device_alloc(&nbr, (size_t)n * 28 * sizeof(int32_t), stream);  // nbr [n,27] + masks [n]
   if (!s.ok()) {
     device_free(tmp, stream);
     device_free(nbr, stream);
@@ -142,12 +165,13 @@ extern "C" int sparse_indice_map_build(const int32_t* coords, int64_t n, hipStre
     return fail(s);
   }
   unsigned char* base = static_cast<unsigned char*>(tmp);
-  uint32_t* partials = reinterpret_cast<uint32_t*>(base + table_bytes);
-  BuildStats* dstats = reinterpret_cast<BuildStats*>(base + table_bytes + partial_bytes);
+  void* partials = base + table_bytes;
+  MapStats* dstats = reinterpret_cast<MapStats*>(base + table_bytes + partial_bytes);
 
-  BuildStats st;
-  hipError_t e = launch_map_build(coords, n, base, slots, partials, pblocks, static_cast<int32_t*>(nbr), dstats, stream);
-  if (e == hipSuccess) e = hipMemcpyAsync(&st, dstats, sizeof(st), hipMemcpyDeviceToHost, stream);
+  int32_t* nbr_rows = static_cast<int32_t*>(nbr);
+  uint32_t* masks = reinterpret_cast<uint32_t*>(nbr_rows + (size_t)n * 27);
+  hipError_t e = launch_map_build(coords, n, mode, base, partials, nbr_rows, masks, dstats, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(host, dstats, sizeof(MapStats), hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   device_free(tmp, stream);
   if (e != hipSuccess) {
@@ -155,37 +179,52 @@ extern "C" int sparse_indice_map_build(const int32_t* coords, int64_t n, hipStre
     delete m;
     return fail(hip_status(e, "indice map build"));
   }
-
+  const MapStats& st = *host;
   int code = SUBM_OK;
-  std::string msg;
+  const char* msg = "";
   if (st.flags & kFlagBatchRange) {
     code = SUBM_ERR_COORD_RANGE;
     msg = "batch index outside [0, 65534]";
+  } else if (st.flags & kFlagExtentRange) {
+    code = SUBM_ERR_COORD_RANGE;
+    msg = "extent (max - min) of z, y or x exceeds 65534";
   } else if (st.flags & kFlagDuplicate) {
     code = SUBM_ERR_DUPLICATE_COORD;
     msg = "two rows share the same (b, z, y, x)";
   } else if (st.flags & kFlagProbeOverflow) {
     code = SUBM_ERR_HIP;
     msg = "internal error: hash table full";
-  } else {
-    static const char* axis[4] = {"b", "z", "y", "x"};
-    for (int a = 1; a < 4; ++a) {
-      if ((int64_t)st.mx[a] - (int64_t)st.mn[a] > SUBM_MAX_EXTENT) {
-        code = SUBM_ERR_COORD_RANGE;
-        msg = std::string("extent of ") + axis[a] + " (max - min) exceeds 65534";
-        break;
-      }
-    }
   }
   if (code != SUBM_OK) {
     device_free(nbr, stream);
     delete m;
-    return fail(code, msg.c_str());
+    return fail(code, msg);
   }
-  m->d.nbr = static_cast<int32_t*>(nbr);
-  m->d.pairs = (int64_t)st.pairs;
-  for (int k = 0; k < 27; ++k) m->d.per_tap[k] = (int64_t)st.per_tap[k];
+  m->d.nbr = nbr_rows;
+  m->d.masks = masks;
+  m->d.mode = st.mode;
+  int64_t total = 0;
+  for (int k = 0; k < 27; ++k) {
+    int64_t c = 0;
+    for (int b = 0; b < kTapBanks; ++b) c += st.tap_counts[b][k];
+    m->d.per_tap[k] = c;
+    total += c;
+  }
+  m->d.pairs = total;
   *out_map = m;
+  return SUBM_OK;
+}
+
+extern "C" int sparse_indice_map_build(const int32_t* coords, int64_t n, hipStream_t stream,
+                                       submconv_map_t* out_map) {
+  return sparse_indice_map_build_ex(coords, n, SUBM_MAP_AUTO, stream, out_map);
+}
+
+extern "C" int sparse_indice_map_mode(submconv_map_t map, int* mode) {
+  g_last_error.clear();
+  if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
+  if (mode == nullptr) return fail(SUBM_ERR_INVALID_ARG, "mode is NULL");
+  *mode = map->d.mode == kModeGrid ? SUBM_MAP_GRID : SUBM_MAP_HASH;
   return SUBM_OK;
 }
 

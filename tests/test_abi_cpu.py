@@ -53,7 +53,9 @@ def test_build_rejects_bad_arguments(lib):
     assert lib.sparse_indice_map_build(None, 5, None, ctypes.byref(out)) == INVALID
     assert b"coords" in lib.subm_last_error()
     assert lib.sparse_indice_map_build(ctypes.c_void_p(16), 2 ** 31, None, ctypes.byref(out)) == INVALID
-    assert lib.sparse_indice_map_build(ctypes.c_void_p(18), 5, None, ctypes.byref(out)) == INVALID  # misaligned
+    assert lib.sparse_indice_map_build(ctypes.c_void_p(24), 5, None, ctypes.byref(out)) == INVALID  # not 16-byte aligned
+    assert lib.sparse_indice_map_build_ex(ctypes.c_void_p(256), 5, 3, None, ctypes.byref(out)) == INVALID  # bad mode
+    assert b"mode" in lib.subm_last_error()
 
 
 def test_map_accessors_reject_null(lib):
@@ -62,6 +64,8 @@ def test_map_accessors_reject_null(lib):
     assert lib.sparse_indice_map_info(None, ctypes.byref(n), None) == INVALID
     assert lib.sparse_indice_map_offset_counts(None, (ctypes.c_int64 * 27)()) == INVALID
     assert lib.sparse_indice_map_copy_nbr(None, ctypes.c_void_p(256), None) == INVALID
+    mode = ctypes.c_int()
+    assert lib.sparse_indice_map_mode(None, ctypes.byref(mode)) == INVALID
 
 
 def fwd(lib, m=None, n=10, k=1, cin=4, cout=4, dtype=0, f=256, w=512, b=None, o=1024):

@@ -94,6 +94,23 @@ def test_rulebook_bit_exact(key):
     print(f"  config {key}: N={len(coords)} pairs={int((want >= 0).sum())}", flush=True)
 
 
+@pytest.mark.parametrize("key", ["1", "2a", "3a", "3b"])
+@pytest.mark.parametrize("mode", ["hash", "grid"])
+def test_rulebook_same_from_both_structures(key, mode):
+    req = {"hash": sc.SUBM_MAP_HASH, "grid": sc.SUBM_MAP_GRID}[mode]
+    with sc.sparse_indice_map_build_ex(torch.from_numpy(coords_of(key)).to(DEV), req) as m:
+        assert m.mode == req
+        assert np.array_equal(gpu_nbr(m), oracle_nbr(key))
+        assert sc.sparse_indice_map_offset_counts(m) == (oracle_nbr(key) >= 0).sum(axis=0).tolist()
+
+
+def test_automatic_structure_choice():
+    # Thin shells and dense boxes in small grids use the dense grid; sparse unions in large grids the hash.
+    for key, want in (("3a", sc.SUBM_MAP_GRID), ("3b", sc.SUBM_MAP_GRID), ("4", sc.SUBM_MAP_HASH), ("5", sc.SUBM_MAP_HASH)):
+        with sc.sparse_indice_map_build(torch.from_numpy(coords_of(key)).to(DEV)) as m:
+            assert m.mode == want, key
+
+
 # ----------------------------------------------------------------- convolution, all configs
 
 def cfg_tensors(key, layer, cin=None, cout=None):
@@ -269,25 +286,28 @@ def test_empty_input():
         assert out.shape == (0, 4)
 
 
-def test_single_voxel_sees_only_centre():
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_single_voxel_sees_only_centre(mode):
     coords = np.array([[3, -7, 100, 2]], dtype=np.int32)
     rng = np.random.default_rng(4)
     f = torch.from_numpy(rng.standard_normal((1, 5)).astype(np.float32))
     w = torch.from_numpy(rng.standard_normal((6, 3, 3, 3, 5)).astype(np.float32))
     b = torch.from_numpy(rng.standard_normal(6).astype(np.float32))
-    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+    with sc.sparse_indice_map_build_ex(torch.from_numpy(coords).to(DEV), mode) as m:
         assert gpu_nbr(m).tolist() == [[-1] * 13 + [0] + [-1] * 13]
         out = forward(m, f, w, b)
     check(out, oracle.conv3(coords, as64(f), as64(w), as64(b)), "f32", "single voxel")
 
 
-def test_shuffled_rows_and_batch_isolation():
+@pytest.mark.parametrize("mode", [1, 2])
+def test_shuffled_rows_and_batch_isolation(mode):
     base = coords_of("2a")
     rng = np.random.default_rng(8)
     two = np.concatenate([base, base * np.array([0, 1, 1, 1], np.int32) + np.array([1, 0, 0, 0], np.int32)])
     perm = rng.permutation(len(two))
     coords = two[perm]
-    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+    with sc.sparse_indice_map_build_ex(torch.from_numpy(coords).to(DEV), mode) as m:
+        assert m.mode == mode
         assert np.array_equal(gpu_nbr(m), oracle.rulebook_sorted(coords))
         f = synth.round_to(rng.standard_normal((len(coords), 16)), "f32")
         w = synth.round_to(rng.standard_normal((8, 3, 3, 3, 16)) * 0.05, "f32")
@@ -295,11 +315,13 @@ def test_shuffled_rows_and_batch_isolation():
     check(out, oracle.conv3_rulebook(oracle.rulebook_sorted(coords), as64(f), as64(w)), "f32", "shuffled 2-batch")
 
 
-def test_translation_to_large_and_negative_coordinates():
+@pytest.mark.parametrize("mode", [1, 2])
+def test_translation_to_large_and_negative_coordinates(mode):
     base = coords_of("1")
     for shift in ([0, -2 ** 31, 5, -7], [0, 2 ** 31 - 20, -2 ** 31, 2 ** 31 - 18], [65533, 0, 0, 0]):
         moved = (base.astype(np.int64) + np.array(shift, np.int64)).astype(np.int32)
-        with sc.sparse_indice_map_build(torch.from_numpy(moved).to(DEV)) as m:
+        with sc.sparse_indice_map_build_ex(torch.from_numpy(moved).to(DEV), mode) as m:
+            assert m.mode == mode
             assert np.array_equal(gpu_nbr(m), oracle_nbr("1")), shift
 
 
@@ -314,10 +336,11 @@ def test_extent_limits():
         assert e.value.name == "SUBM_ERR_COORD_RANGE"
 
 
-def test_duplicates_rejected():
+@pytest.mark.parametrize("mode", [1, 2])
+def test_duplicates_rejected(mode):
     coords = np.concatenate([coords_of("1"), coords_of("1")[17:18]])
     with pytest.raises(sc.SubmError) as e:
-        sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV))
+        sc.sparse_indice_map_build_ex(torch.from_numpy(coords).to(DEV), mode)
     assert e.value.name == "SUBM_ERR_DUPLICATE_COORD"
 
 
@@ -332,3 +355,30 @@ def test_shape_mismatch_and_alias_rejected():
         with pytest.raises(sc.SubmError) as e:
             sc.subm_conv3d_forward(None, fd, w1, out=fd)
         assert e.value.name == "SUBM_ERR_INVALID_ARG"
+
+
+# ----------------------------------------------------------------- fast-path tile heights
+
+@pytest.mark.parametrize("tile_m", ["64", "128", "192", "256"])
+@pytest.mark.parametrize("dtype,cin,cout", [("bf16", 128, 128), ("f16", 64, 64), ("bf16", 32, 32), ("bf16", 96, 48),
+                                            ("f16", 200, 136)])
+def test_tile_heights(monkeypatch, tile_m, dtype, cin, cout):
+    monkeypatch.setenv("SUBMCONV_TILE_M", tile_m)
+    coords, f, w, b = small_case(dtype, cin, cout, key="2a")
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        out = forward(m, f, w, b)
+    check(out, oracle.conv3_rulebook(oracle_nbr("2a"), as64(f), as64(w), as64(b)), dtype,
+          f"tile {tile_m} {dtype} {cin}->{cout}")
+    _, f1, w1, b1 = small_case(dtype, cin, cout, key="1", ksize=1)
+    out1 = forward(None, f1, w1, b1)
+    check(out1, oracle.conv1(as64(f1), as64(w1), as64(b1)), dtype, f"tile {tile_m} k1")
+
+
+@pytest.mark.parametrize("tile_m", ["64", "128", "192", "256"])
+def test_tile_heights_headline_shell(monkeypatch, tile_m):
+    monkeypatch.setenv("SUBMCONV_TILE_M", tile_m)
+    coords = coords_of("3a")
+    f, w, b = cfg_tensors("3a", 0)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        out = forward(m, f, w, b)
+    check(out, oracle.conv3_rulebook(oracle_nbr("3a"), as64(f), as64(w), as64(b)), "bf16", f"3a tile {tile_m}")
