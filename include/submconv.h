@@ -68,7 +68,8 @@ typedef enum {
 typedef enum {
   SUBM_MAP_AUTO = 0,  /* dense grid when the bounding box is small enough, else hash table */
   SUBM_MAP_HASH = 1,  /* always the hash table */
-  SUBM_MAP_GRID = 2   /* dense grid when it fits the grid budget (16 cells per voxel), else hash */
+  SUBM_MAP_GRID = 2   /* dense grid when it fits the grid budget (128 cells per voxel, at most
+                         2^29 cells), else hash */
 } subm_map_mode_t;
 
 #define SUBM_TAPS 27

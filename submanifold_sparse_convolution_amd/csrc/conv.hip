@@ -421,13 +421,14 @@ struct DmaShape {
   static constexpr int DMA = ADMA + BDMA;
   static constexpr int BUF = (BM + BN) * kRowSlice;
   static constexpr int NBR = TAPS == 27 ? BM * 27 * 4 : 0;
-  // Two workgroups per compute unit (two waves per SIMD, so one hides the other's LDS and
-  // barrier waits) when a two-stage ring fits twice in the 160 KB LDS; otherwise one workgroup
-  // with as many ring stages as fit (2 to 4).
+  // Two or four workgroups per compute unit (two or four waves per SIMD, so one hides another's
+  // LDS and barrier waits) when a two-stage ring fits that often in the 160 KB LDS; otherwise
+  // one workgroup with as many ring stages as fit (2 to 4).
   static constexpr int LDS2 = 2 * BUF + NBR + 256;
-  static constexpr int BPC = (BM <= 128 && 2 * LDS2 <= 160 * 1024) ? 2 : 1;
+  static constexpr int FIT2 = (160 * 1024) / LDS2;  // two-stage rings that fit in one CU's LDS
+  static constexpr int BPC = BM > 128 ? 1 : (FIT2 >= 4 ? 4 : (FIT2 >= 2 ? 2 : 1));
   static constexpr int NS_FIT = (160 * 1024 - NBR - 256) / BUF;
-  static constexpr int NS = BPC == 2 ? 2 : (NS_FIT >= 4 ? 4 : (NS_FIT < 2 ? 2 : NS_FIT));
+  static constexpr int NS = BPC > 1 ? 2 : (NS_FIT >= 4 ? 4 : (NS_FIT < 2 ? 2 : NS_FIT));
   static constexpr int LDS = NS * BUF + NBR + 256;
 };
 
@@ -687,17 +688,16 @@ hipError_t launch_dma(const ConvArgs& a0, hipStream_t stream) {
 
 // Estimated relative time of a launch with tile height bm and bpc workgroups per compute unit:
 // whole rounds of tiles over the 256 compute units, each round as long as bpc tiles of bm rows
-// sharing one unit, plus a fixed per-tile overhead (the weight slices are loaded once per tile)
-// worth kTileOverheadRows rows.  Two co-resident workgroups hide each other's waits, measured
-// at about a quarter of the time (kPairEfficiency).
+// sharing one unit, plus a fixed per-tile overhead (the weight slices, bn rows, are loaded once
+// per tile) worth 3/8 of bn rows.  Co-resident workgroups hide each other's waits; measured
+// factors: 0.75 of the time for two per unit, 0.6 for four.
 constexpr int kComputeUnits = 256;
-constexpr int kTileOverheadRows = 48;
-constexpr double kPairEfficiency = 0.75;
-inline double tile_cost(int64_t n, int col_tiles, int bm, int bpc) {
+inline double tile_cost(int64_t n, int col_tiles, int bm, int bn, int bpc) {
   const int64_t tiles = (n + bm - 1) / bm * col_tiles;
   const int64_t slots = (int64_t)kComputeUnits * bpc;
   const int64_t rounds = (tiles + slots - 1) / slots;
-  return (double)rounds * bpc * (bm + kTileOverheadRows) * (bpc == 2 ? kPairEfficiency : 1.0);
+  const double overlap = bpc >= 4 ? 0.6 : (bpc == 2 ? 0.75 : 1.0);
+  return (double)rounds * bpc * (bm + 3.0 * bn / 8.0) * overlap;
 }
 
 template <DT D, int BN, int TAPS>
@@ -708,10 +708,10 @@ hipError_t launch_dma_bn(const ConvArgs& a, hipStream_t stream) {
   const int bpcs[4] = {DmaShape<64, BN, TAPS>::BPC, DmaShape<128, BN, TAPS>::BPC, DmaShape<192, BN, TAPS>::BPC,
                        DmaShape<256, BN, TAPS>::BPC};
   int best = 3;
-  double best_cost = tile_cost(a.n, col_tiles, 256, bpcs[3]);
+  double best_cost = tile_cost(a.n, col_tiles, 256, BN, bpcs[3]);
   for (int i = 2; i >= 0; --i) {
     if (!ok[i]) continue;
-    const double c = tile_cost(a.n, col_tiles, bms[i], bpcs[i]);
+    const double c = tile_cost(a.n, col_tiles, bms[i], BN, bpcs[i]);
     if (c < best_cost) {
       best = i;
       best_cost = c;

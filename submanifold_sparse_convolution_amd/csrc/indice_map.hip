@@ -8,7 +8,7 @@
 //
 //   GRID  a dense int32 volume over the bounding box of the set with a one-cell margin on each
 //         spatial side (cell = row or -1).  Used when the box has at most kGridCellsPerVoxel
-//         cells per voxel (thin shells in small grids, dense grids).  A neighbour is one load at
+//         cells per voxel and 2^29 cells in total.  A neighbour is one load at
 //         a fixed offset from the voxel's own cell; the margin keeps every +-1 step in bounds
 //         and inside the voxel's own batch slab.
 //   HASH  an open-addressing table (linear probing, 16-byte slots, load factor <= 1/2) keyed by
@@ -378,7 +378,7 @@ int clamp_blocks(int64_t b, int64_t cap) { return (int)(b < 1 ? 1 : (b > cap ? c
 int64_t map_hash_slots(int64_t n) { return n * 2 < 64 ? 64 : n * 2; }
 int64_t map_grid_budget_cells(int64_t n) {
   const int64_t c = n * kGridCellsPerVoxel;
-  return c < 4096 ? 4096 : c;
+  return c < 4096 ? 4096 : (c > kGridMaxCells ? kGridMaxCells : c);
 }
 int map_bounds_blocks(int64_t n) { return clamp_blocks((n + 4 * kThreads - 1) / (4 * kThreads), kMaxBoundsBlocks); }
 size_t map_table_bytes(int64_t n) {

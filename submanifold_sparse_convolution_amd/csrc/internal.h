@@ -32,7 +32,8 @@ void device_free(void* ptr, hipStream_t stream);
 
 // Device-side plan and statistics of one map build (copied to the host at its end).
 constexpr int kTapBanks = 16;               // tap hit counters are spread over banks of 27
-constexpr int64_t kGridCellsPerVoxel = 16;  // dense grid allowed up to this many cells per voxel
+constexpr int64_t kGridCellsPerVoxel = 128;       // dense grid allowed up to this many cells per voxel
+constexpr int64_t kGridMaxCells = int64_t(1) << 29;  // ... and at most 2 GiB of int32 cells
 constexpr int kModeNone = -1;               // coordinates out of range: nothing built
 constexpr int kModeHash = 0;
 constexpr int kModeGrid = 1;

@@ -105,6 +105,31 @@ extern "C" const char* subm_last_error(void) { return g_last_error.c_str(); }
 
 namespace {
 
+// Build workspace (hash table or dense grid, bounds partials, statistics): one grow-only device
+// buffer per GPU, held under a mutex for the whole build.  A build ends with a stream
+// synchronisation, so the buffer is idle when the next build takes it; builds on one GPU from
+// several threads are serialised by the mutex.
+struct Workspace {
+  std::mutex mu;
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+Workspace g_workspace[kMaxDevices];
+
+Status workspace_reserve(Workspace& ws, size_t bytes) {
+  if (ws.bytes >= bytes) return Status{};
+  if (ws.ptr != nullptr) {
+    SUBM_HIP_TRY(hipFree(ws.ptr));
+    ws.ptr = nullptr;
+    ws.bytes = 0;
+  }
+  const size_t grain = size_t(64) << 20;
+  const size_t want = (bytes + grain - 1) / grain * grain;
+  SUBM_HIP_TRY(hipMalloc(&ws.ptr, want));
+  ws.bytes = want;
+  return Status{};
+}
+
 // Per-thread pinned host buffer that receives the build statistics (one per device; a thread
 // runs one build at a time).  Pinned memory lets the device-to-host copy be a plain DMA.
 MapStats* pinned_stats(int dev) {
@@ -144,6 +169,10 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
     *out_map = m;
     return SUBM_OK;
   }
+  if (m->d.device < 0 || m->d.device >= kMaxDevices) {
+    delete m;
+    return fail(SUBM_ERR_HIP, "device ordinal out of range");
+  }
   MapStats* host = pinned_stats(m->d.device);
   if (host == nullptr) {
     delete m;
@@ -154,17 +183,17 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
   const size_t partial_bytes = round_up(map_partials_bytes(n), 256);
   const size_t tmp_bytes = table_bytes + partial_bytes + sizeof(MapStats);
 
-  void* tmp = nullptr;
+  Workspace& ws = g_workspace[m->d.device];
+  std::lock_guard<std::mutex> lock(ws.mu);
   void* nbr = nullptr;
-  Status s = device_alloc(&tmp, tmp_bytes, stream);
+  Status s = workspace_reserve(ws, tmp_bytes);
   if (s.ok()) s = device_alloc(&nbr, (size_t)n * 28 * sizeof(int32_t), stream);  // nbr [n,27] + masks [n]
   if (!s.ok()) {
-    device_free(tmp, stream);
     device_free(nbr, stream);
     delete m;
     return fail(s);
   }
-  unsigned char* base = static_cast<unsigned char*>(tmp);
+  unsigned char* base = static_cast<unsigned char*>(ws.ptr);
   void* partials = base + table_bytes;
   MapStats* dstats = reinterpret_cast<MapStats*>(base + table_bytes + partial_bytes);
 
@@ -173,7 +202,6 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
   hipError_t e = launch_map_build(coords, n, mode, base, partials, nbr_rows, masks, dstats, stream);
   if (e == hipSuccess) e = hipMemcpyAsync(host, dstats, sizeof(MapStats), hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  device_free(tmp, stream);
   if (e != hipSuccess) {
     device_free(nbr, stream);
     delete m;

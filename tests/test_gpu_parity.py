@@ -94,7 +94,7 @@ def test_rulebook_bit_exact(key):
     print(f"  config {key}: N={len(coords)} pairs={int((want >= 0).sum())}", flush=True)
 
 
-@pytest.mark.parametrize("key", ["1", "2a", "3a", "3b"])
+@pytest.mark.parametrize("key", ["1", "2a", "3a", "3b", "4", "5"])
 @pytest.mark.parametrize("mode", ["hash", "grid"])
 def test_rulebook_same_from_both_structures(key, mode):
     req = {"hash": sc.SUBM_MAP_HASH, "grid": sc.SUBM_MAP_GRID}[mode]
@@ -105,10 +105,14 @@ def test_rulebook_same_from_both_structures(key, mode):
 
 
 def test_automatic_structure_choice():
-    # Thin shells and dense boxes in small grids use the dense grid; sparse unions in large grids the hash.
-    for key, want in (("3a", sc.SUBM_MAP_GRID), ("3b", sc.SUBM_MAP_GRID), ("4", sc.SUBM_MAP_HASH), ("5", sc.SUBM_MAP_HASH)):
+    # Every workload here has a bounding box within the grid budget; two far-apart voxels do not.
+    for key in ("3a", "3b", "4", "5"):
         with sc.sparse_indice_map_build(torch.from_numpy(coords_of(key)).to(DEV)) as m:
-            assert m.mode == want, key
+            assert m.mode == sc.SUBM_MAP_GRID, key
+    far = torch.tensor([[0, 0, 0, 0], [0, 60000, 60000, 60000]], dtype=torch.int32, device=DEV)
+    with sc.sparse_indice_map_build(far) as m:
+        assert m.mode == sc.SUBM_MAP_HASH
+        assert gpu_nbr(m).tolist() == [[-1] * 13 + [0] + [-1] * 13, [-1] * 13 + [1] + [-1] * 13]
 
 
 # ----------------------------------------------------------------- convolution, all configs
