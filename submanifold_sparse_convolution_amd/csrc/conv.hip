@@ -28,6 +28,7 @@
 // block b goes to tile (b % 8) * per_xcd + b / 8 and each XCD walks one contiguous range of
 // rows, whose neighbourhoods then stay in that XCD's L2.
 #include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "internal.h"
@@ -91,6 +92,7 @@ struct ConvArgs {
   const void* bias;     // may be null
   void* out;
   const int32_t* nbr;   // [n, 27]; null when taps == 1
+  const uint32_t* masks;  // [n]: bit k set when nbr[i, k] >= 0; null when taps == 1
   int64_t n;
   int cin;
   int cout;
@@ -357,8 +359,6 @@ template <> __device__ __forceinline__ f32x16_t mfma32<DT::F16>(const uint4& a, 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
-constexpr int kRowSlice = 128;  // bytes of one row per stage (64 16-bit channels, 8 chunks of 16 B)
-
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits 3:0
 // and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 template <int N>
@@ -408,57 +408,51 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }
 
-template <int BM, int BN, int TAPS>
-struct DmaShape {
-  static constexpr int WM = BN >= 64 ? 2 : 4;    // waves along rows (compute)
-  static constexpr int WN = 4 / WM;              // waves along output channels (compute)
-  static constexpr int WTM = BM / WM;
-  static constexpr int WTN = BN / WN;
-  static constexpr int FM = WTM / 32;
-  static constexpr int FN = WTN / 32;
-  static constexpr int ADMA = BM / 32;           // load instructions per wave per stage (A rows)
-  static constexpr int BDMA = BN / 32;           // (B rows)
+// Tile of the matrix-core kernel.  WM x WN = 4 waves; each wave owns FM 32-row blocks and FN
+// 32-column blocks of the BM x BN output tile.  A stage is one SL-byte slice (SL / 2 channels)
+// of every row of the tile (A) and of every weight row (B).
+constexpr int kMaxStages = 8;
+
+template <int WM, int FM, int FN, int SL, int TAPS>
+struct MmaShape {
+  static constexpr int WN = 4 / WM;
+  static constexpr int WTM = 32 * FM, WTN = 32 * FN;  // rows / columns per wave
+  static constexpr int BM = WM * WTM;                 // rows per tile
+  static constexpr int BN = WN * WTN;                 // output channels per tile
+  static constexpr int CH = SL / 16;                  // 16-byte chunks per row slice
+  static constexpr int RPI = 64 / CH;                 // rows per 1 KB load instruction
+  static constexpr int KSTEPS = SL / 32;              // 16-channel matrix-core steps per stage
+  static constexpr int ADMA = BM / RPI / 4;           // A loads per wave per stage
+  static constexpr int BDMA = (BN + 4 * RPI - 1) / (4 * RPI);  // B loads per wave per stage
+  static constexpr int BNP = 4 * RPI * BDMA;          // B rows per stage (rows past BN load zeros)
   static constexpr int DMA = ADMA + BDMA;
-  static constexpr int BUF = (BM + BN) * kRowSlice;
-  static constexpr int NBR = TAPS == 27 ? BM * 27 * 4 : 0;
-  // Two or four workgroups per compute unit (two or four waves per SIMD, so one hides another's
-  // LDS and barrier waits) when a two-stage ring fits that often in the 160 KB LDS; otherwise
-  // one workgroup with as many ring stages as fit (2 to 4).
-  static constexpr int LDS2 = 2 * BUF + NBR + 256;
-  static constexpr int FIT2 = (160 * 1024) / LDS2;  // two-stage rings that fit in one CU's LDS
-  static constexpr int BPC = BM > 128 ? 1 : (FIT2 >= 4 ? 4 : (FIT2 >= 2 ? 2 : 1));
-  static constexpr int NS_FIT = (160 * 1024 - NBR - 256) / BUF;
-  static constexpr int NS = BPC > 1 ? 2 : (NS_FIT >= 4 ? 4 : (NS_FIT < 2 ? 2 : NS_FIT));
-  static constexpr int LDS = NS * BUF + NBR + 256;
+  static constexpr int BUF = (BM + BNP) * SL;         // one ring slot
+  // The tile's rulebook rows (BM x 27 int32, contiguous in the map) are copied into LDS with
+  // NDMA direct loads per wave (whole 1 KB instructions, so the copy is padded).
+  static constexpr int NDMA = TAPS == 27 ? (BM * 27 * 4 + 4095) / 4096 : 0;
+  static constexpr int NBR = NDMA * 4096;
+  static constexpr int NS_FIT = (160 * 1024 - NBR - 512) / BUF;
+  static constexpr int NS = NS_FIT >= kMaxStages ? kMaxStages : NS_FIT;  // ring depth
+  static_assert(BM % (4 * RPI) == 0, "A rows must split into whole load instructions per wave");
 };
 
 template <int V> using IC = std::integral_constant<int, V>;
 
-template <DT D, int BM, int BN, int TAPS>
-__global__ __launch_bounds__(kThreads, (DmaShape<BM, BN, TAPS>::BPC)) void subm_conv_dma_kernel(const ConvArgs args) {
-  using Sh = DmaShape<BM, BN, TAPS>;
-  constexpr int WM = Sh::WM, WTM = Sh::WTM, WTN = Sh::WTN, FM = Sh::FM, FN = Sh::FN;
+template <DT D, int WM, int FM, int FN, int SL, int TAPS>
+__global__ __launch_bounds__(kThreads, 1) void subm_conv_mma_kernel(const ConvArgs args) {
+  using Sh = MmaShape<WM, FM, FN, SL, TAPS>;
+  constexpr int WTM = Sh::WTM, WTN = Sh::WTN, BM = Sh::BM, BN = Sh::BN, BNP = Sh::BNP;
+  constexpr int CH = Sh::CH, RPI = Sh::RPI, KSTEPS = Sh::KSTEPS;
   constexpr int ADMA = Sh::ADMA, BDMA = Sh::BDMA, DMA = Sh::DMA, BUF = Sh::BUF, NS = Sh::NS;
-  static_assert(FM >= 1 && FN >= 1 && BDMA >= 1, "tile too small");
-  static_assert(NS >= 2 && NS <= 4, "ring depth");
-  static_assert((BM / 2) * BN * 2 <= BUF, "epilogue staging must fit in two ring slots");
-  static_assert((NS - 1) * DMA < 64, "outstanding loads exceed the vmcnt range");
+  static_assert(NS >= 2, "ring depth");
+  static_assert((BM / 2) * BN * 2 <= NS * BUF, "epilogue staging must fit in the ring");
+  static_assert((NS - 1) * DMA < 64 && Sh::NDMA < 64, "outstanding loads exceed the vmcnt range");
 
-  // One array per ring slot: the compiler can then see that the slot being filled by the
-  // asynchronous loads and the slot being read by the matrix-core loop never alias, and does
-  // not insert a wait for all outstanding loads before every LDS read.
-  __shared__ __align__(16) unsigned char ring0[BUF];
-  __shared__ __align__(16) unsigned char ring1[BUF];
-  __shared__ __align__(16) unsigned char ring2[NS > 2 ? BUF : 16];
-  __shared__ __align__(16) unsigned char ring3[NS > 3 ? BUF : 16];
-  __shared__ uint32_t s_off[TAPS == 27 ? BM * 27 : 1];  // byte offset of each (row, tap) source row
+  // The ring of NS stages in one array; slots are addressed at run time.  The direct loads are
+  // invisible to the compiler, so it inserts no waits of its own for them.
+  __shared__ __align__(16) unsigned char ring[NS * BUF];
+  __shared__ __align__(16) int32_t s_nbr[TAPS == 27 ? Sh::NBR / 4 : 4];  // the tile's rulebook rows
   __shared__ uint32_t s_mask;
-  auto ring = [&](auto I) -> unsigned char* {
-    if constexpr (decltype(I)::value == 0) return ring0;
-    else if constexpr (decltype(I)::value == 1) return ring1;
-    else if constexpr (decltype(I)::value == 2) return ring2;
-    else return ring3;
-  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -473,93 +467,130 @@ __global__ __launch_bounds__(kThreads, (DmaShape<BM, BN, TAPS>::BPC)) void subm_
   const int64_t row0 = (int64_t)tile * BM;
   const int o0 = blockIdx.y * BN;
   const int cout = args.cout, row_bytes = args.row_bytes;
-  const unsigned char* feats = static_cast<const unsigned char*>(args.feats);
-  const unsigned char* weight = static_cast<const unsigned char*>(args.weight);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
+  // The tile's rulebook rows go straight into LDS (all loads in flight at once; bytes past the
+  // map read as zeros and belong to rows >= n, which fetch() treats as absent), and the mask of
+  // taps used anywhere in the tile is the OR of the rows' neighbour masks.  Taps no row uses
+  // are skipped.
   if (tid == 0) s_mask = 0;
-  __syncthreads();
   uint32_t local_mask = 0;
   if constexpr (TAPS == 27) {
-    const int32_t* nb = args.nbr + row0 * 27;
-    const int valid = (int)((n - row0) < BM ? (n - row0) : BM);
-    for (int idx = tid; idx < BM * 27; idx += kThreads) {
-      const int r = idx / 27;
-      const int v = r < valid ? nb[idx] : -1;
-      s_off[idx] = v >= 0 ? (uint32_t)v * (uint32_t)row_bytes : kOutOfRange;
-      if (v >= 0) local_mask |= 1u << (idx - r * 27);
+    const i32x4_t rsrc_n = make_rsrc(args.nbr, (uint32_t)(n * 27 * 4));
+    const uint32_t gbase = (uint32_t)(row0 * 27 * 4);
+#pragma unroll
+    for (int d = 0; d < Sh::NDMA; ++d) {
+      const uint32_t blk = (uint32_t)((wave_u * Sh::NDMA + d) * 1024);
+      lds_dma16(rsrc_n, gbase + blk + (uint32_t)lane * 16u, lds_offset(s_nbr) + blk);
+    }
+#pragma unroll
+    for (int u = 0; u < (BM + kThreads - 1) / kThreads; ++u) {
+      const int64_t row = row0 + tid + u * kThreads;
+      if (tid + u * kThreads < BM && row < n) local_mask |= args.masks[row];
     }
   } else {
     local_mask = 1u;
   }
   for (int off = 32; off > 0; off >>= 1) local_mask |= __shfl_xor(local_mask, off, 64);
+  __syncthreads();
   if (lane == 0 && local_mask) atomicOr(&s_mask, local_mask);
+  wait_vmcnt<0>();
   __syncthreads();
   const uint32_t mask = s_mask;
-  const int nq = (row_bytes + kRowSlice - 1) / kRowSlice;
+  const int nq = (row_bytes + SL - 1) / SL;
   const int total = __builtin_popcount(mask) * nq;  // stages in this tile
 
-  // Load-side lane roles: lane l of a load instruction fills row (l / 8) of an 8-row group at
-  // physical chunk l % 8.  Rows are swizzled as physical = logical ^ ((row / 2) % 8), which keeps
-  // every 16-lane pass of a 16-byte fragment read (16 consecutive rows, one chunk) on distinct
-  // banks; so lane l fetches logical chunk (l % 8) ^ ((row / 2) % 8) of its source row.
-  const int lrow8 = lane >> 3;
-  auto lchunk_of = [&](int group_base) { return (lane & 7) ^ (((group_base >> 1) + (lane >> 4)) & 7); };
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const i32x4_t rsrc_a = make_rsrc(feats, args.feats_bytes);
-  const i32x4_t rsrc_b = make_rsrc(weight, args.weight_bytes);
+  // Load-side lane roles: lane l of a load instruction fills row l / CH of an RPI-row group at
+  // physical chunk l % CH.  Rows are swizzled as physical = logical ^ ((row / (16 / CH)) % CH),
+  // which keeps every 16-lane pass of a fragment read (16 consecutive rows, one chunk) on
+  // distinct banks; so lane l fetches logical chunk (l % CH) ^ swizzle(its row).
+  auto swz_of = [](int row) { return (row / (16 / CH)) % CH; };
+  auto chunk_bytes = [&](int group_row) {
+    return (uint32_t)(((lane % CH) ^ swz_of(group_row + lane / CH)) * 16);
+  };
+  const i32x4_t rsrc_a = make_rsrc(args.feats, args.feats_bytes);
+  const i32x4_t rsrc_b = make_rsrc(args.weight, args.weight_bytes);
 
-  // Issue cursor: taps in ascending order, each split into nq channel slices.  prepare()
-  // computes the per-lane source offsets of one stage; issue_range() emits a slice of its loads.
+  // Per-lane constants: the chunk each load fetches, and the weight-row part of the B offsets.
+  uint32_t lane_cb[DMA], base_b[BDMA];
+  bool ok_b[BDMA];
+#pragma unroll
+  for (int d = 0; d < ADMA; ++d) lane_cb[d] = chunk_bytes(wave * (BM / 4) + RPI * d);
+#pragma unroll
+  for (int d = 0; d < BDMA; ++d) {
+    const int g = BM + wave * (BNP / 4) + RPI * d;
+    const int ol = g - BM + lane / CH;
+    const int o = o0 + ol;
+    lane_cb[ADMA + d] = chunk_bytes(g);
+    ok_b[d] = ol < BN && o < cout;
+    base_b[d] = (uint32_t)(ok_b[d] ? o : 0) * TAPS * (uint32_t)row_bytes + lane_cb[ADMA + d];
+  }
+
+  // Issue cursor: taps in ascending order, each split into nq slices of SL bytes.  fetch()
+  // reads the source rows of the next stage from LDS a stage before they are needed; make()
+  // turns them into this lane's load offsets (branch-free, so the scheduler can place it
+  // between matrix-core instructions); issue() emits the stage's loads.
   uint32_t rem = mask;
   int ik = 0, iq = nq;
+  int pk = 0, pq = 0;    // tap and slice of the fetched stage
+  bool pvalid = false;   // the fetched stage exists
+  int32_t raw[ADMA];     // rulebook entries (source rows) of the fetched stage, -1 if absent
   uint32_t offs[DMA];
-  auto prepare = [&](int stage_index) {
-    const bool valid = stage_index < total;
-    if (valid && iq >= nq) {
-      ik = __builtin_ctz(rem);
-      rem &= rem - 1;
-      iq = 0;
-    }
-    const int k = ik, q = iq;
-    if (valid) ++iq;
+  // Rows of this lane's A loads that exist (the last tile may be partial).
+  bool row_ok[ADMA];
+#pragma unroll
+  for (int d = 0; d < ADMA; ++d) row_ok[d] = row0 + wave * (BM / 4) + RPI * d + lane / CH < n;
+  auto fetch = [&](int stage_index) {
+    pvalid = stage_index < total;
+    const bool adv = pvalid && iq >= nq;
+    const int nk = __builtin_ctz(rem | 0x80000000u);
+    ik = adv ? nk : ik;
+    rem = adv ? (rem & (rem - 1)) : rem;
+    iq = adv ? 0 : iq;
+    pk = ik;
+    pq = iq;
+    iq += pvalid ? 1 : 0;
 #pragma unroll
     for (int d = 0; d < ADMA; ++d) {
-      const int g = wave * (BM / 4) + 8 * d;
-      const int r = g + lrow8;
-      const uint32_t cb = (uint32_t)(q * kRowSlice + lchunk_of(g) * 16);
-      uint32_t base_off;
+      const int r = wave * (BM / 4) + RPI * d + lane / CH;
       if constexpr (TAPS == 27) {
-        base_off = s_off[r * 27 + k];
+        raw[d] = s_nbr[r * 27 + pk];
       } else {
-        base_off = (row0 + r < n) ? (uint32_t)(row0 + r) * (uint32_t)row_bytes : kOutOfRange;
+        raw[d] = (int32_t)(row0 + r);
       }
-      offs[d] = (valid && (int)cb < row_bytes) ? base_off + cb : kOutOfRange;
+    }
+  };
+  auto make = [&]() {
+    const uint32_t sq = (uint32_t)(pq * SL);
+    const uint32_t sb = (uint32_t)pk * (uint32_t)row_bytes + sq;
+    const int limit = pvalid ? row_bytes - (int)sq : 0;  // chunks at or past this are padding
+    // Products computed unconditionally and conditions combined with '&': a short-circuit
+    // condition around the multiply becomes exec-masked control flow, which the scheduler cannot
+    // move matrix-core instructions across.
+#pragma unroll
+    for (int d = 0; d < ADMA; ++d) {
+      const uint32_t o = (uint32_t)raw[d] * (uint32_t)row_bytes + sq + lane_cb[d];
+      const bool use = (raw[d] >= 0) & row_ok[d] & ((int)lane_cb[d] < limit);
+      offs[d] = use ? o : kOutOfRange;
     }
 #pragma unroll
     for (int d = 0; d < BDMA; ++d) {
-      const int g = wave * (BN / 4) + 8 * d;
-      const int o = o0 + g + lrow8;
-      const uint32_t cb = (uint32_t)(q * kRowSlice + lchunk_of(g) * 16);
-      offs[ADMA + d] = (valid && (int)cb < row_bytes && o < cout)
-                           ? ((uint32_t)o * TAPS + (uint32_t)k) * (uint32_t)row_bytes + cb
-                           : kOutOfRange;
+      const bool use = ok_b[d] & ((int)lane_cb[ADMA + d] < limit);
+      offs[ADMA + d] = use ? base_b[d] + sb : kOutOfRange;
     }
   };
+  // Loads [d0, d1) of the stage (A loads first, then B).
   auto issue_range = [&](unsigned char* base, int d0, int d1) {
 #pragma unroll
     for (int d = 0; d < DMA; ++d) {
       if (d < d0 || d >= d1) continue;
-      if (d < ADMA) {
-        lds_dma16(rsrc_a, offs[d], lds_offset(base) + (uint32_t)((wave_u * (BM / 4) + 8 * d) * kRowSlice));
-      } else {
-        lds_dma16(rsrc_b, offs[d], lds_offset(base) + (uint32_t)((BM + wave_u * (BN / 4) + 8 * (d - ADMA)) * kRowSlice));
-      }
+      if (d < ADMA)
+        lds_dma16(rsrc_a, offs[d], lds_offset(base) + (uint32_t)((wave_u * (BM / 4) + RPI * d) * SL));
+      else
+        lds_dma16(rsrc_b, offs[d], lds_offset(base) + (uint32_t)((BM + wave_u * (BNP / 4) + RPI * (d - ADMA)) * SL));
     }
   };
-  auto issue = [&](int stage_index, unsigned char* base) {
-    prepare(stage_index);
-    issue_range(base, 0, DMA);
-  };
+  auto issue = [&](unsigned char* base) { issue_range(base, 0, DMA); };
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -569,71 +600,114 @@ __global__ __launch_bounds__(kThreads, (DmaShape<BM, BN, TAPS>::BPC)) void subm_
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // Matrix-core side: a stage is KSTEPS 16-channel steps.  Lane l supplies row (or column)
+  // l % 32 of a 32 x 16 operand block, channels 8 * (l / 32) .. + 7 of the step, from LDS
+  // chunk 2 * step + l / 32 (swizzled).  All fragments of a stage are read one stage ahead, into
+  // the register set that is not being multiplied, so every LDS read has a whole stage of
+  // matrix-core work to hide behind and there is a single wait per stage.
   const int lrow = lane & 31;
   const int lk = lane >> 5;
-  // Consume one stage (up to four 16-channel steps); after step kk, issue the kk-th quarter of
-  // the loads of the stage NS - 1 ahead, so that address work overlaps the matrix cores.
-  constexpr int DPS = (DMA + 3) / 4;
-  // Every stage runs all four 16-channel steps: channels past Cin were loaded as zeros, so a
-  // partial last slice only costs idle matrix-core work, and the straight-line code lets the
-  // compiler keep exact LDS wait counts.
-  auto compute_and_issue = [&](const unsigned char* buf, unsigned char* next) {
-    const int rsw = (lrow >> 1) & 7;
-    // Fragments of step kk + 1 are read while the matrix cores run step kk.
-    uint4 af[2][FM], bf[2][FN];
-    auto load_frags = [&](int kk, int slot) {
-      const int sw = ((2 * kk + lk) ^ rsw) << 4;
+  const int swz = swz_of(lrow);
+  uint4 fa[2][KSTEPS][FM], fb[2][KSTEPS][FN];  // [set][step][block]
+  auto read_step = [&](auto SET, auto KK, const unsigned char* buf) {
+    constexpr int t = decltype(SET)::value, kk = decltype(KK)::value;
+    const int off = ((2 * kk + lk) ^ swz) << 4;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[slot][i] = *reinterpret_cast<const uint4*>(buf + (wm * WTM + i * 32 + lrow) * kRowSlice + sw);
+    for (int i = 0; i < FM; ++i)
+      fa[t][kk][i] = *reinterpret_cast<const uint4*>(buf + (wm * WTM + i * 32 + lrow) * SL + off);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bf[slot][j] = *reinterpret_cast<const uint4*>(buf + (BM + wn * WTN + j * 32 + lrow) * kRowSlice + sw);
-    };
-    load_frags(0, 0);
+    for (int j = 0; j < FN; ++j)
+      fb[t][kk][j] = *reinterpret_cast<const uint4*>(buf + (BM + wn * WTN + j * 32 + lrow) * SL + off);
+  };
+  auto read_stage = [&](auto SET, const unsigned char* buf) {
+    read_step(SET, IC<0>{}, buf);
+    if constexpr (KSTEPS > 1) read_step(SET, IC<1>{}, buf);
+    if constexpr (KSTEPS > 2) read_step(SET, IC<2>{}, buf);
+    if constexpr (KSTEPS > 3) read_step(SET, IC<3>{}, buf);
+  };
+  auto multiply_step = [&](auto SET, auto KK) {
+    constexpr int t = decltype(SET)::value, kk = decltype(KK)::value;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk + 1 < 4) load_frags(kk + 1, (kk + 1) & 1);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<D>(fa[t][kk][i], fb[t][kk][j], acc[i][j]);
+  };
+  // Within a step: one LDS read and a few address instructions after each matrix-core
+  // instruction.  A long run of reads fills the LDS queue and stalls the single wave on the
+  // SIMD, and with it the matrix core; address work left in front of the step idles it.
+  auto interleave = [&]() {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<D>(af[kk & 1][i], bf[kk & 1][j], acc[i][j]);
-      issue_range(next, kk * DPS, (kk + 1) * DPS < DMA ? (kk + 1) * DPS : DMA);
+    for (int g = 0; g < FM * FN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to four VALU
     }
   };
+  constexpr int DPS = (DMA + KSTEPS - 1) / KSTEPS;  // loads issued per step
 
-  // One ring step: the oldest stage (slot S) is complete -> barrier -> consume slot S while
-  // refilling the slot consumed in the previous step with the stage NS - 1 ahead.
-  int st = 0;
-  auto step = [&](auto S) {
-    constexpr int cs = decltype(S)::value;
-    constexpr int is = (cs + NS - 1) % NS;
+  // Prologue: stages 0 .. NS - 1 fill every slot; wait for stage 0 and read it.
+#pragma unroll
+  for (int s0 = 0; s0 < NS; ++s0) {
+    fetch(s0);
+    make();
+    issue(ring + s0 * BUF);
+  }
+  fetch(NS);
+  wait_vmcnt<(NS - 1) * DMA>();
+  barrier_no_fence();
+  read_stage(IC<0>{}, ring);
+
+  // Stage st (slot `slot`, fragments in register set SET):
+  //   wait until this wave's loads of stage st + 1 have landed and its reads of stage st have
+  //   returned; barrier (every wave's loads of st + 1 are in LDS, nobody reads slot st any
+  //   more); read stage st + 1 into the other set; refill slot st with stage st + NS; multiply.
+  // Nothing crosses a stage boundary (sched_barrier): the scheduler would otherwise hoist the
+  // next stage's matrix-core instructions next to the reads that feed them.
+  int st = 0, slot = 0;
+  // Each step of the stage is its own scheduling group: the next stage's fragments for that
+  // step, the step's matrix-core instructions, and a share of the loads that refill slot st.
+  auto step_group = [&](auto SET, auto KK, unsigned char* cur, const unsigned char* next) {
+    constexpr int t = decltype(SET)::value, kk = decltype(KK)::value;
+    if constexpr (kk < KSTEPS) {
+      read_step(IC<1 - t>{}, KK, next);
+      multiply_step(SET, KK);
+      issue_range(cur, kk * DPS, (kk + 1) * DPS < DMA ? (kk + 1) * DPS : DMA);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto step = [&](auto SET) {
+    unsigned char* cur = ring + slot * BUF;
+    const int next_slot = slot + 1 == NS ? 0 : slot + 1;
+    const unsigned char* next = ring + next_slot * BUF;
+    __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<(NS - 2) * DMA>();
+    wait_lgkmcnt0();
     barrier_no_fence();
-    prepare(st + NS - 1);
-    compute_and_issue(ring(IC<cs>{}), ring(IC<is>{}));
+    __builtin_amdgcn_sched_barrier(0);
+    make();                  // stage st + NS, from the rulebook entries fetched a stage ago
+    fetch(st + NS + 1);
+    step_group(SET, IC<0>{}, cur, next);
+    step_group(SET, IC<1>{}, cur, next);
+    step_group(SET, IC<2>{}, cur, next);
+    step_group(SET, IC<3>{}, cur, next);
+    slot = next_slot;
     ++st;
   };
-  // Prologue: stages 0 .. NS - 2 in flight; step s then issues stage s + NS - 1.
-  issue(0, ring(IC<0>{}));
-  if constexpr (NS > 2) issue(1, ring(IC<1>{}));
-  if constexpr (NS > 3) issue(2, ring(IC<2>{}));
-  while (st < total) {
+  // Whole pairs of stages in the loop (one exit, so the accumulators keep their registers),
+  // then an odd last stage.
+  while (st + 1 < total) {
     step(IC<0>{});
-    if (st >= total) break;
     step(IC<1>{});
-    if (st >= total) break;
-    if constexpr (NS > 2) {
-      step(IC<2>{});
-      if (st >= total) break;
-    }
-    if constexpr (NS > 3) {
-      step(IC<3>{});
-    }
   }
+  if (st < total) step(IC<0>{});
+  __builtin_amdgcn_sched_barrier(0);
   wait_vmcnt<0>();
   __syncthreads();
 
-  // Epilogue: + bias (fp32), one RNE rounding, staged through two ring slots (rows below and
-  // above BM / 2) for coalesced 16-byte stores.
+  // Epilogue: + bias (fp32), one RNE rounding, staged through the ring in two halves of the
+  // rows for coalesced 16-byte stores.  Output block layout: lane l holds column l % 32, rows
+  // 8 * (v / 4) + 4 * (l / 32) + v % 4 of accumulator register v.
   using T = typename Elem<D>::T;
   float bcol[FN];
 #pragma unroll
@@ -641,103 +715,127 @@ __global__ __launch_bounds__(kThreads, (DmaShape<BM, BN, TAPS>::BPC)) void subm_
     const int o = o0 + wn * WTN + j * 32 + lrow;
     bcol[j] = (args.bias != nullptr && o < cout) ? to_float<D>(reinterpret_cast<const T*>(args.bias)[o]) : 0.f;
   }
-  T* sC0 = reinterpret_cast<T*>(ring0);
-  T* sC1 = reinterpret_cast<T*>(ring1);
+  T* stage = reinterpret_cast<T*>(ring);
+  T* out = reinterpret_cast<T*>(args.out);
   constexpr int HALF = BM / 2;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int pass = 0; pass < 2; ++pass) {
+    if ((wm * WTM) / HALF == pass) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
-        const int col = wn * WTN + j * 32 + lrow;
-        T* dst = r < HALF ? sC0 + r * BN : sC1 + (r - HALF) * BN;
-        dst[col] = from_float<D>(acc[i][j][v] + bcol[j]);
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lk + (v & 3) - pass * HALF;
+            stage[r * BN + wn * WTN + j * 32 + lrow] = from_float<D>(acc[i][j][v] + bcol[j]);
+          }
+    }
+    __syncthreads();
+    const int64_t rbase = row0 + pass * HALF;
+    if (args.vec_out) {
+      constexpr int CPR = BN * 2 / 16;
+      for (int idx = tid; idx < HALF * CPR; idx += kThreads) {
+        const int r = idx / CPR, c = idx - r * CPR;
+        const int64_t row = rbase + r;
+        const int col = o0 + c * 8;
+        if (row < n && col < cout)
+          *reinterpret_cast<uint4*>(out + row * cout + col) = *reinterpret_cast<const uint4*>(stage + r * BN + c * 8);
       }
-  __syncthreads();
-  T* out = reinterpret_cast<T*>(args.out);
-  if (args.vec_out) {
-    constexpr int CPR = BN * 2 / 16;
-    for (int idx = tid; idx < BM * CPR; idx += kThreads) {
-      const int r = idx / CPR, c = idx - r * CPR;
-      const int64_t row = row0 + r;
-      const int col = o0 + c * 8;
-      const T* src = r < HALF ? sC0 + r * BN : sC1 + (r - HALF) * BN;
-      if (row < n && col < cout) *reinterpret_cast<uint4*>(out + row * cout + col) = *reinterpret_cast<const uint4*>(src + c * 8);
+    } else {
+      for (int idx = tid; idx < HALF * BN; idx += kThreads) {
+        const int r = idx / BN, c = idx - r * BN;
+        const int64_t row = rbase + r;
+        if (row < n && o0 + c < cout) out[row * cout + o0 + c] = stage[r * BN + c];
+      }
     }
-  } else {
-    for (int idx = tid; idx < BM * BN; idx += kThreads) {
-      const int r = idx / BN, c = idx - r * BN;
-      const int64_t row = row0 + r;
-      const T* src = r < HALF ? sC0 + r * BN : sC1 + (r - HALF) * BN;
-      if (row < n && o0 + c < cout) out[row * cout + o0 + c] = src[c];
-    }
+    __syncthreads();
   }
 }
 
-template <DT D, int BM, int BN, int TAPS>
-hipError_t launch_dma(const ConvArgs& a0, hipStream_t stream) {
+template <DT D, int WM, int FM, int FN, int SL, int TAPS>
+hipError_t launch_mma(const ConvArgs& a0, hipStream_t stream) {
+  using Sh = MmaShape<WM, FM, FN, SL, TAPS>;
   ConvArgs a = a0;
-  a.tiles_m = (int)((a.n + BM - 1) / BM);
+  a.tiles_m = (int)((a.n + Sh::BM - 1) / Sh::BM);
   a.per_xcd = (a.tiles_m + 7) / 8;
-  dim3 grid((unsigned)(8 * a.per_xcd), (unsigned)((a.cout + BN - 1) / BN));
-  subm_conv_dma_kernel<D, BM, BN, TAPS><<<grid, kThreads, 0, stream>>>(a);
+  dim3 grid((unsigned)(8 * a.per_xcd), (unsigned)((a.cout + Sh::BN - 1) / Sh::BN));
+  subm_conv_mma_kernel<D, WM, FM, FN, SL, TAPS><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-// Estimated relative time of a launch with tile height bm and bpc workgroups per compute unit:
-// whole rounds of tiles over the 256 compute units, each round as long as bpc tiles of bm rows
-// sharing one unit, plus a fixed per-tile overhead (the weight slices, bn rows, are loaded once
-// per tile) worth 3/8 of bn rows.  Co-resident workgroups hide each other's waits; measured
-// factors: 0.75 of the time for two per unit, 0.6 for four.
-constexpr int kComputeUnits = 256;
-inline double tile_cost(int64_t n, int col_tiles, int bm, int bn, int bpc) {
-  const int64_t tiles = (n + bm - 1) / bm * col_tiles;
-  const int64_t slots = (int64_t)kComputeUnits * bpc;
-  const int64_t rounds = (tiles + slots - 1) / slots;
-  const double overlap = bpc >= 4 ? 0.6 : (bpc == 2 ? 0.75 : 1.0);
-  return (double)rounds * bpc * (bm + 3.0 * bn / 8.0) * overlap;
+// Tile configurations of the matrix-core kernel: waves along rows, row blocks and column blocks
+// per wave, stage slice bytes.
+struct MmaTile {
+  const char* name;
+  int wm, fm, fn, sl;
+};
+constexpr MmaTile kTiles[] = {
+    // 128 output channels per tile
+    {"r192c128s128", 2, 3, 2, 128}, {"r192c128s64", 2, 3, 2, 64}, {"r128c128s64", 2, 2, 2, 64},
+    {"r256c128s64", 2, 4, 2, 64},   {"r384c128s64", 4, 3, 4, 64}, {"r256c128s128", 2, 4, 2, 128},
+    // 64 output channels per tile
+    {"r192c64s128", 2, 3, 1, 128},  {"r256c64s64", 4, 2, 2, 64},  {"r384c64s64", 4, 3, 2, 64},
+    {"r128c64s64", 2, 2, 1, 64},
+    // 32 output channels per tile
+    {"r256c32s64", 4, 2, 1, 64},    {"r128c32s64", 4, 1, 1, 64},
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+template <DT D, int TAPS>
+hipError_t launch_tile_index(int t, const ConvArgs& a, hipStream_t stream) {
+  switch (t) {
+    case 0: return launch_mma<D, 2, 3, 2, 128, TAPS>(a, stream);
+    case 1: return launch_mma<D, 2, 3, 2, 64, TAPS>(a, stream);
+    case 2: return launch_mma<D, 2, 2, 2, 64, TAPS>(a, stream);
+    case 3: return launch_mma<D, 2, 4, 2, 64, TAPS>(a, stream);
+    case 4: return launch_mma<D, 4, 3, 4, 64, TAPS>(a, stream);
+    case 5: return launch_mma<D, 2, 4, 2, 128, TAPS>(a, stream);
+    case 6: return launch_mma<D, 2, 3, 1, 128, TAPS>(a, stream);
+    case 7: return launch_mma<D, 4, 2, 2, 64, TAPS>(a, stream);
+    case 8: return launch_mma<D, 4, 3, 2, 64, TAPS>(a, stream);
+    case 9: return launch_mma<D, 2, 2, 1, 64, TAPS>(a, stream);
+    case 10: return launch_mma<D, 4, 2, 1, 64, TAPS>(a, stream);
+    default: return launch_mma<D, 4, 1, 1, 64, TAPS>(a, stream);
+  }
 }
 
-template <DT D, int BN, int TAPS>
-hipError_t launch_dma_bn(const ConvArgs& a, hipStream_t stream) {
-  const int col_tiles = (a.cout + BN - 1) / BN;
-  const int bms[4] = {64, 128, 192, 256};
-  const bool ok[4] = {BN >= 64, true, BN >= 64, true};
-  const int bpcs[4] = {DmaShape<64, BN, TAPS>::BPC, DmaShape<128, BN, TAPS>::BPC, DmaShape<192, BN, TAPS>::BPC,
-                       DmaShape<256, BN, TAPS>::BPC};
-  int best = 3;
-  double best_cost = tile_cost(a.n, col_tiles, 256, BN, bpcs[3]);
-  for (int i = 2; i >= 0; --i) {
-    if (!ok[i]) continue;
-    const double c = tile_cost(a.n, col_tiles, bms[i], BN, bpcs[i]);
-    if (c < best_cost) {
-      best = i;
-      best_cost = c;
-    }
-  }
-  // SUBMCONV_TILE_M=64|128|192|256 forces the tile height (tuning and tests); ignored when that
-  // height is not built for this channel width.
-  if (const char* env = std::getenv("SUBMCONV_TILE_M")) {
-    const int want = std::atoi(env);
-    for (int i = 0; i < 4; ++i)
-      if (bms[i] == want && ok[i]) best = i;
-  }
-  switch (bms[best]) {
-    case 64: if constexpr (BN >= 64) return launch_dma<D, 64, BN, TAPS>(a, stream); break;
-    case 128: return launch_dma<D, 128, BN, TAPS>(a, stream);
-    case 192: if constexpr (BN >= 64) return launch_dma<D, 192, BN, TAPS>(a, stream); break;
-    default: break;
-  }
-  return launch_dma<D, 256, BN, TAPS>(a, stream);
+// Estimated time of a launch: whole rounds of tiles over the 256 compute units, times a
+// per-tile cost of stages x cycles per stage (the larger of the matrix-core time at the ~80 %
+// the loop sustains and the load time at ~35 bytes per clock per compute unit) plus a fixed
+// per-tile cost (rulebook copy, prologue, epilogue).
+constexpr int kComputeUnits = 256;
+inline double mma_cost(int64_t n, int cout, int cin_bytes, const MmaTile& t) {
+  const int bm = 32 * t.fm * t.wm, bn = 32 * t.fn * (4 / t.wm);
+  const int64_t tiles = (n + bm - 1) / bm * ((cout + bn - 1) / bn);
+  const int64_t rounds = (tiles + kComputeUnits - 1) / kComputeUnits;
+  const double stages = 27.0 * ((cin_bytes + t.sl - 1) / t.sl);
+  const double mfma = (double)bm * bn * (t.sl / 2) * 2.0 / (4 * 1024.0 * 4.0) / 0.8;
+  const double load = (double)(bm + bn) * t.sl / 35.0;
+  return (double)rounds * (stages * ((mfma > load ? mfma : load) + 60.0) + 6000.0);
 }
 
 template <DT D, int TAPS>
-hipError_t launch_dma_shape(const ConvArgs& a, hipStream_t stream) {
-  if (a.cout <= 32) return launch_dma_bn<D, 32, TAPS>(a, stream);
-  if (a.cout <= 64) return launch_dma_bn<D, 64, TAPS>(a, stream);
-  return launch_dma_bn<D, 128, TAPS>(a, stream);
+hipError_t launch_mma_auto(const ConvArgs& a, hipStream_t stream) {
+  // Candidate tiles: the column width that covers Cout in one tile where possible.
+  const int want_bn = a.cout > 64 ? 128 : (a.cout > 32 ? 64 : 32);
+  int best = -1;
+  double best_cost = 0.0;
+  for (int t = 0; t < kNumTiles; ++t) {
+    const int bn = 32 * kTiles[t].fn * (4 / kTiles[t].wm);
+    if (bn != want_bn) continue;
+    const double c = mma_cost(a.n, a.cout, a.row_bytes, kTiles[t]);
+    if (best < 0 || c < best_cost) {
+      best = t;
+      best_cost = c;
+    }
+  }
+  // SUBMCONV_TILE=<name> forces a tile configuration (tuning and tests).
+  if (const char* env = std::getenv("SUBMCONV_TILE")) {
+    for (int t = 0; t < kNumTiles; ++t)
+      if (std::strcmp(env, kTiles[t].name) == 0) best = t;
+  }
+  return launch_tile_index<D, TAPS>(best, a, stream);
 }
 
 template <DT D, int BM, int BN, int WM, bool VEC, int TAPS>
@@ -762,7 +860,7 @@ template <DT D>
 hipError_t launch_dtype(const ConvArgs& a, bool vec_in, int taps, hipStream_t stream) {
   if constexpr (D != DT::F32) {
     if (vec_in && a.cout > 16 && a.feats_bytes != 0 && a.weight_bytes != 0) {
-      return taps == 27 ? launch_dma_shape<D, 27>(a, stream) : launch_dma_shape<D, 1>(a, stream);
+      return taps == 27 ? launch_mma_auto<D, 27>(a, stream) : launch_mma_auto<D, 1>(a, stream);
     }
   }
   if (taps == 27) return vec_in ? launch_shape<D, true, 27>(a, stream) : launch_shape<D, false, 27>(a, stream);
@@ -784,6 +882,7 @@ hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, i
   a.bias = bias;
   a.out = out;
   a.nbr = ksize == 3 ? map->nbr : nullptr;
+  a.masks = ksize == 3 ? map->masks : nullptr;
   a.n = n;
   a.cin = cin;
   a.cout = cout;
@@ -795,7 +894,9 @@ hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, i
   // generic kernel (size 0 marks "does not fit").
   const uint64_t fb = (uint64_t)n * (uint64_t)a.row_bytes;
   const uint64_t wb = (uint64_t)cout * (uint64_t)taps * (uint64_t)a.row_bytes;
-  a.feats_bytes = fb < kOffsetLimit ? (uint32_t)fb : 0u;
+  // The rulebook rows are copied with 32-bit byte offsets too (n x 27 int32).
+  const uint64_t nb = ksize == 3 ? (uint64_t)n * 27u * 4u : 0u;
+  a.feats_bytes = (fb < kOffsetLimit && nb < kOffsetLimit) ? (uint32_t)fb : 0u;
   a.weight_bytes = wb < kOffsetLimit ? (uint32_t)wb : 0u;
   switch (dtype) {
     case SUBM_F32: return launch_dtype<DT::F32>(a, vec_in, taps, stream);

@@ -361,28 +361,32 @@ def test_shape_mismatch_and_alias_rejected():
         assert e.value.name == "SUBM_ERR_INVALID_ARG"
 
 
-# ----------------------------------------------------------------- fast-path tile heights
+# ----------------------------------------------------------------- fast-path tile configurations
 
-@pytest.mark.parametrize("tile_m", ["64", "128", "192", "256"])
-@pytest.mark.parametrize("dtype,cin,cout", [("bf16", 128, 128), ("f16", 64, 64), ("bf16", 32, 32), ("bf16", 96, 48),
-                                            ("f16", 200, 136)])
-def test_tile_heights(monkeypatch, tile_m, dtype, cin, cout):
-    monkeypatch.setenv("SUBMCONV_TILE_M", tile_m)
+TILES = ["r192c128s128", "r192c128s64", "r128c128s64", "r256c128s64", "r384c128s64", "r256c128s128",
+         "r192c64s128", "r256c64s64", "r384c64s64", "r128c64s64", "r256c32s64", "r128c32s64"]
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("dtype,cin,cout", [("bf16", 128, 128), ("f16", 64, 64), ("bf16", 96, 48), ("f16", 200, 136),
+                                            ("bf16", 8, 40), ("bf16", 40, 256)])
+def test_tile_configs(monkeypatch, tile, dtype, cin, cout):
+    monkeypatch.setenv("SUBMCONV_TILE", tile)
     coords, f, w, b = small_case(dtype, cin, cout, key="2a")
     with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
         out = forward(m, f, w, b)
     check(out, oracle.conv3_rulebook(oracle_nbr("2a"), as64(f), as64(w), as64(b)), dtype,
-          f"tile {tile_m} {dtype} {cin}->{cout}")
+          f"tile {tile} {dtype} {cin}->{cout}")
     _, f1, w1, b1 = small_case(dtype, cin, cout, key="1", ksize=1)
     out1 = forward(None, f1, w1, b1)
-    check(out1, oracle.conv1(as64(f1), as64(w1), as64(b1)), dtype, f"tile {tile_m} k1")
+    check(out1, oracle.conv1(as64(f1), as64(w1), as64(b1)), dtype, f"tile {tile} k1")
 
 
-@pytest.mark.parametrize("tile_m", ["64", "128", "192", "256"])
-def test_tile_heights_headline_shell(monkeypatch, tile_m):
-    monkeypatch.setenv("SUBMCONV_TILE_M", tile_m)
+@pytest.mark.parametrize("tile", [t for t in TILES if "c128" in t])
+def test_tile_configs_headline_shell(monkeypatch, tile):
+    monkeypatch.setenv("SUBMCONV_TILE", tile)
     coords = coords_of("3a")
     f, w, b = cfg_tensors("3a", 0)
     with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
         out = forward(m, f, w, b)
-    check(out, oracle.conv3_rulebook(oracle_nbr("3a"), as64(f), as64(w), as64(b)), "bf16", f"3a tile {tile_m}")
+    check(out, oracle.conv3_rulebook(oracle_nbr("3a"), as64(f), as64(w), as64(b)), "bf16", f"3a tile {tile}")
