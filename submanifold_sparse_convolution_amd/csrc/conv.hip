@@ -356,6 +356,24 @@ template <> __device__ __forceinline__ f32x16_t mfma32<DT::F16>(const uint4& a, 
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
+// Four fp32 values -> four 16-bit storage elements packed into 8 bytes, rounded to nearest even
+// (hardware conversions: v_cvt_pk_bf16_f32, v_cvt_f16_f32).
+template <DT D> __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d);
+template <> __device__ __forceinline__ uint2 pack4<DT::BF16>(float a, float b, float c, float d) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t lo = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+  const bf16x2_t hi = __builtin_convertvector((f32x2_t){c, d}, bf16x2_t);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+template <> __device__ __forceinline__ uint2 pack4<DT::F16>(float a, float b, float c, float d) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f16x2_t lo = __builtin_convertvector((f32x2_t){a, b}, f16x2_t);
+  const f16x2_t hi = __builtin_convertvector((f32x2_t){c, d}, f16x2_t);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
@@ -408,6 +426,61 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }
 
+// Output tile epilogue shared by the matrix-core kernels: + bias, one RNE rounding, staged in
+// LDS (rows padded by 16 bytes, which spreads the 8-byte writes of 32 rows over the banks) in
+// two halves of the rows, then coalesced 16-byte global stores by all NT threads.
+template <DT D, int WM, int FM, int FN, int NT>
+__device__ __forceinline__ void epilogue_store(const ConvArgs& args, const f32x16_t (&acc)[FM][FN], unsigned char* ring,
+                                               const float* s_bias, int64_t row0, int o0, int tid, bool has_acc,
+                                               int wm, int wn, int lane) {
+  using T = typename Elem<D>::T;
+  constexpr int WN = 4 / WM, WTM = 32 * FM, WTN = 32 * FN, BM = WM * WTM, BN = WN * WTN;
+  constexpr int HALF = BM / 2;
+  constexpr int SROW = BN * 2 + 16;  // staging row stride in bytes
+  const int64_t n = args.n;
+  const int cout = args.cout;
+  const int lrow = lane & 31, lk = lane >> 5;
+  T* out = reinterpret_cast<T*>(args.out);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    if (has_acc && (wm * WTM) / HALF == pass) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WTM + i * 32 + lrow - pass * HALF;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = wn * WTN + j * 32 + 8 * g + 4 * lk;
+            const float4 bb = *reinterpret_cast<const float4*>(s_bias + c);
+            *reinterpret_cast<uint2*>(ring + r * SROW + c * 2) =
+                pack4<D>(acc[i][j][4 * g] + bb.x, acc[i][j][4 * g + 1] + bb.y, acc[i][j][4 * g + 2] + bb.z,
+                         acc[i][j][4 * g + 3] + bb.w);
+          }
+      }
+    }
+    __syncthreads();
+    const int64_t rbase = row0 + pass * HALF;
+    if (args.vec_out) {
+      constexpr int CPR = BN * 2 / 16;
+      for (int idx = tid; idx < HALF * CPR; idx += NT) {
+        const int r = idx / CPR, c = idx - r * CPR;
+        const int64_t row = rbase + r;
+        const int col = o0 + c * 8;
+        if (row < n && col < cout)
+          *reinterpret_cast<uint4*>(out + row * cout + col) = *reinterpret_cast<const uint4*>(ring + r * SROW + c * 16);
+      }
+    } else {
+      for (int idx = tid; idx < HALF * BN; idx += NT) {
+        const int r = idx / BN, c = idx - r * BN;
+        const int64_t row = rbase + r;
+        if (row < n && o0 + c < cout) out[row * cout + o0 + c] = *reinterpret_cast<const T*>(ring + r * SROW + c * 2);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // Tile of the matrix-core kernel.  WM x WN = 4 waves; each wave owns FM 32-row blocks and FN
 // 32-column blocks of the BM x BN output tile.  A stage is one SL-byte slice (SL / 2 channels)
 // of every row of the tile (A) and of every weight row (B).
@@ -445,13 +518,14 @@ __global__ __launch_bounds__(kThreads, 1) void subm_conv_mma_kernel(const ConvAr
   constexpr int CH = Sh::CH, RPI = Sh::RPI, KSTEPS = Sh::KSTEPS;
   constexpr int ADMA = Sh::ADMA, BDMA = Sh::BDMA, DMA = Sh::DMA, BUF = Sh::BUF, NS = Sh::NS;
   static_assert(NS >= 2, "ring depth");
-  static_assert((BM / 2) * BN * 2 <= NS * BUF, "epilogue staging must fit in the ring");
+  static_assert((BM / 2) * (BN * 2 + 16) <= NS * BUF, "epilogue staging must fit in the ring");
   static_assert((NS - 1) * DMA < 64 && Sh::NDMA < 64, "outstanding loads exceed the vmcnt range");
 
   // The ring of NS stages in one array; slots are addressed at run time.  The direct loads are
   // invisible to the compiler, so it inserts no waits of its own for them.
   __shared__ __align__(16) unsigned char ring[NS * BUF];
   __shared__ __align__(16) int32_t s_nbr[TAPS == 27 ? Sh::NBR / 4 : 4];  // the tile's rulebook rows
+  __shared__ __align__(16) float s_bias[BN];
   __shared__ uint32_t s_mask;
 
   const int tid = threadIdx.x;
@@ -474,6 +548,11 @@ __global__ __launch_bounds__(kThreads, 1) void subm_conv_mma_kernel(const ConvAr
   // taps used anywhere in the tile is the OR of the rows' neighbour masks.  Taps no row uses
   // are skipped.
   if (tid == 0) s_mask = 0;
+  using T = typename Elem<D>::T;
+  if (tid < BN) {
+    const int o = o0 + tid;
+    s_bias[tid] = (args.bias != nullptr && o < cout) ? to_float<D>(reinterpret_cast<const T*>(args.bias)[o]) : 0.f;
+  }
   uint32_t local_mask = 0;
   if constexpr (TAPS == 27) {
     const i32x4_t rsrc_n = make_rsrc(args.nbr, (uint32_t)(n * 27 * 4));
@@ -630,7 +709,7 @@ __global__ __launch_bounds__(kThreads, 1) void subm_conv_mma_kernel(const ConvAr
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<D>(fa[t][kk][i], fb[t][kk][j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<D>(fb[t][kk][j], fa[t][kk][i], acc[i][j]);
   };
   // Within a step: one LDS read and a few address instructions after each matrix-core
   // instruction.  A long run of reads fills the LDS queue and stalls the single wave on the
@@ -706,51 +785,262 @@ __global__ __launch_bounds__(kThreads, 1) void subm_conv_mma_kernel(const ConvAr
   __syncthreads();
 
   // Epilogue: + bias (fp32), one RNE rounding, staged through the ring in two halves of the
-  // rows for coalesced 16-byte stores.  Output block layout: lane l holds column l % 32, rows
-  // 8 * (v / 4) + 4 * (l / 32) + v % 4 of accumulator register v.
+  // rows for coalesced 16-byte stores.  With the weights as the first matrix-core operand, lane
+  // l holds row l % 32 of its 32 x 32 block and, in accumulator registers 4g .. 4g + 3, the four
+  // consecutive columns 8g + 4 (l / 32) .. + 3: one 8-byte LDS write each.
+  epilogue_store<D, WM, FM, FN, kThreads>(args, acc, ring, s_bias, row0, o0, tid, true, wm, wn, lane);
+}
+
+// Warp-specialised variant: 512 threads, four compute waves (one per SIMD) that only read
+// fragments from LDS and issue matrix-core instructions, and four load waves that only turn
+// rulebook entries into addresses and issue the direct-to-LDS loads.  A compute wave therefore
+// never stalls behind a load that cannot issue, and a load wave never waits for the matrix core.
+// One workgroup barrier per stage hands ring slots between the two roles.
+constexpr int kWsThreads = 512;
+
+template <DT D, int WM, int FM, int FN, int SL, int TAPS>
+__global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_kernel(const ConvArgs args) {
+  using Sh = MmaShape<WM, FM, FN, SL, TAPS>;
+  constexpr int WTM = Sh::WTM, WTN = Sh::WTN, BM = Sh::BM, BN = Sh::BN, BNP = Sh::BNP;
+  constexpr int CH = Sh::CH, RPI = Sh::RPI, KSTEPS = Sh::KSTEPS;
+  constexpr int ADMA = Sh::ADMA, BDMA = Sh::BDMA, DMA = Sh::DMA, BUF = Sh::BUF, NS = Sh::NS;
+  static_assert(NS >= 2, "ring depth");
+  static_assert((BM / 2) * (BN * 2 + 16) <= NS * BUF, "epilogue staging must fit in the ring");
+  static_assert((NS - 1) * DMA < 64 && Sh::NDMA < 64, "outstanding loads exceed the vmcnt range");
+
+  __shared__ __align__(16) unsigned char ring[NS * BUF];
+  __shared__ __align__(16) int32_t s_nbr[TAPS == 27 ? Sh::NBR / 4 : 4];
+  __shared__ __align__(16) float s_bias[BN];
+  __shared__ uint32_t s_mask;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool loader = wave >= 4;
+  const int cw = wave & 3;  // index of the wave within its role
+  const int wm = cw % WM;
+  const int wn = cw / WM;
+
+  const int bid = blockIdx.x;
+  const int tile = (bid & 7) * args.per_xcd + (bid >> 3);
+  if (tile >= args.tiles_m) return;
+  const int64_t n = args.n;
+  const int64_t row0 = (int64_t)tile * BM;
+  const int o0 = blockIdx.y * BN;
+  const int cout = args.cout, row_bytes = args.row_bytes;
+  const int cw_u = __builtin_amdgcn_readfirstlane(cw);
+
+  // Rulebook rows into LDS (load waves) and the tap mask from the rows' neighbour masks.
+  if (tid == 0) s_mask = 0;
   using T = typename Elem<D>::T;
-  float bcol[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int o = o0 + wn * WTN + j * 32 + lrow;
-    bcol[j] = (args.bias != nullptr && o < cout) ? to_float<D>(reinterpret_cast<const T*>(args.bias)[o]) : 0.f;
+  if (tid < BN) {
+    const int o = o0 + tid;
+    s_bias[tid] = (args.bias != nullptr && o < cout) ? to_float<D>(reinterpret_cast<const T*>(args.bias)[o]) : 0.f;
   }
-  T* stage = reinterpret_cast<T*>(ring);
-  T* out = reinterpret_cast<T*>(args.out);
-  constexpr int HALF = BM / 2;
+  uint32_t local_mask = 0;
+  if constexpr (TAPS == 27) {
+    if (loader) {
+      const i32x4_t rsrc_n = make_rsrc(args.nbr, (uint32_t)(n * 27 * 4));
+      const uint32_t gbase = (uint32_t)(row0 * 27 * 4);
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    if ((wm * WTM) / HALF == pass) {
+      for (int d = 0; d < Sh::NDMA; ++d) {
+        const uint32_t blk = (uint32_t)((cw_u * Sh::NDMA + d) * 1024);
+        lds_dma16(rsrc_n, gbase + blk + (uint32_t)lane * 16u, lds_offset(s_nbr) + blk);
+      }
+    }
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int u = 0; u < (BM + kWsThreads - 1) / kWsThreads; ++u) {
+      const int64_t row = row0 + tid + u * kWsThreads;
+      if (tid + u * kWsThreads < BM && row < n) local_mask |= args.masks[row];
+    }
+  } else {
+    local_mask = 1u;
+  }
+  for (int off = 32; off > 0; off >>= 1) local_mask |= __shfl_xor(local_mask, off, 64);
+  __syncthreads();
+  if (lane == 0 && local_mask) atomicOr(&s_mask, local_mask);
+  wait_vmcnt<0>();
+  __syncthreads();
+  const uint32_t mask = s_mask;
+  const int nq = (row_bytes + SL - 1) / SL;
+  const int total = __builtin_popcount(mask) * nq;
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int lrow = lane & 31;
+  const int lk = lane >> 5;
+  auto swz_of = [](int row) { return (row / (16 / CH)) % CH; };
+
+  if (loader) {
+    // ---- load waves: the same lane roles, cursor and offsets as the single-role kernel, with
+    // the four load waves taking the places of the four waves there.
+    auto chunk_bytes = [&](int group_row) {
+      return (uint32_t)(((lane % CH) ^ swz_of(group_row + lane / CH)) * 16);
+    };
+    const i32x4_t rsrc_a = make_rsrc(args.feats, args.feats_bytes);
+    const i32x4_t rsrc_b = make_rsrc(args.weight, args.weight_bytes);
+    uint32_t lane_cb[DMA], base_b[BDMA];
+    bool ok_b[BDMA];
+#pragma unroll
+    for (int d = 0; d < ADMA; ++d) lane_cb[d] = chunk_bytes(cw * (BM / 4) + RPI * d);
+#pragma unroll
+    for (int d = 0; d < BDMA; ++d) {
+      const int g = BM + cw * (BNP / 4) + RPI * d;
+      const int ol = g - BM + lane / CH;
+      const int o = o0 + ol;
+      lane_cb[ADMA + d] = chunk_bytes(g);
+      ok_b[d] = ol < BN && o < cout;
+      base_b[d] = (uint32_t)(ok_b[d] ? o : 0) * TAPS * (uint32_t)row_bytes + lane_cb[ADMA + d];
+    }
+    bool row_ok[ADMA];
+#pragma unroll
+    for (int d = 0; d < ADMA; ++d) row_ok[d] = row0 + cw * (BM / 4) + RPI * d + lane / CH < n;
+    uint32_t rem = mask;
+    int ik = 0, iq = nq;
+    int pk = 0, pq = 0;
+    bool pvalid = false;
+    int32_t raw[ADMA];
+    uint32_t offs[DMA];
+    auto fetch = [&](int stage_index) {
+      pvalid = stage_index < total;
+      const bool adv = pvalid && iq >= nq;
+      const int nk = __builtin_ctz(rem | 0x80000000u);
+      ik = adv ? nk : ik;
+      rem = adv ? (rem & (rem - 1)) : rem;
+      iq = adv ? 0 : iq;
+      pk = ik;
+      pq = iq;
+      iq += pvalid ? 1 : 0;
+#pragma unroll
+      for (int d = 0; d < ADMA; ++d) {
+        const int r = cw * (BM / 4) + RPI * d + lane / CH;
+        if constexpr (TAPS == 27) {
+          raw[d] = s_nbr[r * 27 + pk];
+        } else {
+          raw[d] = (int32_t)(row0 + r);
+        }
+      }
+    };
+    auto make = [&]() {
+      const uint32_t sq = (uint32_t)(pq * SL);
+      const uint32_t sb = (uint32_t)pk * (uint32_t)row_bytes + sq;
+      const int limit = pvalid ? row_bytes - (int)sq : 0;
+#pragma unroll
+      for (int d = 0; d < ADMA; ++d) {
+        const uint32_t o = (uint32_t)raw[d] * (uint32_t)row_bytes + sq + lane_cb[d];
+        const bool use = (raw[d] >= 0) & row_ok[d] & ((int)lane_cb[d] < limit);
+        offs[d] = use ? o : kOutOfRange;
+      }
+#pragma unroll
+      for (int d = 0; d < BDMA; ++d) {
+        const bool use = ok_b[d] & ((int)lane_cb[ADMA + d] < limit);
+        offs[ADMA + d] = use ? base_b[d] + sb : kOutOfRange;
+      }
+    };
+    auto issue = [&](unsigned char* base) {
+#pragma unroll
+      for (int d = 0; d < ADMA; ++d)
+        lds_dma16(rsrc_a, offs[d], lds_offset(base) + (uint32_t)((cw_u * (BM / 4) + RPI * d) * SL));
+#pragma unroll
+      for (int d = 0; d < BDMA; ++d)
+        lds_dma16(rsrc_b, offs[ADMA + d], lds_offset(base) + (uint32_t)((BM + cw_u * (BNP / 4) + RPI * d) * SL));
+    };
+#pragma unroll
+    for (int s0 = 0; s0 < NS; ++s0) {
+      fetch(s0);
+      make();
+      issue(ring + s0 * BUF);
+    }
+    fetch(NS);
+    wait_vmcnt<(NS - 1) * DMA>();
+    barrier_no_fence();
+    int slot = 0;
+    for (int st = 0; st < total; ++st) {
+      // Barrier st: this wave's loads of stage st + 1 have landed; afterwards slot st is free.
+      wait_vmcnt<(NS - 2) * DMA>();
+      barrier_no_fence();
+      make();
+      issue(ring + slot * BUF);
+      fetch(st + NS + 1);
+      slot = slot + 1 == NS ? 0 : slot + 1;
+    }
+    wait_vmcnt<0>();
+  } else {
+    // ---- compute waves: fragments of stage st + 1 are read during stage st.
+    const int swz = swz_of(lrow);
+    uint4 fa[2][KSTEPS][FM], fb[2][KSTEPS][FN];
+    auto read_stage = [&](auto SET, const unsigned char* buf) {
+      constexpr int t = decltype(SET)::value;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const int off = ((2 * kk + lk) ^ swz) << 4;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          fa[t][kk][i] = *reinterpret_cast<const uint4*>(buf + (wm * WTM + i * 32 + lrow) * SL + off);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
+          fb[t][kk][j] = *reinterpret_cast<const uint4*>(buf + (BM + wn * WTN + j * 32 + lrow) * SL + off);
+      }
+    };
+    auto multiply = [&](auto SET) {
+      constexpr int t = decltype(SET)::value;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lk + (v & 3) - pass * HALF;
-            stage[r * BN + wn * WTN + j * 32 + lrow] = from_float<D>(acc[i][j][v] + bcol[j]);
-          }
-    }
-    __syncthreads();
-    const int64_t rbase = row0 + pass * HALF;
-    if (args.vec_out) {
-      constexpr int CPR = BN * 2 / 16;
-      for (int idx = tid; idx < HALF * CPR; idx += kThreads) {
-        const int r = idx / CPR, c = idx - r * CPR;
-        const int64_t row = rbase + r;
-        const int col = o0 + c * 8;
-        if (row < n && col < cout)
-          *reinterpret_cast<uint4*>(out + row * cout + col) = *reinterpret_cast<const uint4*>(stage + r * BN + c * 8);
+      for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<D>(fb[t][kk][j], fa[t][kk][i], acc[i][j]);
+    };
+    auto interleave = [&]() {
+#pragma unroll
+      for (int g = 0; g < KSTEPS * FM * FN; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
       }
-    } else {
-      for (int idx = tid; idx < HALF * BN; idx += kThreads) {
-        const int r = idx / BN, c = idx - r * BN;
-        const int64_t row = rbase + r;
-        if (row < n && o0 + c < cout) out[row * cout + o0 + c] = stage[r * BN + c];
-      }
+    };
+    barrier_no_fence();  // stage 0 has landed
+    read_stage(IC<0>{}, ring);
+    int st = 0, slot = 0;
+    auto step = [&](auto SET) {
+      constexpr int t = decltype(SET)::value;
+      const int next_slot = slot + 1 == NS ? 0 : slot + 1;
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkmcnt0();
+      barrier_no_fence();  // barrier st: stage st + 1 in LDS; this wave is done with slot st
+      __builtin_amdgcn_sched_barrier(0);
+      read_stage(IC<1 - t>{}, ring + next_slot * BUF);
+      multiply(IC<t>{});
+      interleave();
+      slot = next_slot;
+      ++st;
+    };
+    while (st + 1 < total) {
+      step(IC<0>{});
+      step(IC<1>{});
     }
-    __syncthreads();
+    if (st < total) step(IC<0>{});
+    __builtin_amdgcn_sched_barrier(0);
   }
+  __syncthreads();
+
+  // Epilogue: compute waves stage + bias, one rounding; all 512 threads store.
+  epilogue_store<D, WM, FM, FN, kWsThreads>(args, acc, ring, s_bias, row0, o0, tid, !loader, wm, wn, lane);
+}
+
+template <DT D, int WM, int FM, int FN, int SL, int TAPS>
+hipError_t launch_ws(const ConvArgs& a0, hipStream_t stream) {
+  using Sh = MmaShape<WM, FM, FN, SL, TAPS>;
+  ConvArgs a = a0;
+  a.tiles_m = (int)((a.n + Sh::BM - 1) / Sh::BM);
+  a.per_xcd = (a.tiles_m + 7) / 8;
+  dim3 grid((unsigned)(8 * a.per_xcd), (unsigned)((a.cout + Sh::BN - 1) / Sh::BN));
+  subm_conv_ws_kernel<D, WM, FM, FN, SL, TAPS><<<grid, kWsThreads, 0, stream>>>(a);
+  return hipGetLastError();
 }
 
 template <DT D, int WM, int FM, int FN, int SL, int TAPS>
@@ -779,6 +1069,9 @@ constexpr MmaTile kTiles[] = {
     {"r128c64s64", 2, 2, 1, 64},
     // 32 output channels per tile
     {"r256c32s64", 4, 2, 1, 64},    {"r128c32s64", 4, 1, 1, 64},
+    // warp-specialised (separate load waves)
+    {"ws256c128s64", 4, 2, 4, 64},  {"ws192c128s64", 2, 3, 2, 64}, {"ws256c128s64b", 2, 4, 2, 64},
+    {"ws384c64s64", 4, 3, 2, 64},   {"ws512c64s64", 4, 4, 2, 64},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -796,44 +1089,52 @@ hipError_t launch_tile_index(int t, const ConvArgs& a, hipStream_t stream) {
     case 8: return launch_mma<D, 4, 3, 2, 64, TAPS>(a, stream);
     case 9: return launch_mma<D, 2, 2, 1, 64, TAPS>(a, stream);
     case 10: return launch_mma<D, 4, 2, 1, 64, TAPS>(a, stream);
-    default: return launch_mma<D, 4, 1, 1, 64, TAPS>(a, stream);
+    case 11: return launch_mma<D, 4, 1, 1, 64, TAPS>(a, stream);
+    case 12: return launch_ws<D, 4, 2, 4, 64, TAPS>(a, stream);
+    case 13: return launch_ws<D, 2, 3, 2, 64, TAPS>(a, stream);
+    case 14: return launch_ws<D, 2, 4, 2, 64, TAPS>(a, stream);
+    case 15: return launch_ws<D, 4, 3, 2, 64, TAPS>(a, stream);
+    default: return launch_ws<D, 4, 4, 2, 64, TAPS>(a, stream);
   }
 }
 
-// Estimated time of a launch: whole rounds of tiles over the 256 compute units, times a
-// per-tile cost of stages x cycles per stage (the larger of the matrix-core time at the ~80 %
-// the loop sustains and the load time at ~35 bytes per clock per compute unit) plus a fixed
-// per-tile cost (rulebook copy, prologue, epilogue).
+// Tile choice.  A launch costs whole rounds of tiles over the 256 compute units; a round of
+// larger tiles takes longer, by the ratio measured for the warp-specialised kernel (bf16, shell
+// and dense workloads): 256 vs 192 rows at 128 output channels 1.18x; 512 vs 384 rows at 64
+// output channels 1.26x with 128 input channels and 1.40x with fewer (fewer stages per tile,
+// and the 512-row ring holds only two stages).
 constexpr int kComputeUnits = 256;
-inline double mma_cost(int64_t n, int cout, int cin_bytes, const MmaTile& t) {
-  const int bm = 32 * t.fm * t.wm, bn = 32 * t.fn * (4 / t.wm);
+inline int64_t launch_rounds(int64_t n, int cout, int bm, int bn) {
   const int64_t tiles = (n + bm - 1) / bm * ((cout + bn - 1) / bn);
-  const int64_t rounds = (tiles + kComputeUnits - 1) / kComputeUnits;
-  const double stages = 27.0 * ((cin_bytes + t.sl - 1) / t.sl);
-  const double mfma = (double)bm * bn * (t.sl / 2) * 2.0 / (4 * 1024.0 * 4.0) / 0.8;
-  const double load = (double)(bm + bn) * t.sl / 35.0;
-  return (double)rounds * (stages * ((mfma > load ? mfma : load) + 60.0) + 6000.0);
+  return (tiles + kComputeUnits - 1) / kComputeUnits;
+}
+
+int tile_index(const char* name) {
+  for (int t = 0; t < kNumTiles; ++t)
+    if (std::strcmp(name, kTiles[t].name) == 0) return t;
+  return -1;
 }
 
 template <DT D, int TAPS>
 hipError_t launch_mma_auto(const ConvArgs& a, hipStream_t stream) {
-  // Candidate tiles: the column width that covers Cout in one tile where possible.
-  const int want_bn = a.cout > 64 ? 128 : (a.cout > 32 ? 64 : 32);
-  int best = -1;
-  double best_cost = 0.0;
-  for (int t = 0; t < kNumTiles; ++t) {
-    const int bn = 32 * kTiles[t].fn * (4 / kTiles[t].wm);
-    if (bn != want_bn) continue;
-    const double c = mma_cost(a.n, a.cout, a.row_bytes, kTiles[t]);
-    if (best < 0 || c < best_cost) {
-      best = t;
-      best_cost = c;
-    }
+  int best;
+  if (a.cout > 64) {
+    const double r192 = (double)launch_rounds(a.n, a.cout, 192, 128);
+    const double r256 = 1.18 * (double)launch_rounds(a.n, a.cout, 256, 128);
+    best = tile_index(r256 < r192 ? "ws256c128s64b" : "ws192c128s64");
+  } else if (a.cout > 32) {
+    const double r384 = (double)launch_rounds(a.n, a.cout, 384, 64);
+    const double r512 = (a.row_bytes >= 256 ? 1.26 : 1.40) * (double)launch_rounds(a.n, a.cout, 512, 64);
+    best = tile_index(r512 < r384 ? "ws512c64s64" : "ws384c64s64");
+  } else {
+    const int64_t r128 = launch_rounds(a.n, a.cout, 128, 32);
+    const int64_t r256 = launch_rounds(a.n, a.cout, 256, 32);
+    best = tile_index(2 * r256 <= r128 + 1 ? "r256c32s64" : "r128c32s64");
   }
   // SUBMCONV_TILE=<name> forces a tile configuration (tuning and tests).
   if (const char* env = std::getenv("SUBMCONV_TILE")) {
-    for (int t = 0; t < kNumTiles; ++t)
-      if (std::strcmp(env, kTiles[t].name) == 0) best = t;
+    const int t = tile_index(env);
+    if (t >= 0) best = t;
   }
   return launch_tile_index<D, TAPS>(best, a, stream);
 }

@@ -17,19 +17,22 @@
 //         axis' extent (max - min) is at most 65534, which the build enforces.
 //
 // The structure is chosen on the device from the set's bounds, so the whole build needs one
-// host synchronisation (to read the error flags and counts at the end).
+// host synchronisation (to read the error flags and counts at the end), and no structure is
+// ever cleared in full: the table area is all 0xFF bytes between builds (an empty cell is -1
+// and an empty slot is key ~0, row -1), and every build resets exactly what it wrote.
 //
 // Kernels, all on the caller's stream:
-//   map_bounds_kernel   per-block min/max of (b, z, y, x) and the batch-range flag -> partials
-//   map_clear_kernel    every block reduces the partials (same result everywhere), picks the
-//                       structure; block 0 publishes the plan and zeroes the counters; all
-//                       blocks clear the chosen structure
-//   map_insert_kernel   GRID: CAS the row into its cell; HASH: CAS the key into the table.
-//                       A cell or key already taken by another row raises the duplicate flag.
+//   map_bounds_kernel   per-block min/max of (b, z, y, x) and the batch-range flag -> partials;
+//                       the last block to finish reduces the partials, picks the structure,
+//                       publishes the plan and zeroes the counters
+//   map_insert_kernel   GRID: CAS the row into its cell; HASH: CAS the key into the table.  A
+//                       cell or key already taken by another row raises the duplicate flag.
 //   map_lookup_kernel   one thread per voxel: 27 loads (GRID) or 27 probe sequences (HASH), nine
 //                       in flight at a time; the block's rows are staged in LDS and written as
 //                       one contiguous run of nbr; per-row 27-bit hit mask; hits counted per tap
 //                       with wave ballots and added to one of 16 counter banks
+//   map_reset_kernel    GRID: -1 back into every voxel's cell; HASH: the used slots emptied;
+//                       block 0 copies the statistics to pinned host memory
 #include "internal.h"
 
 namespace submconv {
@@ -38,7 +41,8 @@ namespace {
 constexpr unsigned long long kEmptyKey = ~0ull;
 constexpr int kThreads = 256;
 constexpr int kMaxBoundsBlocks = 256;
-constexpr int kMaxClearBlocks = 1024;
+constexpr int kMaxWideBlocks = 1024;
+constexpr int kMaxInsertBlocks = 8192;
 
 struct __align__(16) Slot {
   unsigned long long key;
@@ -88,8 +92,14 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
 }
 
 // ------------------------------------------------------------------ bounds
+__device__ void publish_plan(const BoundsPartial* __restrict__ partials, int nparts, int64_t grid_budget_cells,
+                             int64_t slots, int mode_request, MapStats* __restrict__ st);
+
 __global__ __launch_bounds__(kThreads) void map_bounds_kernel(const int32_t* __restrict__ coords, int64_t n,
-                                                              BoundsPartial* __restrict__ partials) {
+                                                              BoundsPartial* __restrict__ partials,
+                                                              int64_t grid_budget_cells, int64_t slots,
+                                                              int mode_request, MapStats* __restrict__ st) {
+  __shared__ bool s_last;
   int mn[4] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX};
   int mx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
   uint32_t flags = 0;
@@ -132,155 +142,182 @@ __global__ __launch_bounds__(kThreads) void map_bounds_kernel(const int32_t* __r
     for (int w = 0; w < kThreads / 64; ++w) f |= sfl[w];
     partials[blockIdx.x].flags = f;
   }
+  // The last block to finish (a few hundred blocks at most, so the counter is cheap) turns the
+  // partials into the plan for the later kernels.
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(&st->bounds_done, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (s_last) {
+    __threadfence();
+    publish_plan(partials, gridDim.x, grid_budget_cells, slots, mode_request, st);
+  }
 }
 
-// ------------------------------------------------------------------ plan + clear
-__global__ __launch_bounds__(kThreads) void map_clear_kernel(const BoundsPartial* __restrict__ partials, int nparts,
-                                                             int64_t n, int64_t grid_budget_cells, int64_t slots,
-                                                             int mode_request, void* __restrict__ table,
-                                                             MapStats* __restrict__ st) {
-  // Every block reduces the (few) partials itself, so all blocks agree on the plan without
-  // another launch.
+// ------------------------------------------------------------------ plan + insert
+// The plan: bounds reduced from the partials, range checks, structure choice and strides.
+struct Plan {
+  int32_t mn[4];
+  uint32_t flags;
+  int mode;
+  int64_t cells, sy, sz, sb;
+};
+
+// Every block reduces the (few) partials itself, so all blocks agree on the plan without
+// another launch.
+__device__ void reduce_plan(const BoundsPartial* __restrict__ partials, int nparts, int64_t grid_budget_cells,
+                            int mode_request, Plan& plan, int32_t (&mx_out)[4]) {
   __shared__ int s_mn[4], s_mx[4];
   __shared__ uint32_t s_fl;
+  __shared__ int rmn[kThreads / 64][4], rmx[kThreads / 64][4];
+  __shared__ uint32_t rfl[kThreads / 64];
   const int t = threadIdx.x;
-  {
-    int mn[4] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX};
-    int mx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
-    uint32_t fl = 0;
-    for (int p = t; p < nparts; p += kThreads) {
-      const BoundsPartial q = partials[p];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        mn[a] = min(mn[a], q.mn[a]);
-        mx[a] = max(mx[a], q.mx[a]);
-      }
-      fl |= q.flags;
-    }
-    __shared__ int rmn[kThreads / 64][4], rmx[kThreads / 64][4];
-    __shared__ uint32_t rfl[kThreads / 64];
-    const int wave = t / 64, lane = t % 64;
+  int mn[4] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX};
+  int mx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
+  uint32_t fl = 0;
+  for (int p = t; p < nparts; p += kThreads) {
+    // Written by other blocks of this kernel: read past the (non-coherent) L1.
+    const int32_t* q = reinterpret_cast<const int32_t*>(partials + p);
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int lo = wave_min(mn[a]);
-      const int hi = wave_max(mx[a]);
-      if (lane == 0) {
-        rmn[wave][a] = lo;
-        rmx[wave][a] = hi;
-      }
+      mn[a] = min(mn[a], __hip_atomic_load(q + a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      mx[a] = max(mx[a], __hip_atomic_load(q + 4 + a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     }
-    fl = wave_or(fl);
-    if (lane == 0) rfl[wave] = fl;
-    __syncthreads();
-    if (t < 4) {
-      int lo = rmn[0][t], hi = rmx[0][t];
-      for (int w = 1; w < kThreads / 64; ++w) {
-        lo = min(lo, rmn[w][t]);
-        hi = max(hi, rmx[w][t]);
-      }
-      s_mn[t] = lo;
-      s_mx[t] = hi;
-    }
-    if (t == 0) {
-      uint32_t f = 0;
-      for (int w = 0; w < kThreads / 64; ++w) f |= rfl[w];
-      s_fl = f;
-    }
-    __syncthreads();
+    fl |= (uint32_t)__hip_atomic_load(q + 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  // Plan (identical in every block).
+  const int wave = t / 64, lane = t % 64;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int lo = wave_min(mn[a]);
+    const int hi = wave_max(mx[a]);
+    if (lane == 0) {
+      rmn[wave][a] = lo;
+      rmx[wave][a] = hi;
+    }
+  }
+  fl = wave_or(fl);
+  if (lane == 0) rfl[wave] = fl;
+  __syncthreads();
+  if (t < 4) {
+    int lo = rmn[0][t], hi = rmx[0][t];
+    for (int w = 1; w < kThreads / 64; ++w) {
+      lo = min(lo, rmn[w][t]);
+      hi = max(hi, rmx[w][t]);
+    }
+    s_mn[t] = lo;
+    s_mx[t] = hi;
+  }
+  if (t == 0) {
+    uint32_t f = 0;
+    for (int w = 0; w < kThreads / 64; ++w) f |= rfl[w];
+    s_fl = f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    plan.mn[a] = s_mn[a];
+    mx_out[a] = s_mx[a];
+  }
   uint32_t flags = s_fl;
   const int64_t ext_b = (int64_t)s_mx[0] - s_mn[0] + 1;
   const int64_t ext_z = (int64_t)s_mx[1] - s_mn[1];
   const int64_t ext_y = (int64_t)s_mx[2] - s_mn[2];
   const int64_t ext_x = (int64_t)s_mx[3] - s_mn[3];
   if (ext_z > SUBM_MAX_EXTENT || ext_y > SUBM_MAX_EXTENT || ext_x > SUBM_MAX_EXTENT) flags |= kFlagExtentRange;
-  int mode = kModeHash;
-  int64_t cells = 0, sx = 1, sy = 0, sz = 0, sb = 0;
+  plan.mode = kModeHash;
+  plan.cells = 0;
+  plan.sy = plan.sz = plan.sb = 0;
   if ((flags & (kFlagBatchRange | kFlagExtentRange)) != 0) {
-    mode = kModeNone;
+    plan.mode = kModeNone;
   } else {
     const int64_t gx = ext_x + 3, gy = ext_y + 3, gz = ext_z + 3;
-    sy = gx;
-    sz = gx * gy;
-    sb = sz * gz;
+    plan.sy = gx;
+    plan.sz = gx * gy;
+    plan.sb = plan.sz * gz;
     // ext_b <= 65535 and each g <= 65537, so compare in steps to avoid overflow.
-    const bool small = sb <= grid_budget_cells && ext_b <= grid_budget_cells / sb;
-    cells = small ? sb * ext_b : 0;
-    if (mode_request == SUBM_MAP_GRID && small) mode = kModeGrid;
-    else if (mode_request == SUBM_MAP_AUTO && small) mode = kModeGrid;
-    else mode = kModeHash;
+    const bool small = plan.sb <= grid_budget_cells && ext_b <= grid_budget_cells / plan.sb;
+    plan.cells = small ? plan.sb * ext_b : 0;
+    plan.mode = (small && mode_request != SUBM_MAP_HASH) ? kModeGrid : kModeHash;
   }
-  if (blockIdx.x == 0) {
-    if (t < 4) {
-      st->mn[t] = s_mn[t];
-      st->mx[t] = s_mx[t];
-    }
-    if (t == 0) {
-      st->flags = flags;
-      st->mode = mode;
-      st->cells = cells;
-      st->slots = slots;
-      st->sy = sy;
-      st->sz = sz;
-      st->sb = sb;
-    }
-    for (int k = t; k < kTapBanks * 27; k += kThreads) (&st->tap_counts[0][0])[k] = 0;
-  }
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  if (mode == kModeGrid) {
-    int4* g4 = static_cast<int4*>(table);
-    const int64_t n4 = (cells + 3) / 4;
-    const int4 m1 = make_int4(-1, -1, -1, -1);
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + t; i < n4; i += stride) g4[i] = m1;
-  } else if (mode == kModeHash) {
-    Slot* tab = static_cast<Slot*>(table);
-    const Slot empty = {kEmptyKey, -1, 0};
-    for (int64_t s = (int64_t)blockIdx.x * kThreads + t; s < slots; s += stride) tab[s] = empty;
-  }
+  plan.flags = flags;
 }
 
-// ------------------------------------------------------------------ insert
+__device__ __forceinline__ int64_t grid_cell(const int32_t (&mn)[4], int64_t sb, int64_t sz, int64_t sy, int b, int z,
+                                             int y, int x) {
+  return (int64_t)(b - mn[0]) * sb + (int64_t)(z - mn[1] + 1) * sz + (int64_t)(y - mn[2] + 1) * sy +
+         (int64_t)(x - mn[3] + 1);
+}
 __device__ __forceinline__ int64_t grid_cell(const MapStats& p, int b, int z, int y, int x) {
-  return (int64_t)(b - p.mn[0]) * p.sb + (int64_t)(z - p.mn[1] + 1) * p.sz + (int64_t)(y - p.mn[2] + 1) * p.sy +
-         (int64_t)(x - p.mn[3] + 1);
+  return grid_cell(p.mn, p.sb, p.sz, p.sy, b, z, y, x);
+}
+
+__device__ void publish_plan(const BoundsPartial* __restrict__ partials, int nparts, int64_t grid_budget_cells,
+                             int64_t slots, int mode_request, MapStats* __restrict__ st) {
+  Plan plan;
+  int32_t mx[4];
+  reduce_plan(partials, nparts, grid_budget_cells, mode_request, plan, mx);
+  const int t = threadIdx.x;
+  if (t < 4) {
+    st->mn[t] = plan.mn[t];
+    st->mx[t] = mx[t];
+  }
+  if (t == 0) {
+    st->flags = plan.flags;
+    st->err_flags = 0;
+    st->mode = plan.mode;
+    st->cells = plan.cells;
+    st->slots = slots;
+    st->sy = plan.sy;
+    st->sz = plan.sz;
+    st->sb = plan.sb;
+    st->bounds_done = 0;  // ready for the next build
+  }
+  for (int k = t; k < kTapBanks * 27; k += kThreads) (&st->tap_counts[0][0])[k] = 0;
 }
 
 __global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __restrict__ coords, int64_t n,
                                                               void* __restrict__ table, MapStats* __restrict__ st) {
-  const int mode = st->mode;
-  if (mode == kModeNone) return;
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n) return;
-  const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
+  Plan plan;
+  plan.mode = st->mode;
+  if (plan.mode == kModeNone) return;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) plan.mn[a] = st->mn[a];
+  plan.sb = st->sb;
+  plan.sz = st->sz;
+  plan.sy = st->sy;
+  const int64_t slots = st->slots;
+  const int t = threadIdx.x;
   bool dup = false, overflow = false;
-  if (mode == kModeGrid) {
-    int32_t* grid = static_cast<int32_t*>(table);
-    const int64_t cell = grid_cell(*st, c.x, c.y, c.z, c.w);
-    dup = atomicCAS(&grid[cell], -1, (int32_t)i) != -1;
-  } else {
-    Slot* tab = static_cast<Slot*>(table);
-    const unsigned long long slots = (unsigned long long)st->slots;
-    const unsigned long long key = pack_key(c.x, c.y, c.z, c.w);
-    unsigned long long s = home_slot(key, slots);
-    overflow = true;
-    for (unsigned long long probe = 0; probe < slots; ++probe) {
-      const unsigned long long prev = atomicCAS(&tab[s].key, kEmptyKey, key);
-      if (prev == kEmptyKey) {
-        tab[s].val = (int32_t)i;
-        overflow = false;
-        break;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + t; i < n; i += (int64_t)gridDim.x * kThreads) {
+    const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
+    if (plan.mode == kModeGrid) {
+      int32_t* grid = static_cast<int32_t*>(table);
+      const int64_t cell = grid_cell(plan.mn, plan.sb, plan.sz, plan.sy, c.x, c.y, c.z, c.w);
+      dup |= atomicCAS(&grid[cell], -1, (int32_t)i) != -1;
+    } else {
+      Slot* tab = static_cast<Slot*>(table);
+      const unsigned long long key = pack_key(c.x, c.y, c.z, c.w);
+      unsigned long long s = home_slot(key, (unsigned long long)slots);
+      bool placed = false;
+      for (unsigned long long probe = 0; probe < (unsigned long long)slots; ++probe) {
+        const unsigned long long prev = atomicCAS(&tab[s].key, kEmptyKey, key);
+        if (prev == kEmptyKey) {
+          tab[s].val = (int32_t)i;
+          placed = true;
+          break;
+        }
+        if (prev == key) {
+          dup = true;
+          placed = true;
+          break;
+        }
+        s = (s + 1 == (unsigned long long)slots) ? 0 : s + 1;
       }
-      if (prev == key) {
-        dup = true;
-        overflow = false;
-        break;
-      }
-      s = (s + 1 == slots) ? 0 : s + 1;
+      overflow |= !placed;
     }
   }
-  if (dup) atomicOr(&st->flags, kFlagDuplicate);
-  if (overflow) atomicOr(&st->flags, kFlagProbeOverflow);
+  if (dup) atomicOr(&st->err_flags, kFlagDuplicate);
+  if (overflow) atomicOr(&st->err_flags, kFlagProbeOverflow);
 }
 
 // ------------------------------------------------------------------ lookup
@@ -371,6 +408,39 @@ __global__ __launch_bounds__(kThreads) void map_lookup_kernel(const int32_t* __r
   if (t < 27 && s_cnt[t] != 0) atomicAdd(&st->tap_counts[blockIdx.x % kTapBanks][t], s_cnt[t]);
 }
 
+// ------------------------------------------------------------------ reset
+// Restores the all-0xFF table area: -1 into every voxel's cell (GRID) or every used slot
+// emptied (HASH, where the probe sequences rule out emptying slots one key at a time).  Block 0
+// also copies the statistics, final once the lookup has completed, to the pinned host buffer,
+// so the host needs no separate copy.
+__global__ __launch_bounds__(kThreads) void map_reset_kernel(const int32_t* __restrict__ coords, int64_t n,
+                                                             void* __restrict__ table,
+                                                             const MapStats* __restrict__ st,
+                                                             uint32_t* __restrict__ host_stats) {
+  if (blockIdx.x == 0) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(st);
+    for (int w = threadIdx.x; w < (int)(sizeof(MapStats) / 4); w += kThreads) host_stats[w] = src[w];
+  }
+  const int mode = st->mode;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  if (mode == kModeGrid) {
+    int32_t* grid = static_cast<int32_t*>(table);
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+      const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
+      grid[grid_cell(*st, c.x, c.y, c.z, c.w)] = -1;
+    }
+  } else if (mode == kModeHash) {
+    int4* tab = static_cast<int4*>(table);
+    const int4 ff = make_int4(-1, -1, -1, -1);
+    for (int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x; s < st->slots; s += stride) tab[s] = ff;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void fill_kernel(int4* __restrict__ p, int64_t n16, int value) {
+  const int4 v = make_int4(value, value, value, value);
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += (int64_t)gridDim.x * kThreads) p[i] = v;
+}
+
 int clamp_blocks(int64_t b, int64_t cap) { return (int)(b < 1 ? 1 : (b > cap ? cap : b)); }
 
 }  // namespace
@@ -389,18 +459,28 @@ size_t map_table_bytes(int64_t n) {
 size_t map_partials_bytes(int64_t n) { return (size_t)map_bounds_blocks(n) * sizeof(BoundsPartial); }
 
 hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, void* table, void* partials,
-                            int32_t* nbr, uint32_t* masks, MapStats* stats, hipStream_t stream) {
+                            int32_t* nbr, uint32_t* masks, MapStats* stats, MapStats* host_stats,
+                            hipStream_t stream) {
   BoundsPartial* parts = static_cast<BoundsPartial*>(partials);
   const int nb = map_bounds_blocks(n);
   const int64_t slots = map_hash_slots(n);
   const int64_t budget = map_grid_budget_cells(n);
-  const int64_t clear_items = budget / 4 > slots ? budget / 4 : slots;  // 16-byte stores
-  map_bounds_kernel<<<nb, kThreads, 0, stream>>>(coords, n, parts);
-  map_clear_kernel<<<clamp_blocks((clear_items + 4 * kThreads - 1) / (4 * kThreads), kMaxClearBlocks), kThreads, 0, stream>>>(
-      parts, nb, n, budget, slots, mode_request, table, stats);
-  map_insert_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, stream>>>(coords, n, table, stats);
+  // One voxel per insert thread (each CAS is a full round trip), up to kMaxInsertBlocks blocks.
+  const int insert_blocks = clamp_blocks((n + kThreads - 1) / kThreads, kMaxInsertBlocks);
+  map_bounds_kernel<<<nb, kThreads, 0, stream>>>(coords, n, parts, budget, slots, mode_request, stats);
+  map_insert_kernel<<<insert_blocks, kThreads, 0, stream>>>(coords, n, table, stats);
   map_lookup_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, stream>>>(coords, n, table, nbr,
                                                                                        masks, stats);
+  const int64_t reset_items = n > slots ? n : slots;
+  map_reset_kernel<<<clamp_blocks((reset_items + 4 * kThreads - 1) / (4 * kThreads), kMaxWideBlocks), kThreads, 0,
+                     stream>>>(coords, n, table, stats, reinterpret_cast<uint32_t*>(host_stats));
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(void* p, size_t bytes, uint32_t value, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  fill_kernel<<<clamp_blocks((n16 + 4 * kThreads - 1) / (4 * kThreads), kMaxWideBlocks), kThreads, 0, stream>>>(
+      static_cast<int4*>(p), n16, (int)value);
   return hipGetLastError();
 }
 

@@ -46,8 +46,10 @@ constexpr uint32_t kFlagExtentRange = 8u;
 struct MapStats {
   int32_t mn[4];       // per-column minimum of (b, z, y, x)
   int32_t mx[4];       // per-column maximum
-  uint32_t flags;      // kFlag* bits
+  uint32_t flags;      // kFlag* bits of the plan (coordinate ranges)
+  uint32_t err_flags;  // kFlag* bits raised while inserting (duplicates, probe overflow)
   int32_t mode;        // kMode*
+  uint32_t bounds_done;  // bounds blocks finished (the last one publishes the plan and resets it)
   int64_t cells;       // GRID: number of cells
   int64_t slots;       // HASH: number of slots
   int64_t sy, sz, sb;  // GRID strides of y, z and the batch slab (x stride is 1)
@@ -66,14 +68,21 @@ struct MapData {
 };
 
 // Map build (indice_map.hip).  Enqueues on `stream`; does not synchronise.  `table` holds
-// map_table_bytes(n), `partials` map_partials_bytes(n), `stats` one MapStats (all device).
+// map_table_bytes(n) and must be all 0xFF bytes on entry (it is again on completion: the build
+// resets what it wrote); `partials` holds map_partials_bytes(n), `stats` one MapStats (device).
+// The statistics end up in `host_stats` (device-visible pinned host memory) when the last
+// kernel completes.
 int64_t map_hash_slots(int64_t n);
 int64_t map_grid_budget_cells(int64_t n);
 int map_bounds_blocks(int64_t n);
 size_t map_table_bytes(int64_t n);
 size_t map_partials_bytes(int64_t n);
 hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, void* table, void* partials,
-                            int32_t* nbr, uint32_t* masks, MapStats* stats, hipStream_t stream);
+                            int32_t* nbr, uint32_t* masks, MapStats* stats, MapStats* host_stats,
+                            hipStream_t stream);
+// Fill `bytes` bytes at `p` (16-byte aligned, bytes a multiple of 16) with `value` (each 32-bit
+// word).
+hipError_t launch_fill(void* p, size_t bytes, uint32_t value, hipStream_t stream);
 
 // Convolution launcher (conv.hip).  Arguments already validated by the caller.
 hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, int cout, int dtype,

@@ -116,7 +116,14 @@ struct Workspace {
 };
 Workspace g_workspace[kMaxDevices];
 
-Status workspace_reserve(Workspace& ws, size_t bytes) {
+// Layout: [statistics | bounds partials | table area].  The table area is all 0xFF bytes
+// whenever no build is running (each build resets what it wrote), so a new allocation is filled.
+constexpr size_t kStatsBytes = 4096;
+constexpr size_t kPartialsBytes = 65536;
+static_assert(sizeof(MapStats) <= kStatsBytes, "statistics block");
+
+Status workspace_reserve(Workspace& ws, size_t table_bytes, hipStream_t stream) {
+  const size_t bytes = kStatsBytes + kPartialsBytes + table_bytes;
   if (ws.bytes >= bytes) return Status{};
   if (ws.ptr != nullptr) {
     SUBM_HIP_TRY(hipFree(ws.ptr));
@@ -127,18 +134,34 @@ Status workspace_reserve(Workspace& ws, size_t bytes) {
   const size_t want = (bytes + grain - 1) / grain * grain;
   SUBM_HIP_TRY(hipMalloc(&ws.ptr, want));
   ws.bytes = want;
+  // Statistics and partials start zeroed (the plan's completion counter lives there); the table
+  // area starts empty.
+  SUBM_HIP_TRY(launch_fill(ws.ptr, kStatsBytes + kPartialsBytes, 0u, stream));
+  SUBM_HIP_TRY(launch_fill(static_cast<unsigned char*>(ws.ptr) + kStatsBytes + kPartialsBytes,
+                           want - kStatsBytes - kPartialsBytes, 0xFFFFFFFFu, stream));
   return Status{};
 }
 
 // Per-thread pinned host buffer that receives the build statistics (one per device; a thread
-// runs one build at a time).  Pinned memory lets the device-to-host copy be a plain DMA.
-MapStats* pinned_stats(int dev) {
-  thread_local MapStats* bufs[kMaxDevices] = {};
-  if (dev < 0 || dev >= kMaxDevices) return nullptr;
-  if (bufs[dev] == nullptr) {
+// runs one build at a time).  The last lookup block writes it directly through its device
+// address, so the build needs no copy command.
+struct PinnedStats {
+  MapStats* host = nullptr;
+  MapStats* dev = nullptr;
+};
+PinnedStats pinned_stats(int dev) {
+  thread_local PinnedStats bufs[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return PinnedStats{};
+  if (bufs[dev].host == nullptr) {
     void* p = nullptr;
-    if (hipHostMalloc(&p, sizeof(MapStats), hipHostMallocDefault) != hipSuccess) return nullptr;
-    bufs[dev] = static_cast<MapStats*>(p);
+    void* d = nullptr;
+    if (hipHostMalloc(&p, sizeof(MapStats), hipHostMallocDefault) != hipSuccess) return PinnedStats{};
+    if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess) {
+      (void)hipHostFree(p);
+      return PinnedStats{};
+    }
+    bufs[dev].host = static_cast<MapStats*>(p);
+    bufs[dev].dev = static_cast<MapStats*>(d);
   }
   return bufs[dev];
 }
@@ -173,20 +196,23 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
     delete m;
     return fail(SUBM_ERR_HIP, "device ordinal out of range");
   }
-  MapStats* host = pinned_stats(m->d.device);
-  if (host == nullptr) {
+  const PinnedStats pinned = pinned_stats(m->d.device);
+  if (pinned.host == nullptr) {
     delete m;
     return fail(SUBM_ERR_OUT_OF_MEMORY, "pinned host buffer for the build statistics");
   }
+  MapStats* host = pinned.host;
 
   const size_t table_bytes = round_up(map_table_bytes(n), 256);
-  const size_t partial_bytes = round_up(map_partials_bytes(n), 256);
-  const size_t tmp_bytes = table_bytes + partial_bytes + sizeof(MapStats);
+  if (map_partials_bytes(n) > kPartialsBytes) {
+    delete m;
+    return fail(SUBM_ERR_HIP, "internal error: bounds partials exceed their workspace block");
+  }
 
   Workspace& ws = g_workspace[m->d.device];
   std::lock_guard<std::mutex> lock(ws.mu);
   void* nbr = nullptr;
-  Status s = workspace_reserve(ws, tmp_bytes);
+  Status s = workspace_reserve(ws, table_bytes, stream);
   if (s.ok()) s = device_alloc(&nbr, (size_t)n * 28 * sizeof(int32_t), stream);  // nbr [n,27] + masks [n]
   if (!s.ok()) {
     device_free(nbr, stream);
@@ -194,13 +220,13 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
     return fail(s);
   }
   unsigned char* base = static_cast<unsigned char*>(ws.ptr);
-  void* partials = base + table_bytes;
-  MapStats* dstats = reinterpret_cast<MapStats*>(base + table_bytes + partial_bytes);
+  MapStats* dstats = reinterpret_cast<MapStats*>(base);
+  void* partials = base + kStatsBytes;
+  void* table = base + kStatsBytes + kPartialsBytes;
 
   int32_t* nbr_rows = static_cast<int32_t*>(nbr);
   uint32_t* masks = reinterpret_cast<uint32_t*>(nbr_rows + (size_t)n * 27);
-  hipError_t e = launch_map_build(coords, n, mode, base, partials, nbr_rows, masks, dstats, stream);
-  if (e == hipSuccess) e = hipMemcpyAsync(host, dstats, sizeof(MapStats), hipMemcpyDeviceToHost, stream);
+  hipError_t e = launch_map_build(coords, n, mode, table, partials, nbr_rows, masks, dstats, pinned.dev, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) {
     device_free(nbr, stream);
@@ -208,18 +234,19 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
     return fail(hip_status(e, "indice map build"));
   }
   const MapStats& st = *host;
+  const uint32_t flags = st.flags | st.err_flags;
   int code = SUBM_OK;
   const char* msg = "";
-  if (st.flags & kFlagBatchRange) {
+  if (flags & kFlagBatchRange) {
     code = SUBM_ERR_COORD_RANGE;
     msg = "batch index outside [0, 65534]";
-  } else if (st.flags & kFlagExtentRange) {
+  } else if (flags & kFlagExtentRange) {
     code = SUBM_ERR_COORD_RANGE;
     msg = "extent (max - min) of z, y or x exceeds 65534";
-  } else if (st.flags & kFlagDuplicate) {
+  } else if (flags & kFlagDuplicate) {
     code = SUBM_ERR_DUPLICATE_COORD;
     msg = "two rows share the same (b, z, y, x)";
-  } else if (st.flags & kFlagProbeOverflow) {
+  } else if (flags & kFlagProbeOverflow) {
     code = SUBM_ERR_HIP;
     msg = "internal error: hash table full";
   }
