@@ -242,7 +242,14 @@ def main():
         achieved = bytes_launch / conv_s / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic}
-    kernel = "subm_conv_dma_kernel" if cfg.dtype in ("bf16", "f16") and cout > 16 else "subm_conv_generic_kernel"
+    # The kernel the library picks for this layer shape (16-bit storage: the warp-specialised
+    # matrix-core kernel above 32 output channels, the single-role one from 17 to 32).
+    if cfg.dtype in ("bf16", "f16") and cout > 32:
+        kernel = "subm_conv_ws_kernel"
+    elif cfg.dtype in ("bf16", "f16") and cout > 16:
+        kernel = "subm_conv_mma_kernel"
+    else:
+        kernel = "subm_conv_generic_kernel"
     roofline.update({"kernel": kernel, "avg_launch_ms": conv_ms, "launches": len(per_layer[dom]),
                      "algorithmic_flop_per_launch": flop_launch, "algorithmic_bytes_per_launch": bytes_launch})
 

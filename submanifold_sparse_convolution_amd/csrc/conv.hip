@@ -798,7 +798,10 @@ __global__ __launch_bounds__(kThreads, 1) void subm_conv_mma_kernel(const ConvAr
 // One workgroup barrier per stage hands ring slots between the two roles.
 constexpr int kWsThreads = 512;
 
-template <DT D, int WM, int FM, int FN, int SL, int TAPS>
+// KP selects how far ahead the compute waves read fragments: 0 = a whole stage (two register
+// sets of a stage), 1 = one 16-channel step (two sets of a step, so wider slices fit the
+// register budget of two waves per SIMD; the stage barrier then sits before the last step).
+template <DT D, int WM, int FM, int FN, int SL, int TAPS, int KP>
 __global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_kernel(const ConvArgs args) {
   using Sh = MmaShape<WM, FM, FN, SL, TAPS>;
   constexpr int WTM = Sh::WTM, WTN = Sh::WTN, BM = Sh::BM, BN = Sh::BN, BNP = Sh::BNP;
@@ -971,8 +974,66 @@ __global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_kernel(const ConvA
     }
     wait_vmcnt<0>();
   } else {
-    // ---- compute waves: fragments of stage st + 1 are read during stage st.
+    // ---- compute waves
     const int swz = swz_of(lrow);
+    if constexpr (KP == 1) {
+      // Fragments one 16-channel step ahead, in two register sets by step parity.
+      uint4 ga[2][FM], gb[2][FN];
+      auto read_step = [&](auto P, auto KK, const unsigned char* buf) {
+        constexpr int p = decltype(P)::value, kk = decltype(KK)::value;
+        const int off = ((2 * kk + lk) ^ swz) << 4;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          ga[p][i] = *reinterpret_cast<const uint4*>(buf + (wm * WTM + i * 32 + lrow) * SL + off);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          gb[p][j] = *reinterpret_cast<const uint4*>(buf + (BM + wn * WTN + j * 32 + lrow) * SL + off);
+      };
+      auto mul_step = [&](auto P) {
+        constexpr int p = decltype(P)::value;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<D>(gb[p][j], ga[p][i], acc[i][j]);
+      };
+      auto interleave_step = [&]() {
+#pragma unroll
+        for (int g = 0; g < FM * FN; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+        }
+      };
+      // Step kk of the stage in slot `cur` (not the last): read step kk + 1, multiply step kk.
+      auto inner = [&](auto KK, const unsigned char* cur) {
+        constexpr int kk = decltype(KK)::value;
+        if constexpr (kk < KSTEPS - 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          read_step(IC<(kk + 1) & 1>{}, IC<kk + 1>{}, cur);
+          mul_step(IC<kk & 1>{});
+          interleave_step();
+        }
+      };
+      barrier_no_fence();  // stage 0 has landed
+      read_step(IC<0>{}, IC<0>{}, ring);
+      int slot = 0;
+      for (int st = 0; st < total; ++st) {
+        const unsigned char* cur = ring + slot * BUF;
+        const int next_slot = slot + 1 == NS ? 0 : slot + 1;
+        inner(IC<0>{}, cur);
+        inner(IC<1>{}, cur);
+        inner(IC<2>{}, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkmcnt0();
+        barrier_no_fence();  // barrier st: stage st + 1 in LDS; this wave is done with slot st
+        __builtin_amdgcn_sched_barrier(0);
+        read_step(IC<KSTEPS & 1>{}, IC<0>{}, ring + next_slot * BUF);
+        mul_step(IC<(KSTEPS - 1) & 1>{});
+        interleave_step();
+        slot = next_slot;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+    // Fragments of stage st + 1 are read during stage st.
     uint4 fa[2][KSTEPS][FM], fb[2][KSTEPS][FN];
     auto read_stage = [&](auto SET, const unsigned char* buf) {
       constexpr int t = decltype(SET)::value;
@@ -1025,6 +1086,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_kernel(const ConvA
     }
     if (st < total) step(IC<0>{});
     __builtin_amdgcn_sched_barrier(0);
+    }
   }
   __syncthreads();
 
@@ -1032,14 +1094,14 @@ __global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_kernel(const ConvA
   epilogue_store<D, WM, FM, FN, kWsThreads>(args, acc, ring, s_bias, row0, o0, tid, !loader, wm, wn, lane);
 }
 
-template <DT D, int WM, int FM, int FN, int SL, int TAPS>
+template <DT D, int WM, int FM, int FN, int SL, int TAPS, int KP = 0>
 hipError_t launch_ws(const ConvArgs& a0, hipStream_t stream) {
   using Sh = MmaShape<WM, FM, FN, SL, TAPS>;
   ConvArgs a = a0;
   a.tiles_m = (int)((a.n + Sh::BM - 1) / Sh::BM);
   a.per_xcd = (a.tiles_m + 7) / 8;
   dim3 grid((unsigned)(8 * a.per_xcd), (unsigned)((a.cout + Sh::BN - 1) / Sh::BN));
-  subm_conv_ws_kernel<D, WM, FM, FN, SL, TAPS><<<grid, kWsThreads, 0, stream>>>(a);
+  subm_conv_ws_kernel<D, WM, FM, FN, SL, TAPS, KP><<<grid, kWsThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -1072,6 +1134,9 @@ constexpr MmaTile kTiles[] = {
     // warp-specialised (separate load waves)
     {"ws256c128s64", 4, 2, 4, 64},  {"ws192c128s64", 2, 3, 2, 64}, {"ws256c128s64b", 2, 4, 2, 64},
     {"ws384c64s64", 4, 3, 2, 64},   {"ws512c64s64", 4, 4, 2, 64},
+    // warp-specialised, fragments one step ahead
+    {"ws192c128s128k", 2, 3, 2, 128}, {"ws192c128s64k", 2, 3, 2, 64}, {"ws256c64s128k", 4, 2, 2, 128},
+    {"ws192c64s128k", 2, 3, 1, 128},
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -1094,15 +1159,19 @@ hipError_t launch_tile_index(int t, const ConvArgs& a, hipStream_t stream) {
     case 13: return launch_ws<D, 2, 3, 2, 64, TAPS>(a, stream);
     case 14: return launch_ws<D, 2, 4, 2, 64, TAPS>(a, stream);
     case 15: return launch_ws<D, 4, 3, 2, 64, TAPS>(a, stream);
-    default: return launch_ws<D, 4, 4, 2, 64, TAPS>(a, stream);
+    case 16: return launch_ws<D, 4, 4, 2, 64, TAPS>(a, stream);
+    case 17: return launch_ws<D, 2, 3, 2, 128, TAPS, 1>(a, stream);
+    case 18: return launch_ws<D, 2, 3, 2, 64, TAPS, 1>(a, stream);
+    case 19: return launch_ws<D, 4, 2, 2, 128, TAPS, 1>(a, stream);
+    default: return launch_ws<D, 2, 3, 1, 128, TAPS, 1>(a, stream);
   }
 }
 
-// Tile choice.  A launch costs whole rounds of tiles over the 256 compute units; a round of
-// larger tiles takes longer, by the ratio measured for the warp-specialised kernel (bf16, shell
-// and dense workloads): 256 vs 192 rows at 128 output channels 1.18x; 512 vs 384 rows at 64
-// output channels 1.26x with 128 input channels and 1.40x with fewer (fewer stages per tile,
-// and the 512-row ring holds only two stages).
+// Tile choice (bf16 on the shell, dense, ellipsoid and subdivided workloads, all tiles measured
+// side by side): above 64 output channels the warp-specialised 192 x 128 tile with 128-byte
+// slices and step-ahead fragments is fastest on every workload; from 33 to 64 channels the
+// 256 x 64 tile of the same kind.  Up to 32 channels, a 256-row tile when it saves rounds of
+// tiles over the 256 compute units.
 constexpr int kComputeUnits = 256;
 inline int64_t launch_rounds(int64_t n, int cout, int bm, int bn) {
   const int64_t tiles = (n + bm - 1) / bm * ((cout + bn - 1) / bn);
@@ -1119,13 +1188,9 @@ template <DT D, int TAPS>
 hipError_t launch_mma_auto(const ConvArgs& a, hipStream_t stream) {
   int best;
   if (a.cout > 64) {
-    const double r192 = (double)launch_rounds(a.n, a.cout, 192, 128);
-    const double r256 = 1.18 * (double)launch_rounds(a.n, a.cout, 256, 128);
-    best = tile_index(r256 < r192 ? "ws256c128s64b" : "ws192c128s64");
+    best = tile_index("ws192c128s128k");
   } else if (a.cout > 32) {
-    const double r384 = (double)launch_rounds(a.n, a.cout, 384, 64);
-    const double r512 = (a.row_bytes >= 256 ? 1.26 : 1.40) * (double)launch_rounds(a.n, a.cout, 512, 64);
-    best = tile_index(r512 < r384 ? "ws512c64s64" : "ws384c64s64");
+    best = tile_index("ws256c64s128k");
   } else {
     const int64_t r128 = launch_rounds(a.n, a.cout, 128, 32);
     const int64_t r256 = launch_rounds(a.n, a.cout, 256, 32);

@@ -22,9 +22,11 @@
 // and an empty slot is key ~0, row -1), and every build resets exactly what it wrote.
 //
 // Kernels, all on the caller's stream:
-//   map_bounds_kernel   per-block min/max of (b, z, y, x) and the batch-range flag -> partials;
-//                       the last block to finish reduces the partials, picks the structure,
-//                       publishes the plan and zeroes the counters
+//   map_bounds_kernel   per-block min/max of (b, z, y, x) and the batch-range flag -> partials
+//   map_plan_kernel     one block reduces the partials, picks the structure, publishes the plan
+//                       and zeroes the counters (a separate launch: signalling between blocks of
+//                       one kernel needs a device-scope fence, which writes back the whole L2 of
+//                       each XCD and costs far more than a launch)
 //   map_insert_kernel   GRID: CAS the row into its cell; HASH: CAS the key into the table.  A
 //                       cell or key already taken by another row raises the duplicate flag.
 //   map_lookup_kernel   one thread per voxel: 27 loads (GRID) or 27 probe sequences (HASH), nine
@@ -92,14 +94,8 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
 }
 
 // ------------------------------------------------------------------ bounds
-__device__ void publish_plan(const BoundsPartial* __restrict__ partials, int nparts, int64_t grid_budget_cells,
-                             int64_t slots, int mode_request, MapStats* __restrict__ st);
-
 __global__ __launch_bounds__(kThreads) void map_bounds_kernel(const int32_t* __restrict__ coords, int64_t n,
-                                                              BoundsPartial* __restrict__ partials,
-                                                              int64_t grid_budget_cells, int64_t slots,
-                                                              int mode_request, MapStats* __restrict__ st) {
-  __shared__ bool s_last;
+                                                              BoundsPartial* __restrict__ partials) {
   int mn[4] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX};
   int mx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
   uint32_t flags = 0;
@@ -142,16 +138,6 @@ __global__ __launch_bounds__(kThreads) void map_bounds_kernel(const int32_t* __r
     for (int w = 0; w < kThreads / 64; ++w) f |= sfl[w];
     partials[blockIdx.x].flags = f;
   }
-  // The last block to finish (a few hundred blocks at most, so the counter is cheap) turns the
-  // partials into the plan for the later kernels.
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&st->bounds_done, 1u) == gridDim.x - 1;
-  __syncthreads();
-  if (s_last) {
-    __threadfence();
-    publish_plan(partials, gridDim.x, grid_budget_cells, slots, mode_request, st);
-  }
 }
 
 // ------------------------------------------------------------------ plan + insert
@@ -176,14 +162,13 @@ __device__ void reduce_plan(const BoundsPartial* __restrict__ partials, int npar
   int mx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
   uint32_t fl = 0;
   for (int p = t; p < nparts; p += kThreads) {
-    // Written by other blocks of this kernel: read past the (non-coherent) L1.
-    const int32_t* q = reinterpret_cast<const int32_t*>(partials + p);
+    const BoundsPartial q = partials[p];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      mn[a] = min(mn[a], __hip_atomic_load(q + a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      mx[a] = max(mx[a], __hip_atomic_load(q + 4 + a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      mn[a] = min(mn[a], q.mn[a]);
+      mx[a] = max(mx[a], q.mx[a]);
     }
-    fl |= (uint32_t)__hip_atomic_load(q + 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    fl |= q.flags;
   }
   const int wave = t / 64, lane = t % 64;
 #pragma unroll
@@ -251,8 +236,9 @@ __device__ __forceinline__ int64_t grid_cell(const MapStats& p, int b, int z, in
   return grid_cell(p.mn, p.sb, p.sz, p.sy, b, z, y, x);
 }
 
-__device__ void publish_plan(const BoundsPartial* __restrict__ partials, int nparts, int64_t grid_budget_cells,
-                             int64_t slots, int mode_request, MapStats* __restrict__ st) {
+__global__ __launch_bounds__(kThreads) void map_plan_kernel(const BoundsPartial* __restrict__ partials, int nparts,
+                                                            int64_t grid_budget_cells, int64_t slots,
+                                                            int mode_request, MapStats* __restrict__ st) {
   Plan plan;
   int32_t mx[4];
   reduce_plan(partials, nparts, grid_budget_cells, mode_request, plan, mx);
@@ -270,7 +256,6 @@ __device__ void publish_plan(const BoundsPartial* __restrict__ partials, int npa
     st->sy = plan.sy;
     st->sz = plan.sz;
     st->sb = plan.sb;
-    st->bounds_done = 0;  // ready for the next build
   }
   for (int k = t; k < kTapBanks * 27; k += kThreads) (&st->tap_counts[0][0])[k] = 0;
 }
@@ -467,7 +452,8 @@ hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, 
   const int64_t budget = map_grid_budget_cells(n);
   // One voxel per insert thread (each CAS is a full round trip), up to kMaxInsertBlocks blocks.
   const int insert_blocks = clamp_blocks((n + kThreads - 1) / kThreads, kMaxInsertBlocks);
-  map_bounds_kernel<<<nb, kThreads, 0, stream>>>(coords, n, parts, budget, slots, mode_request, stats);
+  map_bounds_kernel<<<nb, kThreads, 0, stream>>>(coords, n, parts);
+  map_plan_kernel<<<1, kThreads, 0, stream>>>(parts, nb, budget, slots, mode_request, stats);
   map_insert_kernel<<<insert_blocks, kThreads, 0, stream>>>(coords, n, table, stats);
   map_lookup_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, stream>>>(coords, n, table, nbr,
                                                                                        masks, stats);

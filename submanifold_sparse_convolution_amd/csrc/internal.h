@@ -49,7 +49,7 @@ struct MapStats {
   uint32_t flags;      // kFlag* bits of the plan (coordinate ranges)
   uint32_t err_flags;  // kFlag* bits raised while inserting (duplicates, probe overflow)
   int32_t mode;        // kMode*
-  uint32_t bounds_done;  // bounds blocks finished (the last one publishes the plan and resets it)
+  uint32_t pad;
   int64_t cells;       // GRID: number of cells
   int64_t slots;       // HASH: number of slots
   int64_t sy, sz, sb;  // GRID strides of y, z and the batch slab (x stride is 1)

@@ -365,7 +365,8 @@ def test_shape_mismatch_and_alias_rejected():
 
 TILES = ["r192c128s128", "r192c128s64", "r128c128s64", "r256c128s64", "r384c128s64", "r256c128s128",
          "r192c64s128", "r256c64s64", "r384c64s64", "r128c64s64", "r256c32s64", "r128c32s64",
-         "ws256c128s64", "ws192c128s64", "ws256c128s64b", "ws384c64s64", "ws512c64s64"]
+         "ws256c128s64", "ws192c128s64", "ws256c128s64b", "ws384c64s64", "ws512c64s64",
+         "ws192c128s128k", "ws192c128s64k", "ws256c64s128k", "ws192c64s128k"]
 
 
 @pytest.mark.parametrize("tile", TILES)
