@@ -18,3 +18,4 @@ from .submconv_ref import (  # noqa: F401
     conv1,
     normwise_rel_error,
 )
+from . import structure_ref, norm_ref  # noqa: F401,E402
