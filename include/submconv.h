@@ -68,8 +68,11 @@ typedef enum {
 typedef enum {
   SUBM_MAP_AUTO = 0,  /* dense grid when the bounding box is small enough, else hash table */
   SUBM_MAP_HASH = 1,  /* always the hash table */
-  SUBM_MAP_GRID = 2   /* dense grid when it fits the grid budget (128 cells per voxel, at most
+  SUBM_MAP_GRID = 2,  /* dense grid when it fits the grid budget (128 cells per voxel, at most
                          2^29 cells), else hash */
+  SUBM_MAP_SUBDIVIDED = 3  /* reported only: the map was derived from a parent map by
+                              sparse_indice_map_subdivide (sparse_structure.h); not a build
+                              request */
 } subm_map_mode_t;
 
 #define SUBM_TAPS 27
@@ -105,7 +108,8 @@ int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int mode, hipSt
 
 /*
  * sparse_indice_map_mode -- the structure a built map used: SUBM_MAP_HASH or SUBM_MAP_GRID
- * (SUBM_MAP_HASH for an empty map).  *mode is a host int.
+ * (SUBM_MAP_HASH for an empty map), or SUBM_MAP_SUBDIVIDED for a map derived from a parent map.
+ * *mode is a host int.
  */
 int sparse_indice_map_mode(submconv_map_t map, int* mode);
 

@@ -16,11 +16,15 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsubmconv.so")
 
 SUBM_F32, SUBM_F16, SUBM_BF16 = 0, 1, 2
-SUBM_MAP_AUTO, SUBM_MAP_HASH, SUBM_MAP_GRID = 0, 1, 2
+SUBM_MAP_AUTO, SUBM_MAP_HASH, SUBM_MAP_GRID, SUBM_MAP_SUBDIVIDED = 0, 1, 2, 3
+SUBM_POOL_MAX, SUBM_POOL_MEAN = 1, 2
+SUBM_COARSE, SUBM_FINE, SUBM_PARENT = 0, 1, 2
+SUBM_SUBDIVIDE, SUBM_DOWNSAMPLE, SUBM_UPSAMPLE_MASKED = 0, 1, 2
 _DTYPE_CODES = {torch.float32: SUBM_F32, torch.float16: SUBM_F16, torch.bfloat16: SUBM_BF16}
 TAPS = 27
 
-# Exported C symbols (kept equal to the declarations in include/submconv.h).
+# Exported C symbols (kept equal to the declarations in include/*.h).  Every one but the last
+# two returns an int status.
 C_FUNCTIONS = (
     "sparse_indice_map_build",
     "sparse_indice_map_build_ex",
@@ -30,6 +34,18 @@ C_FUNCTIONS = (
     "sparse_indice_map_offset_counts",
     "sparse_indice_map_copy_nbr",
     "subm_conv3d_forward",
+    "sparse_subdivide",
+    "sparse_downsample_build",
+    "sparse_upsample_masked_build",
+    "sparse_subdivision_info",
+    "sparse_subdivision_kind",
+    "sparse_subdivision_coords",
+    "sparse_subdivision_parent",
+    "sparse_subdivision_copy",
+    "sparse_subdivision_free",
+    "sparse_downsample_forward",
+    "sparse_upsample_forward",
+    "sparse_indice_map_subdivide",
     "subm_status_string",
     "subm_last_error",
 )
@@ -69,7 +85,19 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.sparse_indice_map_offset_counts.argtypes = [vp, ctypes.POINTER(i64)]
         lib.sparse_indice_map_copy_nbr.argtypes = [vp, vp, vp]
         lib.subm_conv3d_forward.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp]
-        for name in C_FUNCTIONS[:8]:
+        lib.sparse_subdivide.argtypes = [vp, i64, vp, ctypes.POINTER(vp)]
+        lib.sparse_downsample_build.argtypes = [vp, i64, vp, ctypes.POINTER(vp)]
+        lib.sparse_upsample_masked_build.argtypes = [vp, vp, i64, vp, ctypes.POINTER(vp)]
+        lib.sparse_subdivision_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        lib.sparse_subdivision_kind.argtypes = [vp, ctypes.POINTER(ci)]
+        lib.sparse_subdivision_coords.argtypes = [vp, ci, ctypes.POINTER(vp)]
+        lib.sparse_subdivision_parent.argtypes = [vp, ctypes.POINTER(vp)]
+        lib.sparse_subdivision_copy.argtypes = [vp, ci, vp, vp]
+        lib.sparse_subdivision_free.argtypes = [vp]
+        lib.sparse_downsample_forward.argtypes = [vp, ci, ci, ci, vp, vp, vp]
+        lib.sparse_upsample_forward.argtypes = [vp, ci, ci, vp, vp, vp]
+        lib.sparse_indice_map_subdivide.argtypes = [vp, vp, vp, ctypes.POINTER(vp)]
+        for name in C_FUNCTIONS[:-2]:
             getattr(lib, name).restype = ci
         lib.subm_status_string.argtypes = [ci]
         lib.subm_status_string.restype = ctypes.c_char_p
@@ -246,3 +274,186 @@ def subm_conv3d_forward(m: IndiceMap | None, feats: torch.Tensor, weight: torch.
                                      weight.data_ptr(), bias_ptr, out.data_ptr(), _stream_ptr(stream, feats.device))
     _check(lib, "subm_conv3d_forward", st)
     return out
+
+
+# --------------------------------------------------------------------------- structure ops
+
+class Subdivision:
+    """Owner of one coarse / fine relation (sparse_subdivision_t): subdivide, downsample or masked
+    upsample structure."""
+
+    def __init__(self, handle: int, device: torch.device):
+        self._handle = handle
+        self.device = device
+        self.n_coarse, self.n_fine = sparse_subdivision_info(self)
+        self.kind = sparse_subdivision_kind(self)
+
+    @property
+    def handle(self) -> int:
+        if self._handle is None:
+            raise ValueError("subdivision already freed")
+        return self._handle
+
+    def coarse_coords(self, stream=None) -> torch.Tensor:
+        return sparse_subdivision_copy(self, SUBM_COARSE, stream=stream)
+
+    def fine_coords(self, stream=None) -> torch.Tensor:
+        return sparse_subdivision_copy(self, SUBM_FINE, stream=stream)
+
+    def parent(self, stream=None) -> torch.Tensor:
+        return sparse_subdivision_copy(self, SUBM_PARENT, stream=stream)
+
+    def free(self) -> None:
+        if self._handle is not None:
+            lib = load_library()
+            h, self._handle = self._handle, None
+            _check(lib, "sparse_subdivision_free", lib.sparse_subdivision_free(h))
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.free()
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def _coords_arg(coords: torch.Tensor) -> None:
+    _device_tensor(coords, "coords")
+    if coords.dtype != torch.int32 or coords.dim() != 2 or coords.shape[1] != 4:
+        raise ValueError("coords must be int32 [N, 4]")
+
+
+def _build_subdivision(func: str, coords: torch.Tensor, args: tuple, stream) -> Subdivision:
+    lib = load_library()
+    out = ctypes.c_void_p()
+    with torch.cuda.device(coords.device):
+        st = getattr(lib, func)(*args, _stream_ptr(stream, coords.device), ctypes.byref(out))
+    _check(lib, func, st)
+    return Subdivision(out.value, coords.device)
+
+
+def sparse_subdivide(coords: torch.Tensor, stream=None) -> Subdivision:
+    """The 8 children of every voxel of int32 [N, 4] (b, z, y, x), C order, parent-major."""
+    _coords_arg(coords)
+    return _build_subdivision("sparse_subdivide", coords, (coords.data_ptr(), coords.shape[0]), stream)
+
+
+def sparse_downsample_build(coords: torch.Tensor, stream=None) -> Subdivision:
+    """The 2x coarse cells of int32 [N, 4] coordinates and the fine-to-coarse relation."""
+    _coords_arg(coords)
+    return _build_subdivision("sparse_downsample_build", coords, (coords.data_ptr(), coords.shape[0]), stream)
+
+
+def sparse_upsample_masked_build(coords: torch.Tensor, mask: torch.Tensor, stream=None) -> Subdivision:
+    """Masked 2x expansion of int32 [N, 4] coordinates by a uint8 [N, 8] child mask."""
+    _coords_arg(coords)
+    _device_tensor(mask, "mask")
+    if mask.dtype != torch.uint8 or tuple(mask.shape) != (coords.shape[0], 8):
+        raise ValueError("mask must be uint8 [N, 8]")
+    return _build_subdivision("sparse_upsample_masked_build", coords,
+                              (coords.data_ptr(), mask.data_ptr(), coords.shape[0]), stream)
+
+
+def sparse_subdivision_info(s: Subdivision) -> tuple[int, int]:
+    """(n_coarse, n_fine)."""
+    lib = load_library()
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib, "sparse_subdivision_info", lib.sparse_subdivision_info(s.handle, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def sparse_subdivision_kind(s: Subdivision) -> int:
+    lib = load_library()
+    k = ctypes.c_int()
+    _check(lib, "sparse_subdivision_kind", lib.sparse_subdivision_kind(s.handle, ctypes.byref(k)))
+    return k.value
+
+
+def sparse_subdivision_coords(s: Subdivision, level: int) -> int:
+    """Raw device address of the handle-owned coarse / fine coordinates (0 when empty)."""
+    lib = load_library()
+    p = ctypes.c_void_p()
+    _check(lib, "sparse_subdivision_coords", lib.sparse_subdivision_coords(s.handle, int(level), ctypes.byref(p)))
+    return p.value or 0
+
+
+def sparse_subdivision_parent(s: Subdivision) -> int:
+    """Raw device address of the handle-owned parent index (0 when empty)."""
+    lib = load_library()
+    p = ctypes.c_void_p()
+    _check(lib, "sparse_subdivision_parent", lib.sparse_subdivision_parent(s.handle, ctypes.byref(p)))
+    return p.value or 0
+
+
+def sparse_subdivision_copy(s: Subdivision, what: int, out: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """Copy of the coarse coords (SUBM_COARSE), fine coords (SUBM_FINE) or parent index (SUBM_PARENT)."""
+    shape = {SUBM_COARSE: (s.n_coarse, 4), SUBM_FINE: (s.n_fine, 4), SUBM_PARENT: (s.n_fine,)}
+    if what not in shape:
+        raise ValueError("what must be SUBM_COARSE, SUBM_FINE or SUBM_PARENT")
+    if out is None:
+        out = torch.empty(shape[what], dtype=torch.int32, device=s.device)
+    _device_tensor(out, "out")
+    if out.dtype != torch.int32 or tuple(out.shape) != shape[what]:
+        raise ValueError(f"out must be int32 {shape[what]}")
+    lib = load_library()
+    with torch.cuda.device(out.device):
+        st = lib.sparse_subdivision_copy(s.handle, int(what), out.data_ptr(), _stream_ptr(stream, out.device))
+    _check(lib, "sparse_subdivision_copy", st)
+    return out
+
+
+def sparse_subdivision_free(s: Subdivision) -> None:
+    s.free()
+
+
+def _feature_pair(inp: torch.Tensor, rows_in: int, out: torch.Tensor | None, rows_out: int, what: str):
+    _device_tensor(inp, what)
+    if inp.dim() != 2 or inp.shape[0] != rows_in or inp.dtype not in _DTYPE_CODES:
+        raise ValueError(f"{what} must be [{rows_in}, C] float32 / float16 / bfloat16")
+    if out is None:
+        out = torch.empty((rows_out, inp.shape[1]), dtype=inp.dtype, device=inp.device)
+    _device_tensor(out, "out")
+    if out.dtype != inp.dtype or tuple(out.shape) != (rows_out, inp.shape[1]):
+        raise ValueError(f"out must be [{rows_out}, {inp.shape[1]}] in the input dtype")
+    return out
+
+
+def sparse_downsample_forward(s: Subdivision, fine: torch.Tensor, mode: int, out: torch.Tensor | None = None,
+                              stream=None) -> torch.Tensor:
+    """Pool fine features [n_fine, C] onto the coarse rows: mode SUBM_POOL_MAX or SUBM_POOL_MEAN."""
+    out = _feature_pair(fine, s.n_fine, out, s.n_coarse, "fine")
+    lib = load_library()
+    with torch.cuda.device(fine.device):
+        st = lib.sparse_downsample_forward(s.handle, fine.shape[1], _DTYPE_CODES[fine.dtype], int(mode),
+                                           fine.data_ptr(), out.data_ptr(), _stream_ptr(stream, fine.device))
+    _check(lib, "sparse_downsample_forward", st)
+    return out
+
+
+def sparse_upsample_forward(s: Subdivision, coarse: torch.Tensor, out: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """Fine features [n_fine, C]: every fine row a copy of its parent's coarse row."""
+    out = _feature_pair(coarse, s.n_coarse, out, s.n_fine, "coarse")
+    lib = load_library()
+    with torch.cuda.device(coarse.device):
+        st = lib.sparse_upsample_forward(s.handle, coarse.shape[1], _DTYPE_CODES[coarse.dtype], coarse.data_ptr(),
+                                         out.data_ptr(), _stream_ptr(stream, coarse.device))
+    _check(lib, "sparse_upsample_forward", st)
+    return out
+
+
+def sparse_indice_map_subdivide(parent: IndiceMap, s: Subdivision, stream=None) -> IndiceMap:
+    """Indice map of a subdivide's fine set, derived from the map of its coarse set."""
+    lib = load_library()
+    out = ctypes.c_void_p()
+    with torch.cuda.device(s.device):
+        st = lib.sparse_indice_map_subdivide(parent.handle, s.handle, _stream_ptr(stream, s.device),
+                                             ctypes.byref(out))
+    _check(lib, "sparse_indice_map_subdivide", st)
+    return IndiceMap(out.value, s.device, s.n_fine)

@@ -30,6 +30,34 @@ Status hip_status(hipError_t e, const char* what);
 Status device_alloc(void** ptr, size_t bytes, hipStream_t stream);
 void device_free(void* ptr, hipStream_t stream);
 
+// Thread-local error detail of the C entry points (submconv_api.hip): clear_error() at entry,
+// fail() stores the message and returns the code.
+void clear_error();
+int fail(const Status& s);
+int fail(int code, const char* msg);
+
+// Per-thread, per-device pinned host block of kPinnedBytes that the device can write (for the
+// few words a build reads back after its synchronisation).  host == nullptr on failure.
+constexpr size_t kPinnedBytes = 4096;
+struct Pinned {
+  void* host = nullptr;
+  void* dev = nullptr;
+};
+Pinned pinned_block(int dev);
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
 // Device-side plan and statistics of one map build (copied to the host at its end).
 constexpr int kTapBanks = 16;               // tap hit counters are spread over banks of 27
 constexpr int64_t kGridCellsPerVoxel = 128;       // dense grid allowed up to this many cells per voxel
@@ -37,6 +65,7 @@ constexpr int64_t kGridMaxCells = int64_t(1) << 29;  // ... and at most 2 GiB of
 constexpr int kModeNone = -1;               // coordinates out of range: nothing built
 constexpr int kModeHash = 0;
 constexpr int kModeGrid = 1;
+constexpr int kModeSubdivided = 2;           // derived from a parent map, no structure
 
 constexpr uint32_t kFlagDuplicate = 1u;
 constexpr uint32_t kFlagBatchRange = 2u;
@@ -84,6 +113,11 @@ hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, 
 // word).
 hipError_t launch_fill(void* p, size_t bytes, uint32_t value, hipStream_t stream);
 
+// Child map of a subdivide (structure.hip): nbr [8 np, 27] and masks [8 np] from the parent
+// rulebook [np, 27].
+hipError_t launch_child_map(const int32_t* parent_nbr, int64_t np, int32_t* nbr, uint32_t* masks,
+                            hipStream_t stream);
+
 // Convolution launcher (conv.hip).  Arguments already validated by the caller.
 hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, int cout, int dtype,
                             const void* feats, const void* weight, const void* bias, void* out,
@@ -91,7 +125,27 @@ hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, i
 
 }  // namespace submconv
 
-// The opaque handle type of the C ABI.
+namespace submconv {
+// Subdivision handle contents (structure.hip): one coarse / fine relation, all arrays in one
+// device allocation owned by the handle.
+struct SubdivData {
+  int device = 0;
+  int kind = 0;                  // subm_subdivision_kind_t
+  int64_t n_coarse = 0;
+  int64_t n_fine = 0;
+  void* block = nullptr;         // the allocation holding the arrays below
+  int32_t* coarse = nullptr;     // [n_coarse, 4]
+  int32_t* fine = nullptr;       // [n_fine, 4]
+  int32_t* parent = nullptr;     // [n_fine]
+  int32_t* seg_off = nullptr;    // [n_coarse + 1]: members of coarse row m are positions seg_off[m] ..
+  int32_t* seg_rows = nullptr;   // ... seg_off[m+1] - 1 of seg_rows [n_fine] (null: position = fine row)
+};
+}  // namespace submconv
+
+// The opaque handle types of the C ABI.
 struct submconv_map {
   submconv::MapData d;
+};
+struct sparse_subdivision {
+  submconv::SubdivData d;
 };

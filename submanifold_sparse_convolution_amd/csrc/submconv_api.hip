@@ -12,7 +12,9 @@ namespace submconv {
 
 namespace {
 thread_local std::string g_last_error;
+}  // namespace
 
+void clear_error() { g_last_error.clear(); }
 int fail(const Status& s) {
   g_last_error = s.msg;
   return s.code;
@@ -21,6 +23,8 @@ int fail(int code, const char* msg) {
   g_last_error = msg;
   return code;
 }
+
+namespace {
 
 constexpr int kMaxDevices = 64;
 std::mutex g_pool_mu;
@@ -42,20 +46,24 @@ Status ensure_pool(int dev) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Restores the caller's current device on scope exit.
-struct DeviceGuard {
-  int prev = -1;
-  explicit DeviceGuard(int dev) {
-    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
-    if (prev != dev) (void)hipSetDevice(dev);
-  }
-  ~DeviceGuard() {
-    int cur = -1;
-    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
-  }
-};
-
 }  // namespace
+
+Pinned pinned_block(int dev) {
+  thread_local Pinned bufs[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return Pinned{};
+  if (bufs[dev].host == nullptr) {
+    void* p = nullptr;
+    void* d = nullptr;
+    if (hipHostMalloc(&p, kPinnedBytes, hipHostMallocDefault) != hipSuccess) return Pinned{};
+    if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess) {
+      (void)hipHostFree(p);
+      return Pinned{};
+    }
+    bufs[dev].host = p;
+    bufs[dev].dev = d;
+  }
+  return bufs[dev];
+}
 
 Status make_status(int code, std::string msg) {
   Status s;
@@ -142,35 +150,16 @@ Status workspace_reserve(Workspace& ws, size_t table_bytes, hipStream_t stream) 
   return Status{};
 }
 
-// Per-thread pinned host buffer that receives the build statistics (one per device; a thread
-// runs one build at a time).  The last lookup block writes it directly through its device
+// The build statistics arrive in the calling thread's pinned block for the device (a thread
+// runs one build at a time): block 0 of the reset kernel writes them through its device
 // address, so the build needs no copy command.
-struct PinnedStats {
-  MapStats* host = nullptr;
-  MapStats* dev = nullptr;
-};
-PinnedStats pinned_stats(int dev) {
-  thread_local PinnedStats bufs[kMaxDevices] = {};
-  if (dev < 0 || dev >= kMaxDevices) return PinnedStats{};
-  if (bufs[dev].host == nullptr) {
-    void* p = nullptr;
-    void* d = nullptr;
-    if (hipHostMalloc(&p, sizeof(MapStats), hipHostMallocDefault) != hipSuccess) return PinnedStats{};
-    if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess) {
-      (void)hipHostFree(p);
-      return PinnedStats{};
-    }
-    bufs[dev].host = static_cast<MapStats*>(p);
-    bufs[dev].dev = static_cast<MapStats*>(d);
-  }
-  return bufs[dev];
-}
+static_assert(sizeof(MapStats) <= kPinnedBytes, "statistics fit the pinned block");
 
 }  // namespace
 
 extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int mode, hipStream_t stream,
                                           submconv_map_t* out_map) {
-  g_last_error.clear();
+  clear_error();
   if (out_map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "out_map is NULL");
   *out_map = nullptr;
   if (mode != SUBM_MAP_AUTO && mode != SUBM_MAP_HASH && mode != SUBM_MAP_GRID)
@@ -196,12 +185,12 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
     delete m;
     return fail(SUBM_ERR_HIP, "device ordinal out of range");
   }
-  const PinnedStats pinned = pinned_stats(m->d.device);
+  const Pinned pinned = pinned_block(m->d.device);
   if (pinned.host == nullptr) {
     delete m;
     return fail(SUBM_ERR_OUT_OF_MEMORY, "pinned host buffer for the build statistics");
   }
-  MapStats* host = pinned.host;
+  MapStats* host = static_cast<MapStats*>(pinned.host);
 
   const size_t table_bytes = round_up(map_table_bytes(n), 256);
   if (map_partials_bytes(n) > kPartialsBytes) {
@@ -226,7 +215,7 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
 
   int32_t* nbr_rows = static_cast<int32_t*>(nbr);
   uint32_t* masks = reinterpret_cast<uint32_t*>(nbr_rows + (size_t)n * 27);
-  hipError_t e = launch_map_build(coords, n, mode, table, partials, nbr_rows, masks, dstats, pinned.dev, stream);
+  hipError_t e = launch_map_build(coords, n, mode, table, partials, nbr_rows, masks, dstats, static_cast<MapStats*>(pinned.dev), stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) {
     device_free(nbr, stream);
@@ -276,15 +265,15 @@ extern "C" int sparse_indice_map_build(const int32_t* coords, int64_t n, hipStre
 }
 
 extern "C" int sparse_indice_map_mode(submconv_map_t map, int* mode) {
-  g_last_error.clear();
+  clear_error();
   if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
   if (mode == nullptr) return fail(SUBM_ERR_INVALID_ARG, "mode is NULL");
-  *mode = map->d.mode == kModeGrid ? SUBM_MAP_GRID : SUBM_MAP_HASH;
+  *mode = map->d.mode == kModeGrid ? SUBM_MAP_GRID : map->d.mode == kModeSubdivided ? SUBM_MAP_SUBDIVIDED : SUBM_MAP_HASH;
   return SUBM_OK;
 }
 
 extern "C" int sparse_indice_map_free(submconv_map_t map) {
-  g_last_error.clear();
+  clear_error();
   if (map == nullptr) return SUBM_OK;
   if (map->d.nbr != nullptr) {
     DeviceGuard guard(map->d.device);
@@ -295,7 +284,7 @@ extern "C" int sparse_indice_map_free(submconv_map_t map) {
 }
 
 extern "C" int sparse_indice_map_info(submconv_map_t map, int64_t* n, int64_t* pairs) {
-  g_last_error.clear();
+  clear_error();
   if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
   if (n != nullptr) *n = map->d.n;
   if (pairs != nullptr) *pairs = map->d.pairs;
@@ -303,7 +292,7 @@ extern "C" int sparse_indice_map_info(submconv_map_t map, int64_t* n, int64_t* p
 }
 
 extern "C" int sparse_indice_map_offset_counts(submconv_map_t map, int64_t* counts) {
-  g_last_error.clear();
+  clear_error();
   if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
   if (counts == nullptr) return fail(SUBM_ERR_INVALID_ARG, "counts is NULL");
   std::memcpy(counts, map->d.per_tap, sizeof(map->d.per_tap));
@@ -311,7 +300,7 @@ extern "C" int sparse_indice_map_offset_counts(submconv_map_t map, int64_t* coun
 }
 
 extern "C" int sparse_indice_map_copy_nbr(submconv_map_t map, int32_t* nbr, hipStream_t stream) {
-  g_last_error.clear();
+  clear_error();
   if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
   if (map->d.n == 0) return SUBM_OK;
   if (nbr == nullptr) return fail(SUBM_ERR_INVALID_ARG, "nbr is NULL");
@@ -323,7 +312,7 @@ extern "C" int sparse_indice_map_copy_nbr(submconv_map_t map, int32_t* nbr, hipS
 extern "C" int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int cin, int cout, int dtype,
                                    const void* feats, const void* weight, const void* bias, void* out,
                                    hipStream_t stream) {
-  g_last_error.clear();
+  clear_error();
   if (ksize != 1 && ksize != 3) return fail(SUBM_ERR_UNSUPPORTED, "ksize must be 1 or 3");
   if (dtype != SUBM_F32 && dtype != SUBM_F16 && dtype != SUBM_BF16) return fail(SUBM_ERR_UNSUPPORTED, "dtype must be SUBM_F32, SUBM_F16 or SUBM_BF16");
   if (n < 0) return fail(SUBM_ERR_INVALID_ARG, "n is negative");

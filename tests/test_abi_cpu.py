@@ -4,6 +4,7 @@ No compute call is made: every case here fails validation before any HIP call,
 so it runs identically on a machine without a GPU.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -12,15 +13,18 @@ import pytest
 import submanifold_sparse_convolution_amd as sc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "submconv.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 OK, INVALID, DUP, RANGE, SHAPE, UNSUPPORTED, OOM, HIP = range(8)
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for header in HEADERS:
+        text = open(header).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -100,3 +104,39 @@ def test_python_binding_validates_before_calling(lib):
     import torch
     with pytest.raises(ValueError):
         sc.sparse_indice_map_build(torch.zeros((4, 4), dtype=torch.int32))  # CPU tensor
+
+
+def test_structure_builders_reject_bad_arguments(lib):
+    out = ctypes.c_void_p(12345)
+    for name in ("sparse_subdivide", "sparse_downsample_build"):
+        f = getattr(lib, name)
+        assert f(None, 4, None, None) == INVALID
+        assert f(None, -1, None, ctypes.byref(out)) == INVALID
+        assert out.value is None
+        assert f(None, 5, None, ctypes.byref(out)) == INVALID
+        assert b"coords" in lib.subm_last_error()
+        assert f(ctypes.c_void_p(24), 5, None, ctypes.byref(out)) == INVALID  # not 16-byte aligned
+    assert lib.sparse_subdivide(ctypes.c_void_p(256), 2 ** 28, None, ctypes.byref(out)) == INVALID
+    assert lib.sparse_downsample_build(ctypes.c_void_p(256), 2 ** 31, None, ctypes.byref(out)) == INVALID
+    assert lib.sparse_upsample_masked_build(ctypes.c_void_p(256), None, 3, None, ctypes.byref(out)) == INVALID
+    assert b"mask" in lib.subm_last_error()
+    assert lib.sparse_upsample_masked_build(ctypes.c_void_p(256), ctypes.c_void_p(512), 2 ** 28, None,
+                                            ctypes.byref(out)) == INVALID
+
+
+def test_structure_accessors_reject_null(lib):
+    assert lib.sparse_subdivision_free(None) == OK
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.sparse_subdivision_info(None, ctypes.byref(a), ctypes.byref(b)) == INVALID
+    k = ctypes.c_int()
+    assert lib.sparse_subdivision_kind(None, ctypes.byref(k)) == INVALID
+    p = ctypes.c_void_p()
+    assert lib.sparse_subdivision_coords(None, 0, ctypes.byref(p)) == INVALID
+    assert lib.sparse_subdivision_parent(None, ctypes.byref(p)) == INVALID
+    assert lib.sparse_subdivision_copy(None, 0, ctypes.c_void_p(256), None) == INVALID
+    assert lib.sparse_downsample_forward(None, 4, 2, 1, ctypes.c_void_p(256), ctypes.c_void_p(512), None) == INVALID
+    assert lib.sparse_upsample_forward(None, 4, 2, ctypes.c_void_p(256), ctypes.c_void_p(512), None) == INVALID
+    out = ctypes.c_void_p(1)
+    assert lib.sparse_indice_map_subdivide(None, None, None, ctypes.byref(out)) == INVALID
+    assert out.value is None
+    assert lib.sparse_indice_map_subdivide(None, None, None, None) == INVALID
