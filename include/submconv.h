@@ -168,6 +168,29 @@ int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int cin, int c
                         int dtype, const void* feats, const void* weight, const void* bias,
                         void* out, hipStream_t stream);
 
+/*
+ * subm_conv3d_forward_per_offset -- the same SubMConv3d (ksize 3) as subm_conv3d_forward, computed
+ * the per-offset way: for each of the 27 offsets, gather the neighbour rows of that offset,
+ * multiply them by that offset's weight slice, and add the products into the output rows.  This
+ * is the "obvious per-offset loop" the pages time their implementation against
+ * (trellis_sparse_mrp_mlx commit log, "Extracted from lato.2_mrp_mlx" commit), kept as a second
+ * design for comparison and for very sparse tap sets.
+ *   Arguments as subm_conv3d_forward with ksize = 3, plus these limits (else
+ *   SUBM_ERR_UNSUPPORTED): dtype SUBM_F16 or SUBM_BF16; cin a multiple of 8; cout a multiple of
+ *   4; feats and weight 16-byte aligned, out 8-byte aligned; n * cin and 27 * cout * cin
+ *   elements below 2^30.
+ * Products are accumulated in float32 in a scratch buffer [n, cout] from the library's pool:
+ * offset 13 (the centre) first, then offsets 0 .. 26 in order; the result is rounded once to the
+ * storage dtype.  Bitwise reproducible run to run; it differs from subm_conv3d_forward only by
+ * float32 summation order.  The first call on a map builds and caches the per-offset pair lists
+ * (that call synchronises `stream` once); later calls never synchronise.
+ * Errors: SUBM_ERR_INVALID_ARG, SUBM_ERR_SHAPE_MISMATCH, SUBM_ERR_UNSUPPORTED,
+ *         SUBM_ERR_OUT_OF_MEMORY, SUBM_ERR_HIP.
+ */
+int subm_conv3d_forward_per_offset(submconv_map_t map, int64_t n, int cin, int cout, int dtype,
+                                   const void* feats, const void* weight, const void* bias, void* out,
+                                   hipStream_t stream);
+
 /* Static string naming a status code ("SUBM_OK", ...); "unknown status" otherwise. */
 const char* subm_status_string(int status);
 

@@ -34,6 +34,7 @@ C_FUNCTIONS = (
     "sparse_indice_map_offset_counts",
     "sparse_indice_map_copy_nbr",
     "subm_conv3d_forward",
+    "subm_conv3d_forward_per_offset",
     "sparse_subdivide",
     "sparse_downsample_build",
     "sparse_upsample_masked_build",
@@ -85,6 +86,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.sparse_indice_map_offset_counts.argtypes = [vp, ctypes.POINTER(i64)]
         lib.sparse_indice_map_copy_nbr.argtypes = [vp, vp, vp]
         lib.subm_conv3d_forward.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp]
+        lib.subm_conv3d_forward_per_offset.argtypes = [vp, i64, ci, ci, ci, vp, vp, vp, vp, vp]
         lib.sparse_subdivide.argtypes = [vp, i64, vp, ctypes.POINTER(vp)]
         lib.sparse_downsample_build.argtypes = [vp, i64, vp, ctypes.POINTER(vp)]
         lib.sparse_upsample_masked_build.argtypes = [vp, vp, i64, vp, ctypes.POINTER(vp)]
@@ -237,6 +239,49 @@ def sparse_indice_map_copy_nbr(m: IndiceMap, out: torch.Tensor | None = None, st
     with torch.cuda.device(out.device):
         st = lib.sparse_indice_map_copy_nbr(m.handle, out.data_ptr(), _stream_ptr(stream, out.device))
     _check(lib, "sparse_indice_map_copy_nbr", st)
+    return out
+
+
+def _conv_args(feats, weight, bias, out):
+    _device_tensor(feats, "feats")
+    _device_tensor(weight, "weight")
+    if feats.dim() != 2 or weight.dim() != 5:
+        raise ValueError("feats must be [N, Cin] and weight KRSC [Cout, k, k, k, Cin]")
+    k = weight.shape[1]
+    if weight.shape[2] != k or weight.shape[3] != k:
+        raise ValueError("weight spatial dims must be equal (KRSC [Cout, k, k, k, Cin])")
+    if weight.shape[4] != feats.shape[1]:
+        raise ValueError("weight Cin does not match feats")
+    if feats.dtype not in _DTYPE_CODES or weight.dtype != feats.dtype:
+        raise ValueError("feats and weight must share one of float32 / float16 / bfloat16")
+    n, cout = feats.shape[0], weight.shape[0]
+    bias_ptr = None
+    if bias is not None:
+        _device_tensor(bias, "bias")
+        if bias.dtype != feats.dtype or tuple(bias.shape) != (cout,):
+            raise ValueError("bias must be [Cout] in the feats dtype")
+        bias_ptr = bias.data_ptr()
+    if out is None:
+        out = torch.empty((n, cout), dtype=feats.dtype, device=feats.device)
+    _device_tensor(out, "out")
+    if out.dtype != feats.dtype or tuple(out.shape) != (n, cout):
+        raise ValueError("out must be [N, Cout] in the feats dtype")
+    return k, bias_ptr, out
+
+
+def subm_conv3d_forward_per_offset(m: IndiceMap, feats: torch.Tensor, weight: torch.Tensor,
+                                   bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                                   stream=None) -> torch.Tensor:
+    """SubMConv3d (k = 3) computed as a per-offset gather -> GEMM -> scatter-add loop."""
+    k, bias_ptr, out = _conv_args(feats, weight, bias, out)
+    if k != 3:
+        raise ValueError("the per-offset path is the k = 3 convolution")
+    lib = load_library()
+    with torch.cuda.device(feats.device):
+        st = lib.subm_conv3d_forward_per_offset(m.handle, feats.shape[0], feats.shape[1], weight.shape[0],
+                                                _DTYPE_CODES[feats.dtype], feats.data_ptr(), weight.data_ptr(),
+                                                bias_ptr, out.data_ptr(), _stream_ptr(stream, feats.device))
+    _check(lib, "subm_conv3d_forward_per_offset", st)
     return out
 
 

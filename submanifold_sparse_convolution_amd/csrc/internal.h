@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <string>
 
 #include "submconv.h"
@@ -94,6 +95,12 @@ struct MapData {
   int64_t per_tap[27] = {};
   int32_t* nbr = nullptr;     // device [n, 27], input row order
   uint32_t* masks = nullptr;  // device [n]: bit k set when nbr[i, k] >= 0 (same allocation as nbr)
+  // Per-tap pair lists of the per-offset convolution, built on first use: the pairs of tap k
+  // (k != 13) are pair_out / pair_in [pair_off[k] .. pair_off[k] + per_tap[k]), output row
+  // ascending.  One allocation, pair_out first.
+  int32_t* pair_out = nullptr;
+  int32_t* pair_in = nullptr;
+  int64_t pair_off[27] = {};
 };
 
 // Map build (indice_map.hip).  Enqueues on `stream`; does not synchronise.  `table` holds
@@ -117,6 +124,16 @@ hipError_t launch_fill(void* p, size_t bytes, uint32_t value, hipStream_t stream
 // rulebook [np, 27].
 hipError_t launch_child_map(const int32_t* parent_nbr, int64_t np, int32_t* nbr, uint32_t* masks,
                             hipStream_t stream);
+
+// Per-offset convolution (conv_offsets.hip).  launch_pair_lists fills pair_out / pair_in of a
+// map (sizes pairs - n) using pair_scratch_ints(n) int32 of scratch; launch_subm_conv_per_offset
+// needs the pair lists, 16-bit storage, cin % 8 == 0, cout % 4 == 0 and acc = float32 [n, cout].
+hipError_t launch_pair_lists(const MapData& m, int32_t* pair_out, int32_t* pair_in, int32_t* scratch,
+                             hipStream_t stream);
+size_t pair_scratch_ints(int64_t n);
+hipError_t launch_subm_conv_per_offset(const MapData& m, int cin, int cout, int dtype, const void* feats,
+                                       const void* weight, const void* bias, void* out, float* acc,
+                                       hipStream_t stream);
 
 // Convolution launcher (conv.hip).  Arguments already validated by the caller.
 hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, int cout, int dtype,
@@ -145,6 +162,7 @@ struct SubdivData {
 // The opaque handle types of the C ABI.
 struct submconv_map {
   submconv::MapData d;
+  std::mutex pairs_mu;  // guards the lazy build of the per-tap pair lists
 };
 struct sparse_subdivision {
   submconv::SubdivData d;

@@ -275,9 +275,10 @@ extern "C" int sparse_indice_map_mode(submconv_map_t map, int* mode) {
 extern "C" int sparse_indice_map_free(submconv_map_t map) {
   clear_error();
   if (map == nullptr) return SUBM_OK;
-  if (map->d.nbr != nullptr) {
+  if (map->d.nbr != nullptr || map->d.pair_out != nullptr) {
     DeviceGuard guard(map->d.device);
     device_free(map->d.nbr, nullptr);
+    device_free(map->d.pair_out, nullptr);
   }
   delete map;
   return SUBM_OK;
@@ -336,5 +337,65 @@ extern "C" int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int
   }
   hipError_t e = launch_subm_conv(map == nullptr ? nullptr : &map->d, n, ksize, cin, cout, dtype, feats, weight, bias, out, stream);
   if (e != hipSuccess) return fail(hip_status(e, "subm_conv3d_forward launch"));
+  return SUBM_OK;
+}
+
+extern "C" int subm_conv3d_forward_per_offset(submconv_map_t map, int64_t n, int cin, int cout, int dtype,
+                                              const void* feats, const void* weight, const void* bias, void* out,
+                                              hipStream_t stream) {
+  clear_error();
+  if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
+  if (dtype != SUBM_F16 && dtype != SUBM_BF16) return fail(SUBM_ERR_UNSUPPORTED, "dtype must be SUBM_F16 or SUBM_BF16");
+  if (n < 0) return fail(SUBM_ERR_INVALID_ARG, "n is negative");
+  if (cin < 1 || cout < 1) return fail(SUBM_ERR_INVALID_ARG, "cin and cout must be >= 1");
+  if (cin % 8 != 0 || cout % 4 != 0) return fail(SUBM_ERR_UNSUPPORTED, "cin must be a multiple of 8 and cout of 4");
+  if (map->d.n != n) return fail(SUBM_ERR_SHAPE_MISMATCH, "n differs from the map's voxel count");
+  if ((uint64_t)n * (uint64_t)cin >= (1ull << 30) || (uint64_t)cout * 27u * (uint64_t)cin >= (1ull << 30))
+    return fail(SUBM_ERR_UNSUPPORTED, "feats or weight exceed 2^30 elements");
+  if (n == 0) return SUBM_OK;
+  if (feats == nullptr || weight == nullptr || out == nullptr) return fail(SUBM_ERR_INVALID_ARG, "feats, weight or out is NULL");
+  if (out == feats) return fail(SUBM_ERR_INVALID_ARG, "out must not alias feats");
+  if (((reinterpret_cast<uintptr_t>(feats) | reinterpret_cast<uintptr_t>(weight)) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(out) & 7u) != 0 || (reinterpret_cast<uintptr_t>(bias) & 1u) != 0)
+    return fail(SUBM_ERR_UNSUPPORTED, "feats / weight must be 16-byte aligned, out 8-byte, bias 2-byte");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(hip_status(e, "hipGetDevice"));
+  if (dev != map->d.device) return fail(SUBM_ERR_INVALID_ARG, "the map was built on another device");
+  {
+    std::lock_guard<std::mutex> lock(map->pairs_mu);
+    const int64_t off_centre = map->d.pairs - map->d.per_tap[13];
+    if (map->d.pair_out == nullptr && off_centre > 0) {
+      void* pairs = nullptr;
+      void* scratch = nullptr;
+      Status s = device_alloc(&pairs, (size_t)off_centre * 2 * sizeof(int32_t), stream);
+      if (s.ok()) s = device_alloc(&scratch, pair_scratch_ints(n) * sizeof(int32_t), stream);
+      if (!s.ok()) {
+        device_free(pairs, stream);
+        return fail(s);
+      }
+      int32_t* po = static_cast<int32_t*>(pairs);
+      e = launch_pair_lists(map->d, po, po + off_centre, static_cast<int32_t*>(scratch), stream);
+      device_free(scratch, stream);
+      if (e == hipSuccess) e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) {
+        device_free(pairs, stream);
+        return fail(hip_status(e, "pair lists"));
+      }
+      int64_t run = 0;
+      for (int k = 0; k < 27; ++k) {
+        map->d.pair_off[k] = run;
+        if (k != 13) run += map->d.per_tap[k];
+      }
+      map->d.pair_in = po + off_centre;
+      map->d.pair_out = po;
+    }
+  }
+  void* acc = nullptr;
+  Status s = device_alloc(&acc, (size_t)n * cout * sizeof(float), stream);
+  if (!s.ok()) return fail(s);
+  e = launch_subm_conv_per_offset(map->d, cin, cout, dtype, feats, weight, bias, out, static_cast<float*>(acc), stream);
+  device_free(acc, stream);
+  if (e != hipSuccess) return fail(hip_status(e, "subm_conv3d_forward_per_offset launch"));
   return SUBM_OK;
 }

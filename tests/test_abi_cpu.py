@@ -140,3 +140,11 @@ def test_structure_accessors_reject_null(lib):
     assert lib.sparse_indice_map_subdivide(None, None, None, ctypes.byref(out)) == INVALID
     assert out.value is None
     assert lib.sparse_indice_map_subdivide(None, None, None, None) == INVALID
+
+
+def test_per_offset_rejects_bad_arguments(lib):
+    def po(m=None, n=10, cin=8, cout=8, dtype=2, f=256, w=512, b=None, o=1024):
+        return lib.subm_conv3d_forward_per_offset(m, n, cin, cout, dtype, f, w, b, o, None)
+
+    assert po() == INVALID  # the per-offset path always needs a map
+    assert b"map" in lib.subm_last_error()
