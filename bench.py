@@ -2,6 +2,7 @@
 """Benchmark of the SubMConv3d hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload 3a] [--no-cpu-baseline]
+    python bench.py --op per-offset|subdivide|downsample|groupnorm [...]
 
 One step = the whole hot path over one coordinate set already resident in HBM:
 build the indice map (hash insert + 27-neighbour lookup + one sync for the
@@ -14,6 +15,13 @@ Printed: one JSON line with the step throughput (effective TFLOP/s =
 time), the roofline position of the convolution kernel (its average duration
 from HIP events around back-to-back launches on the stream it runs on), and
 the CPU oracle timed on a bounded sample of the same workload.
+
+--op selects another row of the path, each printed as one JSON line of its own:
+per-offset (the same convolution computed offset by offset: gather -> GEMM ->
+scatter-add), subdivide (children, their features and the derived child map of
+the config-5 structure at its last level), downsample (2x cells, max pooling
+and the cache-paired upsample of the config-5 coordinate set) and groupnorm
+(group normalisation + SiLU over the config-5 set, 64 channels, 32 groups).
 """
 from __future__ import annotations
 
@@ -42,6 +50,7 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="3a", help="1, 2a (k3 + k1 layer), 3a, 3b, 4, 5")
+    p.add_argument("--op", default="conv", choices=["conv", "per-offset", "subdivide", "downsample", "groupnorm"])
     p.add_argument("--conv-reps", type=int, default=200, help="back-to-back launches timed for the roofline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target duration of the oracle sample")
@@ -130,6 +139,14 @@ def cpu_baseline(key, coords, feats, weight, bias, nbr_pairs_per_row, cin, cout,
     }
 
 
+def per_offset_bytes(n, pairs, cin, cout, s):
+    """Algorithmic bytes of one per-offset convolution: every pair reads its input row, the
+    weights once, the pair indices, the float32 accumulator rows (written by the centre offset,
+    read and written by every other pair, read by the final rounding) and the output."""
+    return float(pairs * cin * s + 27 * cin * cout * s + (pairs - n) * 8 + n * cout * 4
+                 + (pairs - n) * cout * 8 + n * cout * 4 + n * cout * s)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -139,6 +156,10 @@ def main():
         print("bench.py measures one GPU only: the submanifold convolution path here is a single-GPU "
               "build (see the sharding paragraph of the design notes); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.op in ("subdivide", "downsample", "groupnorm"):
+        bench_structure(args)
+        return
+    per_offset = args.op == "per-offset"
 
     import numpy as np
     import torch
@@ -165,11 +186,16 @@ def main():
     x0_dev = x0.to(dev)
     outs = [torch.empty((n, cout), dtype=x0_dev.dtype, device=dev) for (_, _, cout, *_r) in layers]
 
+    def conv(m, ks, x, w, b, out):
+        if per_offset and ks == 3:
+            return sc.subm_conv3d_forward_per_offset(m, x, w, b, out=out)
+        return sc.subm_conv3d_forward(m if ks == 3 else None, x, w, b, out=out)
+
     def step():
         m = sc.sparse_indice_map_build(coords)
         x = x0_dev
         for (ks, cin, cout, w, b, _, _), out in zip(layers, outs):
-            sc.subm_conv3d_forward(m if ks == 3 else None, x, w, b, out=out)
+            conv(m, ks, x, w, b, out)
             if chained:
                 x = out
         m.free()
@@ -190,6 +216,10 @@ def main():
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / args.steps
 
+    if per_offset:
+        # The step above builds a new map every time, so each per-offset call also built that
+        # map's pair lists (and synchronised once); the kernel timing below reuses one map.
+        pass
     # Map build alone (includes its one stream synchronisation).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -208,7 +238,7 @@ def main():
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for r in range(min(reps, 20)):  # warm
             ks, cin, cout, w, b = k3[r % len(k3)]
-            sc.subm_conv3d_forward(m if ks == 3 else None, x0_dev if not chained else outs[0], w, b, out=outs[-1])
+            conv(m, ks, x0_dev if not chained else outs[0], w, b, outs[-1])
         torch.cuda.synchronize()
         per_layer = {i: [] for i in range(len(k3))}
         for r in range(reps):
@@ -216,7 +246,7 @@ def main():
             ks, cin, cout, w, b = k3[i]
             src = x0_dev if not chained else outs[0]
             evs[r][0].record(stream)
-            sc.subm_conv3d_forward(m if ks == 3 else None, src, w, b, out=outs[-1])
+            conv(m, ks, src, w, b, outs[-1])
             evs[r][1].record(stream)
         torch.cuda.synchronize()
         for r in range(reps):
@@ -229,11 +259,13 @@ def main():
     p_layer = pairs if ks == 3 else n
     flop_launch = 2.0 * p_layer * cin * cout
     bytes_launch = float(n * cin * s + n * cout * s + ks ** 3 * cin * cout * s + cout * s + (n * 27 * 4 if ks == 3 else 0))
+    if per_offset and ks == 3:
+        bytes_launch = per_offset_bytes(n, pairs, cin, cout, s)
     t_mfma = flop_launch / (PEAK_TFLOPS[cfg.dtype] * 1e12)
     t_hbm = bytes_launch / (PEAK_HBM_GBS * 1e9)
     conv_s = conv_ms / 1e3
     kernel_hash = source_hash(CONV_SOURCE)
-    traffic = load_traffic(key, kernel_hash)
+    traffic = None if per_offset else load_traffic(key, kernel_hash)
     if t_mfma >= t_hbm:
         achieved = flop_launch / conv_s / 1e12
         roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s",
@@ -244,7 +276,9 @@ def main():
                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic}
     # The kernel the library picks for this layer shape (16-bit storage: the warp-specialised
     # matrix-core kernel above 32 output channels, the single-role one from 17 to 32).
-    if cfg.dtype in ("bf16", "f16") and cout > 32:
+    if per_offset and ks == 3:
+        kernel = "offset_gemm_kernel (27 launches, one per offset) + round_out_kernel, per call"
+    elif cfg.dtype in ("bf16", "f16") and cout > 32:
         kernel = "subm_conv_ws_kernel"
     elif cfg.dtype in ("bf16", "f16") and cout > 16:
         kernel = "subm_conv_mma_kernel"
@@ -255,7 +289,7 @@ def main():
 
     value = flops_per_step / step_s / 1e12
     result = {
-        "metric": METRIC,
+        "metric": METRIC if not per_offset else "SubMConv3d per-offset design (gather -> GEMM -> scatter-add): effective TFLOP/s (1 GPU)",
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -267,7 +301,7 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.workload, "key": key, "batch": cfg.batch, "grid": cfg.grid, "voxels": n,
+        "config": {"workload": cfg.workload, "key": key, "op": args.op, "batch": cfg.batch, "grid": cfg.grid, "voxels": n,
                    "pairs": pairs, "cin": cfg.cin, "cout": cfg.cout,
                    "layers": [f"k{ks} {ci}->{co}" for ks, ci, co, *_ in layers], "chained": chained},
         "roofline": roofline,
@@ -283,6 +317,207 @@ def main():
         result["cpu_baseline"] = cpu_baseline(key, coords_np, x0, w_cpu, b_cpu, nbr_rows, cin, cout,
                                               args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+STRUCTURE_METRIC = {
+    "subdivide": "subdivide + child features + derived child map: children per second (1 GPU)",
+    "downsample": "2x downsample build + max pooling + cached upsample: fine voxels per second (1 GPU)",
+    "groupnorm": "group normalisation (32 groups) + SiLU per batch item: voxels per second (1 GPU)",
+}
+
+
+def time_events(fn, reps, stream):
+    """Average milliseconds of fn() from HIP events on `stream` around each of `reps` calls."""
+    import torch
+    for _ in range(min(reps, 10)):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+def bench_structure(args):
+    """Structure rows of the path on the config-5 coordinate sets (two 512^3 items).
+
+    subdivide: input = the 256^3 level of the config-5 chain (three subdivisions of the r = 28
+    shell, before the 25 % selection; 2 x 637,568 voxels), 64 bf16 channels.  One step =
+    sparse_subdivide (coords, parent) + sparse_upsample_forward (children's features) +
+    sparse_indice_map_subdivide (child map from the parent map) + frees.
+    downsample: input = the config-5 set (2,550,313 voxels), 64 bf16 channels.  One step =
+    sparse_downsample_build + max pooling + cache-paired upsample + free.
+    """
+    import numpy as np
+    import torch
+
+    import submanifold_sparse_convolution_amd as sc
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sc.load_library()
+    stream = torch.cuda.current_stream(dev)
+    ch, s = 64, 2
+    if args.op == "subdivide":
+        base = synth.coords_for("5_parent")
+        workload = ("level 2 -> 3 of the config-5 chain: 2 x 256^3 subdivided r = 28 shells "
+                    f"({len(base)} voxels) -> 2 x 512^3 ({8 * len(base)} children), 64 bf16 channels")
+    elif args.op == "downsample":
+        base = synth.coords_for("5")
+        workload = ("config-5 coordinate set: 2 x 512^3 subdivided shells keeping 25 % "
+                    f"({len(base)} voxels) -> 2x cells, 64 bf16 channels")
+    else:
+        base = synth.coords_for("5")
+        workload = ("config-5 coordinate set: 2 x 512^3 subdivided shells keeping 25 % "
+                    f"({len(base)} voxels, 2 items), 64 bf16 channels, 32 groups, SiLU")
+    n = len(base)
+    coords = torch.from_numpy(base).to(dev)
+    feats = synth.round_to(np.random.default_rng(77).standard_normal((n, ch)), "bf16").to(dev)
+
+    if args.op == "subdivide":
+        pm = sc.sparse_indice_map_build(coords)
+        child_feats = torch.empty((8 * n, ch), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            sub = sc.sparse_subdivide(coords)
+            sc.sparse_upsample_forward(sub, feats, out=child_feats)
+            cm = sc.sparse_indice_map_subdivide(pm, sub)
+            cm.free()
+            sub.free()
+
+        items = 8 * n
+        sub = sc.sparse_subdivide(coords)
+        kern = {
+            "expand_kernel": (lambda: sc.sparse_upsample_forward(sub, feats, out=child_feats),
+                              float(n * ch * s + 8 * n * 4 + 8 * n * ch * s)),
+        }
+        cm_holder = []
+
+        def child_map():
+            cm_holder.append(sc.sparse_indice_map_subdivide(pm, sub))
+
+        kern["child_map_kernel"] = (child_map, float(n * 108 + 8 * n * 112))
+    elif args.op == "groupnorm":
+        counts = np.bincount(base[:, 0])
+        offsets = torch.tensor([0] + np.cumsum(counts).tolist(), dtype=torch.int64, device=dev)
+        gamma = synth.round_to(1.0 + 0.1 * np.random.default_rng(78).standard_normal(ch), "bf16").to(dev)
+        beta = synth.round_to(0.1 * np.random.default_rng(79).standard_normal(ch), "bf16").to(dev)
+        normed = torch.empty_like(feats)
+
+        def step():
+            sc.sparse_group_norm_act(feats, offsets, 32, gamma, beta, 1e-5, sc.SUBM_ACT_SILU, out=normed)
+
+        items = n
+        sub = None
+        kern = {"gn (partials + statistics + apply)": (step, float(2 * n * ch * s + n * ch * s))}
+    else:
+        coarse_out = None
+
+        def step():
+            nonlocal coarse_out
+            d = sc.sparse_downsample_build(coords)
+            coarse_out = sc.sparse_downsample_forward(d, feats, sc.SUBM_POOL_MAX, out=None)
+            sc.sparse_upsample_forward(d, coarse_out)
+            d.free()
+
+        items = n
+        sub = sc.sparse_downsample_build(coords)
+        m_cells = sub.n_coarse
+        pooled = torch.empty((m_cells, ch), dtype=torch.bfloat16, device=dev)
+        up = torch.empty((n, ch), dtype=torch.bfloat16, device=dev)
+        kern = {
+            "pool_kernel": (lambda: sc.sparse_downsample_forward(sub, feats, sc.SUBM_POOL_MAX, out=pooled),
+                            float(n * ch * s + n * 4 + (m_cells + 1) * 4 + m_cells * ch * s)),
+            "expand_kernel": (lambda: sc.sparse_upsample_forward(sub, pooled, out=up),
+                              float(m_cells * ch * s + n * 4 + n * ch * s)),
+        }
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+
+    per_kernel = {}
+    for name, (fn, nbytes) in kern.items():
+        ms = time_events(fn, 50, stream)
+        per_kernel[name] = {"avg_launch_ms": ms, "algorithmic_bytes_per_launch": nbytes,
+                            "achieved_GBps": nbytes / (ms / 1e3) / 1e9}
+    if args.op == "subdivide":
+        for cm in cm_holder:
+            cm.free()
+        pm.free()
+    if sub is not None:
+        sub.free()
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["avg_launch_ms"])
+    achieved = per_kernel[dom]["achieved_GBps"]
+    result = {
+        "metric": STRUCTURE_METRIC[args.op],
+        "value": items / step_s,
+        "unit": "voxels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32 coordinates, bf16 features",
+        "data": "synthetic",
+        "config": {"workload": workload, "op": args.op, "voxels_in": n, "channels": ch},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": dom,
+                     "avg_launch_ms": per_kernel[dom]["avg_launch_ms"],
+                     "algorithmic_bytes_per_launch": per_kernel[dom]["algorithmic_bytes_per_launch"]},
+        "breakdown": per_kernel,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = structure_cpu_baseline(args.op, base, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def structure_cpu_baseline(op, base, budget_s):
+    """The oracle's subdivide / downsample (pure Python) on a leading sample of the rows."""
+    import numpy as np
+
+    from oracle import structure_ref
+
+    rows = 2000
+    t0 = time.perf_counter()
+    from oracle import norm_ref
+
+    def run(k):
+        if op == "subdivide":
+            structure_ref.subdivide(base[:k])
+        elif op == "downsample":
+            structure_ref.downsample(base[:k])
+        else:
+            x = np.random.default_rng(1).standard_normal((k, 64))
+            norm_ref.group_norm_act(x, [0, k], 32, None, None, 1e-5, "silu")
+
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        run(rows)
+        per_row = (time.perf_counter() - t0) / rows
+        rows = int(min(len(base), max(rows, budget_s / max(per_row, 1e-9))))
+        t0 = time.perf_counter()
+        run(rows)
+        elapsed = time.perf_counter() - t0
+    out_rows = 8 * rows if op == "subdivide" else rows
+    what = {"subdivide": "structure_ref.subdivide", "downsample": "structure_ref.downsample",
+            "groupnorm": "norm_ref.group_norm_act (numpy, 64 channels, 32 groups, one item)"}[op]
+    return {"value": out_rows / elapsed, "unit": "voxels/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle {what} on the first {rows} of {len(base)} input rows; {elapsed:.2f} s"}
 
 
 if __name__ == "__main__":

@@ -20,6 +20,7 @@ SUBM_MAP_AUTO, SUBM_MAP_HASH, SUBM_MAP_GRID, SUBM_MAP_SUBDIVIDED = 0, 1, 2, 3
 SUBM_POOL_MAX, SUBM_POOL_MEAN = 1, 2
 SUBM_COARSE, SUBM_FINE, SUBM_PARENT = 0, 1, 2
 SUBM_SUBDIVIDE, SUBM_DOWNSAMPLE, SUBM_UPSAMPLE_MASKED = 0, 1, 2
+SUBM_ACT_NONE, SUBM_ACT_SILU, SUBM_ACT_RELU = 0, 1, 2
 _DTYPE_CODES = {torch.float32: SUBM_F32, torch.float16: SUBM_F16, torch.bfloat16: SUBM_BF16}
 TAPS = 27
 
@@ -47,6 +48,7 @@ C_FUNCTIONS = (
     "sparse_downsample_forward",
     "sparse_upsample_forward",
     "sparse_indice_map_subdivide",
+    "sparse_group_norm_act",
     "subm_status_string",
     "subm_last_error",
 )
@@ -99,6 +101,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.sparse_downsample_forward.argtypes = [vp, ci, ci, ci, vp, vp, vp]
         lib.sparse_upsample_forward.argtypes = [vp, ci, ci, vp, vp, vp]
         lib.sparse_indice_map_subdivide.argtypes = [vp, vp, vp, ctypes.POINTER(vp)]
+        lib.sparse_group_norm_act.argtypes = [vp, i64, ci, ci, vp, ci, ci, vp, vp, ctypes.c_float, ci, vp, vp]
         for name in C_FUNCTIONS[:-2]:
             getattr(lib, name).restype = ci
         lib.subm_status_string.argtypes = [ci]
@@ -502,3 +505,41 @@ def sparse_indice_map_subdivide(parent: IndiceMap, s: Subdivision, stream=None) 
                                              ctypes.byref(out))
     _check(lib, "sparse_indice_map_subdivide", st)
     return IndiceMap(out.value, s.device, s.n_fine)
+
+
+# --------------------------------------------------------------------------- normalisation
+
+def sparse_group_norm_act(x: torch.Tensor, item_offsets: torch.Tensor, groups: int,
+                          gamma: torch.Tensor | None = None, beta: torch.Tensor | None = None,
+                          eps: float = 1e-5, act: int = SUBM_ACT_NONE, out: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """Group normalisation per batch item (rows item_offsets[b] .. item_offsets[b+1] - 1, int64
+    device tensor) then an activation (SUBM_ACT_NONE / _SILU / _RELU).  out may be x (in place)."""
+    _device_tensor(x, "x")
+    if x.dim() != 2 or x.dtype not in _DTYPE_CODES:
+        raise ValueError("x must be [N, C] float32 / float16 / bfloat16")
+    _device_tensor(item_offsets, "item_offsets")
+    if item_offsets.dtype != torch.int64 or item_offsets.dim() != 1 or item_offsets.shape[0] < 2:
+        raise ValueError("item_offsets must be int64 [num_items + 1]")
+    c = x.shape[1]
+    ptrs = []
+    for t, name in ((gamma, "gamma"), (beta, "beta")):
+        if t is None:
+            ptrs.append(None)
+            continue
+        _device_tensor(t, name)
+        if t.dtype != x.dtype or tuple(t.shape) != (c,):
+            raise ValueError(f"{name} must be [C] in the dtype of x")
+        ptrs.append(t.data_ptr())
+    if out is None:
+        out = torch.empty_like(x)
+    _device_tensor(out, "out")
+    if out.dtype != x.dtype or out.shape != x.shape:
+        raise ValueError("out must match x")
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        st = lib.sparse_group_norm_act(x.data_ptr(), x.shape[0], c, _DTYPE_CODES[x.dtype], item_offsets.data_ptr(),
+                                       item_offsets.shape[0] - 1, int(groups), ptrs[0], ptrs[1], float(eps), int(act),
+                                       out.data_ptr(), _stream_ptr(stream, x.device))
+    _check(lib, "sparse_group_norm_act", st)
+    return out

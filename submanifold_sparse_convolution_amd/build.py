@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsubmconv.so")
-SOURCES = ["submconv_api.hip", "indice_map.hip", "conv.hip", "conv_offsets.hip", "structure.hip"]
+SOURCES = ["submconv_api.hip", "indice_map.hip", "conv.hip", "conv_offsets.hip", "structure.hip", "norm.hip"]
 
 ARCH = "gfx950"
 COMMON = [

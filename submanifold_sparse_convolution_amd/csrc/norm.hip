@@ -1,0 +1,347 @@
+// Group normalisation per batch item in float32 followed by an activation (sparse_norm.h states
+// the operation and where the pages name it).
+//
+// Three passes:
+//   1. partials: the rows of every item are cut into segments of at most R consecutive rows
+//      (segment s = b + k holds rows [max(off[b], kR), min(off[b+1], (k+1)R)) of item b, so the
+//      segment index needs no search table); one block per segment reads its rows once and
+//      forms, per group, the sums of x - K and (x - K)^2 with K the group's first value in the
+//      segment (shifted sums: no cancellation when the mean is large against the spread), in
+//      float32 and a fixed order, and stores the segment's mean and sum of squared deviations;
+//   2. statistics: one block per item combines its segments, per group, with the pairwise update
+//      of Chan, Golub and LeVeque in float64 (strided partial chains, then a fixed tree) and
+//      stores the mean and 1 / sqrt(var + eps);
+//   3. apply: one block per segment (a single item), per-channel scale rstd * gamma and shift
+//      beta - mean * rstd * gamma in LDS, then y = act(x * scale + shift), rounded once.
+// Every reduction runs in a fixed order, so the result is bitwise reproducible.
+#include <algorithm>
+#include <cmath>
+
+#include "device_common.h"
+#include "internal.h"
+#include "sparse_norm.h"
+
+namespace submconv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxSegmentsPerRun = 4096;  // segment length R grows with n to keep this bound
+
+__device__ __forceinline__ int64_t clamp_off(const int64_t* off, int b, int64_t n) {
+  const int64_t v = off[b];
+  return v < 0 ? 0 : (v > n ? n : v);
+}
+
+// 16 bytes of storage -> E floats, and back (E = 16 / element size).
+template <DT D, int E> __device__ __forceinline__ void unpack(const uint4& raw, float (&v)[E]) {
+  const unsigned char* b = reinterpret_cast<const unsigned char*>(&raw);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if constexpr (D == DT::F32) v[e] = reinterpret_cast<const float*>(b)[e];
+    else v[e] = to_float<D>(reinterpret_cast<const uint16_t*>(b)[e]);
+  }
+}
+
+template <int ACT> __device__ __forceinline__ float activate(float y) {
+  if constexpr (ACT == SUBM_ACT_SILU) return y / (1.f + __expf(-y));
+  if constexpr (ACT == SUBM_ACT_RELU) return fmaxf(y, 0.f);
+  return y;
+}
+
+// Segment s -> (item, rows [r0, r1)): the item is the largest b with b + off[b] / R <= s, which
+// is strictly increasing in b.
+struct Segment {
+  int b;
+  int64_t r0, r1;
+};
+__device__ __forceinline__ Segment find_segment(const int64_t* off, int items, int64_t n, int64_t R, int64_t s) {
+  int lo = 0, hi = items - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (mid + clamp_off(off, mid, n) / R <= s) lo = mid;
+    else hi = mid - 1;
+  }
+  const int64_t k = s - lo;
+  Segment g;
+  g.b = lo;
+  g.r0 = std::max(clamp_off(off, lo, n), k * R);
+  g.r1 = std::min(clamp_off(off, lo + 1, n), (k + 1) * R);
+  return g;
+}
+
+// Pass 1.  T = channels / E chunk lanes x RT = 256 / T row lanes.
+template <DT D, int E>
+__global__ __launch_bounds__(kThreads) void gn_partial_kernel(const void* __restrict__ x, int64_t n, int channels,
+                                                              const int64_t* __restrict__ off, int items, int64_t R,
+                                                              int groups, float2* __restrict__ part,
+                                                              int32_t* __restrict__ part_rows) {
+  __shared__ float s_acc[2][kThreads * E];
+  __shared__ float s_shift[2048];
+  const int tid = threadIdx.x;
+  const int64_t s = blockIdx.x;
+  const Segment seg = find_segment(off, items, n, R, s);
+  const int64_t rows = seg.r1 > seg.r0 ? seg.r1 - seg.r0 : 0;
+  const int cpg = channels / groups;
+  if (rows == 0) {
+    for (int g = tid; g < groups; g += kThreads) part[s * groups + g] = make_float2(0.f, 0.f);
+    if (tid == 0) part_rows[s] = 0;
+    return;
+  }
+  const unsigned char* xb = static_cast<const unsigned char*>(x);
+  using T = typename Elem<D>::T;
+  for (int g = tid; g < groups; g += kThreads) {
+    const int64_t idx = seg.r0 * channels + (int64_t)g * cpg;
+    s_shift[g] = D == DT::F32 ? reinterpret_cast<const float*>(xb)[idx] : to_float<D>(reinterpret_cast<const T*>(xb)[idx]);
+  }
+  __syncthreads();
+  const int T_ = channels / E;  // chunk lanes (<= 256)
+  const int RT = kThreads / T_;
+  const int rl = tid / T_, cl = tid - (tid / T_) * T_;
+  float a1[E], a2[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) a1[e] = a2[e] = 0.f;
+  if (rl < RT) {
+    float k[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) k[e] = s_shift[(cl * E + e) / cpg];
+#pragma unroll 4
+    for (int64_t r = seg.r0 + rl; r < seg.r1; r += RT) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(xb + (r * channels + (int64_t)cl * E) * (16 / E));
+      float v[E];
+      unpack<D, E>(raw, v);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float d = v[e] - k[e];
+        a1[e] += d;
+        a2[e] += d * d;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    s_acc[0][tid * E + e] = a1[e];
+    s_acc[1][tid * E + e] = a2[e];
+  }
+  __syncthreads();
+  // per group: row lanes, then the group's channels, in order
+  const float cnt = (float)(rows * cpg);
+  for (int g = tid; g < groups; g += kThreads) {
+    float t1 = 0.f, t2 = 0.f;
+    for (int c = g * cpg; c < (g + 1) * cpg; ++c) {
+      const int lane = c / E, e = c - (c / E) * E;
+      for (int q = 0; q < RT; ++q) {
+        t1 += s_acc[0][(q * T_ + lane) * E + e];
+        t2 += s_acc[1][(q * T_ + lane) * E + e];
+      }
+    }
+    const float mean_d = t1 / cnt;
+    part[s * groups + g] = make_float2(s_shift[g] + mean_d, fmaxf(t2 - t1 * mean_d, 0.f));
+  }
+  if (tid == 0) part_rows[s] = (int32_t)rows;
+}
+
+// Pass 2: one block of kStatThreads per item; per group, TG threads combine strided subsets of
+// the item's segments, then a fixed pairwise tree over the TG partial results.
+constexpr int kStatThreads = 1024;
+
+__device__ __forceinline__ void chan_combine(double& na, double& ma, double& m2a, double nb, double mb, double m2b) {
+  if (nb == 0.0) return;
+  const double n = na + nb;
+  const double d = mb - ma;
+  ma += d * (nb / n);
+  m2a += m2b + d * d * (na * nb / n);
+  na = n;
+}
+
+__global__ __launch_bounds__(kStatThreads) void gn_stats_kernel(const float2* __restrict__ part,
+                                                                const int32_t* __restrict__ part_rows,
+                                                                const int64_t* __restrict__ off, int64_t n, int64_t R,
+                                                                int groups, int cpg, float eps,
+                                                                float2* __restrict__ stats) {
+  __shared__ double s_n[kStatThreads], s_m[kStatThreads], s_q[kStatThreads];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int64_t lo = clamp_off(off, b, n), hi = clamp_off(off, b + 1, n);
+  if (hi <= lo) {
+    for (int g = tid; g < groups; g += kStatThreads) stats[(int64_t)b * groups + g] = make_float2(0.f, 0.f);
+    return;
+  }
+  const int64_t s0 = b + lo / R, s1 = b + (hi - 1) / R;  // inclusive
+  // TG = threads per group: the largest power of two with TG * groups <= kStatThreads (>= 1)
+  int tg = 1;
+  while (tg * 2 * groups <= kStatThreads) tg *= 2;
+  const int gpb = kStatThreads / tg;  // groups per pass
+  for (int g0 = 0; g0 < groups; g0 += gpb) {
+    const int g = g0 + tid / tg, j = tid % tg;
+    const bool on = tid / tg < gpb && g < groups;
+    double na = 0.0, ma = 0.0, m2a = 0.0;
+    if (on)
+      for (int64_t sg = s0 + j; sg <= s1; sg += tg) {
+        const float2 p = part[sg * groups + g];
+        chan_combine(na, ma, m2a, (double)part_rows[sg] * cpg, p.x, p.y);
+      }
+    s_n[tid] = na;
+    s_m[tid] = ma;
+    s_q[tid] = m2a;
+    __syncthreads();
+    for (int h = 1; h < tg; h <<= 1) {
+      if (on && (j % (2 * h)) == 0) {
+        double a = s_n[tid], m = s_m[tid], q = s_q[tid];
+        chan_combine(a, m, q, s_n[tid + h], s_m[tid + h], s_q[tid + h]);
+        s_n[tid] = a;
+        s_m[tid] = m;
+        s_q[tid] = q;
+      }
+      __syncthreads();
+    }
+    if (on && j == 0) {
+      const double var = s_n[tid] > 0.0 ? s_q[tid] / s_n[tid] : 0.0;
+      stats[(int64_t)b * groups + g] = make_float2((float)s_m[tid], (float)(1.0 / sqrt(var + (double)eps)));
+    }
+    __syncthreads();
+  }
+}
+
+// Pass 3: one block per segment (one item).
+template <DT D, int E, int ACT>
+__global__ __launch_bounds__(kThreads) void gn_apply_kernel(const void* __restrict__ x, void* __restrict__ y, int64_t n,
+                                                            int channels, const int64_t* __restrict__ off, int items,
+                                                            int64_t R, int groups, const float2* __restrict__ stats,
+                                                            const void* __restrict__ gamma,
+                                                            const void* __restrict__ beta) {
+  using T = typename Elem<D>::T;
+  __shared__ float s_scale[2048], s_shift[2048];
+  const Segment seg = find_segment(off, items, n, R, blockIdx.x);
+  if (seg.r1 <= seg.r0) return;
+  const int cpg = channels / groups;
+  const float2* st = stats + (int64_t)seg.b * groups;
+  for (int c = threadIdx.x; c < channels; c += kThreads) {
+    const float2 ms = st[c / cpg];
+    const float ga = gamma != nullptr ? to_float<D>(static_cast<const T*>(gamma)[c]) : 1.f;
+    const float be = beta != nullptr ? to_float<D>(static_cast<const T*>(beta)[c]) : 0.f;
+    s_scale[c] = ms.y * ga;
+    s_shift[c] = be - ms.x * ms.y * ga;
+  }
+  __syncthreads();
+  const int words = channels / E;
+  const int rpb = kThreads / words;  // words <= 256
+  const int rl = threadIdx.x / words, w = threadIdx.x - rl * words;
+  if (rl >= rpb) return;
+  const unsigned char* xb = static_cast<const unsigned char*>(x);
+  unsigned char* yb = static_cast<unsigned char*>(y);
+  float sc[E], sh[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    sc[e] = s_scale[w * E + e];
+    sh[e] = s_shift[w * E + e];
+  }
+#pragma unroll 4
+  for (int64_t r = seg.r0 + rl; r < seg.r1; r += rpb) {
+    const int64_t byte = (r * words + w) * 16;
+    const uint4 raw = *reinterpret_cast<const uint4*>(xb + byte);
+    float v[E];
+    unpack<D, E>(raw, v);
+    uint4 outw;
+    unsigned char* ob = reinterpret_cast<unsigned char*>(&outw);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float o = activate<ACT>(fmaf(v[e], sc[e], sh[e]));
+      if constexpr (D == DT::F32) reinterpret_cast<float*>(ob)[e] = o;
+      else reinterpret_cast<uint16_t*>(ob)[e] = from_float<D>(o);
+    }
+    *reinterpret_cast<uint4*>(yb + byte) = outw;
+  }
+}
+
+template <DT D, int E, int ACT>
+hipError_t launch_apply(const void* x, void* y, int64_t n, int channels, const int64_t* off, int items, int groups,
+                        const float2* stats, const void* gamma, const void* beta, int64_t R, int64_t segments,
+                        hipStream_t stream) {
+  gn_apply_kernel<D, E, ACT><<<(unsigned)segments, kThreads, 0, stream>>>(x, y, n, channels, off, items, R, groups,
+                                                                          stats, gamma, beta);
+  return hipGetLastError();
+}
+
+template <DT D>
+hipError_t launch_dtype(const void* x, int64_t n, int channels, const int64_t* off, int items, int groups,
+                        const void* gamma, const void* beta, float eps, int act, void* y, float2* part,
+                        int32_t* part_rows, float2* stats, int64_t R, int64_t segments, hipStream_t stream) {
+  constexpr int E = D == DT::F32 ? 4 : 8;
+  gn_partial_kernel<D, E><<<(unsigned)segments, kThreads, 0, stream>>>(x, n, channels, off, items, R, groups, part,
+                                                                       part_rows);
+  gn_stats_kernel<<<(unsigned)items, kStatThreads, 0, stream>>>(part, part_rows, off, n, R, groups, channels / groups,
+                                                                eps, stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (act) {
+    case SUBM_ACT_SILU:
+      return launch_apply<D, E, SUBM_ACT_SILU>(x, y, n, channels, off, items, groups, stats, gamma, beta, R, segments,
+                                       stream);
+    case SUBM_ACT_RELU:
+      return launch_apply<D, E, SUBM_ACT_RELU>(x, y, n, channels, off, items, groups, stats, gamma, beta, R, segments,
+                                       stream);
+    default:
+      return launch_apply<D, E, SUBM_ACT_NONE>(x, y, n, channels, off, items, groups, stats, gamma, beta, R, segments,
+                                       stream);
+  }
+}
+
+}  // namespace
+}  // namespace submconv
+
+using namespace submconv;
+
+extern "C" int sparse_group_norm_act(const void* x, int64_t n, int channels, int dtype, const int64_t* item_offsets,
+                                     int num_items, int groups, const void* gamma, const void* beta, float eps, int act,
+                                     void* y, hipStream_t stream) {
+  clear_error();
+  if (dtype != SUBM_F32 && dtype != SUBM_F16 && dtype != SUBM_BF16)
+    return fail(SUBM_ERR_UNSUPPORTED, "dtype must be SUBM_F32, SUBM_F16 or SUBM_BF16");
+  if (act != SUBM_ACT_NONE && act != SUBM_ACT_SILU && act != SUBM_ACT_RELU)
+    return fail(SUBM_ERR_INVALID_ARG, "act must be SUBM_ACT_NONE, SUBM_ACT_SILU or SUBM_ACT_RELU");
+  if (n < 0 || n > INT32_MAX) return fail(SUBM_ERR_INVALID_ARG, "n must be in [0, 2^31 - 1]");
+  if (channels < 1 || channels > 4096) return fail(SUBM_ERR_INVALID_ARG, "channels must be in [1, 4096]");
+  if (groups < 1 || channels % groups != 0) return fail(SUBM_ERR_INVALID_ARG, "groups must divide channels");
+  if (num_items < 1 || num_items > 65535) return fail(SUBM_ERR_INVALID_ARG, "num_items must be in [1, 65535]");
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(SUBM_ERR_INVALID_ARG, "eps must be a positive finite number");
+  const int elem = dtype == SUBM_F32 ? 4 : 2;
+  if ((channels * elem) % 16 != 0 || channels * elem > 4096)
+    return fail(SUBM_ERR_UNSUPPORTED, "rows must be a multiple of 16 bytes and at most 4096 bytes");
+  if (n == 0) return SUBM_OK;
+  if (x == nullptr || y == nullptr || item_offsets == nullptr) return fail(SUBM_ERR_INVALID_ARG, "x, y or item_offsets is NULL");
+  if (((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) != 0)
+    return fail(SUBM_ERR_UNSUPPORTED, "x and y must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(item_offsets) & 7u) != 0) return fail(SUBM_ERR_INVALID_ARG, "item_offsets is not 8-byte aligned");
+  if (((reinterpret_cast<uintptr_t>(gamma) | reinterpret_cast<uintptr_t>(beta)) % elem) != 0)
+    return fail(SUBM_ERR_INVALID_ARG, "gamma / beta not aligned to the element size");
+  const int64_t rmul = std::max<int64_t>(1, (n + 256 * (int64_t)kMaxSegmentsPerRun - 1) / (256 * (int64_t)kMaxSegmentsPerRun));
+  const int64_t R = 256 * rmul;
+  const int64_t segments = num_items + (n + R - 1) / R;
+  const size_t part_bytes = (size_t)segments * groups * sizeof(float2);
+  const size_t rows_bytes = ((size_t)segments * sizeof(int32_t) + 255) / 256 * 256;
+  const size_t stats_bytes = (size_t)num_items * groups * sizeof(float2);
+  void* scratch = nullptr;
+  Status s = device_alloc(&scratch, part_bytes + rows_bytes + stats_bytes, stream);
+  if (!s.ok()) return fail(s);
+  unsigned char* base = static_cast<unsigned char*>(scratch);
+  float2* part = reinterpret_cast<float2*>(base);
+  int32_t* part_rows = reinterpret_cast<int32_t*>(base + part_bytes);
+  float2* stats = reinterpret_cast<float2*>(base + part_bytes + rows_bytes);
+  hipError_t e;
+  switch (dtype) {
+    case SUBM_F32:
+      e = launch_dtype<DT::F32>(x, n, channels, item_offsets, num_items, groups, gamma, beta, eps, act, y, part,
+                                part_rows, stats, R, segments, stream);
+      break;
+    case SUBM_F16:
+      e = launch_dtype<DT::F16>(x, n, channels, item_offsets, num_items, groups, gamma, beta, eps, act, y, part,
+                                part_rows, stats, R, segments, stream);
+      break;
+    default:
+      e = launch_dtype<DT::BF16>(x, n, channels, item_offsets, num_items, groups, gamma, beta, eps, act, y, part,
+                                 part_rows, stats, R, segments, stream);
+      break;
+  }
+  device_free(scratch, stream);
+  if (e != hipSuccess) return fail(hip_status(e, "sparse_group_norm_act launch"));
+  return SUBM_OK;
+}

@@ -7,6 +7,7 @@
 // inclusive scan (the downsample's distinct cells in ascending order, and the masked upsample's
 // child positions).
 #include <cstring>
+#include <algorithm>
 #include <climits>
 #include <mutex>
 #include <new>
@@ -29,20 +30,15 @@ int grid_for(int64_t items, int per_thread = 1) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Per-column minimum and maximum of (b, z, y, x).  Integer min / max atomics are order-free, so
-// the result is exact whatever the schedule.
+// Per-column minimum and maximum of (b, z, y, x): per-block partials, then one block reduces them
+// (no atomics: with every wave hitting the same eight words they serialise in L2).
 
 struct CoordRange {
   int32_t mn[4];
   int32_t mx[4];
 };
 
-__global__ void range_init_kernel(CoordRange* r) {
-  if (threadIdx.x < 4) {
-    r->mn[threadIdx.x] = INT_MAX;
-    r->mx[threadIdx.x] = INT_MIN;
-  }
-}
+constexpr int kRangeBlocks = 256;
 
 __device__ __forceinline__ int wave_min(int v) {
 #pragma unroll
@@ -55,8 +51,33 @@ __device__ __forceinline__ int wave_max(int v) {
   return v;
 }
 
-__global__ __launch_bounds__(kThreads) void range_kernel(const int4* __restrict__ coords, int64_t n,
-                                                         CoordRange* __restrict__ r) {
+// Block-wide min / max of 4 columns; the result is valid in thread 0.
+__device__ __forceinline__ void block_range(int (&mn)[4], int (&mx)[4]) {
+  __shared__ int s[kThreads / 64][8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    mn[c] = wave_min(mn[c]);
+    mx[c] = wave_max(mx[c]);
+  }
+  if (lane == 0)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      s[wave][c] = mn[c];
+      s[wave][4 + c] = mx[c];
+    }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int w = 1; w < kThreads / 64; ++w)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        mn[c] = min(mn[c], s[w][c]);
+        mx[c] = max(mx[c], s[w][4 + c]);
+      }
+}
+
+__global__ __launch_bounds__(kThreads) void range_partial_kernel(const int4* __restrict__ coords, int64_t n,
+                                                                 CoordRange* __restrict__ partials) {
   int mn[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
   int mx[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
@@ -66,15 +87,32 @@ __global__ __launch_bounds__(kThreads) void range_kernel(const int4* __restrict_
     mn[2] = min(mn[2], c.z); mx[2] = max(mx[2], c.z);
     mn[3] = min(mn[3], c.w); mx[3] = max(mx[3], c.w);
   }
+  block_range(mn, mx);
+  if (threadIdx.x == 0)
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int a = wave_min(mn[c]);
-    const int b = wave_max(mx[c]);
-    if ((threadIdx.x & 63) == 0) {
-      atomicMin(&r->mn[c], a);
-      atomicMax(&r->mx[c], b);
+    for (int c = 0; c < 4; ++c) {
+      partials[blockIdx.x].mn[c] = mn[c];
+      partials[blockIdx.x].mx[c] = mx[c];
     }
-  }
+}
+
+__global__ __launch_bounds__(kThreads) void range_final_kernel(const CoordRange* __restrict__ partials, int nparts,
+                                                               CoordRange* __restrict__ r) {
+  int mn[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+  int mx[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+  for (int b = threadIdx.x; b < nparts; b += kThreads)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      mn[c] = min(mn[c], partials[b].mn[c]);
+      mx[c] = max(mx[c], partials[b].mx[c]);
+    }
+  block_range(mn, mx);
+  if (threadIdx.x == 0)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      r->mn[c] = mn[c];
+      r->mx[c] = mx[c];
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -221,64 +259,92 @@ template <> __device__ __forceinline__ void store_f<DT::BF16>(void* p, int64_t i
   static_cast<uint16_t*>(p)[idx] = (uint16_t)(__builtin_bit_cast(uint32_t, h) & 0xFFFFu);
 }
 
-// One thread per (coarse row, element group of E elements); E = 16 bytes / element size on the
-// vector path, 1 otherwise.
+// Row-by-word thread layout shared by the feature kernels: a block covers rpb rows per step,
+// words consecutive threads per row (words = 16-byte chunks or elements of a row), so no thread
+// divides its item index.  Rows wider than the block take several passes of the same threads.
+struct RowLanes {
+  int rpb;    // rows per block step
+  int r;      // this thread's row within the step (r >= rpb: idle)
+  int w0;     // first word of this thread
+  int wstep;  // word stride
+  __device__ RowLanes(int words) {
+    if (words >= kThreads) {
+      rpb = 1, r = 0, w0 = threadIdx.x, wstep = kThreads;
+    } else {
+      rpb = kThreads / words;
+      r = threadIdx.x / words;
+      w0 = threadIdx.x - r * words;
+      wstep = words;
+    }
+  }
+};
+
+// Pooling: for every coarse row m and element group of E elements (E = 16 bytes / element size
+// on the vector path, 1 otherwise), max or mean over the members.
 template <DT D, int E, bool MAX>
 __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__ fine, void* __restrict__ coarse,
                                                         int64_t n_coarse, int channels,
                                                         const int32_t* __restrict__ seg_off,
                                                         const int32_t* __restrict__ seg_rows) {
-  const int groups = channels / E;
-  const int64_t items = n_coarse * groups;
-  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < items; t += (int64_t)gridDim.x * kThreads) {
-    const int64_t m = t / groups;
-    const int c0 = (int)(t - m * groups) * E;
+  const int words = channels / E;
+  const RowLanes L(words);
+  if (L.r >= L.rpb) return;
+  for (int64_t m = (int64_t)blockIdx.x * L.rpb + L.r; m < n_coarse; m += (int64_t)gridDim.x * L.rpb) {
     const int32_t lo = seg_off[m], hi = seg_off[m + 1];
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = MAX ? -__builtin_inff() : 0.f;
-    for (int32_t q = lo; q < hi; ++q) {
-      const int64_t f = seg_rows != nullptr ? seg_rows[q] : q;
-      const int64_t base = f * channels + c0;
-      if constexpr (E > 1) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(fine) +
-                                                          base * (16 / E));
-        const unsigned char* b = reinterpret_cast<const unsigned char*>(&raw);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float v = load_f<D>(b, e);
-          acc[e] = MAX ? fmaxf(acc[e], v) : acc[e] + v;
-        }
-      } else {
-        const float v = load_f<D>(fine, base);
-        acc[0] = MAX ? fmaxf(acc[0], v) : acc[0] + v;
-      }
-    }
     const int cnt = hi - lo;
-    const int64_t obase = m * channels + c0;
-    if constexpr (E > 1) {
-      uint4 raw;
-      unsigned char* b = reinterpret_cast<unsigned char*>(&raw);
+    for (int w = L.w0; w < words; w += L.wstep) {
+      const int c0 = w * E;
+      float acc[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) store_f<D>(b, e, cnt == 0 ? 0.f : (MAX ? acc[e] : acc[e] / (float)cnt));
-      *reinterpret_cast<uint4*>(static_cast<unsigned char*>(coarse) + obase * (16 / E)) = raw;
-    } else {
-      store_f<D>(coarse, obase, cnt == 0 ? 0.f : (MAX ? acc[0] : acc[0] / (float)cnt));
+      for (int e = 0; e < E; ++e) acc[e] = MAX ? -__builtin_inff() : 0.f;
+      for (int32_t q = lo; q < hi; ++q) {
+        const int64_t f = seg_rows != nullptr ? seg_rows[q] : q;
+        const int64_t base = f * channels + c0;
+        if constexpr (E > 1) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(fine) + base * (16 / E));
+          const unsigned char* b = reinterpret_cast<const unsigned char*>(&raw);
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float v = load_f<D>(b, e);
+            acc[e] = MAX ? fmaxf(acc[e], v) : acc[e] + v;
+          }
+        } else {
+          const float v = load_f<D>(fine, base);
+          acc[0] = MAX ? fmaxf(acc[0], v) : acc[0] + v;
+        }
+      }
+      const int64_t obase = m * channels + c0;
+      if constexpr (E > 1) {
+        uint4 raw;
+        unsigned char* b = reinterpret_cast<unsigned char*>(&raw);
+#pragma unroll
+        for (int e = 0; e < E; ++e) store_f<D>(b, e, cnt == 0 ? 0.f : (MAX ? acc[e] : acc[e] / (float)cnt));
+        *reinterpret_cast<uint4*>(static_cast<unsigned char*>(coarse) + obase * (16 / E)) = raw;
+      } else {
+        store_f<D>(coarse, obase, cnt == 0 ? 0.f : (MAX ? acc[0] : acc[0] / (float)cnt));
+      }
     }
   }
 }
 
-// fine[f] = coarse[parent[f]], W bytes per thread (16, 4 or 2).
+// fine[f] = coarse[parent[f]], copied in words W (16, 4 or 2 bytes).
 template <typename W>
 __global__ __launch_bounds__(kThreads) void expand_kernel(const W* __restrict__ coarse, W* __restrict__ fine,
                                                           int64_t n_fine, int words,
                                                           const int32_t* __restrict__ parent) {
-  const int64_t items = n_fine * words;
-  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < items; t += (int64_t)gridDim.x * kThreads) {
-    const int64_t f = t / words;
-    const int w = (int)(t - f * words);
-    fine[t] = coarse[(int64_t)parent[f] * words + w];
+  const RowLanes L(words);
+  if (L.r >= L.rpb) return;
+  for (int64_t f = (int64_t)blockIdx.x * L.rpb + L.r; f < n_fine; f += (int64_t)gridDim.x * L.rpb) {
+    const int64_t src = (int64_t)parent[f] * words;
+    for (int w = L.w0; w < words; w += L.wstep) fine[f * words + w] = coarse[src + w];
   }
+}
+
+// Blocks for a row-by-word launch over `rows` rows of `words` words.
+int row_grid(int64_t rows, int words) {
+  const int rpb = words >= kThreads ? 1 : kThreads / words;
+  const int64_t b = (rows + rpb - 1) / rpb;
+  return (int)(b < 1 ? 1 : (b > 16384 ? 16384 : b));
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -345,11 +411,16 @@ Status alloc_subdiv(SubdivData& d, bool with_seg_rows, hipStream_t stream) {
   return Status{};
 }
 
-// Launches the range reduction into `dev_range` and a copy of it into pinned host memory.
+// Device scratch of enqueue_range: the result followed by the per-block partials.
+constexpr size_t kRangeScratch = sizeof(CoordRange) * (kRangeBlocks + 1);
+
+// Launches the range reduction into `dev_range` (kRangeScratch bytes) and a copy of the result
+// into pinned host memory.
 hipError_t enqueue_range(const int32_t* coords, int64_t n, CoordRange* dev_range, CoordRange* host_range,
                          hipStream_t stream) {
-  range_init_kernel<<<1, 64, 0, stream>>>(dev_range);
-  range_kernel<<<grid_for(n, 4), kThreads, 0, stream>>>(reinterpret_cast<const int4*>(coords), n, dev_range);
+  const int blocks = (int)std::min<int64_t>(kRangeBlocks, (n + 4 * kThreads - 1) / (4 * kThreads));
+  range_partial_kernel<<<blocks, kThreads, 0, stream>>>(reinterpret_cast<const int4*>(coords), n, dev_range + 1);
+  range_final_kernel<<<1, kThreads, 0, stream>>>(dev_range + 1, blocks, dev_range);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return hipMemcpyAsync(host_range, dev_range, sizeof(CoordRange), hipMemcpyDeviceToHost, stream);
@@ -451,7 +522,7 @@ Status validate_features(const SubdivData& d, int channels, int dtype, const voi
 
 template <DT D, int E>
 hipError_t launch_pool(const SubdivData& d, int channels, bool max, const void* fine, void* coarse, hipStream_t stream) {
-  const int g = grid_for(d.n_coarse * (channels / E));
+  const int g = row_grid(d.n_coarse, channels / E);
   if (max)
     pool_kernel<D, E, true><<<g, kThreads, 0, stream>>>(fine, coarse, d.n_coarse, channels, d.seg_off, d.seg_rows);
   else
@@ -501,7 +572,7 @@ extern "C" int sparse_subdivide(const int32_t* coords, int64_t n, hipStream_t st
   const Pinned pin = pinned_block(d.device);
   Scratch range_buf(stream);
   Status s = pin.host == nullptr ? make_status(SUBM_ERR_OUT_OF_MEMORY, "pinned host block") : alloc_subdiv(d, false, stream);
-  if (s.ok()) s = device_alloc(&range_buf.p, 256, stream);
+  if (s.ok()) s = device_alloc(&range_buf.p, kRangeScratch, stream);
   if (!s.ok()) {
     device_free(d.block, stream);
     delete h;
@@ -565,16 +636,17 @@ extern "C" int sparse_upsample_masked_build(const int32_t* coords, const uint8_t
   }
   const size_t cb = align256((size_t)n * 4);
   Scratch scratch(stream);
-  Status s = device_alloc(&scratch.p, 256 + 2 * cb + align256(scan_tmp), stream);
+  const size_t rb = align256(kRangeScratch);
+  Status s = device_alloc(&scratch.p, rb + 2 * cb + align256(scan_tmp), stream);
   if (!s.ok()) {
     delete h;
     return fail(s);
   }
   unsigned char* b = static_cast<unsigned char*>(scratch.p);
   CoordRange* dev_range = reinterpret_cast<CoordRange*>(b);
-  int32_t* count = reinterpret_cast<int32_t*>(b + 256);
-  int32_t* incl = reinterpret_cast<int32_t*>(b + 256 + cb);
-  void* tmp_p = b + 256 + 2 * cb;
+  int32_t* count = reinterpret_cast<int32_t*>(b + rb);
+  int32_t* incl = reinterpret_cast<int32_t*>(b + rb + cb);
+  void* tmp_p = b + rb + 2 * cb;
   CoordRange* host_range = static_cast<CoordRange*>(pin.host);
   int32_t* host_total = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(pin.host) + 64);
 
@@ -639,7 +711,7 @@ extern "C" int sparse_downsample_build(const int32_t* coords, int64_t n, hipStre
     return fail(SUBM_ERR_OUT_OF_MEMORY, "pinned host block");
   }
   Scratch range_buf(stream);
-  Status s = device_alloc(&range_buf.p, 256, stream);
+  Status s = device_alloc(&range_buf.p, kRangeScratch, stream);
   if (!s.ok()) {
     delete h;
     return fail(s);
@@ -778,15 +850,15 @@ extern "C" int sparse_upsample_forward(sparse_subdivision_t s, int channels, int
   const int64_t nf = s->d.n_fine;
   if (row % 16 == 0 && ptrs % 16 == 0) {
     const int w = (int)(row / 16);
-    expand_kernel<uint4><<<grid_for(nf * w, 4), kThreads, 0, stream>>>(static_cast<const uint4*>(coarse),
+    expand_kernel<uint4><<<row_grid(nf, w), kThreads, 0, stream>>>(static_cast<const uint4*>(coarse),
                                                                        static_cast<uint4*>(fine), nf, w, s->d.parent);
   } else if (row % 4 == 0 && ptrs % 4 == 0) {
     const int w = (int)(row / 4);
-    expand_kernel<uint32_t><<<grid_for(nf * w, 4), kThreads, 0, stream>>>(static_cast<const uint32_t*>(coarse),
+    expand_kernel<uint32_t><<<row_grid(nf, w), kThreads, 0, stream>>>(static_cast<const uint32_t*>(coarse),
                                                                           static_cast<uint32_t*>(fine), nf, w, s->d.parent);
   } else {
     const int w = (int)(row / 2);
-    expand_kernel<uint16_t><<<grid_for(nf * w, 4), kThreads, 0, stream>>>(static_cast<const uint16_t*>(coarse),
+    expand_kernel<uint16_t><<<row_grid(nf, w), kThreads, 0, stream>>>(static_cast<const uint16_t*>(coarse),
                                                                           static_cast<uint16_t*>(fine), nf, w, s->d.parent);
   }
   hipError_t e = hipGetLastError();

@@ -146,7 +146,15 @@ def _zyx_rows(zyx: np.ndarray, b: int) -> np.ndarray:
 
 
 def coords_for(key: str) -> np.ndarray:
-    """int32 [N, 4] (b, z, y, x) coordinates of a config, deterministic."""
+    """int32 [N, 4] (b, z, y, x) coordinates of a config, deterministic.
+
+    "5_parent" is the level before config 5's last subdivision: the r = 28 shell subdivided twice
+    (2 x 256^3, every child kept), one copy per batch item.
+    """
+    if key == "5_parent":
+        base = np.argwhere(sphere_shell(64, 28.0, 1.0))
+        rows = [_zyx_rows(subdivide_keep(base, 2, 1.0, np.random.default_rng(0)), m) for m in range(2)]
+        return np.concatenate(rows, axis=0)
     cfg = CONFIGS[key]
     if key == "1":
         return _mask_rows(sphere_shell(16, 6.0, 1.0), 0)

@@ -148,3 +148,23 @@ def test_per_offset_rejects_bad_arguments(lib):
 
     assert po() == INVALID  # the per-offset path always needs a map
     assert b"map" in lib.subm_last_error()
+
+
+def test_group_norm_rejects_bad_arguments(lib):
+    def gn(x=256, n=10, c=64, dtype=2, off=512, items=1, groups=32, eps=1e-5, act=0, y=1024):
+        return lib.sparse_group_norm_act(x, n, c, dtype, off, items, groups, None, None, eps, act, y, None)
+
+    assert gn(dtype=3) == UNSUPPORTED
+    assert gn(act=7) == INVALID
+    assert gn(n=-1) == INVALID
+    assert gn(c=0) == INVALID
+    assert gn(groups=0) == INVALID
+    assert gn(groups=24) == INVALID  # does not divide 64
+    assert gn(items=0) == INVALID
+    assert gn(eps=0.0) == INVALID
+    assert gn(eps=float("nan")) == INVALID
+    assert gn(c=36, groups=4) == UNSUPPORTED  # 72-byte rows
+    assert gn(dtype=0, c=2048, groups=32) == UNSUPPORTED  # 8 KB rows
+    assert gn(n=0, x=None, y=None, off=None) == OK
+    assert gn(x=None) == INVALID
+    assert gn(x=264) == UNSUPPORTED  # not 16-byte aligned

@@ -64,3 +64,11 @@ def test_subdivide_children_c_order():
     rng = np.random.default_rng(0)
     kids = synth.subdivide_keep(base, 1, 1.1, rng)  # keep all
     assert kids.tolist() == [[2 + i, 4 + j, 6 + k] for i in (0, 1) for j in (0, 1) for k in (0, 1)]
+
+
+def test_config5_parent_level_count():
+    # two subdivisions of the 9,962-voxel shell, two items: 2 x 9,962 x 64
+    c = synth.coords_for("5_parent")
+    assert c.shape == (2 * 9962 * 64, 4)
+    # the shell spans 4 .. 60 of the 64^3 grid, so its children span 16 .. 243 of 256^3
+    assert c[:, 1:].min() == 16 and c[:, 1:].max() == 243
