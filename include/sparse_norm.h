@@ -52,7 +52,7 @@ typedef enum {
  *   x, y          16-byte aligned.
  *   y             device [n, channels] in `dtype`; may be the same pointer as x (in place);
  *                 any other overlap is undefined.
- * Scratch of about (num_items + min(n / 256, 4096)) * groups * 8 bytes comes from the library's
+ * Scratch of about (num_items + min(n / 256, 1024)) * groups * 8 bytes comes from the library's
  * pool.  The statistics of a group are exact up to float32 rounding within blocks of rows and
  * float64 combination across them; the result is bitwise reproducible run to run.  Never
  * synchronises.

@@ -17,24 +17,28 @@
 //         axis' extent (max - min) is at most 65534, which the build enforces.
 //
 // The structure is chosen on the device from the set's bounds, so the whole build needs one
-// host synchronisation (to read the error flags and counts at the end), and no structure is
+// host synchronisation, taken as soon as the insert kernel has finished: by then the plan and
+// insert kernels have written the error flags straight into pinned host memory, and the lookup
+// and reset kernels go on running while the caller enqueues its convolutions.  No structure is
 // ever cleared in full: the table area is all 0xFF bytes between builds (an empty cell is -1
 // and an empty slot is key ~0, row -1), and every build resets exactly what it wrote.
 //
 // Kernels, all on the caller's stream:
 //   map_bounds_kernel   per-block min/max of (b, z, y, x) and the batch-range flag -> partials
 //   map_plan_kernel     one block reduces the partials, picks the structure, publishes the plan
-//                       and zeroes the counters (a separate launch: signalling between blocks of
-//                       one kernel needs a device-scope fence, which writes back the whole L2 of
-//                       each XCD and costs far more than a launch)
+//                       (and its range flags and mode to the host) and zeroes the counters (a
+//                       separate launch: signalling between blocks of one kernel needs a
+//                       device-scope fence, which writes back the whole L2 of each XCD and costs
+//                       far more than a launch)
 //   map_insert_kernel   GRID: CAS the row into its cell; HASH: CAS the key into the table.  A
-//                       cell or key already taken by another row raises the duplicate flag.
+//                       cell or key already taken by another row raises the duplicate flag in
+//                       host memory (a plain store of a constant, so concurrent writers agree).
 //   map_lookup_kernel   one thread per voxel: 27 loads (GRID) or 27 probe sequences (HASH), nine
 //                       in flight at a time; the block's rows are staged in LDS and written as
 //                       one contiguous run of nbr; per-row 27-bit hit mask; hits counted per tap
 //                       with wave ballots and added to one of 16 counter banks
 //   map_reset_kernel    GRID: -1 back into every voxel's cell; HASH: the used slots emptied;
-//                       block 0 copies the statistics to pinned host memory
+//                       block 0 sums the per-tap counter banks into the map's own counts
 #include "internal.h"
 
 namespace submconv {
@@ -238,7 +242,8 @@ __device__ __forceinline__ int64_t grid_cell(const MapStats& p, int b, int z, in
 
 __global__ __launch_bounds__(kThreads) void map_plan_kernel(const BoundsPartial* __restrict__ partials, int nparts,
                                                             int64_t grid_budget_cells, int64_t slots,
-                                                            int mode_request, MapStats* __restrict__ st) {
+                                                            int mode_request, MapStats* __restrict__ st,
+                                                            MapHostFlags* __restrict__ host) {
   Plan plan;
   int32_t mx[4];
   reduce_plan(partials, nparts, grid_budget_cells, mode_request, plan, mx);
@@ -248,6 +253,8 @@ __global__ __launch_bounds__(kThreads) void map_plan_kernel(const BoundsPartial*
     st->mx[t] = mx[t];
   }
   if (t == 0) {
+    host->flags = plan.flags;
+    host->mode = plan.mode;
     st->flags = plan.flags;
     st->err_flags = 0;
     st->mode = plan.mode;
@@ -261,7 +268,8 @@ __global__ __launch_bounds__(kThreads) void map_plan_kernel(const BoundsPartial*
 }
 
 __global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __restrict__ coords, int64_t n,
-                                                              void* __restrict__ table, MapStats* __restrict__ st) {
+                                                              void* __restrict__ table, const MapStats* __restrict__ st,
+                                                              MapHostFlags* __restrict__ host) {
   Plan plan;
   plan.mode = st->mode;
   if (plan.mode == kModeNone) return;
@@ -301,8 +309,8 @@ __global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __r
       overflow |= !placed;
     }
   }
-  if (dup) atomicOr(&st->err_flags, kFlagDuplicate);
-  if (overflow) atomicOr(&st->err_flags, kFlagProbeOverflow);
+  if (dup) host->duplicate = 1u;
+  if (overflow) host->overflow = 1u;
 }
 
 // ------------------------------------------------------------------ lookup
@@ -396,15 +404,15 @@ __global__ __launch_bounds__(kThreads) void map_lookup_kernel(const int32_t* __r
 // ------------------------------------------------------------------ reset
 // Restores the all-0xFF table area: -1 into every voxel's cell (GRID) or every used slot
 // emptied (HASH, where the probe sequences rule out emptying slots one key at a time).  Block 0
-// also copies the statistics, final once the lookup has completed, to the pinned host buffer,
-// so the host needs no separate copy.
+// also sums the counter banks, final once the lookup has completed, into the map's counts.
 __global__ __launch_bounds__(kThreads) void map_reset_kernel(const int32_t* __restrict__ coords, int64_t n,
                                                              void* __restrict__ table,
                                                              const MapStats* __restrict__ st,
-                                                             uint32_t* __restrict__ host_stats) {
-  if (blockIdx.x == 0) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(st);
-    for (int w = threadIdx.x; w < (int)(sizeof(MapStats) / 4); w += kThreads) host_stats[w] = src[w];
+                                                             uint32_t* __restrict__ counts) {
+  if (blockIdx.x == 0 && threadIdx.x < 27) {
+    uint32_t c = 0;
+    for (int b = 0; b < kTapBanks; ++b) c += st->tap_counts[b][threadIdx.x];
+    counts[threadIdx.x] = c;
   }
   const int mode = st->mode;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -444,8 +452,8 @@ size_t map_table_bytes(int64_t n) {
 size_t map_partials_bytes(int64_t n) { return (size_t)map_bounds_blocks(n) * sizeof(BoundsPartial); }
 
 hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, void* table, void* partials,
-                            int32_t* nbr, uint32_t* masks, MapStats* stats, MapStats* host_stats,
-                            hipStream_t stream) {
+                            int32_t* nbr, uint32_t* masks, uint32_t* counts, MapStats* stats,
+                            MapHostFlags* host_flags, hipEvent_t inserted, hipStream_t stream) {
   BoundsPartial* parts = static_cast<BoundsPartial*>(partials);
   const int nb = map_bounds_blocks(n);
   const int64_t slots = map_hash_slots(n);
@@ -453,13 +461,15 @@ hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, 
   // One voxel per insert thread (each CAS is a full round trip), up to kMaxInsertBlocks blocks.
   const int insert_blocks = clamp_blocks((n + kThreads - 1) / kThreads, kMaxInsertBlocks);
   map_bounds_kernel<<<nb, kThreads, 0, stream>>>(coords, n, parts);
-  map_plan_kernel<<<1, kThreads, 0, stream>>>(parts, nb, budget, slots, mode_request, stats);
-  map_insert_kernel<<<insert_blocks, kThreads, 0, stream>>>(coords, n, table, stats);
+  map_plan_kernel<<<1, kThreads, 0, stream>>>(parts, nb, budget, slots, mode_request, stats, host_flags);
+  map_insert_kernel<<<insert_blocks, kThreads, 0, stream>>>(coords, n, table, stats, host_flags);
+  hipError_t e = hipEventRecord(inserted, stream);
+  if (e != hipSuccess) return e;
   map_lookup_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, stream>>>(coords, n, table, nbr,
                                                                                        masks, stats);
   const int64_t reset_items = n > slots ? n : slots;
   map_reset_kernel<<<clamp_blocks((reset_items + 4 * kThreads - 1) / (4 * kThreads), kMaxWideBlocks), kThreads, 0,
-                     stream>>>(coords, n, table, stats, reinterpret_cast<uint32_t*>(host_stats));
+                     stream>>>(coords, n, table, stats, counts);
   return hipGetLastError();
 }
 

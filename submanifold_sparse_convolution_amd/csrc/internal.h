@@ -73,6 +73,15 @@ constexpr uint32_t kFlagBatchRange = 2u;
 constexpr uint32_t kFlagProbeOverflow = 4u;
 constexpr uint32_t kFlagExtentRange = 8u;
 
+// Words the plan and insert kernels write straight into pinned host memory; the host reads them
+// once the insert kernel has completed.
+struct MapHostFlags {
+  uint32_t flags;      // kFlag* range bits of the plan
+  int32_t mode;        // kMode* of the plan
+  uint32_t duplicate;  // 1: a cell or key was taken twice
+  uint32_t overflow;   // 1: the hash probe ran out of slots
+};
+
 struct MapStats {
   int32_t mn[4];       // per-column minimum of (b, z, y, x)
   int32_t mx[4];       // per-column maximum
@@ -91,10 +100,15 @@ struct MapData {
   int device = 0;
   int mode = kModeHash;
   int64_t n = 0;
+  // Pair counts: valid once counts_ready (the build's lookup may still run when it returns; the
+  // counts arrive in dev_counts and are read on first use, see map_counts()).
+  bool counts_ready = false;
   int64_t pairs = 0;
   int64_t per_tap[27] = {};
   int32_t* nbr = nullptr;     // device [n, 27], input row order
   uint32_t* masks = nullptr;  // device [n]: bit k set when nbr[i, k] >= 0 (same allocation as nbr)
+  uint32_t* dev_counts = nullptr;  // device [27] per-tap pair counts (same allocation as nbr)
+  hipEvent_t ready = nullptr;      // recorded after the build's last kernel
   // Per-tap pair lists of the per-offset convolution, built on first use: the pairs of tap k
   // (k != 13) are pair_out / pair_in [pair_off[k] .. pair_off[k] + per_tap[k]), output row
   // ascending.  One allocation, pair_out first.
@@ -106,16 +120,17 @@ struct MapData {
 // Map build (indice_map.hip).  Enqueues on `stream`; does not synchronise.  `table` holds
 // map_table_bytes(n) and must be all 0xFF bytes on entry (it is again on completion: the build
 // resets what it wrote); `partials` holds map_partials_bytes(n), `stats` one MapStats (device).
-// The statistics end up in `host_stats` (device-visible pinned host memory) when the last
-// kernel completes.
+// `host_flags` (device address of pinned host memory, zeroed by the caller) holds the plan's
+// flags and mode and the insert's error flags once `inserted` (recorded after the insert
+// kernel) has completed; the per-tap counts reach `counts` (device [27]) with the last kernel.
 int64_t map_hash_slots(int64_t n);
 int64_t map_grid_budget_cells(int64_t n);
 int map_bounds_blocks(int64_t n);
 size_t map_table_bytes(int64_t n);
 size_t map_partials_bytes(int64_t n);
 hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, void* table, void* partials,
-                            int32_t* nbr, uint32_t* masks, MapStats* stats, MapStats* host_stats,
-                            hipStream_t stream);
+                            int32_t* nbr, uint32_t* masks, uint32_t* counts, MapStats* stats,
+                            MapHostFlags* host_flags, hipEvent_t inserted, hipStream_t stream);
 // Fill `bytes` bytes at `p` (16-byte aligned, bytes a multiple of 16) with `value` (each 32-bit
 // word).
 hipError_t launch_fill(void* p, size_t bytes, uint32_t value, hipStream_t stream);
@@ -162,8 +177,13 @@ struct SubdivData {
 // The opaque handle types of the C ABI.
 struct submconv_map {
   submconv::MapData d;
-  std::mutex pairs_mu;  // guards the lazy build of the per-tap pair lists
+  std::mutex mu;  // guards the lazy reads of the counts and the lazy build of the pair lists
 };
+
+namespace submconv {
+// Makes map->d.pairs / per_tap valid (waits for the build's last kernel on first use).
+Status map_counts(submconv_map* map);
+}  // namespace submconv
 struct sparse_subdivision {
   submconv::SubdivData d;
 };

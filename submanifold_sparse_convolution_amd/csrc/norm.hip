@@ -25,7 +25,7 @@ namespace submconv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxSegmentsPerRun = 4096;  // segment length R grows with n to keep this bound
+constexpr int kMaxSegmentsPerRun = 1024;  // segment length R grows with n to keep this bound
 
 __device__ __forceinline__ int64_t clamp_off(const int64_t* off, int b, int64_t n) {
   const int64_t v = off[b];

@@ -877,6 +877,8 @@ extern "C" int sparse_indice_map_subdivide(submconv_map_t parent_map, sparse_sub
   if (parent_map->d.device != s->d.device) return fail(SUBM_ERR_INVALID_ARG, "map and handle are on different devices");
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != s->d.device) return fail(SUBM_ERR_INVALID_ARG, "the handle was built on another device");
+  Status cs = map_counts(parent_map);
+  if (!cs.ok()) return fail(cs);
   submconv_map* m = new (std::nothrow) submconv_map;
   if (m == nullptr) return fail(SUBM_ERR_OUT_OF_MEMORY, "host allocation of the map handle failed");
   const int64_t np = s->d.n_coarse;
@@ -899,6 +901,7 @@ extern "C" int sparse_indice_map_subdivide(submconv_map_t parent_map, sparse_sub
     total += c;
   }
   m->d.pairs = total;
+  m->d.counts_ready = true;
   if (np == 0) {
     *out_map = m;
     return SUBM_OK;
@@ -912,7 +915,12 @@ extern "C" int sparse_indice_map_subdivide(submconv_map_t parent_map, sparse_sub
   m->d.nbr = static_cast<int32_t*>(nbr);
   m->d.masks = reinterpret_cast<uint32_t*>(m->d.nbr + (size_t)nc * 27);
   hipError_t e = launch_child_map(parent_map->d.nbr, np, m->d.nbr, m->d.masks, stream);
+  // The kernel writes the map's memory after this call returns; freeing the map waits for it.
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->d.ready, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(m->d.ready, stream);
   if (e != hipSuccess) {
+    (void)hipStreamSynchronize(stream);
+    if (m->d.ready != nullptr) (void)hipEventDestroy(m->d.ready);
     device_free(nbr, stream);
     delete m;
     return fail(hip_status(e, "child map launch"));

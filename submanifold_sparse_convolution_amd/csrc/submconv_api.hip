@@ -121,8 +121,19 @@ struct Workspace {
   std::mutex mu;
   void* ptr = nullptr;
   size_t bytes = 0;
+  // Recorded after the last kernel of the latest build: a build returns once its insert kernel
+  // is done, so the next build's kernels wait for this event (on the device) before they touch
+  // the shared structure.
+  hipEvent_t last = nullptr;
 };
 Workspace g_workspace[kMaxDevices];
+
+// Per-thread, per-device event recorded after the insert kernel; the build waits for it.
+hipEvent_t inserted_event(int dev) {
+  thread_local hipEvent_t ev[kMaxDevices] = {};
+  if (ev[dev] == nullptr && hipEventCreateWithFlags(&ev[dev], hipEventDisableTiming) != hipSuccess) ev[dev] = nullptr;
+  return ev[dev];
+}
 
 // Layout: [statistics | bounds partials | table area].  The table area is all 0xFF bytes
 // whenever no build is running (each build resets what it wrote), so a new allocation is filled.
@@ -150,10 +161,20 @@ Status workspace_reserve(Workspace& ws, size_t table_bytes, hipStream_t stream) 
   return Status{};
 }
 
-// The build statistics arrive in the calling thread's pinned block for the device (a thread
-// runs one build at a time): block 0 of the reset kernel writes them through its device
-// address, so the build needs no copy command.
-static_assert(sizeof(MapStats) <= kPinnedBytes, "statistics fit the pinned block");
+// The plan's flags and mode and the insert's error flags arrive in the calling thread's pinned
+// block for the device (a thread runs one build at a time): the kernels write them through its
+// device address, so the build needs no copy command.
+static_assert(sizeof(MapHostFlags) <= kPinnedBytes, "host flags fit the pinned block");
+
+void release_map(submconv_map* m, hipStream_t stream) {
+  if (m->d.ready != nullptr) {
+    (void)hipEventSynchronize(m->d.ready);  // the build's own kernels write the map memory
+    (void)hipEventDestroy(m->d.ready);
+  }
+  device_free(m->d.nbr, stream);
+  device_free(m->d.pair_out, stream);
+  delete m;
+}
 
 }  // namespace
 
@@ -186,11 +207,12 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
     return fail(SUBM_ERR_HIP, "device ordinal out of range");
   }
   const Pinned pinned = pinned_block(m->d.device);
-  if (pinned.host == nullptr) {
+  const hipEvent_t inserted = inserted_event(m->d.device);
+  if (pinned.host == nullptr || inserted == nullptr) {
     delete m;
-    return fail(SUBM_ERR_OUT_OF_MEMORY, "pinned host buffer for the build statistics");
+    return fail(SUBM_ERR_OUT_OF_MEMORY, "pinned host flags or build event");
   }
-  MapStats* host = static_cast<MapStats*>(pinned.host);
+  volatile MapHostFlags* host = static_cast<volatile MapHostFlags*>(pinned.host);
 
   const size_t table_bytes = round_up(map_table_bytes(n), 256);
   if (map_partials_bytes(n) > kPartialsBytes) {
@@ -200,11 +222,21 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
 
   Workspace& ws = g_workspace[m->d.device];
   std::lock_guard<std::mutex> lock(ws.mu);
+  hipError_t e = ws.last == nullptr ? hipEventCreateWithFlags(&ws.last, hipEventDisableTiming)
+                                    : hipStreamWaitEvent(stream, ws.last, 0);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->d.ready, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    if (m->d.ready != nullptr) (void)hipEventDestroy(m->d.ready);
+    delete m;
+    return fail(hip_status(e, "build events"));
+  }
   void* nbr = nullptr;
   Status s = workspace_reserve(ws, table_bytes, stream);
-  if (s.ok()) s = device_alloc(&nbr, (size_t)n * 28 * sizeof(int32_t), stream);  // nbr [n,27] + masks [n]
+  // nbr [n, 27], masks [n], counts [27]
+  if (s.ok()) s = device_alloc(&nbr, (size_t)n * 28 * sizeof(int32_t) + 128, stream);
   if (!s.ok()) {
     device_free(nbr, stream);
+    (void)hipEventDestroy(m->d.ready);
     delete m;
     return fail(s);
   }
@@ -213,17 +245,24 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
   void* partials = base + kStatsBytes;
   void* table = base + kStatsBytes + kPartialsBytes;
 
-  int32_t* nbr_rows = static_cast<int32_t*>(nbr);
-  uint32_t* masks = reinterpret_cast<uint32_t*>(nbr_rows + (size_t)n * 27);
-  hipError_t e = launch_map_build(coords, n, mode, table, partials, nbr_rows, masks, dstats, static_cast<MapStats*>(pinned.dev), stream);
-  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  m->d.nbr = static_cast<int32_t*>(nbr);
+  m->d.masks = reinterpret_cast<uint32_t*>(m->d.nbr + (size_t)n * 27);
+  m->d.dev_counts = m->d.masks + n;
+  host->flags = 0;
+  host->mode = kModeNone;
+  host->duplicate = 0;
+  host->overflow = 0;
+  e = launch_map_build(coords, n, mode, table, partials, m->d.nbr, m->d.masks, m->d.dev_counts, dstats,
+                       static_cast<MapHostFlags*>(pinned.dev), inserted, stream);
+  if (e == hipSuccess) e = hipEventRecord(m->d.ready, stream);
+  if (e == hipSuccess) e = hipEventRecord(ws.last, stream);
+  if (e == hipSuccess) e = hipEventSynchronize(inserted);
   if (e != hipSuccess) {
-    device_free(nbr, stream);
-    delete m;
+    (void)hipStreamSynchronize(stream);
+    release_map(m, stream);
     return fail(hip_status(e, "indice map build"));
   }
-  const MapStats& st = *host;
-  const uint32_t flags = st.flags | st.err_flags;
+  const uint32_t flags = host->flags;
   int code = SUBM_OK;
   const char* msg = "";
   if (flags & kFlagBatchRange) {
@@ -232,29 +271,18 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
   } else if (flags & kFlagExtentRange) {
     code = SUBM_ERR_COORD_RANGE;
     msg = "extent (max - min) of z, y or x exceeds 65534";
-  } else if (flags & kFlagDuplicate) {
+  } else if (host->duplicate) {
     code = SUBM_ERR_DUPLICATE_COORD;
     msg = "two rows share the same (b, z, y, x)";
-  } else if (flags & kFlagProbeOverflow) {
+  } else if (host->overflow) {
     code = SUBM_ERR_HIP;
     msg = "internal error: hash table full";
   }
   if (code != SUBM_OK) {
-    device_free(nbr, stream);
-    delete m;
+    release_map(m, stream);
     return fail(code, msg);
   }
-  m->d.nbr = nbr_rows;
-  m->d.masks = masks;
-  m->d.mode = st.mode;
-  int64_t total = 0;
-  for (int k = 0; k < 27; ++k) {
-    int64_t c = 0;
-    for (int b = 0; b < kTapBanks; ++b) c += st.tap_counts[b][k];
-    m->d.per_tap[k] = c;
-    total += c;
-  }
-  m->d.pairs = total;
+  m->d.mode = host->mode;
   *out_map = m;
   return SUBM_OK;
 }
@@ -272,15 +300,30 @@ extern "C" int sparse_indice_map_mode(submconv_map_t map, int* mode) {
   return SUBM_OK;
 }
 
+Status submconv::map_counts(submconv_map* map) {
+  std::lock_guard<std::mutex> lock(map->mu);
+  if (map->d.counts_ready) return Status{};
+  uint32_t c[27] = {};
+  if (map->d.n > 0) {
+    DeviceGuard guard(map->d.device);
+    if (map->d.ready != nullptr) SUBM_HIP_TRY(hipEventSynchronize(map->d.ready));
+    SUBM_HIP_TRY(hipMemcpy(c, map->d.dev_counts, sizeof(c), hipMemcpyDeviceToHost));
+  }
+  int64_t total = 0;
+  for (int k = 0; k < 27; ++k) {
+    map->d.per_tap[k] = c[k];
+    total += c[k];
+  }
+  map->d.pairs = total;
+  map->d.counts_ready = true;
+  return Status{};
+}
+
 extern "C" int sparse_indice_map_free(submconv_map_t map) {
   clear_error();
   if (map == nullptr) return SUBM_OK;
-  if (map->d.nbr != nullptr || map->d.pair_out != nullptr) {
-    DeviceGuard guard(map->d.device);
-    device_free(map->d.nbr, nullptr);
-    device_free(map->d.pair_out, nullptr);
-  }
-  delete map;
+  DeviceGuard guard(map->d.device);
+  release_map(map, nullptr);
   return SUBM_OK;
 }
 
@@ -288,7 +331,11 @@ extern "C" int sparse_indice_map_info(submconv_map_t map, int64_t* n, int64_t* p
   clear_error();
   if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
   if (n != nullptr) *n = map->d.n;
-  if (pairs != nullptr) *pairs = map->d.pairs;
+  if (pairs != nullptr) {
+    Status s = map_counts(map);
+    if (!s.ok()) return fail(s);
+    *pairs = map->d.pairs;
+  }
   return SUBM_OK;
 }
 
@@ -296,6 +343,8 @@ extern "C" int sparse_indice_map_offset_counts(submconv_map_t map, int64_t* coun
   clear_error();
   if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
   if (counts == nullptr) return fail(SUBM_ERR_INVALID_ARG, "counts is NULL");
+  Status s = map_counts(map);
+  if (!s.ok()) return fail(s);
   std::memcpy(counts, map->d.per_tap, sizeof(map->d.per_tap));
   return SUBM_OK;
 }
@@ -363,7 +412,9 @@ extern "C" int subm_conv3d_forward_per_offset(submconv_map_t map, int64_t n, int
   if (e != hipSuccess) return fail(hip_status(e, "hipGetDevice"));
   if (dev != map->d.device) return fail(SUBM_ERR_INVALID_ARG, "the map was built on another device");
   {
-    std::lock_guard<std::mutex> lock(map->pairs_mu);
+    Status cs = map_counts(map);
+    if (!cs.ok()) return fail(cs);
+    std::lock_guard<std::mutex> lock(map->mu);
     const int64_t off_centre = map->d.pairs - map->d.per_tap[13];
     if (map->d.pair_out == nullptr && off_centre > 0) {
       void* pairs = nullptr;
