@@ -172,7 +172,7 @@ int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int cin, int c
  * subm_conv3d_forward_per_offset -- the same SubMConv3d (ksize 3) as subm_conv3d_forward, computed
  * the per-offset way: for each of the 27 offsets, gather the neighbour rows of that offset,
  * multiply them by that offset's weight slice, and add the products into the output rows.  This
- * is the "obvious per-offset loop" the pages time their implementation against
+ * is the straightforward loop over the offsets that the pages time their implementation against
  * (trellis_sparse_mrp_mlx commit log, "Extracted from lato.2_mrp_mlx" commit), kept as a second
  * design for comparison and for very sparse tap sets.
  *   Arguments as subm_conv3d_forward with ksize = 3, plus these limits (else

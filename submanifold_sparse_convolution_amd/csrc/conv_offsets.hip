@@ -1,6 +1,6 @@
 // SubMConv3d as a loop over the 27 offsets: gather -> GEMM -> scatter-add per offset.
 //
-// This is the "obvious per-offset loop" the pages time their vectorised implementation against
+// This is the straightforward loop over the offsets that the pages time their vectorised version against
 // (trellis_sparse_mrp_mlx commit log, "Extracted from lato.2_mrp_mlx" commit: 5.9x slower on an
 // M3 Ultra), built here as a second MI355X design beside the output-stationary kernel of
 // conv.hip, computing the same
