@@ -2,7 +2,7 @@
 """Benchmark of the SubMConv3d hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload 3a] [--no-cpu-baseline]
-    python bench.py --op per-offset|subdivide|downsample|groupnorm [...]
+    python bench.py --op per-offset|subdivide|downsample|groupnorm|conv-groupnorm [...]
 
 One step = the whole hot path over one coordinate set already resident in HBM:
 build the indice map (hash insert + 27-neighbour lookup + one sync for the
@@ -20,8 +20,10 @@ the CPU oracle timed on a bounded sample of the same workload.
 per-offset (the same convolution computed offset by offset: gather -> GEMM ->
 scatter-add), subdivide (children, their features and the derived child map of
 the config-5 structure at its last level), downsample (2x cells, max pooling
-and the cache-paired upsample of the config-5 coordinate set) and groupnorm
-(group normalisation + SiLU over the config-5 set, 64 channels, 32 groups).
+and the cache-paired upsample of the config-5 coordinate set), groupnorm
+(group normalisation + SiLU over the config-5 set, 64 channels, 32 groups) and
+conv-groupnorm (one config-5 layer followed by that normalisation, with the
+statistics taken in the convolution's epilogue, timed beside conv + norm).
 """
 from __future__ import annotations
 
@@ -50,7 +52,8 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="3a", help="1, 2a (k3 + k1 layer), 3a, 3b, 4, 5")
-    p.add_argument("--op", default="conv", choices=["conv", "per-offset", "subdivide", "downsample", "groupnorm"])
+    p.add_argument("--op", default="conv",
+                   choices=["conv", "per-offset", "subdivide", "downsample", "groupnorm", "conv-groupnorm"])
     p.add_argument("--conv-reps", type=int, default=200, help="back-to-back launches timed for the roofline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target duration of the oracle sample")
@@ -156,7 +159,7 @@ def main():
         print("bench.py measures one GPU only: the submanifold convolution path here is a single-GPU "
               "build (see the sharding paragraph of the design notes); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    if args.op in ("subdivide", "downsample", "groupnorm"):
+    if args.op in ("subdivide", "downsample", "groupnorm", "conv-groupnorm"):
         bench_structure(args)
         return
     per_offset = args.op == "per-offset"
@@ -323,6 +326,7 @@ STRUCTURE_METRIC = {
     "subdivide": "subdivide + child features + derived child map: children per second (1 GPU)",
     "downsample": "2x downsample build + max pooling + cached upsample: fine voxels per second (1 GPU)",
     "groupnorm": "group normalisation (32 groups) + SiLU per batch item: voxels per second (1 GPU)",
+    "conv-groupnorm": "SubMConv3d + group normalisation + SiLU, statistics in the conv epilogue: voxels per second (1 GPU)",
 }
 
 
@@ -370,10 +374,14 @@ def bench_structure(args):
         base = synth.coords_for("5")
         workload = ("config-5 coordinate set: 2 x 512^3 subdivided shells keeping 25 % "
                     f"({len(base)} voxels) -> 2x cells, 64 bf16 channels")
-    else:
+    elif args.op == "groupnorm":
         base = synth.coords_for("5")
         workload = ("config-5 coordinate set: 2 x 512^3 subdivided shells keeping 25 % "
                     f"({len(base)} voxels, 2 items), 64 bf16 channels, 32 groups, SiLU")
+    else:
+        base = synth.coords_for("5")
+        workload = ("config-5 layer 0 (2 x 512^3 subdivided shells keeping 25 %, "
+                    f"{len(base)} voxels, 2 items, 64->64 bf16, k3) + group norm (32 groups) + SiLU")
     n = len(base)
     coords = torch.from_numpy(base).to(dev)
     feats = synth.round_to(np.random.default_rng(77).standard_normal((n, ch)), "bf16").to(dev)
@@ -401,6 +409,33 @@ def bench_structure(args):
             cm_holder.append(sc.sparse_indice_map_subdivide(pm, sub))
 
         kern["child_map_kernel"] = (child_map, float(n * 108 + 8 * n * 112))
+    elif args.op == "conv-groupnorm":
+        cfg = synth.config("5")
+        counts = np.bincount(base[:, 0])
+        offsets = torch.tensor([0] + np.cumsum(counts).tolist(), dtype=torch.int64, device=dev)
+        w = synth.weight_for(cfg.number, 0, 3, ch, ch, "bf16").to(dev)
+        bias = synth.bias_for(cfg.number, 0, ch, "bf16").to(dev)
+        gamma = synth.round_to(1.0 + 0.1 * np.random.default_rng(78).standard_normal(ch), "bf16").to(dev)
+        beta = synth.round_to(0.1 * np.random.default_rng(79).standard_normal(ch), "bf16").to(dev)
+        cmap = sc.sparse_indice_map_build(coords)
+        fused_out = torch.empty_like(feats)
+        conv_out = torch.empty_like(feats)
+        normed = torch.empty_like(feats)
+
+        def fused():
+            sc.subm_conv3d_forward_group_norm_act(cmap, feats, w, bias, offsets, 32, gamma, beta, 1e-5,
+                                                  sc.SUBM_ACT_SILU, out=fused_out)
+
+        def split():
+            sc.subm_conv3d_forward(cmap, feats, w, bias, out=conv_out)
+            sc.sparse_group_norm_act(conv_out, offsets, 32, gamma, beta, 1e-5, sc.SUBM_ACT_SILU, out=normed)
+
+        step = fused
+        items = n
+        sub = None
+        layer_bytes = float(n * ch * s + n * 108 + 27 * ch * ch * s + n * ch * s)  # conv alone, algorithmic
+        kern = {"conv + group norm, statistics in the epilogue": (fused, layer_bytes + 2 * n * ch * s),
+                "conv, then separate group norm": (split, layer_bytes + 3 * n * ch * s)}
     elif args.op == "groupnorm":
         counts = np.bincount(base[:, 0])
         offsets = torch.tensor([0] + np.cumsum(counts).tolist(), dtype=torch.int64, device=dev)
@@ -454,9 +489,13 @@ def bench_structure(args):
         for cm in cm_holder:
             cm.free()
         pm.free()
+    if args.op == "conv-groupnorm":
+        cmap.free()
     if sub is not None:
         sub.free()
     dom = max(per_kernel, key=lambda k: per_kernel[k]["avg_launch_ms"])
+    if args.op == "conv-groupnorm":
+        dom = "conv + group norm, statistics in the epilogue"
     achieved = per_kernel[dom]["achieved_GBps"]
     result = {
         "metric": STRUCTURE_METRIC[args.op],
@@ -515,7 +554,8 @@ def structure_cpu_baseline(op, base, budget_s):
         elapsed = time.perf_counter() - t0
     out_rows = 8 * rows if op == "subdivide" else rows
     what = {"subdivide": "structure_ref.subdivide", "downsample": "structure_ref.downsample",
-            "groupnorm": "norm_ref.group_norm_act (numpy, 64 channels, 32 groups, one item)"}[op]
+            "groupnorm": "norm_ref.group_norm_act (numpy, 64 channels, 32 groups, one item)",
+            "conv-groupnorm": "norm_ref.group_norm_act only (numpy, 64 channels, 32 groups, one item)"}[op]
     return {"value": out_rows / elapsed, "unit": "voxels/s", "cores": 1, "kind": "oracle",
             "sample": f"oracle {what} on the first {rows} of {len(base)} input rows; {elapsed:.2f} s"}
 

@@ -62,6 +62,28 @@ int sparse_group_norm_act(const void* x, int64_t n, int channels, int dtype, con
                           int num_items, int groups, const void* gamma, const void* beta, float eps, int act,
                           void* y, hipStream_t stream);
 
+/*
+ * subm_conv3d_forward_group_norm_act -- out = act(group_norm(SubMConv3d(feats))), the
+ * convolution followed by the normalisation of the residual blocks, with the group statistics
+ * gathered in the convolution's epilogue.
+ *   map .. bias   as subm_conv3d_forward (ksize 1 or 3); the convolution result is rounded to
+ *                 the storage dtype exactly as subm_conv3d_forward rounds it, and the statistics
+ *                 are taken of those rounded values, as a separate norm would see them.
+ *   item_offsets .. act  as sparse_group_norm_act, with channels = cout.
+ *   out           device [n, cout]; receives the convolution, then is normalised in place.
+ * On the 16-bit fast path (more than 32 output channels, groups not straddling a 64- or
+ * 128-channel column tile) the epilogue of the convolution kernel writes per-tile, per-group
+ * partial sums, so the output is read once less than conv + sparse_group_norm_act; other shapes
+ * run exactly those two calls.  Never synchronises.
+ * Errors: those of subm_conv3d_forward and sparse_group_norm_act.
+ * Source: the per-voxel layers that sandwich the convolution in the sparse blocks
+ * (lato.2_mrp_mlx README, "Status").
+ */
+int subm_conv3d_forward_group_norm_act(submconv_map_t map, int64_t n, int ksize, int cin, int cout, int dtype,
+                                       const void* feats, const void* weight, const void* bias,
+                                       const int64_t* item_offsets, int num_items, int groups, const void* gamma,
+                                       const void* beta, float eps, int act, void* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,7 @@ C_FUNCTIONS = (
     "sparse_upsample_forward",
     "sparse_indice_map_subdivide",
     "sparse_group_norm_act",
+    "subm_conv3d_forward_group_norm_act",
     "subm_status_string",
     "subm_last_error",
 )
@@ -102,6 +103,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.sparse_upsample_forward.argtypes = [vp, ci, ci, vp, vp, vp]
         lib.sparse_indice_map_subdivide.argtypes = [vp, vp, vp, ctypes.POINTER(vp)]
         lib.sparse_group_norm_act.argtypes = [vp, i64, ci, ci, vp, ci, ci, vp, vp, ctypes.c_float, ci, vp, vp]
+        lib.subm_conv3d_forward_group_norm_act.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, ci, ci, vp, vp,
+                                                           ctypes.c_float, ci, vp, vp]
         for name in C_FUNCTIONS[:-2]:
             getattr(lib, name).restype = ci
         lib.subm_status_string.argtypes = [ci]
@@ -509,6 +512,45 @@ def sparse_indice_map_subdivide(parent: IndiceMap, s: Subdivision, stream=None) 
 
 # --------------------------------------------------------------------------- normalisation
 
+def _norm_affine(c, dtype, gamma, beta):
+    ptrs = []
+    for t, name in ((gamma, "gamma"), (beta, "beta")):
+        if t is None:
+            ptrs.append(None)
+            continue
+        _device_tensor(t, name)
+        if t.dtype != dtype or tuple(t.shape) != (c,):
+            raise ValueError(f"{name} must be [C] in the activation dtype")
+        ptrs.append(t.data_ptr())
+    return ptrs
+
+
+def _offsets_arg(item_offsets):
+    _device_tensor(item_offsets, "item_offsets")
+    if item_offsets.dtype != torch.int64 or item_offsets.dim() != 1 or item_offsets.shape[0] < 2:
+        raise ValueError("item_offsets must be int64 [num_items + 1]")
+
+
+def subm_conv3d_forward_group_norm_act(m: IndiceMap | None, feats: torch.Tensor, weight: torch.Tensor,
+                                       bias: torch.Tensor | None, item_offsets: torch.Tensor, groups: int,
+                                       gamma: torch.Tensor | None = None, beta: torch.Tensor | None = None,
+                                       eps: float = 1e-5, act: int = SUBM_ACT_NONE,
+                                       out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """act(group_norm(SubMConv3d(feats))) with the group statistics taken in the conv epilogue."""
+    k, bias_ptr, out = _conv_args(feats, weight, bias, out)
+    _offsets_arg(item_offsets)
+    ptrs = _norm_affine(weight.shape[0], feats.dtype, gamma, beta)
+    lib = load_library()
+    handle = None if m is None else m.handle
+    with torch.cuda.device(feats.device):
+        st = lib.subm_conv3d_forward_group_norm_act(
+            handle, feats.shape[0], k, feats.shape[1], weight.shape[0], _DTYPE_CODES[feats.dtype], feats.data_ptr(),
+            weight.data_ptr(), bias_ptr, item_offsets.data_ptr(), item_offsets.shape[0] - 1, int(groups), ptrs[0],
+            ptrs[1], float(eps), int(act), out.data_ptr(), _stream_ptr(stream, feats.device))
+    _check(lib, "subm_conv3d_forward_group_norm_act", st)
+    return out
+
+
 def sparse_group_norm_act(x: torch.Tensor, item_offsets: torch.Tensor, groups: int,
                           gamma: torch.Tensor | None = None, beta: torch.Tensor | None = None,
                           eps: float = 1e-5, act: int = SUBM_ACT_NONE, out: torch.Tensor | None = None,
@@ -518,19 +560,9 @@ def sparse_group_norm_act(x: torch.Tensor, item_offsets: torch.Tensor, groups: i
     _device_tensor(x, "x")
     if x.dim() != 2 or x.dtype not in _DTYPE_CODES:
         raise ValueError("x must be [N, C] float32 / float16 / bfloat16")
-    _device_tensor(item_offsets, "item_offsets")
-    if item_offsets.dtype != torch.int64 or item_offsets.dim() != 1 or item_offsets.shape[0] < 2:
-        raise ValueError("item_offsets must be int64 [num_items + 1]")
+    _offsets_arg(item_offsets)
     c = x.shape[1]
-    ptrs = []
-    for t, name in ((gamma, "gamma"), (beta, "beta")):
-        if t is None:
-            ptrs.append(None)
-            continue
-        _device_tensor(t, name)
-        if t.dtype != x.dtype or tuple(t.shape) != (c,):
-            raise ValueError(f"{name} must be [C] in the dtype of x")
-        ptrs.append(t.data_ptr())
+    ptrs = _norm_affine(c, x.dtype, gamma, beta)
     if out is None:
         out = torch.empty_like(x)
     _device_tensor(out, "out")

@@ -54,6 +54,12 @@ struct ConvArgs {
   int vec_out;          // 16-byte output stores allowed
   uint32_t feats_bytes;  // n * row_bytes (fast path: < 2^31)
   uint32_t weight_bytes; // cout * taps * row_bytes (fast path: < 2^31)
+  // Group-norm partial sums of the rounded output (epilogue variant with statistics only):
+  // gn_part[tile * gn_groups + g] = (mean, sum of squared deviations) of group g over the tile's
+  // rows, groups of gn_cpg consecutive channels.
+  float2* gn_part;
+  int gn_cpg;
+  int gn_groups;
 };
 
 constexpr int kThreads = 256;
@@ -301,10 +307,15 @@ __global__ __launch_bounds__(kThreads, 2) void subm_conv_generic_kernel(const Co
 // Output tile epilogue shared by the matrix-core kernels: + bias, one RNE rounding, staged in
 // LDS (rows padded by 16 bytes, which spreads the 8-byte writes of 32 rows over the banks) in
 // two halves of the rows, then coalesced 16-byte global stores by all NT threads.
-template <DT D, int WM, int FM, int FN, int NT>
+//
+// STATS: also the group-norm partial sums of the tile's rounded outputs, read back from the
+// staged halves: per group of cpg channels, thread (g, row lane) sums x - K and (x - K)^2 over
+// its rows, with K the group's first value in the tile's first row (shifted sums stay accurate
+// when the mean is large against the spread); the row lanes are then added in order.
+template <DT D, int WM, int FM, int FN, int NT, bool STATS = false>
 __device__ __forceinline__ void epilogue_store(const ConvArgs& args, const f32x16_t (&acc)[FM][FN], unsigned char* ring,
                                                const float* s_bias, int64_t row0, int o0, int tid, bool has_acc,
-                                               int wm, int wn, int lane) {
+                                               int wm, int wn, int lane, int tile = 0) {
   using T = typename Elem<D>::T;
   constexpr int WN = 4 / WM, WTM = 32 * FM, WTN = 32 * FN, BM = WM * WTM, BN = WN * WTN;
   constexpr int HALF = BM / 2;
@@ -313,6 +324,13 @@ __device__ __forceinline__ void epilogue_store(const ConvArgs& args, const f32x1
   const int cout = args.cout;
   const int lrow = lane & 31, lk = lane >> 5;
   T* out = reinterpret_cast<T*>(args.out);
+  // statistics lanes: group g of the tile's columns, row lane rl of RL
+  const int cpg = STATS ? args.gn_cpg : 1;
+  const int gt = STATS ? BN / cpg : 1;
+  const int rl = tid / gt, gl = tid - (tid / gt) * gt, RL = NT / gt;
+  const int vrows = (int)((n - row0) < BM ? (n - row0) : BM);
+  const bool gvalid = STATS && rl < RL && o0 + gl * cpg < cout;
+  float sh = 0.f, s1 = 0.f, s2 = 0.f;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     if (has_acc && (wm * WTM) / HALF == pass) {
@@ -332,6 +350,21 @@ __device__ __forceinline__ void epilogue_store(const ConvArgs& args, const f32x1
       }
     }
     __syncthreads();
+    if constexpr (STATS) {
+      if (gvalid) {
+        const T* col = reinterpret_cast<const T*>(ring) + gl * cpg;
+        if (pass == 0) sh = to_float<D>(col[0]);  // tile row 0 is always a valid row
+        const int rend = vrows - pass * HALF < HALF ? vrows - pass * HALF : HALF;
+        for (int r = rl; r < rend; r += RL) {
+          const T* x = reinterpret_cast<const T*>(ring + r * SROW) + gl * cpg;
+          for (int c = 0; c < cpg; ++c) {
+            const float d = to_float<D>(x[c]) - sh;
+            s1 += d;
+            s2 += d * d;
+          }
+        }
+      }
+    }
     const int64_t rbase = row0 + pass * HALF;
     if (args.vec_out) {
       constexpr int CPR = BN * 2 / 16;
@@ -350,6 +383,22 @@ __device__ __forceinline__ void epilogue_store(const ConvArgs& args, const f32x1
       }
     }
     __syncthreads();
+  }
+  if constexpr (STATS) {
+    float* red = reinterpret_cast<float*>(ring);
+    red[tid] = s1;
+    red[NT + tid] = s2;
+    __syncthreads();
+    if (tid < gt && o0 + tid * cpg < cout) {
+      float t1 = 0.f, t2 = 0.f;
+      for (int q = 0; q < RL; ++q) {
+        t1 += red[q * gt + tid];
+        t2 += red[NT + q * gt + tid];
+      }
+      // thread tid < gt is row lane 0 of group tid: its own shift is the group's K
+      const float mean_d = t1 / (float)(vrows * cpg);
+      args.gn_part[(int64_t)tile * args.gn_groups + o0 / cpg + tid] = make_float2(sh + mean_d, fmaxf(t2 - t1 * mean_d, 0.f));
+    }
   }
 }
 
@@ -673,7 +722,7 @@ constexpr int kWsThreads = 512;
 // KP selects how far ahead the compute waves read fragments: 0 = a whole stage (two register
 // sets of a stage), 1 = one 16-channel step (two sets of a step, so wider slices fit the
 // register budget of two waves per SIMD; the stage barrier then sits before the last step).
-template <DT D, int WM, int FM, int FN, int SL, int TAPS, int KP>
+template <DT D, int WM, int FM, int FN, int SL, int TAPS, int KP, bool STATS = false>
 __global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_kernel(const ConvArgs args) {
   using Sh = MmaShape<WM, FM, FN, SL, TAPS>;
   constexpr int WTM = Sh::WTM, WTN = Sh::WTN, BM = Sh::BM, BN = Sh::BN, BNP = Sh::BNP;
@@ -963,17 +1012,17 @@ __global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_kernel(const ConvA
   __syncthreads();
 
   // Epilogue: compute waves stage + bias, one rounding; all 512 threads store.
-  epilogue_store<D, WM, FM, FN, kWsThreads>(args, acc, ring, s_bias, row0, o0, tid, !loader, wm, wn, lane);
+  epilogue_store<D, WM, FM, FN, kWsThreads, STATS>(args, acc, ring, s_bias, row0, o0, tid, !loader, wm, wn, lane, tile);
 }
 
-template <DT D, int WM, int FM, int FN, int SL, int TAPS, int KP = 0>
+template <DT D, int WM, int FM, int FN, int SL, int TAPS, int KP = 0, bool STATS = false>
 hipError_t launch_ws(const ConvArgs& a0, hipStream_t stream) {
   using Sh = MmaShape<WM, FM, FN, SL, TAPS>;
   ConvArgs a = a0;
   a.tiles_m = (int)((a.n + Sh::BM - 1) / Sh::BM);
   a.per_xcd = (a.tiles_m + 7) / 8;
   dim3 grid((unsigned)(8 * a.per_xcd), (unsigned)((a.cout + Sh::BN - 1) / Sh::BN));
-  subm_conv_ws_kernel<D, WM, FM, FN, SL, TAPS, KP><<<grid, kWsThreads, 0, stream>>>(a);
+  subm_conv_ws_kernel<D, WM, FM, FN, SL, TAPS, KP, STATS><<<grid, kWsThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -1109,6 +1158,49 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr uint64_t kOffsetLimit = 0x7FFFF000ull;  // below kOutOfRange with room for a row slice
 
 }  // namespace
+
+// Convolution whose epilogue also writes group-norm partial sums per (row tile, group).  Taken
+// only on the warp-specialised 16-bit fast path with groups that do not straddle column tiles;
+// otherwise returns hipErrorNotSupported and writes nothing (the caller runs the plain
+// convolution and a separate statistics pass).  *tile_rows receives the row-tile height.
+hipError_t launch_subm_conv_gn_partials(const MapData* map, int64_t n, int ksize, int cin, int cout, int dtype,
+                                        const void* feats, const void* weight, const void* bias, void* out,
+                                        float2* part, int cpg, int groups, int* tile_rows, hipStream_t stream) {
+  if (dtype == SUBM_F32 || cout <= 32) return hipErrorNotSupported;
+  ConvArgs a{};
+  a.feats = feats;
+  a.weight = weight;
+  a.bias = bias;
+  a.out = out;
+  a.nbr = ksize == 3 ? map->nbr : nullptr;
+  a.masks = ksize == 3 ? map->masks : nullptr;
+  a.n = n;
+  a.cin = cin;
+  a.cout = cout;
+  a.row_bytes = cin * 2;
+  a.vec_out = ((cout * 2) % 16 == 0) && aligned16(out);
+  const bool vec_in = (a.row_bytes % 16 == 0) && aligned16(feats) && aligned16(weight);
+  const int taps = ksize == 3 ? 27 : 1;
+  const uint64_t fb = (uint64_t)n * (uint64_t)a.row_bytes;
+  const uint64_t wb = (uint64_t)cout * (uint64_t)taps * (uint64_t)a.row_bytes;
+  const uint64_t nb = ksize == 3 ? (uint64_t)n * 27u * 4u : 0u;
+  if (!vec_in || fb >= kOffsetLimit || nb >= kOffsetLimit || wb >= kOffsetLimit) return hipErrorNotSupported;
+  a.feats_bytes = (uint32_t)fb;
+  a.weight_bytes = (uint32_t)wb;
+  a.gn_part = part;
+  a.gn_cpg = cpg;
+  a.gn_groups = groups;
+  const bool wide = cout > 64;  // the tiles launch_mma_auto picks: 192 x 128 above 64 channels, 256 x 64 below
+  const int bn = wide ? 128 : 64;
+  if (bn % cpg != 0) return hipErrorNotSupported;
+  *tile_rows = wide ? 192 : 256;
+  if (dtype == SUBM_F16) {
+    if (taps == 27) return wide ? launch_ws<DT::F16, 2, 3, 2, 128, 27, 1, true>(a, stream) : launch_ws<DT::F16, 4, 2, 2, 128, 27, 1, true>(a, stream);
+    return wide ? launch_ws<DT::F16, 2, 3, 2, 128, 1, 1, true>(a, stream) : launch_ws<DT::F16, 4, 2, 2, 128, 1, 1, true>(a, stream);
+  }
+  if (taps == 27) return wide ? launch_ws<DT::BF16, 2, 3, 2, 128, 27, 1, true>(a, stream) : launch_ws<DT::BF16, 4, 2, 2, 128, 27, 1, true>(a, stream);
+  return wide ? launch_ws<DT::BF16, 2, 3, 2, 128, 1, 1, true>(a, stream) : launch_ws<DT::BF16, 4, 2, 2, 128, 1, 1, true>(a, stream);
+}
 
 hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, int cout, int dtype,
                             const void* feats, const void* weight, const void* bias, void* out,

@@ -150,6 +150,12 @@ hipError_t launch_subm_conv_per_offset(const MapData& m, int cin, int cout, int 
                                        const void* weight, const void* bias, void* out, float* acc,
                                        hipStream_t stream);
 
+// Convolution whose epilogue also stores group-norm partials per (row tile, group) (conv.hip):
+// hipErrorNotSupported (nothing launched) when the shape does not take that path.
+hipError_t launch_subm_conv_gn_partials(const MapData* map, int64_t n, int ksize, int cin, int cout, int dtype,
+                                        const void* feats, const void* weight, const void* bias, void* out,
+                                        float2* part, int cpg, int groups, int* tile_rows, hipStream_t stream);
+
 // Convolution launcher (conv.hip).  Arguments already validated by the caller.
 hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, int cout, int dtype,
                             const void* feats, const void* weight, const void* bias, void* out,
@@ -183,6 +189,9 @@ struct submconv_map {
 namespace submconv {
 // Makes map->d.pairs / per_tap valid (waits for the build's last kernel on first use).
 Status map_counts(submconv_map* map);
+// Host-side checks of a convolution call (subm_conv3d_forward's rules).
+Status check_conv(submconv_map_t map, int64_t n, int ksize, int cin, int cout, int dtype, const void* feats,
+                  const void* weight, const void* bias, const void* out);
 }  // namespace submconv
 struct sparse_subdivision {
   submconv::SubdivData d;

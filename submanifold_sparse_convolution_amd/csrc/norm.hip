@@ -201,6 +201,144 @@ __global__ __launch_bounds__(kStatThreads) void gn_stats_kernel(const float2* __
   }
 }
 
+// Fused variant (statistics from the convolution epilogue).  The epilogue leaves per (row tile of
+// BM rows, group) partials over whole tiles; a tile that straddles an item boundary is recomputed
+// here from the stored output, only for the rows of the item (at most two such tiles per item).
+struct ItemTiles {
+  int64_t lo, hi;     // the item's rows
+  int64_t t0, t1;     // its first and last tile
+  bool b0, b1;        // first / last tile straddles an item boundary
+};
+__device__ __forceinline__ int64_t tile_rows(int64_t t, int64_t BM, int64_t n) {
+  return std::min(BM, n - t * BM);
+}
+__device__ __forceinline__ ItemTiles item_tiles(const int64_t* off, int b, int64_t n, int64_t BM) {
+  ItemTiles it;
+  it.lo = clamp_off(off, b, n);
+  it.hi = clamp_off(off, b + 1, n);
+  it.t0 = it.lo / BM;
+  it.t1 = it.hi > it.lo ? (it.hi - 1) / BM : it.t0;
+  it.b0 = !(it.t0 * BM >= it.lo && it.t0 * BM + tile_rows(it.t0, BM, n) <= it.hi);
+  it.b1 = !(it.t1 * BM >= it.lo && it.t1 * BM + tile_rows(it.t1, BM, n) <= it.hi);
+  return it;
+}
+
+// One block per (item, side): the item's rows in its first (side 0) or last (side 1) tile when that
+// tile straddles a boundary; an item inside one tile is side 0's alone.  bpart = (mean, M2) per
+// group, brows = rows (0: nothing to add).
+template <DT D>
+__global__ __launch_bounds__(kThreads) void gn_boundary_kernel(const void* __restrict__ y, int64_t n, int channels,
+                                                               const int64_t* __restrict__ off, int64_t BM, int groups,
+                                                               float2* __restrict__ bpart, int32_t* __restrict__ brows) {
+  using T = typename Elem<D>::T;
+  __shared__ float s1s[kThreads], s2s[kThreads];
+  const int b = blockIdx.x >> 1, side = blockIdx.x & 1;
+  const ItemTiles it = item_tiles(off, b, n, BM);
+  int64_t a = 0, e = 0;
+  if (it.hi > it.lo) {
+    if (side == 0 && it.b0) {
+      a = it.lo;
+      e = std::min(it.hi, it.t0 * BM + tile_rows(it.t0, BM, n));
+    } else if (side == 1 && it.b1 && it.t1 != it.t0) {
+      a = it.t1 * BM;
+      e = it.hi;
+    }
+  }
+  const int64_t slot = (int64_t)blockIdx.x;
+  if (threadIdx.x == 0) brows[slot] = (int32_t)(e > a ? e - a : 0);
+  const int cpg = channels / groups;
+  const T* x = static_cast<const T*>(y);
+  for (int g0 = 0; g0 < groups; g0 += kThreads) {
+    const int gn = std::min(kThreads, groups - g0);
+    const int RL = kThreads / gn;
+    const int g = g0 + threadIdx.x % gn, rl = threadIdx.x / gn;
+    float sh = 0.f, t1 = 0.f, t2 = 0.f;
+    if (e > a && rl < RL) {
+      sh = D == DT::F32 ? reinterpret_cast<const float*>(y)[a * channels + (int64_t)g * cpg]
+                        : to_float<D>(x[a * channels + (int64_t)g * cpg]);
+      for (int64_t r = a + rl; r < e; r += RL)
+        for (int c = 0; c < cpg; ++c) {
+          const int64_t idx = r * channels + (int64_t)g * cpg + c;
+          const float v = D == DT::F32 ? reinterpret_cast<const float*>(y)[idx] : to_float<D>(x[idx]);
+          const float d = v - sh;
+          t1 += d;
+          t2 += d * d;
+        }
+    }
+    s1s[threadIdx.x] = t1;
+    s2s[threadIdx.x] = t2;
+    __syncthreads();
+    if ((int)threadIdx.x < gn) {
+      float u1 = 0.f, u2 = 0.f;
+      for (int q = 0; q < RL; ++q) {
+        u1 += s1s[q * gn + threadIdx.x];
+        u2 += s2s[q * gn + threadIdx.x];
+      }
+      const float cnt = (float)((e > a ? e - a : 1) * cpg);
+      const float mean_d = u1 / cnt;
+      bpart[slot * groups + g] = e > a ? make_float2(sh + mean_d, fmaxf(u2 - u1 * mean_d, 0.f)) : make_float2(0.f, 0.f);
+    }
+    __syncthreads();
+  }
+}
+
+// One block per item: first boundary piece, then the interior tiles (strided chains and a fixed
+// tree, as in gn_stats_kernel), then the last boundary piece.
+__global__ __launch_bounds__(kStatThreads) void gn_stats_tiles_kernel(const float2* __restrict__ part,
+                                                                      const float2* __restrict__ bpart,
+                                                                      const int32_t* __restrict__ brows,
+                                                                      const int64_t* __restrict__ off, int64_t n,
+                                                                      int64_t BM, int groups, int cpg, float eps,
+                                                                      float2* __restrict__ stats) {
+  __shared__ double s_n[kStatThreads], s_m[kStatThreads], s_q[kStatThreads];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const ItemTiles it = item_tiles(off, b, n, BM);
+  if (it.hi <= it.lo) {
+    for (int g = tid; g < groups; g += kStatThreads) stats[(int64_t)b * groups + g] = make_float2(0.f, 0.f);
+    return;
+  }
+  const int64_t i0 = it.t0 + (it.b0 ? 1 : 0);
+  const int64_t i1 = it.t1 - ((it.b1 && it.t1 != it.t0) ? 1 : 0);  // interior tiles [i0, i1]
+  int tg = 1;
+  while (tg * 2 * groups <= kStatThreads) tg *= 2;
+  const int gpb = kStatThreads / tg;
+  for (int g0 = 0; g0 < groups; g0 += gpb) {
+    const int g = g0 + tid / tg, j = tid % tg;
+    const bool on = tid / tg < gpb && g < groups;
+    double na = 0.0, ma = 0.0, m2a = 0.0;
+    if (on)
+      for (int64_t t = i0 + j; t <= i1; t += tg) {
+        const float2 p = part[t * groups + g];
+        chan_combine(na, ma, m2a, (double)tile_rows(t, BM, n) * cpg, p.x, p.y);
+      }
+    s_n[tid] = na;
+    s_m[tid] = ma;
+    s_q[tid] = m2a;
+    __syncthreads();
+    for (int h = 1; h < tg; h <<= 1) {
+      if (on && (j % (2 * h)) == 0) {
+        double a = s_n[tid], m = s_m[tid], q = s_q[tid];
+        chan_combine(a, m, q, s_n[tid + h], s_m[tid + h], s_q[tid + h]);
+        s_n[tid] = a;
+        s_m[tid] = m;
+        s_q[tid] = q;
+      }
+      __syncthreads();
+    }
+    if (on && j == 0) {
+      double cn = 0.0, cm = 0.0, cq = 0.0;
+      const float2 f = bpart[(int64_t)(2 * b) * groups + g];
+      chan_combine(cn, cm, cq, (double)brows[2 * b] * cpg, f.x, f.y);
+      chan_combine(cn, cm, cq, s_n[tid], s_m[tid], s_q[tid]);
+      const float2 l = bpart[(int64_t)(2 * b + 1) * groups + g];
+      chan_combine(cn, cm, cq, (double)brows[2 * b + 1] * cpg, l.x, l.y);
+      const double var = cn > 0.0 ? cq / cn : 0.0;
+      stats[(int64_t)b * groups + g] = make_float2((float)cm, (float)(1.0 / sqrt(var + (double)eps)));
+    }
+    __syncthreads();
+  }
+}
+
 // Pass 3: one block per segment (one item).
 template <DT D, int E, int ACT>
 __global__ __launch_bounds__(kThreads) void gn_apply_kernel(const void* __restrict__ x, void* __restrict__ y, int64_t n,
@@ -285,6 +423,70 @@ hipError_t launch_dtype(const void* x, int64_t n, int channels, const int64_t* o
   }
 }
 
+// Host checks shared by both entry points (no HIP call).
+Status check_norm(int64_t n, int channels, int dtype, int num_items, int groups, float eps, int act) {
+  if (dtype != SUBM_F32 && dtype != SUBM_F16 && dtype != SUBM_BF16)
+    return make_status(SUBM_ERR_UNSUPPORTED, "dtype must be SUBM_F32, SUBM_F16 or SUBM_BF16");
+  if (act != SUBM_ACT_NONE && act != SUBM_ACT_SILU && act != SUBM_ACT_RELU)
+    return make_status(SUBM_ERR_INVALID_ARG, "act must be SUBM_ACT_NONE, SUBM_ACT_SILU or SUBM_ACT_RELU");
+  if (n < 0 || n > INT32_MAX) return make_status(SUBM_ERR_INVALID_ARG, "n must be in [0, 2^31 - 1]");
+  if (channels < 1 || channels > 4096) return make_status(SUBM_ERR_INVALID_ARG, "channels must be in [1, 4096]");
+  if (groups < 1 || channels % groups != 0) return make_status(SUBM_ERR_INVALID_ARG, "groups must divide channels");
+  if (num_items < 1 || num_items > 65535) return make_status(SUBM_ERR_INVALID_ARG, "num_items must be in [1, 65535]");
+  if (!(eps > 0.f) || !std::isfinite(eps)) return make_status(SUBM_ERR_INVALID_ARG, "eps must be a positive finite number");
+  const int elem = dtype == SUBM_F32 ? 4 : 2;
+  if ((channels * elem) % 16 != 0 || channels * elem > 4096)
+    return make_status(SUBM_ERR_UNSUPPORTED, "rows must be a multiple of 16 bytes and at most 4096 bytes");
+  return Status{};
+}
+
+Status check_norm_pointers(const void* x, const void* y, const int64_t* off, const void* gamma, const void* beta,
+                           int dtype) {
+  const int elem = dtype == SUBM_F32 ? 4 : 2;
+  if (x == nullptr || y == nullptr || off == nullptr) return make_status(SUBM_ERR_INVALID_ARG, "x, y or item_offsets is NULL");
+  if (((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) != 0)
+    return make_status(SUBM_ERR_UNSUPPORTED, "x and y must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(off) & 7u) != 0) return make_status(SUBM_ERR_INVALID_ARG, "item_offsets is not 8-byte aligned");
+  if (((reinterpret_cast<uintptr_t>(gamma) | reinterpret_cast<uintptr_t>(beta)) % elem) != 0)
+    return make_status(SUBM_ERR_INVALID_ARG, "gamma / beta not aligned to the element size");
+  return Status{};
+}
+
+// Segment length of the partials / apply passes for n rows.
+int64_t segment_rows(int64_t n) {
+  const int64_t rmul = std::max<int64_t>(1, (n + 256 * (int64_t)kMaxSegmentsPerRun - 1) / (256 * (int64_t)kMaxSegmentsPerRun));
+  return 256 * rmul;
+}
+
+template <DT D>
+hipError_t launch_apply_act(const void* x, void* y, int64_t n, int channels, const int64_t* off, int items, int groups,
+                            const float2* stats, const void* gamma, const void* beta, int act, hipStream_t stream) {
+  constexpr int E = D == DT::F32 ? 4 : 8;
+  const int64_t R = segment_rows(n);
+  const int64_t segments = items + (n + R - 1) / R;
+  switch (act) {
+    case SUBM_ACT_SILU:
+      return launch_apply<D, E, SUBM_ACT_SILU>(x, y, n, channels, off, items, groups, stats, gamma, beta, R, segments, stream);
+    case SUBM_ACT_RELU:
+      return launch_apply<D, E, SUBM_ACT_RELU>(x, y, n, channels, off, items, groups, stats, gamma, beta, R, segments, stream);
+    default:
+      return launch_apply<D, E, SUBM_ACT_NONE>(x, y, n, channels, off, items, groups, stats, gamma, beta, R, segments, stream);
+  }
+}
+
+// Statistics from the convolution's tile partials, then the apply pass in place.
+template <DT D>
+hipError_t launch_from_tiles(void* y, int64_t n, int channels, const int64_t* off, int items, int groups,
+                             const void* gamma, const void* beta, float eps, int act, const float2* part, int64_t BM,
+                             float2* bpart, int32_t* brows, float2* stats, hipStream_t stream) {
+  gn_boundary_kernel<D><<<(unsigned)(2 * items), kThreads, 0, stream>>>(y, n, channels, off, BM, groups, bpart, brows);
+  gn_stats_tiles_kernel<<<(unsigned)items, kStatThreads, 0, stream>>>(part, bpart, brows, off, n, BM, groups,
+                                                                      channels / groups, eps, stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_apply_act<D>(y, y, n, channels, off, items, groups, stats, gamma, beta, act, stream);
+}
+
 }  // namespace
 }  // namespace submconv
 
@@ -294,34 +496,19 @@ extern "C" int sparse_group_norm_act(const void* x, int64_t n, int channels, int
                                      int num_items, int groups, const void* gamma, const void* beta, float eps, int act,
                                      void* y, hipStream_t stream) {
   clear_error();
-  if (dtype != SUBM_F32 && dtype != SUBM_F16 && dtype != SUBM_BF16)
-    return fail(SUBM_ERR_UNSUPPORTED, "dtype must be SUBM_F32, SUBM_F16 or SUBM_BF16");
-  if (act != SUBM_ACT_NONE && act != SUBM_ACT_SILU && act != SUBM_ACT_RELU)
-    return fail(SUBM_ERR_INVALID_ARG, "act must be SUBM_ACT_NONE, SUBM_ACT_SILU or SUBM_ACT_RELU");
-  if (n < 0 || n > INT32_MAX) return fail(SUBM_ERR_INVALID_ARG, "n must be in [0, 2^31 - 1]");
-  if (channels < 1 || channels > 4096) return fail(SUBM_ERR_INVALID_ARG, "channels must be in [1, 4096]");
-  if (groups < 1 || channels % groups != 0) return fail(SUBM_ERR_INVALID_ARG, "groups must divide channels");
-  if (num_items < 1 || num_items > 65535) return fail(SUBM_ERR_INVALID_ARG, "num_items must be in [1, 65535]");
-  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(SUBM_ERR_INVALID_ARG, "eps must be a positive finite number");
-  const int elem = dtype == SUBM_F32 ? 4 : 2;
-  if ((channels * elem) % 16 != 0 || channels * elem > 4096)
-    return fail(SUBM_ERR_UNSUPPORTED, "rows must be a multiple of 16 bytes and at most 4096 bytes");
+  Status st = check_norm(n, channels, dtype, num_items, groups, eps, act);
+  if (!st.ok()) return fail(st);
   if (n == 0) return SUBM_OK;
-  if (x == nullptr || y == nullptr || item_offsets == nullptr) return fail(SUBM_ERR_INVALID_ARG, "x, y or item_offsets is NULL");
-  if (((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) != 0)
-    return fail(SUBM_ERR_UNSUPPORTED, "x and y must be 16-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(item_offsets) & 7u) != 0) return fail(SUBM_ERR_INVALID_ARG, "item_offsets is not 8-byte aligned");
-  if (((reinterpret_cast<uintptr_t>(gamma) | reinterpret_cast<uintptr_t>(beta)) % elem) != 0)
-    return fail(SUBM_ERR_INVALID_ARG, "gamma / beta not aligned to the element size");
-  const int64_t rmul = std::max<int64_t>(1, (n + 256 * (int64_t)kMaxSegmentsPerRun - 1) / (256 * (int64_t)kMaxSegmentsPerRun));
-  const int64_t R = 256 * rmul;
+  st = check_norm_pointers(x, y, item_offsets, gamma, beta, dtype);
+  if (!st.ok()) return fail(st);
+  const int64_t R = segment_rows(n);
   const int64_t segments = num_items + (n + R - 1) / R;
   const size_t part_bytes = (size_t)segments * groups * sizeof(float2);
   const size_t rows_bytes = ((size_t)segments * sizeof(int32_t) + 255) / 256 * 256;
   const size_t stats_bytes = (size_t)num_items * groups * sizeof(float2);
   void* scratch = nullptr;
-  Status s = device_alloc(&scratch, part_bytes + rows_bytes + stats_bytes, stream);
-  if (!s.ok()) return fail(s);
+  st = device_alloc(&scratch, part_bytes + rows_bytes + stats_bytes, stream);
+  if (!st.ok()) return fail(st);
   unsigned char* base = static_cast<unsigned char*>(scratch);
   float2* part = reinterpret_cast<float2*>(base);
   int32_t* part_rows = reinterpret_cast<int32_t*>(base + part_bytes);
@@ -343,5 +530,59 @@ extern "C" int sparse_group_norm_act(const void* x, int64_t n, int channels, int
   }
   device_free(scratch, stream);
   if (e != hipSuccess) return fail(hip_status(e, "sparse_group_norm_act launch"));
+  return SUBM_OK;
+}
+
+extern "C" int subm_conv3d_forward_group_norm_act(submconv_map_t map, int64_t n, int ksize, int cin, int cout,
+                                                  int dtype, const void* feats, const void* weight, const void* bias,
+                                                  const int64_t* item_offsets, int num_items, int groups,
+                                                  const void* gamma, const void* beta, float eps, int act, void* out,
+                                                  hipStream_t stream) {
+  clear_error();
+  Status st = check_conv(map, n, ksize, cin, cout, dtype, feats, weight, bias, out);
+  if (st.ok()) st = check_norm(n, cout, dtype, num_items, groups, eps, act);
+  if (!st.ok()) return fail(st);
+  if (n == 0) return SUBM_OK;
+  st = check_norm_pointers(out, out, item_offsets, gamma, beta, dtype);
+  if (!st.ok()) return fail(st);
+  const MapData* md = map == nullptr ? nullptr : &map->d;
+  // Scratch for the fused path (tile partials for the shortest tiles, boundary pieces, statistics).
+  const int64_t max_tiles = (n + 191) / 192;
+  const size_t part_bytes = ((size_t)max_tiles * groups * sizeof(float2) + 255) / 256 * 256;
+  const size_t bpart_bytes = ((size_t)2 * num_items * groups * sizeof(float2) + 255) / 256 * 256;
+  const size_t brows_bytes = ((size_t)2 * num_items * sizeof(int32_t) + 255) / 256 * 256;
+  const size_t stats_bytes = (size_t)num_items * groups * sizeof(float2);
+  void* scratch = nullptr;
+  st = device_alloc(&scratch, part_bytes + bpart_bytes + brows_bytes + stats_bytes, stream);
+  if (!st.ok()) return fail(st);
+  unsigned char* base = static_cast<unsigned char*>(scratch);
+  float2* part = reinterpret_cast<float2*>(base);
+  float2* bpart = reinterpret_cast<float2*>(base + part_bytes);
+  int32_t* brows = reinterpret_cast<int32_t*>(base + part_bytes + bpart_bytes);
+  float2* stats = reinterpret_cast<float2*>(base + part_bytes + bpart_bytes + brows_bytes);
+  int tile_rows = 0;
+  hipError_t e = launch_subm_conv_gn_partials(md, n, ksize, cin, cout, dtype, feats, weight, bias, out, part,
+                                              cout / groups, groups, &tile_rows, stream);
+  if (e == hipSuccess) {
+    e = dtype == SUBM_F16
+            ? launch_from_tiles<DT::F16>(out, n, cout, item_offsets, num_items, groups, gamma, beta, eps, act, part,
+                                         tile_rows, bpart, brows, stats, stream)
+            : launch_from_tiles<DT::BF16>(out, n, cout, item_offsets, num_items, groups, gamma, beta, eps, act, part,
+                                          tile_rows, bpart, brows, stats, stream);
+    device_free(scratch, stream);
+  } else if (e == hipErrorNotSupported) {
+    (void)hipGetLastError();
+    device_free(scratch, stream);
+    // Plain convolution, then the separate normalisation in place.
+    e = launch_subm_conv(md, n, ksize, cin, cout, dtype, feats, weight, bias, out, stream);
+    if (e == hipSuccess) {
+      const int rc = sparse_group_norm_act(out, n, cout, dtype, item_offsets, num_items, groups, gamma, beta, eps, act,
+                                           out, stream);
+      if (rc != SUBM_OK) return rc;
+    }
+  } else {
+    device_free(scratch, stream);
+  }
+  if (e != hipSuccess) return fail(hip_status(e, "subm_conv3d_forward_group_norm_act launch"));
   return SUBM_OK;
 }

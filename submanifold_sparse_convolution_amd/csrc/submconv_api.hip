@@ -359,31 +359,40 @@ extern "C" int sparse_indice_map_copy_nbr(submconv_map_t map, int32_t* nbr, hipS
   return SUBM_OK;
 }
 
+Status submconv::check_conv(submconv_map_t map, int64_t n, int ksize, int cin, int cout, int dtype, const void* feats,
+                            const void* weight, const void* bias, const void* out) {
+  if (ksize != 1 && ksize != 3) return make_status(SUBM_ERR_UNSUPPORTED, "ksize must be 1 or 3");
+  if (dtype != SUBM_F32 && dtype != SUBM_F16 && dtype != SUBM_BF16)
+    return make_status(SUBM_ERR_UNSUPPORTED, "dtype must be SUBM_F32, SUBM_F16 or SUBM_BF16");
+  if (n < 0) return make_status(SUBM_ERR_INVALID_ARG, "n is negative");
+  if (cin < 1 || cout < 1) return make_status(SUBM_ERR_INVALID_ARG, "cin and cout must be >= 1");
+  if (cin > (1 << 24) || cout > (1 << 24)) return make_status(SUBM_ERR_INVALID_ARG, "cin / cout above 2^24");
+  if (ksize == 3 && map == nullptr) return make_status(SUBM_ERR_INVALID_ARG, "map is NULL but ksize == 3");
+  if (map != nullptr && map->d.n != n) return make_status(SUBM_ERR_SHAPE_MISMATCH, "n differs from the map's voxel count");
+  if (n > INT32_MAX) return make_status(SUBM_ERR_INVALID_ARG, "n exceeds 2^31 - 1");
+  if (n == 0) return Status{};
+  if (feats == nullptr || weight == nullptr || out == nullptr)
+    return make_status(SUBM_ERR_INVALID_ARG, "feats, weight or out is NULL");
+  if (out == feats) return make_status(SUBM_ERR_INVALID_ARG, "out must not alias feats");
+  const uintptr_t elem = dtype == SUBM_F32 ? 4 : 2;
+  if ((reinterpret_cast<uintptr_t>(feats) | reinterpret_cast<uintptr_t>(weight) | reinterpret_cast<uintptr_t>(out) |
+       reinterpret_cast<uintptr_t>(bias)) % elem != 0)
+    return make_status(SUBM_ERR_INVALID_ARG, "a pointer is not aligned to the element size");
+  if (map != nullptr) {
+    int dev = -1;
+    SUBM_HIP_TRY(hipGetDevice(&dev));
+    if (dev != map->d.device) return make_status(SUBM_ERR_INVALID_ARG, "the map was built on another device");
+  }
+  return Status{};
+}
+
 extern "C" int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int cin, int cout, int dtype,
                                    const void* feats, const void* weight, const void* bias, void* out,
                                    hipStream_t stream) {
   clear_error();
-  if (ksize != 1 && ksize != 3) return fail(SUBM_ERR_UNSUPPORTED, "ksize must be 1 or 3");
-  if (dtype != SUBM_F32 && dtype != SUBM_F16 && dtype != SUBM_BF16) return fail(SUBM_ERR_UNSUPPORTED, "dtype must be SUBM_F32, SUBM_F16 or SUBM_BF16");
-  if (n < 0) return fail(SUBM_ERR_INVALID_ARG, "n is negative");
-  if (cin < 1 || cout < 1) return fail(SUBM_ERR_INVALID_ARG, "cin and cout must be >= 1");
-  if (cin > (1 << 24) || cout > (1 << 24)) return fail(SUBM_ERR_INVALID_ARG, "cin / cout above 2^24");
-  if (ksize == 3 && map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL but ksize == 3");
-  if (map != nullptr && map->d.n != n) return fail(SUBM_ERR_SHAPE_MISMATCH, "n differs from the map's voxel count");
-  if (n > INT32_MAX) return fail(SUBM_ERR_INVALID_ARG, "n exceeds 2^31 - 1");
+  Status s = check_conv(map, n, ksize, cin, cout, dtype, feats, weight, bias, out);
+  if (!s.ok()) return fail(s);
   if (n == 0) return SUBM_OK;
-  if (feats == nullptr || weight == nullptr || out == nullptr) return fail(SUBM_ERR_INVALID_ARG, "feats, weight or out is NULL");
-  if (out == feats) return fail(SUBM_ERR_INVALID_ARG, "out must not alias feats");
-  const uintptr_t elem = dtype == SUBM_F32 ? 4 : 2;
-  if ((reinterpret_cast<uintptr_t>(feats) | reinterpret_cast<uintptr_t>(weight) | reinterpret_cast<uintptr_t>(out) |
-       reinterpret_cast<uintptr_t>(bias)) % elem != 0)
-    return fail(SUBM_ERR_INVALID_ARG, "a pointer is not aligned to the element size");
-  if (map != nullptr) {
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(hip_status(e, "hipGetDevice"));
-    if (dev != map->d.device) return fail(SUBM_ERR_INVALID_ARG, "the map was built on another device");
-  }
   hipError_t e = launch_subm_conv(map == nullptr ? nullptr : &map->d, n, ksize, cin, cout, dtype, feats, weight, bias, out, stream);
   if (e != hipSuccess) return fail(hip_status(e, "subm_conv3d_forward launch"));
   return SUBM_OK;

@@ -168,3 +168,18 @@ def test_group_norm_rejects_bad_arguments(lib):
     assert gn(n=0, x=None, y=None, off=None) == OK
     assert gn(x=None) == INVALID
     assert gn(x=264) == UNSUPPORTED  # not 16-byte aligned
+
+
+def test_fused_conv_norm_rejects_bad_arguments(lib):
+    def f(m=None, n=10, k=1, cin=64, cout=64, dtype=2, x=256, w=512, b=None, off=768, items=1, groups=32,
+          eps=1e-5, act=1, o=1024):
+        return lib.subm_conv3d_forward_group_norm_act(m, n, k, cin, cout, dtype, x, w, b, off, items, groups, None,
+                                                      None, eps, act, o, None)
+
+    assert f(k=2) == UNSUPPORTED
+    assert f(k=3) == INVALID  # needs a map
+    assert f(groups=24) == INVALID
+    assert f(act=9) == INVALID
+    assert f(items=0) == INVALID
+    assert f(o=256) == INVALID  # aliases feats
+    assert f(n=0, x=None, w=None, o=None, off=None) == OK

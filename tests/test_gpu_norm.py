@@ -105,3 +105,65 @@ def test_invalid_arguments():
     assert e.value.name == "SUBM_ERR_INVALID_ARG"
     with pytest.raises(ValueError):
         sc.sparse_group_norm_act(x, off.int(), 32)
+
+
+# ----------------------------------------------------------------- conv + group norm, fused
+
+def multi_item_sites(seed, sizes, lo=-10, hi=10):
+    """Items of roughly the given voxel counts (random subsets of a box), rows item by item."""
+    rng = np.random.default_rng(seed)
+    g = hi - lo
+    rows = []
+    for b, target in enumerate(sizes):
+        occ = min(1.0, target / g ** 3)
+        zyx = np.argwhere(rng.random((g, g, g)) < occ) + lo
+        rows.append(np.concatenate([np.full((len(zyx), 1), b), zyx], axis=1))
+    c = np.ascontiguousarray(np.concatenate(rows, axis=0), dtype=np.int32)
+    offsets = [0] + np.cumsum([len(r) for r in rows]).tolist()
+    return c, offsets
+
+
+def conv_norm_oracle(coords, f, w, b, offsets, groups, gamma, beta, act, dtype):
+    """conv (float64) -> rounded to the storage dtype -> group norm + act (float64)."""
+    conv = oracle.conv3_rulebook(oracle.rulebook_sorted(coords), f.double().numpy(), w.double().numpy(),
+                                 None if b is None else b.double().numpy())
+    conv = synth.round_to(conv, dtype).double().numpy()
+    return norm_ref.group_norm_act(conv, offsets, groups, None if gamma is None else gamma.double().numpy(),
+                                   None if beta is None else beta.double().numpy(), 1e-5, act)
+
+
+FUSED_CASES = [
+    # (seed, item sizes, cin, cout, groups, dtype, act): the fast path (cout > 32, groups inside
+    # one 64- or 128-channel tile) and shapes that fall back to conv + separate norm
+    (1, [3000, 150, 5000, 40, 2600], 64, 128, 32, "bf16", "silu"),
+    (2, [4000, 4000, 4000], 64, 64, 32, "f16", "relu"),
+    (3, [7, 3, 900, 1, 2, 5000], 32, 256, 64, "bf16", "silu"),
+    (4, [2500, 2500], 40, 96, 32, "bf16", "silu"),   # 3 channels per group: fallback
+    (5, [2500, 2500], 32, 32, 8, "bf16", "none"),    # 32 output channels: fallback
+    (6, [3000, 1000], 16, 64, 4, "f32", "silu"),     # float32: fallback
+]
+
+
+@pytest.mark.parametrize("seed,sizes,cin,cout,groups,dtype,act", FUSED_CASES)
+def test_fused_conv_group_norm(seed, sizes, cin, cout, groups, dtype, act):
+    coords, offsets = multi_item_sites(seed, sizes)
+    rng = np.random.default_rng(100 + seed)
+    n = len(coords)
+    f = synth.round_to(rng.standard_normal((n, cin)), dtype)
+    w = synth.round_to(rng.standard_normal((cout, 3, 3, 3, cin)) / np.sqrt(27 * cin), dtype)
+    b = synth.round_to(rng.standard_normal(cout) * 2.0, dtype)
+    gamma = synth.round_to(1.0 + 0.2 * rng.standard_normal(cout), dtype)
+    beta = synth.round_to(0.2 * rng.standard_normal(cout), dtype)
+    off = torch.tensor(offsets, dtype=torch.int64, device=DEV)
+    print(f"fused {dtype} n={n} items={len(sizes)} {cin}->{cout} G={groups} {act}", flush=True)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        fd, wd, bd, gd, bed = (t.to(DEV) for t in (f, w, b, gamma, beta))
+        fused = sc.subm_conv3d_forward_group_norm_act(m, fd, wd, bd, off, groups, gd, bed, 1e-5, ACT[act])
+        fused2 = sc.subm_conv3d_forward_group_norm_act(m, fd, wd, bd, off, groups, gd, bed, 1e-5, ACT[act])
+        conv = sc.subm_conv3d_forward(m, fd, wd, bd)
+        split = sc.sparse_group_norm_act(conv, off, groups, gd, bed, 1e-5, ACT[act])
+        torch.cuda.synchronize()
+    assert torch.equal(fused, fused2), "fused path is not bitwise reproducible"
+    ref = conv_norm_oracle(coords, f, w, b, offsets, groups, gamma, beta, act, dtype)
+    check(fused.cpu(), ref, dtype, "fused vs oracle")
+    check(split.cpu(), ref, dtype, "conv + norm vs oracle")
