@@ -71,10 +71,13 @@ int sparse_group_norm_act(const void* x, int64_t n, int channels, int dtype, con
  *                 are taken of those rounded values, as a separate norm would see them.
  *   item_offsets .. act  as sparse_group_norm_act, with channels = cout.
  *   out           device [n, cout]; receives the convolution, then is normalised in place.
- * On the 16-bit fast path (more than 32 output channels, groups not straddling a 64- or
- * 128-channel column tile) the epilogue of the convolution kernel writes per-tile, per-group
- * partial sums, so the output is read once less than conv + sparse_group_norm_act; other shapes
- * run exactly those two calls.  Never synchronises.
+ * By default this runs the convolution and then the three-pass normalisation in place.  With
+ * the environment variable SUBMCONV_GN_EPILOGUE=1, on the 16-bit fast path (more than 32 output
+ * channels, groups not straddling a 64- or 128-channel column tile), the epilogue of the
+ * convolution kernel writes per-tile, per-group partial sums instead, so the output is read
+ * once less; measured on MI355X that costs more in the convolution (one workgroup per compute
+ * unit leaves the epilogue's latency exposed) than the pass it saves, hence not the default.
+ * Never synchronises.
  * Errors: those of subm_conv3d_forward and sparse_group_norm_act.
  * Source: the per-voxel layers that sandwich the convolution in the sparse blocks
  * (lato.2_mrp_mlx README, "Status").

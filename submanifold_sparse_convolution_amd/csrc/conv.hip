@@ -309,9 +309,10 @@ __global__ __launch_bounds__(kThreads, 2) void subm_conv_generic_kernel(const Co
 // two halves of the rows, then coalesced 16-byte global stores by all NT threads.
 //
 // STATS: also the group-norm partial sums of the tile's rounded outputs, read back from the
-// staged halves: per group of cpg channels, thread (g, row lane) sums x - K and (x - K)^2 over
-// its rows, with K the group's first value in the tile's first row (shifted sums stay accurate
-// when the mean is large against the spread); the row lanes are then added in order.
+// staged halves in 16-byte chunks: thread (chunk, row lane) sums x - K and (x - K)^2 per channel
+// over its rows, with K the first value of the channel's group in the tile's first row (shifted
+// sums stay accurate when the mean is large against the spread); the row lanes, then the
+// channels of each group, are added in a fixed order.
 template <DT D, int WM, int FM, int FN, int NT, bool STATS = false>
 __device__ __forceinline__ void epilogue_store(const ConvArgs& args, const f32x16_t (&acc)[FM][FN], unsigned char* ring,
                                                const float* s_bias, int64_t row0, int o0, int tid, bool has_acc,
@@ -324,13 +325,16 @@ __device__ __forceinline__ void epilogue_store(const ConvArgs& args, const f32x1
   const int cout = args.cout;
   const int lrow = lane & 31, lk = lane >> 5;
   T* out = reinterpret_cast<T*>(args.out);
-  // statistics lanes: group g of the tile's columns, row lane rl of RL
+  // statistics lanes: 16-byte column chunk ck (8 channels) and row lane rl of RLS
+  static_assert(!STATS || D != DT::F32, "statistics epilogue is for 16-bit storage");
+  constexpr int NCK = BN / 8, RLS = NT / NCK;
+  static_assert(64 % NCK == 0, "a wave holds whole rows of chunks");
   const int cpg = STATS ? args.gn_cpg : 1;
-  const int gt = STATS ? BN / cpg : 1;
-  const int rl = tid / gt, gl = tid - (tid / gt) * gt, RL = NT / gt;
+  const int ck = tid % NCK, rl = tid / NCK;
   const int vrows = (int)((n - row0) < BM ? (n - row0) : BM);
-  const bool gvalid = STATS && rl < RL && o0 + gl * cpg < cout;
-  float sh = 0.f, s1 = 0.f, s2 = 0.f;
+  float kk[8], a1[8], a2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) kk[e] = a1[e] = a2[e] = 0.f;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     if (has_acc && (wm * WTM) / HALF == pass) {
@@ -351,17 +355,22 @@ __device__ __forceinline__ void epilogue_store(const ConvArgs& args, const f32x1
     }
     __syncthreads();
     if constexpr (STATS) {
-      if (gvalid) {
-        const T* col = reinterpret_cast<const T*>(ring) + gl * cpg;
-        if (pass == 0) sh = to_float<D>(col[0]);  // tile row 0 is always a valid row
-        const int rend = vrows - pass * HALF < HALF ? vrows - pass * HALF : HALF;
-        for (int r = rl; r < rend; r += RL) {
-          const T* x = reinterpret_cast<const T*>(ring + r * SROW) + gl * cpg;
-          for (int c = 0; c < cpg; ++c) {
-            const float d = to_float<D>(x[c]) - sh;
-            s1 += d;
-            s2 += d * d;
-          }
+      if (pass == 0) {
+        // K of each of this chunk's channels: its group's first channel in tile row 0 (a valid row)
+        const T* row_0 = reinterpret_cast<const T*>(ring);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kk[e] = to_float<D>(row_0[(ck * 8 + e) / cpg * cpg]);
+      }
+      const int rend = vrows - pass * HALF < HALF ? vrows - pass * HALF : HALF;
+#pragma unroll 4
+      for (int r = rl; r < rend; r += RLS) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(ring + r * SROW + ck * 16);
+        const T* x = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = to_float<D>(x[e]) - kk[e];
+          a1[e] += d;
+          a2[e] += d * d;
         }
       }
     }
@@ -385,19 +394,50 @@ __device__ __forceinline__ void epilogue_store(const ConvArgs& args, const f32x1
     __syncthreads();
   }
   if constexpr (STATS) {
-    float* red = reinterpret_cast<float*>(ring);
-    red[tid] = s1;
-    red[NT + tid] = s2;
+    // Row lanes of one wave share their chunk with lanes l ^ NCK, l ^ 2 NCK, ...: a butterfly
+    // of shuffles leaves the wave's sums in every lane; then the waves are added in order in LDS
+    // (the ring is free now), and one thread per group adds its channels.
+    constexpr int NW = NT / 64;
+#pragma unroll
+    for (int o = NCK; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a1[e] += __shfl_xor(a1[e], o);
+        a2[e] += __shfl_xor(a2[e], o);
+      }
+    float* red = reinterpret_cast<float*>(ring);  // [2][NW][BN]
+    float* tot = red + 2 * NW * BN;               // [2][BN]
+    float* shf = tot + 2 * BN;                    // [BN]
+    const int w = tid >> 6;
+    if (lane < NCK)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        red[w * BN + ck * 8 + e] = a1[e];
+        red[(NW + w) * BN + ck * 8 + e] = a2[e];
+        if (w == 0) shf[ck * 8 + e] = kk[e];
+      }
     __syncthreads();
+    if (tid < BN) {
+      float t1 = 0.f, t2 = 0.f;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        t1 += red[q * BN + tid];
+        t2 += red[(NW + q) * BN + tid];
+      }
+      tot[tid] = t1;
+      tot[BN + tid] = t2;
+    }
+    __syncthreads();
+    const int gt = BN / cpg;
     if (tid < gt && o0 + tid * cpg < cout) {
       float t1 = 0.f, t2 = 0.f;
-      for (int q = 0; q < RL; ++q) {
-        t1 += red[q * gt + tid];
-        t2 += red[NT + q * gt + tid];
+      for (int c = tid * cpg; c < (tid + 1) * cpg; ++c) {
+        t1 += tot[c];
+        t2 += tot[BN + c];
       }
-      // thread tid < gt is row lane 0 of group tid: its own shift is the group's K
       const float mean_d = t1 / (float)(vrows * cpg);
-      args.gn_part[(int64_t)tile * args.gn_groups + o0 / cpg + tid] = make_float2(sh + mean_d, fmaxf(t2 - t1 * mean_d, 0.f));
+      args.gn_part[(int64_t)tile * args.gn_groups + o0 / cpg + tid] =
+          make_float2(shf[tid * cpg] + mean_d, fmaxf(t2 - t1 * mean_d, 0.f));
     }
   }
 }

@@ -16,6 +16,7 @@
 // Every reduction runs in a fixed order, so the result is bitwise reproducible.
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 
 #include "device_common.h"
 #include "internal.h"
@@ -140,44 +141,52 @@ __global__ __launch_bounds__(kThreads) void gn_partial_kernel(const void* __rest
   if (tid == 0) part_rows[s] = (int32_t)rows;
 }
 
-// Pass 2: one block of kStatThreads per item; per group, TG threads combine strided subsets of
-// the item's segments, then a fixed pairwise tree over the TG partial results.
+// Pass 2: the partials of an item are combined with the pairwise update of Chan, Golub and
+// LeVeque in float64, in two levels so that every compute unit takes part: level 1 combines
+// chunks of kChunk consecutive partials of one item (slot s = b + p / kChunk for partial p of
+// item b: the slots of consecutive items never collide, so no table is needed), level 2 combines
+// the slots of each item.  Within a block, per group, TG threads run strided chains that are
+// then added by a fixed pairwise tree, so the order never changes.
 constexpr int kStatThreads = 1024;
+constexpr int kChunkThreads = 256;
+constexpr int kChunk = 64;      // partials per level-1 slot
+constexpr int kChainLoads = 8;  // partials loaded ahead in each combination chain
 
 __device__ __forceinline__ void chan_combine(double& na, double& ma, double& m2a, double nb, double mb, double m2b) {
   if (nb == 0.0) return;
   const double n = na + nb;
   const double d = mb - ma;
-  ma += d * (nb / n);
-  m2a += m2b + d * d * (na * nb / n);
+  const double r = nb / n;
+  ma += d * r;
+  m2a += m2b + d * d * na * r;
   na = n;
 }
 
-__global__ __launch_bounds__(kStatThreads) void gn_stats_kernel(const float2* __restrict__ part,
-                                                                const int32_t* __restrict__ part_rows,
-                                                                const int64_t* __restrict__ off, int64_t n, int64_t R,
-                                                                int groups, int cpg, float eps,
-                                                                float2* __restrict__ stats) {
-  __shared__ double s_n[kStatThreads], s_m[kStatThreads], s_q[kStatThreads];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int64_t lo = clamp_off(off, b, n), hi = clamp_off(off, b + 1, n);
-  if (hi <= lo) {
-    for (int g = tid; g < groups; g += kStatThreads) stats[(int64_t)b * groups + g] = make_float2(0.f, 0.f);
-    return;
-  }
-  const int64_t s0 = b + lo / R, s1 = b + (hi - 1) / R;  // inclusive
-  // TG = threads per group: the largest power of two with TG * groups <= kStatThreads (>= 1)
-  int tg = 1;
-  while (tg * 2 * groups <= kStatThreads) tg *= 2;
-  const int gpb = kStatThreads / tg;  // groups per pass
+// Block-wide combination, per group g < groups, of the entries q in [q0, q1] given by
+// get(q, g) -> (count, mean, M2); thread 0 of each group's lanes receives the result through
+// `done(g, n, mean, M2)`.  NT threads; s_* hold NT doubles each.
+template <int NT, typename Get, typename Done>
+__device__ __forceinline__ void block_combine(int groups, int64_t q0, int64_t q1, Get get, Done done, double* s_n,
+                                              double* s_m, double* s_q) {
+  const int tid = threadIdx.x;
+  int tg = 1;  // threads per group: the largest power of two with TG * groups <= NT
+  while (tg * 2 * groups <= NT) tg *= 2;
+  const int gpb = NT / tg;
   for (int g0 = 0; g0 < groups; g0 += gpb) {
     const int g = g0 + tid / tg, j = tid % tg;
     const bool on = tid / tg < gpb && g < groups;
     double na = 0.0, ma = 0.0, m2a = 0.0;
     if (on)
-      for (int64_t sg = s0 + j; sg <= s1; sg += tg) {
-        const float2 p = part[sg * groups + g];
-        chan_combine(na, ma, m2a, (double)part_rows[sg] * cpg, p.x, p.y);
+      for (int64_t q = q0 + j; q <= q1; q += (int64_t)kChainLoads * tg) {
+        double c[kChainLoads], m[kChainLoads], v[kChainLoads];
+#pragma unroll
+        for (int u = 0; u < kChainLoads; ++u) {  // loads in flight before the dependent updates
+          const int64_t qq = q + (int64_t)u * tg;
+          get(qq <= q1 ? qq : q1, g, c[u], m[u], v[u]);  // clamped: no branches around the loads
+          if (qq > q1) c[u] = 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < kChainLoads; ++u) chan_combine(na, ma, m2a, c[u], m[u], v[u]);
       }
     s_n[tid] = na;
     s_m[tid] = ma;
@@ -185,21 +194,112 @@ __global__ __launch_bounds__(kStatThreads) void gn_stats_kernel(const float2* __
     __syncthreads();
     for (int h = 1; h < tg; h <<= 1) {
       if (on && (j % (2 * h)) == 0) {
-        double a = s_n[tid], m = s_m[tid], q = s_q[tid];
-        chan_combine(a, m, q, s_n[tid + h], s_m[tid + h], s_q[tid + h]);
-        s_n[tid] = a;
-        s_m[tid] = m;
-        s_q[tid] = q;
+        double x = s_n[tid], y = s_m[tid], z = s_q[tid];
+        chan_combine(x, y, z, s_n[tid + h], s_m[tid + h], s_q[tid + h]);
+        s_n[tid] = x;
+        s_m[tid] = y;
+        s_q[tid] = z;
       }
       __syncthreads();
     }
-    if (on && j == 0) {
-      const double var = s_n[tid] > 0.0 ? s_q[tid] / s_n[tid] : 0.0;
-      stats[(int64_t)b * groups + g] = make_float2((float)s_m[tid], (float)(1.0 / sqrt(var + (double)eps)));
-    }
+    if (on && j == 0) done(g, s_n[tid], s_m[tid], s_q[tid]);
     __syncthreads();
   }
 }
+
+// Where the partials of item b live: segments (the separate statistics pass, count from
+// part_rows) or row tiles of the convolution epilogue (interior tiles only, count from the tile
+// height).  key(b) orders the items for the slot search; range(b) is [first, last] (first > last
+// when empty).
+template <bool TILES>
+struct PartialSpace {
+  const float2* part;
+  const int32_t* part_rows;  // segments only
+  const int64_t* off;
+  int64_t n;
+  int64_t R;  // segment length or tile height
+  int cpg;
+  __device__ int64_t key(int b) const {
+    const int64_t lo = clamp_off(off, b, n);
+    return TILES ? lo / R : b + lo / R;
+  }
+  __device__ void range(int b, int64_t& first, int64_t& last) const;
+  __device__ void get(int64_t p, int g, int groups, double& c, double& m, double& v) const {
+    const float2 x = part[p * groups + g];
+    c = TILES ? (double)std::min(R, n - p * R) * cpg : (double)part_rows[p] * cpg;
+    m = x.x;
+    v = x.y;
+  }
+};
+
+// Level 1: slot s = b + first-partial-chunk index; combines partials [max(first, kC), min(last, kC + kChunk - 1)].
+template <bool TILES>
+__global__ __launch_bounds__(kChunkThreads) void gn_chunk_kernel(PartialSpace<TILES> ps, int items, int groups,
+                                                                 double* __restrict__ sn, double* __restrict__ sm,
+                                                                 double* __restrict__ sq) {
+  __shared__ double s_n[kChunkThreads], s_m[kChunkThreads], s_q[kChunkThreads];
+  const int64_t s = blockIdx.x;
+  int lo = 0, hi = items - 1;  // item: the largest b with b + key(b) / kChunk <= s
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (mid + ps.key(mid) / kChunk <= s) lo = mid;
+    else hi = mid - 1;
+  }
+  int64_t first, last;
+  ps.range(lo, first, last);
+  const int64_t k = s - lo;
+  const int64_t q0 = std::max(first, k * kChunk), q1 = std::min(last, k * kChunk + kChunk - 1);
+  block_combine<kChunkThreads>(
+      groups, q0, q1, [&](int64_t q, int g, double& c, double& m, double& v) { ps.get(q, g, groups, c, m, v); },
+      [&](int g, double c, double m, double v) {
+        sn[s * groups + g] = c;
+        sm[s * groups + g] = m;
+        sq[s * groups + g] = v;
+      },
+      s_n, s_m, s_q);
+}
+
+// Level 2: one block per item: (first boundary piece,) its slots, (last boundary piece).
+template <bool TILES>
+__global__ __launch_bounds__(kStatThreads) void gn_finish_kernel(PartialSpace<TILES> ps, int groups, float eps,
+                                                                 const double* __restrict__ sn,
+                                                                 const double* __restrict__ sm,
+                                                                 const double* __restrict__ sq,
+                                                                 const float2* __restrict__ bpart,
+                                                                 const int32_t* __restrict__ brows,
+                                                                 float2* __restrict__ stats) {
+  __shared__ double s_n[kStatThreads], s_m[kStatThreads], s_q[kStatThreads];
+  const int b = blockIdx.x;
+  int64_t first, last;
+  ps.range(b, first, last);
+  const int64_t q0 = b + (first <= last ? first / kChunk : 0), q1 = first <= last ? b + last / kChunk : q0 - 1;
+  block_combine<kStatThreads>(
+      groups, q0, q1,
+      [&](int64_t q, int g, double& c, double& m, double& v) {
+        c = sn[q * groups + g];
+        m = sm[q * groups + g];
+        v = sq[q * groups + g];
+      },
+      [&](int g, double c, double m, double v) {
+        double cn = 0.0, cm = 0.0, cq = 0.0;
+        if (TILES) {
+          const float2 f = bpart[(int64_t)(2 * b) * groups + g];
+          chan_combine(cn, cm, cq, (double)brows[2 * b] * ps.cpg, f.x, f.y);
+        }
+        chan_combine(cn, cm, cq, c, m, v);
+        if (TILES) {
+          const float2 l = bpart[(int64_t)(2 * b + 1) * groups + g];
+          chan_combine(cn, cm, cq, (double)brows[2 * b + 1] * ps.cpg, l.x, l.y);
+        }
+        const double var = cn > 0.0 ? cq / cn : 0.0;
+        stats[(int64_t)b * groups + g] =
+            cn > 0.0 ? make_float2((float)cm, (float)(1.0 / sqrt(var + (double)eps))) : make_float2(0.f, 0.f);
+      },
+      s_n, s_m, s_q);
+}
+
+// Number of level-1 slots for `items` items over `partials` partial indices.
+int64_t chunk_slots(int items, int64_t partials) { return items + partials / kChunk + 1; }
 
 // Fused variant (statistics from the convolution epilogue).  The epilogue leaves per (row tile of
 // BM rows, group) partials over whole tiles; a tile that straddles an item boundary is recomputed
@@ -282,61 +382,22 @@ __global__ __launch_bounds__(kThreads) void gn_boundary_kernel(const void* __res
   }
 }
 
-// One block per item: first boundary piece, then the interior tiles (strided chains and a fixed
-// tree, as in gn_stats_kernel), then the last boundary piece.
-__global__ __launch_bounds__(kStatThreads) void gn_stats_tiles_kernel(const float2* __restrict__ part,
-                                                                      const float2* __restrict__ bpart,
-                                                                      const int32_t* __restrict__ brows,
-                                                                      const int64_t* __restrict__ off, int64_t n,
-                                                                      int64_t BM, int groups, int cpg, float eps,
-                                                                      float2* __restrict__ stats) {
-  __shared__ double s_n[kStatThreads], s_m[kStatThreads], s_q[kStatThreads];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const ItemTiles it = item_tiles(off, b, n, BM);
+template <>
+__device__ void PartialSpace<false>::range(int b, int64_t& first, int64_t& last) const {
+  const int64_t lo = clamp_off(off, b, n), hi = clamp_off(off, b + 1, n);
+  first = b + lo / R;
+  last = hi > lo ? b + (hi - 1) / R : first - 1;
+}
+template <>
+__device__ void PartialSpace<true>::range(int b, int64_t& first, int64_t& last) const {
+  const ItemTiles it = item_tiles(off, b, n, R);
   if (it.hi <= it.lo) {
-    for (int g = tid; g < groups; g += kStatThreads) stats[(int64_t)b * groups + g] = make_float2(0.f, 0.f);
+    first = it.t0 + 1;
+    last = it.t0;
     return;
   }
-  const int64_t i0 = it.t0 + (it.b0 ? 1 : 0);
-  const int64_t i1 = it.t1 - ((it.b1 && it.t1 != it.t0) ? 1 : 0);  // interior tiles [i0, i1]
-  int tg = 1;
-  while (tg * 2 * groups <= kStatThreads) tg *= 2;
-  const int gpb = kStatThreads / tg;
-  for (int g0 = 0; g0 < groups; g0 += gpb) {
-    const int g = g0 + tid / tg, j = tid % tg;
-    const bool on = tid / tg < gpb && g < groups;
-    double na = 0.0, ma = 0.0, m2a = 0.0;
-    if (on)
-      for (int64_t t = i0 + j; t <= i1; t += tg) {
-        const float2 p = part[t * groups + g];
-        chan_combine(na, ma, m2a, (double)tile_rows(t, BM, n) * cpg, p.x, p.y);
-      }
-    s_n[tid] = na;
-    s_m[tid] = ma;
-    s_q[tid] = m2a;
-    __syncthreads();
-    for (int h = 1; h < tg; h <<= 1) {
-      if (on && (j % (2 * h)) == 0) {
-        double a = s_n[tid], m = s_m[tid], q = s_q[tid];
-        chan_combine(a, m, q, s_n[tid + h], s_m[tid + h], s_q[tid + h]);
-        s_n[tid] = a;
-        s_m[tid] = m;
-        s_q[tid] = q;
-      }
-      __syncthreads();
-    }
-    if (on && j == 0) {
-      double cn = 0.0, cm = 0.0, cq = 0.0;
-      const float2 f = bpart[(int64_t)(2 * b) * groups + g];
-      chan_combine(cn, cm, cq, (double)brows[2 * b] * cpg, f.x, f.y);
-      chan_combine(cn, cm, cq, s_n[tid], s_m[tid], s_q[tid]);
-      const float2 l = bpart[(int64_t)(2 * b + 1) * groups + g];
-      chan_combine(cn, cm, cq, (double)brows[2 * b + 1] * cpg, l.x, l.y);
-      const double var = cn > 0.0 ? cq / cn : 0.0;
-      stats[(int64_t)b * groups + g] = make_float2((float)cm, (float)(1.0 / sqrt(var + (double)eps)));
-    }
-    __syncthreads();
-  }
+  first = it.t0 + (it.b0 ? 1 : 0);
+  last = it.t1 - ((it.b1 && it.t1 != it.t0) ? 1 : 0);  // interior tiles [first, last]
 }
 
 // Pass 3: one block per segment (one item).
@@ -402,12 +463,19 @@ hipError_t launch_apply(const void* x, void* y, int64_t n, int channels, const i
 template <DT D>
 hipError_t launch_dtype(const void* x, int64_t n, int channels, const int64_t* off, int items, int groups,
                         const void* gamma, const void* beta, float eps, int act, void* y, float2* part,
-                        int32_t* part_rows, float2* stats, int64_t R, int64_t segments, hipStream_t stream) {
+                        int32_t* part_rows, double* slots, float2* stats, int64_t R, int64_t segments,
+                        hipStream_t stream) {
   constexpr int E = D == DT::F32 ? 4 : 8;
   gn_partial_kernel<D, E><<<(unsigned)segments, kThreads, 0, stream>>>(x, n, channels, off, items, R, groups, part,
                                                                        part_rows);
-  gn_stats_kernel<<<(unsigned)items, kStatThreads, 0, stream>>>(part, part_rows, off, n, R, groups, channels / groups,
-                                                                eps, stats);
+  const PartialSpace<false> ps{part, part_rows, off, n, R, channels / groups};
+  const int64_t ns = chunk_slots(items, segments);
+  double* sn = slots;
+  double* sm = slots + ns * groups;
+  double* sq = slots + 2 * ns * groups;
+  gn_chunk_kernel<false><<<(unsigned)ns, kChunkThreads, 0, stream>>>(ps, items, groups, sn, sm, sq);
+  gn_finish_kernel<false><<<(unsigned)items, kStatThreads, 0, stream>>>(ps, groups, eps, sn, sm, sq, nullptr, nullptr,
+                                                                        stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (act) {
@@ -452,6 +520,15 @@ Status check_norm_pointers(const void* x, const void* y, const int64_t* off, con
   return Status{};
 }
 
+// The statistics in the convolution epilogue cost more than the separate pass they replace on
+// this GPU (the kernel runs one workgroup per compute unit, so the epilogue's extra latency is
+// exposed: config 5 layer, 64 channels, 32 groups: 1.09 ms fused vs 0.95 ms conv + norm), so the
+// separate pass is the default; SUBMCONV_GN_EPILOGUE=1 selects the epilogue statistics.
+bool epilogue_statistics_enabled() {
+  const char* v = std::getenv("SUBMCONV_GN_EPILOGUE");
+  return v != nullptr && v[0] == '1';
+}
+
 // Segment length of the partials / apply passes for n rows.
 int64_t segment_rows(int64_t n) {
   const int64_t rmul = std::max<int64_t>(1, (n + 256 * (int64_t)kMaxSegmentsPerRun - 1) / (256 * (int64_t)kMaxSegmentsPerRun));
@@ -478,10 +555,16 @@ hipError_t launch_apply_act(const void* x, void* y, int64_t n, int channels, con
 template <DT D>
 hipError_t launch_from_tiles(void* y, int64_t n, int channels, const int64_t* off, int items, int groups,
                              const void* gamma, const void* beta, float eps, int act, const float2* part, int64_t BM,
-                             float2* bpart, int32_t* brows, float2* stats, hipStream_t stream) {
+                             float2* bpart, int32_t* brows, double* slots, float2* stats, hipStream_t stream) {
   gn_boundary_kernel<D><<<(unsigned)(2 * items), kThreads, 0, stream>>>(y, n, channels, off, BM, groups, bpart, brows);
-  gn_stats_tiles_kernel<<<(unsigned)items, kStatThreads, 0, stream>>>(part, bpart, brows, off, n, BM, groups,
-                                                                      channels / groups, eps, stats);
+  const PartialSpace<true> ps{part, nullptr, off, n, BM, channels / groups};
+  const int64_t ns = chunk_slots(items, (n + BM - 1) / BM);
+  double* sn = slots;
+  double* sm = slots + ns * groups;
+  double* sq = slots + 2 * ns * groups;
+  gn_chunk_kernel<true><<<(unsigned)ns, kChunkThreads, 0, stream>>>(ps, items, groups, sn, sm, sq);
+  gn_finish_kernel<true><<<(unsigned)items, kStatThreads, 0, stream>>>(ps, groups, eps, sn, sm, sq, bpart, brows,
+                                                                       stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_apply_act<D>(y, y, n, channels, off, items, groups, stats, gamma, beta, act, stream);
@@ -505,27 +588,29 @@ extern "C" int sparse_group_norm_act(const void* x, int64_t n, int channels, int
   const int64_t segments = num_items + (n + R - 1) / R;
   const size_t part_bytes = (size_t)segments * groups * sizeof(float2);
   const size_t rows_bytes = ((size_t)segments * sizeof(int32_t) + 255) / 256 * 256;
-  const size_t stats_bytes = (size_t)num_items * groups * sizeof(float2);
+  const size_t stats_bytes = ((size_t)num_items * groups * sizeof(float2) + 255) / 256 * 256;
+  const size_t slot_bytes = (size_t)chunk_slots(num_items, segments) * groups * 3 * sizeof(double);
   void* scratch = nullptr;
-  st = device_alloc(&scratch, part_bytes + rows_bytes + stats_bytes, stream);
+  st = device_alloc(&scratch, part_bytes + rows_bytes + stats_bytes + slot_bytes, stream);
   if (!st.ok()) return fail(st);
   unsigned char* base = static_cast<unsigned char*>(scratch);
   float2* part = reinterpret_cast<float2*>(base);
   int32_t* part_rows = reinterpret_cast<int32_t*>(base + part_bytes);
   float2* stats = reinterpret_cast<float2*>(base + part_bytes + rows_bytes);
+  double* slots = reinterpret_cast<double*>(base + part_bytes + rows_bytes + stats_bytes);
   hipError_t e;
   switch (dtype) {
     case SUBM_F32:
       e = launch_dtype<DT::F32>(x, n, channels, item_offsets, num_items, groups, gamma, beta, eps, act, y, part,
-                                part_rows, stats, R, segments, stream);
+                                part_rows, slots, stats, R, segments, stream);
       break;
     case SUBM_F16:
       e = launch_dtype<DT::F16>(x, n, channels, item_offsets, num_items, groups, gamma, beta, eps, act, y, part,
-                                part_rows, stats, R, segments, stream);
+                                part_rows, slots, stats, R, segments, stream);
       break;
     default:
       e = launch_dtype<DT::BF16>(x, n, channels, item_offsets, num_items, groups, gamma, beta, eps, act, y, part,
-                                 part_rows, stats, R, segments, stream);
+                                 part_rows, slots, stats, R, segments, stream);
       break;
   }
   device_free(scratch, stream);
@@ -551,24 +636,28 @@ extern "C" int subm_conv3d_forward_group_norm_act(submconv_map_t map, int64_t n,
   const size_t part_bytes = ((size_t)max_tiles * groups * sizeof(float2) + 255) / 256 * 256;
   const size_t bpart_bytes = ((size_t)2 * num_items * groups * sizeof(float2) + 255) / 256 * 256;
   const size_t brows_bytes = ((size_t)2 * num_items * sizeof(int32_t) + 255) / 256 * 256;
-  const size_t stats_bytes = (size_t)num_items * groups * sizeof(float2);
+  const size_t stats_bytes = ((size_t)num_items * groups * sizeof(float2) + 255) / 256 * 256;
+  const size_t slot_bytes = (size_t)chunk_slots(num_items, max_tiles) * groups * 3 * sizeof(double);
   void* scratch = nullptr;
-  st = device_alloc(&scratch, part_bytes + bpart_bytes + brows_bytes + stats_bytes, stream);
+  st = device_alloc(&scratch, part_bytes + bpart_bytes + brows_bytes + stats_bytes + slot_bytes, stream);
   if (!st.ok()) return fail(st);
   unsigned char* base = static_cast<unsigned char*>(scratch);
   float2* part = reinterpret_cast<float2*>(base);
   float2* bpart = reinterpret_cast<float2*>(base + part_bytes);
   int32_t* brows = reinterpret_cast<int32_t*>(base + part_bytes + bpart_bytes);
   float2* stats = reinterpret_cast<float2*>(base + part_bytes + bpart_bytes + brows_bytes);
+  double* slots = reinterpret_cast<double*>(base + part_bytes + bpart_bytes + brows_bytes + stats_bytes);
   int tile_rows = 0;
-  hipError_t e = launch_subm_conv_gn_partials(md, n, ksize, cin, cout, dtype, feats, weight, bias, out, part,
-                                              cout / groups, groups, &tile_rows, stream);
+  hipError_t e = epilogue_statistics_enabled()
+                     ? launch_subm_conv_gn_partials(md, n, ksize, cin, cout, dtype, feats, weight, bias, out, part,
+                                                    cout / groups, groups, &tile_rows, stream)
+                     : hipErrorNotSupported;
   if (e == hipSuccess) {
     e = dtype == SUBM_F16
             ? launch_from_tiles<DT::F16>(out, n, cout, item_offsets, num_items, groups, gamma, beta, eps, act, part,
-                                         tile_rows, bpart, brows, stats, stream)
+                                         tile_rows, bpart, brows, slots, stats, stream)
             : launch_from_tiles<DT::BF16>(out, n, cout, item_offsets, num_items, groups, gamma, beta, eps, act, part,
-                                          tile_rows, bpart, brows, stats, stream);
+                                          tile_rows, bpart, brows, slots, stats, stream);
     device_free(scratch, stream);
   } else if (e == hipErrorNotSupported) {
     (void)hipGetLastError();

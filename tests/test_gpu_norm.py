@@ -144,8 +144,12 @@ FUSED_CASES = [
 ]
 
 
+@pytest.mark.parametrize("epilogue", ["0", "1"])
 @pytest.mark.parametrize("seed,sizes,cin,cout,groups,dtype,act", FUSED_CASES)
-def test_fused_conv_group_norm(seed, sizes, cin, cout, groups, dtype, act):
+def test_fused_conv_group_norm(seed, sizes, cin, cout, groups, dtype, act, epilogue, monkeypatch):
+    # "1": group statistics from the convolution epilogue where the shape allows it; "0": the
+    # default conv + separate statistics pass
+    monkeypatch.setenv("SUBMCONV_GN_EPILOGUE", epilogue)
     coords, offsets = multi_item_sites(seed, sizes)
     rng = np.random.default_rng(100 + seed)
     n = len(coords)
@@ -155,7 +159,7 @@ def test_fused_conv_group_norm(seed, sizes, cin, cout, groups, dtype, act):
     gamma = synth.round_to(1.0 + 0.2 * rng.standard_normal(cout), dtype)
     beta = synth.round_to(0.2 * rng.standard_normal(cout), dtype)
     off = torch.tensor(offsets, dtype=torch.int64, device=DEV)
-    print(f"fused {dtype} n={n} items={len(sizes)} {cin}->{cout} G={groups} {act}", flush=True)
+    print(f"fused {dtype} n={n} items={len(sizes)} {cin}->{cout} G={groups} {act} epilogue={epilogue}", flush=True)
     with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
         fd, wd, bd, gd, bed = (t.to(DEV) for t in (f, w, b, gamma, beta))
         fused = sc.subm_conv3d_forward_group_norm_act(m, fd, wd, bd, off, groups, gd, bed, 1e-5, ACT[act])
