@@ -278,9 +278,13 @@ def main():
         roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic}
     # The kernel the library picks for this layer shape (16-bit storage: the warp-specialised
-    # matrix-core kernel above 32 output channels, the single-role one from 17 to 32).
+    # matrix-core kernel above 32 output channels, walking several tiles per workgroup for k = 3
+    # with whole 16-byte output groups; the single-role one from 17 to 32).
     if per_offset and ks == 3:
         kernel = "offset_gemm_kernel (27 launches, one per offset) + round_out_kernel, per call"
+    elif (cfg.dtype in ("bf16", "f16") and cout > 32 and ks == 3 and cout % 8 == 0
+          and os.environ.get("SUBMCONV_PERSISTENT", "1")[:1] != "0"):
+        kernel = "subm_conv_ws_persistent_kernel"
     elif cfg.dtype in ("bf16", "f16") and cout > 32:
         kernel = "subm_conv_ws_kernel"
     elif cfg.dtype in ("bf16", "f16") and cout > 16:

@@ -1055,6 +1055,312 @@ __global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_kernel(const ConvA
   epilogue_store<D, WM, FM, FN, kWsThreads, STATS>(args, acc, ring, s_bias, row0, o0, tid, !loader, wm, wn, lane, tile);
 }
 
+// Persistent variant of the warp-specialised kernel (16-bit storage, k = 3, step-ahead
+// fragments).  One workgroup per compute unit walks several row tiles in a row: the load waves
+// keep filling the ring across tile boundaries, and the compute waves write a finished tile
+// straight from their accumulators (bias, one RNE rounding, 8-byte stores; no LDS staging and
+// no barrier), so the epilogue of one tile and the rulebook and first stages of the next overlap
+// the loads in flight.  The tiles of a workgroup and their tap masks are computed by every wave
+// before the roles split, so both roles run exactly the same number of stage barriers.
+constexpr int kMaxBlockTiles = 256;
+constexpr int kPersistentBlocks = 256;  // one workgroup per compute unit
+
+// Orders ordinary LDS accesses against the direct loads, which the compiler does not see.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+template <DT D, int WM, int FM, int FN, int SL>
+__global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_persistent_kernel(const ConvArgs args) {
+  using Sh = MmaShape<WM, FM, FN, SL, 27>;
+  constexpr int WTM = Sh::WTM, WTN = Sh::WTN, BM = Sh::BM, BN = Sh::BN, BNP = Sh::BNP;
+  constexpr int CH = Sh::CH, RPI = Sh::RPI, KSTEPS = Sh::KSTEPS;
+  constexpr int ADMA = Sh::ADMA, BDMA = Sh::BDMA, DMA = Sh::DMA, BUF = Sh::BUF, NS = Sh::NS;
+  constexpr int QROWS = BM / 4;                          // rulebook rows per load wave
+  constexpr int QDMA = (QROWS * 27 * 4 + 1023) / 1024;   // 1 KB direct loads per load wave
+  static_assert(NS >= 2, "ring depth");
+  static_assert(4 * QDMA * 1024 <= Sh::NBR, "per-wave rulebook slots fit the rulebook area");
+  static_assert((NS - 1) * DMA < 64 && QDMA < 64, "outstanding loads exceed the vmcnt range");
+  static_assert((QROWS * 27 * 4) % 16 == 0 && (BM * 27 * 4) % 16 == 0, "rulebook rows in whole 16-byte chunks");
+  static_assert(KSTEPS <= 4, "step-ahead schedule covers up to four steps per stage");
+
+  __shared__ __align__(16) unsigned char ring[NS * BUF];
+  __shared__ __align__(16) int32_t s_nbr[4 * QDMA * 256];  // one slot of QDMA KB per load wave
+  __shared__ __align__(16) float s_bias[BN];
+  __shared__ uint32_t s_tmask[kMaxBlockTiles];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool loader = wave >= 4;
+  const int cw = wave & 3;
+  const int wm = cw % WM;
+  const int wn = cw / WM;
+  const int cw_u = __builtin_amdgcn_readfirstlane(cw);
+  const int64_t n = args.n;
+  const int o0 = blockIdx.y * BN;
+  const int cout = args.cout, row_bytes = args.row_bytes;
+
+  // This workgroup's tiles: virtual block bid + k * gridDim.x, mapped XCD-aware (gridDim.x is a
+  // multiple of 8, so all of them stay on this workgroup's XCD).
+  const int nblk = (int)gridDim.x, bid = (int)blockIdx.x;
+  auto tile_of = [&](int k) { return (bid & 7) * args.per_xcd + (bid >> 3) + k * (nblk >> 3); };
+  int ntiles = 0;
+  while (ntiles < kMaxBlockTiles && (bid >> 3) + ntiles * (nblk >> 3) < args.per_xcd && tile_of(ntiles) < args.tiles_m)
+    ++ntiles;
+  if (ntiles == 0) return;  // whole workgroup: no barrier has run yet
+
+  using T = typename Elem<D>::T;
+  if (tid < BN) {
+    const int o = o0 + tid;
+    s_bias[tid] = (args.bias != nullptr && o < cout) ? to_float<D>(reinterpret_cast<const T*>(args.bias)[o]) : 0.f;
+  }
+  for (int k = tid; k < ntiles; k += kWsThreads) s_tmask[k] = 0;
+  __syncthreads();
+  // Tap masks of all tiles: OR of the rows' neighbour masks, eight independent loads in flight.
+  // BM is a multiple of 64, so the 64 consecutive rows of a wave's load lie in one tile: OR them
+  // across the wave, then one LDS atomic per wave and load.
+  static_assert(BM % 64 == 0, "a wave's rows lie in one tile");
+  for (int idx0 = tid; idx0 < ntiles * BM; idx0 += 8 * kWsThreads) {
+    uint32_t m[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = idx0 + u * kWsThreads;
+      const int k = idx / BM;
+      const int64_t row = (int64_t)tile_of(k < ntiles ? k : 0) * BM + (idx - k * BM);
+      const bool ok = idx < ntiles * BM && row < n;
+      m[u] = ok ? args.masks[row] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      uint32_t v = m[u];
+      for (int off = 32; off > 0; off >>= 1) v |= __shfl_xor(v, off, 64);
+      const int k = (idx0 + u * kWsThreads) / BM;
+      if (lane == 0 && v != 0u) atomicOr(&s_tmask[k], v);
+    }
+  }
+  __syncthreads();
+  const int nq = (row_bytes + SL - 1) / SL;
+  int total = 0;  // stages of the whole workgroup, identical in every wave
+  for (int k = 0; k < ntiles; ++k) total += __builtin_popcount(s_tmask[k]) * nq;
+
+  auto swz_of = [](int row) { return (row / (16 / CH)) % CH; };
+
+  if (loader) {
+    auto chunk_bytes = [&](int group_row) {
+      return (uint32_t)(((lane % CH) ^ swz_of(group_row + lane / CH)) * 16);
+    };
+    const i32x4_t rsrc_a = make_rsrc(args.feats, args.feats_bytes);
+    const i32x4_t rsrc_b = make_rsrc(args.weight, args.weight_bytes);
+    const i32x4_t rsrc_n = make_rsrc(args.nbr, (uint32_t)(n * 27 * 4));
+    int32_t* my_nbr = s_nbr + cw * (QDMA * 256);
+    uint32_t lane_cb[DMA], base_b[BDMA];
+    bool ok_b[BDMA];
+#pragma unroll
+    for (int d = 0; d < ADMA; ++d) lane_cb[d] = chunk_bytes(cw * QROWS + RPI * d);
+#pragma unroll
+    for (int d = 0; d < BDMA; ++d) {
+      const int g = BM + cw * (BNP / 4) + RPI * d;
+      const int ol = g - BM + lane / CH;
+      const int o = o0 + ol;
+      lane_cb[ADMA + d] = chunk_bytes(g);
+      ok_b[d] = ol < BN && o < cout;
+      base_b[d] = (uint32_t)(ok_b[d] ? o : 0) * 27u * (uint32_t)row_bytes + lane_cb[ADMA + d];
+    }
+    bool row_ok[ADMA];
+    // Rulebook rows of tile k for this wave's quarter, into this wave's own slot (only this wave
+    // reads it, so its own wait is enough).  At a tile change the wait also drains the ring loads
+    // in flight, which have to land anyway; prefetching the rows one stage earlier, with waits
+    // that leave them in flight, measured 3-6 % slower.
+    auto load_rows = [&](int k) {
+      const int64_t r0 = (int64_t)tile_of(k) * BM + cw * QROWS;
+      const uint32_t gbase = (uint32_t)(r0 * 27 * 4);
+#pragma unroll
+      for (int d = 0; d < QDMA; ++d) {
+        const uint32_t blk = (uint32_t)(d * 1024);
+        const uint32_t off = blk + (uint32_t)lane * 16u;
+        lds_dma16(rsrc_n, off < (uint32_t)(QROWS * 27 * 4) ? gbase + off : kOutOfRange,
+                  lds_offset(s_nbr) + (uint32_t)(cw_u * QDMA * 1024) + blk);
+      }
+#pragma unroll
+      for (int d = 0; d < ADMA; ++d) row_ok[d] = r0 + RPI * d + lane / CH < n;
+      wait_vmcnt<0>();
+      compiler_fence();
+    };
+    int ck = 0;  // tile of the fetch cursor
+    uint32_t rem = s_tmask[0];
+    int ik = 0, iq = nq;
+    int pk = 0, pq = 0;
+    bool pvalid = false;
+    int32_t raw[ADMA];
+    uint32_t offs[DMA];
+    load_rows(0);
+    auto fetch = [&](int stage_index) {
+      pvalid = stage_index < total;
+      if (pvalid && iq >= nq && rem == 0u) {  // this tile's stages are done: next tile with taps
+        do {
+          ++ck;
+          rem = s_tmask[ck];
+        } while (rem == 0u && ck + 1 < ntiles);
+        compiler_fence();  // the last rows of the previous tile have been read
+        load_rows(ck);
+      }
+      const bool adv = pvalid && iq >= nq;
+      const int nk = __builtin_ctz(rem | 0x80000000u);
+      ik = adv ? nk : ik;
+      rem = adv ? (rem & (rem - 1)) : rem;
+      iq = adv ? 0 : iq;
+      pk = ik;
+      pq = iq;
+      iq += pvalid ? 1 : 0;
+#pragma unroll
+      for (int d = 0; d < ADMA; ++d) raw[d] = my_nbr[(RPI * d + lane / CH) * 27 + pk];
+    };
+    auto make = [&]() {
+      const uint32_t sq = (uint32_t)(pq * SL);
+      const uint32_t sb = (uint32_t)pk * (uint32_t)row_bytes + sq;
+      const int limit = pvalid ? row_bytes - (int)sq : 0;
+#pragma unroll
+      for (int d = 0; d < ADMA; ++d) {
+        const uint32_t o = (uint32_t)raw[d] * (uint32_t)row_bytes + sq + lane_cb[d];
+        const bool use = (raw[d] >= 0) & row_ok[d] & ((int)lane_cb[d] < limit);
+        offs[d] = use ? o : kOutOfRange;
+      }
+#pragma unroll
+      for (int d = 0; d < BDMA; ++d) {
+        const bool use = ok_b[d] & ((int)lane_cb[ADMA + d] < limit);
+        offs[ADMA + d] = use ? base_b[d] + sb : kOutOfRange;
+      }
+    };
+    auto issue = [&](unsigned char* base) {
+#pragma unroll
+      for (int d = 0; d < ADMA; ++d)
+        lds_dma16(rsrc_a, offs[d], lds_offset(base) + (uint32_t)((cw_u * QROWS + RPI * d) * SL));
+#pragma unroll
+      for (int d = 0; d < BDMA; ++d)
+        lds_dma16(rsrc_b, offs[ADMA + d], lds_offset(base) + (uint32_t)((BM + cw_u * (BNP / 4) + RPI * d) * SL));
+    };
+#pragma unroll
+    for (int s0 = 0; s0 < NS; ++s0) {
+      fetch(s0);
+      make();
+      issue(ring + s0 * BUF);
+    }
+    fetch(NS);
+    wait_vmcnt<(NS - 1) * DMA>();
+    barrier_no_fence();
+    int slot = 0;
+    for (int st = 0; st < total; ++st) {
+      // Barrier st: this wave's loads of stage st + 1 have landed; afterwards slot st is free.
+      wait_vmcnt<(NS - 2) * DMA>();
+      barrier_no_fence();
+      make();
+      issue(ring + slot * BUF);
+      fetch(st + NS + 1);
+      slot = slot + 1 == NS ? 0 : slot + 1;
+    }
+    wait_vmcnt<0>();
+  } else {
+    f32x16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    const int lrow = lane & 31;
+    const int lk = lane >> 5;
+    const int swz = swz_of(lrow);
+    uint4 ga[2][FM], gb[2][FN];
+    auto read_step = [&](auto P, auto KK, const unsigned char* buf) {
+      constexpr int p = decltype(P)::value, kk = decltype(KK)::value;
+      const int off = ((2 * kk + lk) ^ swz) << 4;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        ga[p][i] = *reinterpret_cast<const uint4*>(buf + (wm * WTM + i * 32 + lrow) * SL + off);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        gb[p][j] = *reinterpret_cast<const uint4*>(buf + (BM + wn * WTN + j * 32 + lrow) * SL + off);
+    };
+    auto mul_step = [&](auto P) {
+      constexpr int p = decltype(P)::value;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<D>(gb[p][j], ga[p][i], acc[i][j]);
+    };
+    auto interleave_step = [&]() {
+#pragma unroll
+      for (int g = 0; g < FM * FN; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+      }
+    };
+    auto inner = [&](auto KK, const unsigned char* cur) {
+      constexpr int kk = decltype(KK)::value;
+      if constexpr (kk < KSTEPS - 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        read_step(IC<(kk + 1) & 1>{}, IC<kk + 1>{}, cur);
+        mul_step(IC<kk & 1>{});
+        interleave_step();
+      }
+    };
+    // Finished tile: + bias, one rounding, each lane's four consecutive channels as 8 bytes.
+    T* out = reinterpret_cast<T*>(args.out);
+    auto write_tile = [&](int k) {
+      const int64_t row0 = (int64_t)tile_of(k) * BM;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t row = row0 + wm * WTM + i * 32 + lrow;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = wn * WTN + j * 32 + 8 * g + 4 * lk;
+            const float4 bb = *reinterpret_cast<const float4*>(s_bias + c);
+            if (row < n && o0 + c < cout)
+              *reinterpret_cast<uint2*>(out + row * cout + o0 + c) =
+                  pack4<D>(acc[i][j][4 * g] + bb.x, acc[i][j][4 * g + 1] + bb.y, acc[i][j][4 * g + 2] + bb.z,
+                           acc[i][j][4 * g + 3] + bb.w);
+            acc[i][j][4 * g] = acc[i][j][4 * g + 1] = acc[i][j][4 * g + 2] = acc[i][j][4 * g + 3] = 0.f;
+          }
+      }
+    };
+    int k = 0;
+    int left = __builtin_popcount(s_tmask[0]) * nq;  // stages left in tile k
+    // A tile with no taps (no valid row: not produced by the tiling, kept for safety) is bias only.
+    auto next_tiles = [&]() {
+      while (left == 0 && k < ntiles) {
+        write_tile(k);
+        ++k;
+        left = k < ntiles ? __builtin_popcount(s_tmask[k]) * nq : 0;
+      }
+    };
+    next_tiles();
+    barrier_no_fence();  // stage 0 has landed
+    read_step(IC<0>{}, IC<0>{}, ring);
+    int slot = 0;
+    for (int st = 0; st < total; ++st) {
+      const unsigned char* cur = ring + slot * BUF;
+      const int next_slot = slot + 1 == NS ? 0 : slot + 1;
+      inner(IC<0>{}, cur);
+      inner(IC<1>{}, cur);
+      inner(IC<2>{}, cur);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkmcnt0();
+      barrier_no_fence();  // barrier st: stage st + 1 in LDS; this wave is done with slot st
+      __builtin_amdgcn_sched_barrier(0);
+      read_step(IC<KSTEPS & 1>{}, IC<0>{}, ring + next_slot * BUF);
+      mul_step(IC<(KSTEPS - 1) & 1>{});
+      interleave_step();
+      slot = next_slot;
+      if (--left == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        next_tiles();
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <DT D, int WM, int FM, int FN, int SL, int TAPS, int KP = 0, bool STATS = false>
 hipError_t launch_ws(const ConvArgs& a0, hipStream_t stream) {
   using Sh = MmaShape<WM, FM, FN, SL, TAPS>;
@@ -1074,6 +1380,23 @@ hipError_t launch_mma(const ConvArgs& a0, hipStream_t stream) {
   a.per_xcd = (a.tiles_m + 7) / 8;
   dim3 grid((unsigned)(8 * a.per_xcd), (unsigned)((a.cout + Sh::BN - 1) / Sh::BN));
   subm_conv_mma_kernel<D, WM, FM, FN, SL, TAPS><<<grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// Persistent launch: one workgroup per compute unit (a multiple of 8, for the XCD mapping), each
+// walking its tiles.  hipErrorNotSupported when a workgroup would get more than kMaxBlockTiles
+// tiles or the output rows cannot take 8-byte stores (the caller then uses launch_ws).
+template <DT D, int WM, int FM, int FN, int SL>
+hipError_t launch_ws_persistent(const ConvArgs& a0, hipStream_t stream) {
+  using Sh = MmaShape<WM, FM, FN, SL, 27>;
+  ConvArgs a = a0;
+  a.tiles_m = (int)((a.n + Sh::BM - 1) / Sh::BM);
+  a.per_xcd = (a.tiles_m + 7) / 8;
+  const int nblk = std::min(kPersistentBlocks, 8 * a.per_xcd);
+  const int per_block = (a.per_xcd + nblk / 8 - 1) / (nblk / 8);
+  if (per_block > kMaxBlockTiles || !a.vec_out || a.cout % 8 != 0) return hipErrorNotSupported;
+  dim3 grid((unsigned)nblk, (unsigned)((a.cout + Sh::BN - 1) / Sh::BN));
+  subm_conv_ws_persistent_kernel<D, WM, FM, FN, SL><<<grid, kWsThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -1134,6 +1457,12 @@ hipError_t launch_tile_index(int t, const ConvArgs& a, hipStream_t stream) {
 // 256 x 64 tile of the same kind.  Up to 32 channels, a 256-row tile when it saves rounds of
 // tiles over the 256 compute units.
 constexpr int kComputeUnits = 256;
+constexpr bool persistent_enabled_default = true;
+// SUBMCONV_PERSISTENT=0 selects the one-tile-per-workgroup launch (timing and tests).
+inline bool persistent_enabled() {
+  const char* v = std::getenv("SUBMCONV_PERSISTENT");
+  return v == nullptr ? persistent_enabled_default : v[0] != '0';
+}
 inline int64_t launch_rounds(int64_t n, int cout, int bm, int bn) {
   const int64_t tiles = (n + bm - 1) / bm * ((cout + bn - 1) / bn);
   return (tiles + kComputeUnits - 1) / kComputeUnits;
@@ -1148,6 +1477,13 @@ int tile_index(const char* name) {
 template <DT D, int TAPS>
 hipError_t launch_mma_auto(const ConvArgs& a, hipStream_t stream) {
   int best;
+  const char* forced = std::getenv("SUBMCONV_TILE");
+  if (TAPS == 27 && a.cout > 32 && (forced == nullptr || tile_index(forced) < 0) && persistent_enabled()) {
+    // the persistent walk of the same tiles the one-tile launch below would use
+    const hipError_t e = a.cout > 64 ? launch_ws_persistent<D, 2, 3, 2, 128>(a, stream)
+                                     : launch_ws_persistent<D, 4, 2, 2, 128>(a, stream);
+    if (e != hipErrorNotSupported) return e;
+  }
   if (a.cout > 64) {
     best = tile_index("ws192c128s128k");
   } else if (a.cout > 32) {

@@ -392,3 +392,45 @@ def test_tile_configs_headline_shell(monkeypatch, tile):
     with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
         out = forward(m, f, w, b)
     check(out, oracle.conv3_rulebook(oracle_nbr("3a"), as64(f), as64(w), as64(b)), "bf16", f"3a tile {tile}")
+
+
+# ----------------------------------------------------------------- persistent tile walk
+
+# The default 16-bit k = 3 launch above 32 output channels walks several row tiles per workgroup
+# (one workgroup per compute unit); SUBMCONV_PERSISTENT=0 selects one tile per workgroup.  Both
+# run the same stages in the same order and round once, so their outputs agree bit for bit.
+PERSISTENT_CASES = [("bf16", 128, 128, "2a"), ("f16", 64, 64, "2a"), ("bf16", 96, 48, "1"), ("f16", 200, 136, "2a"),
+                    ("bf16", 40, 256, "2a"), ("bf16", 64, 40, "2a"), ("bf16", 8, 72, "1"), ("f16", 64, 36, "2a")]
+
+
+@pytest.mark.parametrize("dtype,cin,cout,key", PERSISTENT_CASES)
+def test_persistent_walk_matches_oracle_and_one_tile_launch(monkeypatch, dtype, cin, cout, key):
+    monkeypatch.delenv("SUBMCONV_TILE", raising=False)
+    coords, f, w, b = small_case(dtype, cin, cout, key=key, seed=3)
+    outs = {}
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        for mode in ("1", "0"):
+            monkeypatch.setenv("SUBMCONV_PERSISTENT", mode)
+            outs[mode] = forward(m, f, w, b)
+    check(outs["1"], oracle.conv3_rulebook(oracle_nbr(key), as64(f), as64(w), as64(b)), dtype,
+          f"persistent {dtype} {cin}->{cout} on {key}")
+    assert torch.equal(outs["1"], outs["0"])
+
+
+@pytest.mark.parametrize("key", ["3a", "3b", "4"])
+def test_persistent_walk_full_size(monkeypatch, key):
+    # 3a: 708 tiles, two or three per workgroup; 3b: 43 per workgroup; 4: the 64-channel tile.
+    monkeypatch.delenv("SUBMCONV_TILE", raising=False)
+    coords = coords_of(key)
+    f, w, b = cfg_tensors(key, 0)
+    fd, wd, bd = f.to(DEV), w.to(DEV), b.to(DEV)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        monkeypatch.setenv("SUBMCONV_PERSISTENT", "1")
+        y1 = sc.subm_conv3d_forward(m, fd, wd, bd)
+        monkeypatch.setenv("SUBMCONV_PERSISTENT", "0")
+        y0 = sc.subm_conv3d_forward(m, fd, wd, bd)
+        torch.cuda.synchronize()
+    assert torch.equal(y1, y0), f"{key}: persistent and one-tile launches differ"
+    rows = sample_rows(len(coords), count=1024, seed=5)
+    ref = oracle.conv3_rulebook(oracle_nbr(key), as64(f), as64(w), as64(b), rows=rows)
+    check(y1.cpu()[rows], ref, synth.config(key).dtype, f"persistent {key}")
