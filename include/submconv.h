@@ -160,6 +160,9 @@ int sparse_indice_map_copy_nbr(submconv_map_t map, int32_t* nbr, hipStream_t str
  *            host only.  n == 0 returns SUBM_OK with no launch.
  * Row i of out is written only from rows of feats that are neighbours of i, so the result does
  * not depend on launch order and is bitwise reproducible run to run (no float atomics).
+ * Tuning and tests: the environment variable SUBMCONV_TILE=<name> forces one of the library's
+ * tile configurations, and SUBMCONV_PERSISTENT=0 launches one workgroup per row tile instead of
+ * one per compute unit walking several tiles (the two agree bit for bit).
  * Errors: SUBM_ERR_INVALID_ARG, SUBM_ERR_SHAPE_MISMATCH, SUBM_ERR_UNSUPPORTED, SUBM_ERR_HIP.
  * Source: lato.2_mrp_mlx README, header summary and "Correctness"; trellis_sparse_mrp_mlx
  * commit log, "Extracted from lato.2_mrp_mlx" commit (the 128^3 / 128-channel timing).

@@ -123,12 +123,35 @@ def _check(lib, func: str, status: int) -> None:
         raise SubmError(func, status, name, detail)
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_ptr(stream, device) -> int:
     if stream is None:
+        if _raw_stream is not None:  # the current stream's handle without building a Stream object
+            return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
         return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+class _Current:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *exc):
+        return False
+
+
+_CURRENT = _Current()
+
+
+def _on_device(device):
+    """Make `device` current for a call, skipping the switch when it already is."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return _CURRENT
+    return torch.cuda.device(device)
 
 
 def _device_tensor(t: torch.Tensor, what: str) -> None:
@@ -199,7 +222,7 @@ def sparse_indice_map_build_ex(coords: torch.Tensor, mode: int, stream=None) -> 
         raise ValueError("coords must be int32 [N, 4]")
     lib = load_library()
     out = ctypes.c_void_p()
-    with torch.cuda.device(coords.device):
+    with _on_device(coords.device):
         st = lib.sparse_indice_map_build_ex(coords.data_ptr(), coords.shape[0], int(mode),
                                             _stream_ptr(stream, coords.device), ctypes.byref(out))
     _check(lib, "sparse_indice_map_build_ex", st)
@@ -242,7 +265,7 @@ def sparse_indice_map_copy_nbr(m: IndiceMap, out: torch.Tensor | None = None, st
     if out.dtype != torch.int32 or tuple(out.shape) != (m.n, TAPS):
         raise ValueError("out must be int32 [N, 27]")
     lib = load_library()
-    with torch.cuda.device(out.device):
+    with _on_device(out.device):
         st = lib.sparse_indice_map_copy_nbr(m.handle, out.data_ptr(), _stream_ptr(stream, out.device))
     _check(lib, "sparse_indice_map_copy_nbr", st)
     return out
@@ -283,7 +306,7 @@ def subm_conv3d_forward_per_offset(m: IndiceMap, feats: torch.Tensor, weight: to
     if k != 3:
         raise ValueError("the per-offset path is the k = 3 convolution")
     lib = load_library()
-    with torch.cuda.device(feats.device):
+    with _on_device(feats.device):
         st = lib.subm_conv3d_forward_per_offset(m.handle, feats.shape[0], feats.shape[1], weight.shape[0],
                                                 _DTYPE_CODES[feats.dtype], feats.data_ptr(), weight.data_ptr(),
                                                 bias_ptr, out.data_ptr(), _stream_ptr(stream, feats.device))
@@ -320,7 +343,7 @@ def subm_conv3d_forward(m: IndiceMap | None, feats: torch.Tensor, weight: torch.
         raise ValueError("out must be [N, Cout] in the feats dtype")
     lib = load_library()
     handle = None if m is None else m.handle
-    with torch.cuda.device(feats.device):
+    with _on_device(feats.device):
         st = lib.subm_conv3d_forward(handle, n, k, cin, cout, _DTYPE_CODES[feats.dtype], feats.data_ptr(),
                                      weight.data_ptr(), bias_ptr, out.data_ptr(), _stream_ptr(stream, feats.device))
     _check(lib, "subm_conv3d_forward", st)
@@ -382,7 +405,7 @@ def _coords_arg(coords: torch.Tensor) -> None:
 def _build_subdivision(func: str, coords: torch.Tensor, args: tuple, stream) -> Subdivision:
     lib = load_library()
     out = ctypes.c_void_p()
-    with torch.cuda.device(coords.device):
+    with _on_device(coords.device):
         st = getattr(lib, func)(*args, _stream_ptr(stream, coords.device), ctypes.byref(out))
     _check(lib, func, st)
     return Subdivision(out.value, coords.device)
@@ -453,7 +476,7 @@ def sparse_subdivision_copy(s: Subdivision, what: int, out: torch.Tensor | None 
     if out.dtype != torch.int32 or tuple(out.shape) != shape[what]:
         raise ValueError(f"out must be int32 {shape[what]}")
     lib = load_library()
-    with torch.cuda.device(out.device):
+    with _on_device(out.device):
         st = lib.sparse_subdivision_copy(s.handle, int(what), out.data_ptr(), _stream_ptr(stream, out.device))
     _check(lib, "sparse_subdivision_copy", st)
     return out
@@ -480,7 +503,7 @@ def sparse_downsample_forward(s: Subdivision, fine: torch.Tensor, mode: int, out
     """Pool fine features [n_fine, C] onto the coarse rows: mode SUBM_POOL_MAX or SUBM_POOL_MEAN."""
     out = _feature_pair(fine, s.n_fine, out, s.n_coarse, "fine")
     lib = load_library()
-    with torch.cuda.device(fine.device):
+    with _on_device(fine.device):
         st = lib.sparse_downsample_forward(s.handle, fine.shape[1], _DTYPE_CODES[fine.dtype], int(mode),
                                            fine.data_ptr(), out.data_ptr(), _stream_ptr(stream, fine.device))
     _check(lib, "sparse_downsample_forward", st)
@@ -492,7 +515,7 @@ def sparse_upsample_forward(s: Subdivision, coarse: torch.Tensor, out: torch.Ten
     """Fine features [n_fine, C]: every fine row a copy of its parent's coarse row."""
     out = _feature_pair(coarse, s.n_coarse, out, s.n_fine, "coarse")
     lib = load_library()
-    with torch.cuda.device(coarse.device):
+    with _on_device(coarse.device):
         st = lib.sparse_upsample_forward(s.handle, coarse.shape[1], _DTYPE_CODES[coarse.dtype], coarse.data_ptr(),
                                          out.data_ptr(), _stream_ptr(stream, coarse.device))
     _check(lib, "sparse_upsample_forward", st)
@@ -503,7 +526,7 @@ def sparse_indice_map_subdivide(parent: IndiceMap, s: Subdivision, stream=None) 
     """Indice map of a subdivide's fine set, derived from the map of its coarse set."""
     lib = load_library()
     out = ctypes.c_void_p()
-    with torch.cuda.device(s.device):
+    with _on_device(s.device):
         st = lib.sparse_indice_map_subdivide(parent.handle, s.handle, _stream_ptr(stream, s.device),
                                              ctypes.byref(out))
     _check(lib, "sparse_indice_map_subdivide", st)
@@ -542,7 +565,7 @@ def subm_conv3d_forward_group_norm_act(m: IndiceMap | None, feats: torch.Tensor,
     ptrs = _norm_affine(weight.shape[0], feats.dtype, gamma, beta)
     lib = load_library()
     handle = None if m is None else m.handle
-    with torch.cuda.device(feats.device):
+    with _on_device(feats.device):
         st = lib.subm_conv3d_forward_group_norm_act(
             handle, feats.shape[0], k, feats.shape[1], weight.shape[0], _DTYPE_CODES[feats.dtype], feats.data_ptr(),
             weight.data_ptr(), bias_ptr, item_offsets.data_ptr(), item_offsets.shape[0] - 1, int(groups), ptrs[0],
@@ -569,7 +592,7 @@ def sparse_group_norm_act(x: torch.Tensor, item_offsets: torch.Tensor, groups: i
     if out.dtype != x.dtype or out.shape != x.shape:
         raise ValueError("out must match x")
     lib = load_library()
-    with torch.cuda.device(x.device):
+    with _on_device(x.device):
         st = lib.sparse_group_norm_act(x.data_ptr(), x.shape[0], c, _DTYPE_CODES[x.dtype], item_offsets.data_ptr(),
                                        item_offsets.shape[0] - 1, int(groups), ptrs[0], ptrs[1], float(eps), int(act),
                                        out.data_ptr(), _stream_ptr(stream, x.device))

@@ -17,26 +17,27 @@
 //         axis' extent (max - min) is at most 65534, which the build enforces.
 //
 // The structure is chosen on the device from the set's bounds, so the whole build needs one
-// host synchronisation, taken as soon as the insert kernel has finished: by then the plan and
-// insert kernels have written the error flags straight into pinned host memory, and the lookup
+// host synchronisation, taken as soon as the insert kernel has finished: by then it has written
+// the plan's range flags and its own error flags straight into pinned host memory, and the lookup
 // and reset kernels go on running while the caller enqueues its convolutions.  No structure is
 // ever cleared in full: the table area is all 0xFF bytes between builds (an empty cell is -1
 // and an empty slot is key ~0, row -1), and every build resets exactly what it wrote.
 //
 // Kernels, all on the caller's stream:
-//   map_bounds_kernel   per-block min/max of (b, z, y, x) and the batch-range flag -> partials
-//   map_plan_kernel     one block reduces the partials, picks the structure, publishes the plan
-//                       (and its range flags and mode to the host) and zeroes the counters (a
-//                       separate launch: signalling between blocks of one kernel needs a
-//                       device-scope fence, which writes back the whole L2 of each XCD and costs
-//                       far more than a launch)
-//   map_insert_kernel   GRID: CAS the row into its cell; HASH: CAS the key into the table.  A
-//                       cell or key already taken by another row raises the duplicate flag in
-//                       host memory (a plain store of a constant, so concurrent writers agree).
-//   map_lookup_kernel   one thread per voxel: 27 loads (GRID) or 27 probe sequences (HASH), nine
-//                       in flight at a time; the block's rows are staged in LDS and written as
-//                       one contiguous run of nbr; per-row 27-bit hit mask; hits counted per tap
-//                       with wave ballots and added to one of 16 counter banks
+//   map_bounds_kernel   per-block min/max of (b, z, y, x) -> partials (at most 256)
+//   map_insert_kernel   every block first reduces the partials itself and so derives the same
+//                       plan (range checks, structure, strides) with no second launch and no
+//                       signalling between blocks (that needs a device-scope fence, which writes
+//                       back the whole L2 of each XCD); block 0 publishes it (and the range flags
+//                       and mode to the host) and zeroes the counters.  Then GRID: CAS the row
+//                       into its cell, up to four voxels per thread in flight; HASH: CAS the key
+//                       into the table.  A cell or key already taken by another row raises the
+//                       duplicate flag in host memory (a plain store of a constant, so
+//                       concurrent writers agree).
+//   map_lookup_kernel   three threads per voxel, one per dz plane: 9 loads (GRID) or 9 probe
+//                       sequences (HASH) each, all in flight; the block's rows are staged in LDS
+//                       and written as one contiguous run of nbr; per-row 27-bit hit mask; hits
+//                       counted per tap with wave ballots and added to one of 16 counter banks
 //   map_reset_kernel    GRID: -1 back into every voxel's cell; HASH: the used slots emptied;
 //                       block 0 sums the per-tap counter banks into the map's own counts
 #include "internal.h"
@@ -48,7 +49,8 @@ constexpr unsigned long long kEmptyKey = ~0ull;
 constexpr int kThreads = 256;
 constexpr int kMaxBoundsBlocks = 256;
 constexpr int kMaxWideBlocks = 1024;
-constexpr int kMaxInsertBlocks = 8192;
+constexpr int kMaxInsertBlocks = 2048;  // with four voxels per thread in flight
+constexpr int kLookupVoxels = 256;      // voxels per lookup block (three threads each)
 
 struct __align__(16) Slot {
   unsigned long long key;
@@ -57,11 +59,11 @@ struct __align__(16) Slot {
 };
 static_assert(sizeof(Slot) == 16, "slot must be 16 bytes");
 
-struct BoundsPartial {
+// The batch-range check needs no flag of its own: some b lies outside [0, SUBM_MAX_BATCH) exactly
+// when the minimum or the maximum of b does.
+struct __align__(16) BoundsPartial {
   int32_t mn[4];
   int32_t mx[4];
-  uint32_t flags;
-  uint32_t pad[3];
 };
 
 __device__ __forceinline__ unsigned long long pack_key(int32_t b, int32_t z, int32_t y, int32_t x) {
@@ -92,28 +94,21 @@ __device__ __forceinline__ int wave_max(int v) {
   for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
   return v;
 }
-__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-  for (int off = 32; off > 0; off >>= 1) v |= __shfl_xor(v, off, 64);
-  return v;
-}
 
 // ------------------------------------------------------------------ bounds
 __global__ __launch_bounds__(kThreads) void map_bounds_kernel(const int32_t* __restrict__ coords, int64_t n,
                                                               BoundsPartial* __restrict__ partials) {
   int mn[4] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX};
   int mx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
-  uint32_t flags = 0;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
     const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
     mn[0] = min(mn[0], c.x); mx[0] = max(mx[0], c.x);
     mn[1] = min(mn[1], c.y); mx[1] = max(mx[1], c.y);
     mn[2] = min(mn[2], c.z); mx[2] = max(mx[2], c.z);
     mn[3] = min(mn[3], c.w); mx[3] = max(mx[3], c.w);
-    if (c.x < 0 || c.x >= SUBM_MAX_BATCH) flags |= kFlagBatchRange;
   }
   __shared__ int smn[kThreads / 64][4];
   __shared__ int smx[kThreads / 64][4];
-  __shared__ uint32_t sfl[kThreads / 64];
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -124,8 +119,6 @@ __global__ __launch_bounds__(kThreads) void map_bounds_kernel(const int32_t* __r
       smx[wave][a] = hi;
     }
   }
-  flags = wave_or(flags);
-  if (lane == 0) sfl[wave] = flags;
   __syncthreads();
   if (threadIdx.x < 4) {
     const int a = threadIdx.x;
@@ -136,11 +129,6 @@ __global__ __launch_bounds__(kThreads) void map_bounds_kernel(const int32_t* __r
     }
     partials[blockIdx.x].mn[a] = lo;
     partials[blockIdx.x].mx[a] = hi;
-  }
-  if (threadIdx.x == 0) {
-    uint32_t f = 0;
-    for (int w = 0; w < kThreads / 64; ++w) f |= sfl[w];
-    partials[blockIdx.x].flags = f;
   }
 }
 
@@ -153,18 +141,15 @@ struct Plan {
   int64_t cells, sy, sz, sb;
 };
 
-// Every block reduces the (few) partials itself, so all blocks agree on the plan without
-// another launch.
+// Every insert block reduces the (at most 256) partials itself, so all blocks agree on the plan
+// without another launch.
 __device__ void reduce_plan(const BoundsPartial* __restrict__ partials, int nparts, int64_t grid_budget_cells,
                             int mode_request, Plan& plan, int32_t (&mx_out)[4]) {
   __shared__ int s_mn[4], s_mx[4];
-  __shared__ uint32_t s_fl;
   __shared__ int rmn[kThreads / 64][4], rmx[kThreads / 64][4];
-  __shared__ uint32_t rfl[kThreads / 64];
   const int t = threadIdx.x;
   int mn[4] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX};
   int mx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
-  uint32_t fl = 0;
   for (int p = t; p < nparts; p += kThreads) {
     const BoundsPartial q = partials[p];
 #pragma unroll
@@ -172,7 +157,6 @@ __device__ void reduce_plan(const BoundsPartial* __restrict__ partials, int npar
       mn[a] = min(mn[a], q.mn[a]);
       mx[a] = max(mx[a], q.mx[a]);
     }
-    fl |= q.flags;
   }
   const int wave = t / 64, lane = t % 64;
 #pragma unroll
@@ -184,8 +168,6 @@ __device__ void reduce_plan(const BoundsPartial* __restrict__ partials, int npar
       rmx[wave][a] = hi;
     }
   }
-  fl = wave_or(fl);
-  if (lane == 0) rfl[wave] = fl;
   __syncthreads();
   if (t < 4) {
     int lo = rmn[0][t], hi = rmx[0][t];
@@ -196,18 +178,13 @@ __device__ void reduce_plan(const BoundsPartial* __restrict__ partials, int npar
     s_mn[t] = lo;
     s_mx[t] = hi;
   }
-  if (t == 0) {
-    uint32_t f = 0;
-    for (int w = 0; w < kThreads / 64; ++w) f |= rfl[w];
-    s_fl = f;
-  }
   __syncthreads();
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     plan.mn[a] = s_mn[a];
     mx_out[a] = s_mx[a];
   }
-  uint32_t flags = s_fl;
+  uint32_t flags = (s_mn[0] < 0 || s_mx[0] >= SUBM_MAX_BATCH) ? kFlagBatchRange : 0u;
   const int64_t ext_b = (int64_t)s_mx[0] - s_mn[0] + 1;
   const int64_t ext_z = (int64_t)s_mx[1] - s_mn[1];
   const int64_t ext_y = (int64_t)s_mx[2] - s_mn[2];
@@ -240,55 +217,64 @@ __device__ __forceinline__ int64_t grid_cell(const MapStats& p, int b, int z, in
   return grid_cell(p.mn, p.sb, p.sz, p.sy, b, z, y, x);
 }
 
-__global__ __launch_bounds__(kThreads) void map_plan_kernel(const BoundsPartial* __restrict__ partials, int nparts,
-                                                            int64_t grid_budget_cells, int64_t slots,
-                                                            int mode_request, MapStats* __restrict__ st,
-                                                            MapHostFlags* __restrict__ host) {
+__global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __restrict__ coords, int64_t n,
+                                                              const BoundsPartial* __restrict__ partials, int nparts,
+                                                              int64_t grid_budget_cells, int64_t slots,
+                                                              int mode_request, void* __restrict__ table,
+                                                              MapStats* __restrict__ st,
+                                                              MapHostFlags* __restrict__ host) {
   Plan plan;
   int32_t mx[4];
   reduce_plan(partials, nparts, grid_budget_cells, mode_request, plan, mx);
   const int t = threadIdx.x;
-  if (t < 4) {
-    st->mn[t] = plan.mn[t];
-    st->mx[t] = mx[t];
-  }
-  if (t == 0) {
-    host->flags = plan.flags;
-    host->mode = plan.mode;
-    st->flags = plan.flags;
-    st->err_flags = 0;
-    st->mode = plan.mode;
-    st->cells = plan.cells;
-    st->slots = slots;
-    st->sy = plan.sy;
-    st->sz = plan.sz;
-    st->sb = plan.sb;
-  }
-  for (int k = t; k < kTapBanks * 27; k += kThreads) (&st->tap_counts[0][0])[k] = 0;
-}
-
-__global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __restrict__ coords, int64_t n,
-                                                              void* __restrict__ table, const MapStats* __restrict__ st,
-                                                              MapHostFlags* __restrict__ host) {
-  Plan plan;
-  plan.mode = st->mode;
-  if (plan.mode == kModeNone) return;
+  if (blockIdx.x == 0) {  // publish the plan for the lookup and reset kernels and the host
+    if (t == 0) {
+      // (constant indices: indexing the plan's arrays by thread would move them into LDS)
 #pragma unroll
-  for (int a = 0; a < 4; ++a) plan.mn[a] = st->mn[a];
-  plan.sb = st->sb;
-  plan.sz = st->sz;
-  plan.sy = st->sy;
-  const int64_t slots = st->slots;
-  const int t = threadIdx.x;
+      for (int a = 0; a < 4; ++a) {
+        st->mn[a] = plan.mn[a];
+        st->mx[a] = mx[a];
+      }
+      host->flags = plan.flags;
+      host->mode = plan.mode;
+      st->flags = plan.flags;
+      st->err_flags = 0;
+      st->mode = plan.mode;
+      st->cells = plan.cells;
+      st->slots = slots;
+      st->sy = plan.sy;
+      st->sz = plan.sz;
+      st->sb = plan.sb;
+    }
+    for (int k = t; k < kTapBanks * 27; k += kThreads) (&st->tap_counts[0][0])[k] = 0;
+  }
+  if (plan.mode == kModeNone) return;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
   bool dup = false, overflow = false;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + t; i < n; i += (int64_t)gridDim.x * kThreads) {
-    const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
-    if (plan.mode == kModeGrid) {
-      int32_t* grid = static_cast<int32_t*>(table);
-      const int64_t cell = grid_cell(plan.mn, plan.sb, plan.sz, plan.sy, c.x, c.y, c.z, c.w);
-      dup |= atomicCAS(&grid[cell], -1, (int32_t)i) != -1;
-    } else {
-      Slot* tab = static_cast<Slot*>(table);
+  if (plan.mode == kModeGrid) {
+    int32_t* grid = static_cast<int32_t*>(table);
+    for (int64_t i0 = (int64_t)blockIdx.x * kThreads + t; i0 < n; i0 += 4 * stride) {
+      // up to four voxels, their compare-and-swaps in flight together
+      int64_t cell[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t i = i0 + u * stride;
+        cell[u] = -1;
+        if (i < n) {
+          const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
+          cell[u] = grid_cell(plan.mn, plan.sb, plan.sz, plan.sy, c.x, c.y, c.z, c.w);
+        }
+      }
+      int32_t prev[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) prev[u] = cell[u] >= 0 ? atomicCAS(&grid[cell[u]], -1, (int32_t)(i0 + u * stride)) : -1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dup |= prev[u] != -1;
+    }
+  } else {
+    Slot* tab = static_cast<Slot*>(table);
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + t; i < n; i += stride) {
+      const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
       const unsigned long long key = pack_key(c.x, c.y, c.z, c.w);
       unsigned long long s = home_slot(key, (unsigned long long)slots);
       bool placed = false;
@@ -314,8 +300,9 @@ __global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __r
 }
 
 // ------------------------------------------------------------------ lookup
-// One thread per voxel: the 27 neighbours are resolved one dz-plane (9 taps) at a time with
-// all 9 loads in flight, staged in LDS, and written back as one contiguous block of rows.
+// Three threads per voxel, one per dz plane (the plane index is uniform over each group of four
+// waves): the plane's 9 neighbours are resolved with all 9 loads in flight, staged in LDS, and
+// the block's rows written back as one contiguous block of nbr.
 __device__ __forceinline__ int32_t probe_rest(const Slot* __restrict__ tab, unsigned long long slots,
                                               unsigned long long key, unsigned long long s) {
   // Continue a probe sequence after its home slot held another key.
@@ -328,73 +315,79 @@ __device__ __forceinline__ int32_t probe_rest(const Slot* __restrict__ tab, unsi
   return -1;
 }
 
-__global__ __launch_bounds__(kThreads) void map_lookup_kernel(const int32_t* __restrict__ coords, int64_t n,
-                                                              const void* __restrict__ table,
-                                                              int32_t* __restrict__ nbr, uint32_t* __restrict__ masks,
-                                                              MapStats* __restrict__ st) {
-  __shared__ int32_t s_out[kThreads * 27];
+__global__ __launch_bounds__(3 * kLookupVoxels) void map_lookup_kernel(const int32_t* __restrict__ coords, int64_t n,
+                                                                      const void* __restrict__ table,
+                                                                      int32_t* __restrict__ nbr,
+                                                                      uint32_t* __restrict__ masks,
+                                                                      MapStats* __restrict__ st) {
+  __shared__ int32_t s_out[kLookupVoxels * 27];
+  __shared__ uint32_t s_pm[3][kLookupVoxels];
   __shared__ uint32_t s_cnt[27];
   const int mode = st->mode;
   if (mode == kModeNone) return;
   const int t = threadIdx.x;
   const int lane = t & 63;
+  const int plane = t / kLookupVoxels;
+  const int v = t - plane * kLookupVoxels;
   if (t < 27) s_cnt[t] = 0;
-  const int64_t i0 = (int64_t)blockIdx.x * kThreads;
-  const int64_t i = i0 + t;
-  uint32_t mask = 0;
+  const int64_t i0 = (int64_t)blockIdx.x * kLookupVoxels;
+  const int64_t i = i0 + v;
+  uint32_t pm = 0;  // hit bits of this plane's taps, at their tap positions
   if (i < n) {
     const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
     if (mode == kModeGrid) {
       const int32_t* grid = static_cast<const int32_t*>(table);
       const int64_t sy = st->sy, sz = st->sz;
-      const int64_t base = grid_cell(*st, c.x, c.y, c.z, c.w);
+      const int64_t base = grid_cell(*st, c.x, c.y, c.z, c.w) + (plane - 1) * sz;
+      int32_t val[9];
 #pragma unroll
-      for (int k = 0; k < 27; ++k) {
-        const int dz = k / 9 - 1, dy = (k / 3) % 3 - 1, dx = k % 3 - 1;
-        const int32_t v = grid[base + dz * sz + dy * sy + dx];
-        s_out[t * 27 + k] = v;
-        mask |= (v >= 0 ? 1u : 0u) << k;
+      for (int q = 0; q < 9; ++q) val[q] = grid[base + (q / 3 - 1) * sy + (q % 3 - 1)];
+#pragma unroll
+      for (int q = 0; q < 9; ++q) {
+        const int k = plane * 9 + q;
+        s_out[v * 27 + k] = val[q];
+        pm |= (val[q] >= 0 ? 1u : 0u) << k;
       }
     } else {
       const Slot* tab = static_cast<const Slot*>(table);
       const unsigned long long slots = (unsigned long long)st->slots;
+      unsigned long long key[9], home[9];
+      Slot e[9];
+      const int dz = plane - 1;
 #pragma unroll
-      for (int plane = 0; plane < 3; ++plane) {
-        unsigned long long key[9], home[9];
-        Slot e[9];
+      for (int q = 0; q < 9; ++q) {
+        const int dy = q / 3 - 1, dx = q % 3 - 1;
+        // Unsigned adds: wrap-around is harmless because only the low 16 bits enter the key.
+        key[q] = pack_key(c.x, (int32_t)((uint32_t)c.y + (uint32_t)dz), (int32_t)((uint32_t)c.z + (uint32_t)dy),
+                          (int32_t)((uint32_t)c.w + (uint32_t)dx));
+        home[q] = home_slot(key[q], slots);
+      }
 #pragma unroll
-        for (int q = 0; q < 9; ++q) {
-          const int dz = plane - 1, dy = q / 3 - 1, dx = q % 3 - 1;
-          // Unsigned adds: wrap-around is harmless because only the low 16 bits enter the key.
-          key[q] = pack_key(c.x, (int32_t)((uint32_t)c.y + (uint32_t)dz), (int32_t)((uint32_t)c.z + (uint32_t)dy),
-                            (int32_t)((uint32_t)c.w + (uint32_t)dx));
-          home[q] = home_slot(key[q], slots);
-        }
+      for (int q = 0; q < 9; ++q) e[q] = tab[home[q]];
 #pragma unroll
-        for (int q = 0; q < 9; ++q) e[q] = tab[home[q]];
-#pragma unroll
-        for (int q = 0; q < 9; ++q) {
-          int32_t v;
-          if (e[q].key == key[q]) v = e[q].val;
-          else if (e[q].key == kEmptyKey) v = -1;
-          else v = probe_rest(tab, slots, key[q], home[q]);
-          const int k = plane * 9 + q;
-          s_out[t * 27 + k] = v;
-          mask |= (v >= 0 ? 1u : 0u) << k;
-        }
+      for (int q = 0; q < 9; ++q) {
+        int32_t r;
+        if (e[q].key == key[q]) r = e[q].val;
+        else if (e[q].key == kEmptyKey) r = -1;
+        else r = probe_rest(tab, slots, key[q], home[q]);
+        const int k = plane * 9 + q;
+        s_out[v * 27 + k] = r;
+        pm |= (r >= 0 ? 1u : 0u) << k;
       }
     }
-    masks[i] = mask;
   }
+  s_pm[plane][v] = pm;
   __syncthreads();
-  const int64_t rows = (n - i0) < kThreads ? (n - i0) : kThreads;
+  const int64_t rows = (n - i0) < kLookupVoxels ? (n - i0) : kLookupVoxels;
   const int total = (int)rows * 27;
   int32_t* dst = nbr + i0 * 27;
-  for (int e = t; e < total; e += kThreads) dst[e] = s_out[e];
-  // Per-tap hit counts: one ballot per tap and wave, 27 LDS adds per wave, 27 global adds per block.
+  for (int e = t; e < total; e += 3 * kLookupVoxels) dst[e] = s_out[e];
+  if (plane == 0 && i < n) masks[i] = s_pm[0][v] | s_pm[1][v] | s_pm[2][v];
+  // Per-tap hit counts: one ballot per tap of the plane and wave, LDS adds, 27 global adds per block.
 #pragma unroll
-  for (int k = 0; k < 27; ++k) {
-    const unsigned long long b = __ballot((mask >> k) & 1u);
+  for (int q = 0; q < 9; ++q) {
+    const int k = plane * 9 + q;
+    const unsigned long long b = __ballot((pm >> k) & 1u);
     if (lane == 0 && b) atomicAdd(&s_cnt[k], (uint32_t)__popcll(b));
   }
   __syncthreads();
@@ -458,15 +451,16 @@ hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, 
   const int nb = map_bounds_blocks(n);
   const int64_t slots = map_hash_slots(n);
   const int64_t budget = map_grid_budget_cells(n);
-  // One voxel per insert thread (each CAS is a full round trip), up to kMaxInsertBlocks blocks.
+  // One voxel per insert thread (each CAS is a full round trip) up to kMaxInsertBlocks blocks,
+  // then up to four per thread with their CASes in flight together.
   const int insert_blocks = clamp_blocks((n + kThreads - 1) / kThreads, kMaxInsertBlocks);
   map_bounds_kernel<<<nb, kThreads, 0, stream>>>(coords, n, parts);
-  map_plan_kernel<<<1, kThreads, 0, stream>>>(parts, nb, budget, slots, mode_request, stats, host_flags);
-  map_insert_kernel<<<insert_blocks, kThreads, 0, stream>>>(coords, n, table, stats, host_flags);
+  map_insert_kernel<<<insert_blocks, kThreads, 0, stream>>>(coords, n, parts, nb, budget, slots, mode_request, table,
+                                                            stats, host_flags);
   hipError_t e = hipEventRecord(inserted, stream);
   if (e != hipSuccess) return e;
-  map_lookup_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, stream>>>(coords, n, table, nbr,
-                                                                                       masks, stats);
+  map_lookup_kernel<<<(unsigned)((n + kLookupVoxels - 1) / kLookupVoxels), 3 * kLookupVoxels, 0, stream>>>(
+      coords, n, table, nbr, masks, stats);
   const int64_t reset_items = n > slots ? n : slots;
   map_reset_kernel<<<clamp_blocks((reset_items + 4 * kThreads - 1) / (4 * kThreads), kMaxWideBlocks), kThreads, 0,
                      stream>>>(coords, n, table, stats, counts);

@@ -256,6 +256,8 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
                        static_cast<MapHostFlags*>(pinned.dev), inserted, stream);
   if (e == hipSuccess) e = hipEventRecord(m->d.ready, stream);
   if (e == hipSuccess) e = hipEventRecord(ws.last, stream);
+  // (Spinning on a host word that the lookup kernel stores as it starts measured slower than
+  // this event wait.)
   if (e == hipSuccess) e = hipEventSynchronize(inserted);
   if (e != hipSuccess) {
     (void)hipStreamSynchronize(stream);
