@@ -194,13 +194,17 @@ def main():
             return sc.subm_conv3d_forward_per_offset(m, x, w, b, out=out)
         return sc.subm_conv3d_forward(m if ks == 3 else None, x, w, b, out=out)
 
+    # One step: the map build, enqueued with no host wait, then every layer behind it on the
+    # same stream; the build's coordinate check (duplicates, ranges) follows the enqueued layers,
+    # so the host never stands between the build and the convolutions.
     def step():
-        m = sc.sparse_indice_map_build(coords)
+        m = sc.sparse_indice_map_build(coords, sync=False)
         x = x0_dev
         for (ks, cin, cout, w, b, _, _), out in zip(layers, outs):
             conv(m, ks, x, w, b, out)
             if chained:
                 x = out
+        m.check()
         m.free()
         return m
 

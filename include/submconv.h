@@ -89,7 +89,9 @@ typedef enum {
  *   out_map  host pointer; receives the new handle.  Set to NULL first, left NULL on error.
  * The map stores nbr[n, 27] (int32, row = ORIGINAL input row of the neighbour, -1 if absent),
  * the total pair count (entries >= 0, centre included) and the per-tap pair counts.
- * The call synchronises `stream` once, to read the duplicate / range flags and the counts.
+ * The call waits on the host until the build's insert kernel has run, to report the duplicate /
+ * range errors; the rest of the build (the lookup) is still running on `stream` when it returns,
+ * and the pair counts are read on first use.
  * Errors: SUBM_ERR_INVALID_ARG, SUBM_ERR_DUPLICATE_COORD, SUBM_ERR_COORD_RANGE,
  *         SUBM_ERR_OUT_OF_MEMORY, SUBM_ERR_HIP.
  * Source: lato.2_mrp_mlx README, header summary (indice map with 27 lookups per voxel,
@@ -105,6 +107,31 @@ int sparse_indice_map_build(const int32_t* coords, int64_t n, hipStream_t stream
  */
 int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int mode, hipStream_t stream,
                                submconv_map_t* out_map);
+
+/*
+ * sparse_indice_map_build_async -- sparse_indice_map_build_ex without any host wait: returns as
+ * soon as the build is enqueued on `stream`, so a caller can enqueue its convolutions behind it
+ * and keep the GPU busy.  Arguments and argument errors as sparse_indice_map_build_ex.
+ * Coordinate errors (SUBM_ERR_DUPLICATE_COORD, SUBM_ERR_COORD_RANGE) are not reported by this
+ * call but by sparse_indice_map_status and by every later call that reads the map on the host
+ * (sparse_indice_map_info with pairs, _offset_counts, _mode, _copy_nbr, the per-offset
+ * convolution, sparse_indice_map_subdivide); the map must still be freed.  Work enqueued on a map
+ * whose status is not known yet is safe: every rulebook entry is -1 or a row of the set (all -1
+ * for out-of-range coordinates), so kernels stay in bounds, but their results mean nothing if the
+ * status turns out to be an error.  Several asynchronous builds may be in flight at once.
+ * Source of the rulebook: as sparse_indice_map_build.
+ */
+int sparse_indice_map_build_async(const int32_t* coords, int64_t n, int mode, hipStream_t stream,
+                                  submconv_map_t* out_map);
+
+/*
+ * sparse_indice_map_status -- the coordinate status of a map's build: SUBM_OK, or the error a
+ * synchronous build would have returned (SUBM_ERR_DUPLICATE_COORD, SUBM_ERR_COORD_RANGE,
+ * SUBM_ERR_HIP).  For a map from sparse_indice_map_build_async the first call waits on the host
+ * for the build's kernels (not for work enqueued after them); later calls, and calls on
+ * synchronously built or derived maps, return at once.  NULL returns SUBM_ERR_INVALID_ARG.
+ */
+int sparse_indice_map_status(submconv_map_t map);
 
 /*
  * sparse_indice_map_mode -- the structure a built map used: SUBM_MAP_HASH or SUBM_MAP_GRID

@@ -29,6 +29,8 @@ TAPS = 27
 C_FUNCTIONS = (
     "sparse_indice_map_build",
     "sparse_indice_map_build_ex",
+    "sparse_indice_map_build_async",
+    "sparse_indice_map_status",
     "sparse_indice_map_mode",
     "sparse_indice_map_free",
     "sparse_indice_map_info",
@@ -83,6 +85,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.sparse_indice_map_build.argtypes = [vp, i64, vp, ctypes.POINTER(vp)]
         lib.sparse_indice_map_build_ex.argtypes = [vp, i64, ci, vp, ctypes.POINTER(vp)]
+        lib.sparse_indice_map_build_async.argtypes = [vp, i64, ci, vp, ctypes.POINTER(vp)]
+        lib.sparse_indice_map_status.argtypes = [vp]
         lib.sparse_indice_map_mode.argtypes = [vp, ctypes.POINTER(ci)]
         lib.sparse_indice_map_free.argtypes = [vp]
         lib.sparse_indice_map_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -190,6 +194,10 @@ class IndiceMap:
             raise ValueError("indice map already freed")
         return self._handle
 
+    def check(self) -> None:
+        """Raise the build's coordinate error, if any (waits for an asynchronous build's insert)."""
+        sparse_indice_map_status(self)
+
     def free(self) -> None:
         """Release the map.  No work using it may still be in flight."""
         if self._handle is not None:
@@ -210,22 +218,43 @@ class IndiceMap:
             pass
 
 
-def sparse_indice_map_build(coords: torch.Tensor, stream=None) -> IndiceMap:
-    """Build the indice map of int32 device coordinates [N, 4] = (b, z, y, x)."""
+def sparse_indice_map_build(coords: torch.Tensor, stream=None, sync: bool = True) -> IndiceMap:
+    """Build the indice map of int32 device coordinates [N, 4] = (b, z, y, x).
+
+    sync=False enqueues the build without any host wait (sparse_indice_map_build_async):
+    coordinate errors are then raised by IndiceMap.check() or by the first call that reads the
+    map on the host."""
+    if not sync:
+        return sparse_indice_map_build_async(coords, SUBM_MAP_AUTO, stream)
     return sparse_indice_map_build_ex(coords, SUBM_MAP_AUTO, stream)
+
+
+def sparse_indice_map_build_async(coords: torch.Tensor, mode: int = SUBM_MAP_AUTO, stream=None) -> IndiceMap:
+    """Enqueue the build with no host wait; see IndiceMap.check for its coordinate status."""
+    return _build(coords, mode, stream, "sparse_indice_map_build_async")
+
+
+def sparse_indice_map_status(m: IndiceMap) -> None:
+    """Raise SubmError with the build's coordinate error, if any."""
+    lib = load_library()
+    _check(lib, "sparse_indice_map_status", lib.sparse_indice_map_status(m.handle))
 
 
 def sparse_indice_map_build_ex(coords: torch.Tensor, mode: int, stream=None) -> IndiceMap:
     """Build the indice map with an explicit structure request (SUBM_MAP_AUTO / _HASH / _GRID)."""
+    return _build(coords, mode, stream, "sparse_indice_map_build_ex")
+
+
+def _build(coords: torch.Tensor, mode: int, stream, func: str) -> IndiceMap:
     _device_tensor(coords, "coords")
     if coords.dtype != torch.int32 or coords.dim() != 2 or coords.shape[1] != 4:
         raise ValueError("coords must be int32 [N, 4]")
     lib = load_library()
     out = ctypes.c_void_p()
     with _on_device(coords.device):
-        st = lib.sparse_indice_map_build_ex(coords.data_ptr(), coords.shape[0], int(mode),
-                                            _stream_ptr(stream, coords.device), ctypes.byref(out))
-    _check(lib, "sparse_indice_map_build_ex", st)
+        st = getattr(lib, func)(coords.data_ptr(), coords.shape[0], int(mode), _stream_ptr(stream, coords.device),
+                                ctypes.byref(out))
+    _check(lib, func, st)
     return IndiceMap(out.value, coords.device, coords.shape[0])
 
 

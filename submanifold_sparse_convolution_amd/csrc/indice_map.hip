@@ -16,30 +16,35 @@
 //         modular reduction is injective on every coordinate and +-1 neighbour as long as each
 //         axis' extent (max - min) is at most 65534, which the build enforces.
 //
-// The structure is chosen on the device from the set's bounds, so the whole build needs one
-// host synchronisation, taken as soon as the insert kernel has finished: by then it has written
-// the plan's range flags and its own error flags straight into pinned host memory, and the lookup
-// and reset kernels go on running while the caller enqueues its convolutions.  No structure is
-// ever cleared in full: the table area is all 0xFF bytes between builds (an empty cell is -1
-// and an empty slot is key ~0, row -1), and every build resets exactly what it wrote.
+// The structure is chosen on the device from the set's bounds, so the whole build needs at most
+// one host synchronisation, taken as soon as the insert kernel has finished: by then it has
+// written the plan's range flags and its own error flags straight into pinned host memory, and
+// the lookup kernel goes on running while the caller enqueues its convolutions (an asynchronous
+// build skips even that wait).  No structure is ever cleared in full: the table area is all
+// 0xFF bytes whenever no build is inserting (an empty cell is -1 and an empty slot is key ~0,
+// row -1); each build records the cells it wrote, and the next build's first kernel puts
+// exactly those back.
 //
 // Kernels, all on the caller's stream:
-//   map_bounds_kernel   per-block min/max of (b, z, y, x) -> partials (at most 256)
+//   map_bounds_kernel   puts back the previous build's cells (GRID: from its cell list) or slots
+//                       (HASH: all of its table), then per-block min/max of (b, z, y, x) ->
+//                       partials (at most 256)
 //   map_insert_kernel   every block first reduces the partials itself and so derives the same
 //                       plan (range checks, structure, strides) with no second launch and no
 //                       signalling between blocks (that needs a device-scope fence, which writes
 //                       back the whole L2 of each XCD); block 0 publishes it (and the range flags
-//                       and mode to the host) and zeroes the counters.  Then GRID: CAS the row
-//                       into its cell, up to four voxels per thread in flight; HASH: CAS the key
-//                       into the table.  A cell or key already taken by another row raises the
-//                       duplicate flag in host memory (a plain store of a constant, so
-//                       concurrent writers agree).
+//                       and mode to the host) and zeroes the map's counters.  Then GRID: CAS the
+//                       row into its cell and record the cell, up to four voxels per thread in
+//                       flight; HASH: CAS the key into the table.  A cell or key already taken by
+//                       another row raises the duplicate flag in host memory (a plain store of a
+//                       constant, so concurrent writers agree).
 //   map_lookup_kernel   three threads per voxel, one per dz plane: 9 loads (GRID) or 9 probe
 //                       sequences (HASH) each, all in flight; the block's rows are staged in LDS
 //                       and written as one contiguous run of nbr; per-row 27-bit hit mask; hits
-//                       counted per tap with wave ballots and added to one of 16 counter banks
-//   map_reset_kernel    GRID: -1 back into every voxel's cell; HASH: the used slots emptied;
-//                       block 0 sums the per-tap counter banks into the map's own counts
+//                       counted per tap with wave ballots and added to one of 16 counter banks of
+//                       the map, summed on the host when first needed
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 
 namespace submconv {
@@ -97,10 +102,26 @@ __device__ __forceinline__ int wave_max(int v) {
 
 // ------------------------------------------------------------------ bounds
 __global__ __launch_bounds__(kThreads) void map_bounds_kernel(const int32_t* __restrict__ coords, int64_t n,
-                                                              BoundsPartial* __restrict__ partials) {
+                                                              int nparts, BoundsPartial* __restrict__ partials,
+                                                              const MapStats* __restrict__ prev,
+                                                              const int32_t* __restrict__ cells,
+                                                              void* __restrict__ table) {
+  // The previous build's entries back to empty (its lookup has finished: stream order).
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (prev->mode == kModeGrid) {
+    int32_t* grid = static_cast<int32_t*>(table);
+    for (int64_t i = t0; i < prev->inserted; i += stride) grid[cells[i]] = -1;
+  } else if (prev->mode == kModeHash) {
+    int4* tab = static_cast<int4*>(table);
+    const int4 ff = make_int4(-1, -1, -1, -1);
+    for (int64_t i = t0; i < prev->slots; i += stride) tab[i] = ff;
+  }
+  // Bounds: the first nparts blocks (the grid may be wider for a large previous build).
+  if ((int)blockIdx.x >= nparts) return;
   int mn[4] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX};
   int mx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)nparts * kThreads) {
     const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
     mn[0] = min(mn[0], c.x); mx[0] = max(mx[0], c.x);
     mn[1] = min(mn[1], c.y); mx[1] = max(mx[1], c.y);
@@ -221,13 +242,15 @@ __global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __r
                                                               const BoundsPartial* __restrict__ partials, int nparts,
                                                               int64_t grid_budget_cells, int64_t slots,
                                                               int mode_request, void* __restrict__ table,
+                                                              int32_t* __restrict__ cells,
+                                                              uint32_t* __restrict__ banks,
                                                               MapStats* __restrict__ st,
                                                               MapHostFlags* __restrict__ host) {
   Plan plan;
   int32_t mx[4];
   reduce_plan(partials, nparts, grid_budget_cells, mode_request, plan, mx);
   const int t = threadIdx.x;
-  if (blockIdx.x == 0) {  // publish the plan for the lookup and reset kernels and the host
+  if (blockIdx.x == 0) {  // publish the plan for the lookup kernel, the next build and the host
     if (t == 0) {
       // (constant indices: indexing the plan's arrays by thread would move them into LDS)
 #pragma unroll
@@ -245,8 +268,9 @@ __global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __r
       st->sy = plan.sy;
       st->sz = plan.sz;
       st->sb = plan.sb;
+      st->inserted = n;
     }
-    for (int k = t; k < kTapBanks * 27; k += kThreads) (&st->tap_counts[0][0])[k] = 0;
+    for (int k = t; k < kTapBanks * 27; k += kThreads) banks[k] = 0;
   }
   if (plan.mode == kModeNone) return;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -269,7 +293,10 @@ __global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __r
 #pragma unroll
       for (int u = 0; u < 4; ++u) prev[u] = cell[u] >= 0 ? atomicCAS(&grid[cell[u]], -1, (int32_t)(i0 + u * stride)) : -1;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) dup |= prev[u] != -1;
+      for (int u = 0; u < 4; ++u) {
+        dup |= prev[u] != -1;
+        if (cell[u] >= 0) cells[i0 + u * stride] = (int32_t)cell[u];  // grid cells < 2^29
+      }
     }
   } else {
     Slot* tab = static_cast<Slot*>(table);
@@ -319,12 +346,14 @@ __global__ __launch_bounds__(3 * kLookupVoxels) void map_lookup_kernel(const int
                                                                       const void* __restrict__ table,
                                                                       int32_t* __restrict__ nbr,
                                                                       uint32_t* __restrict__ masks,
-                                                                      MapStats* __restrict__ st) {
+                                                                      uint32_t* __restrict__ banks,
+                                                                      const MapStats* __restrict__ st) {
   __shared__ int32_t s_out[kLookupVoxels * 27];
   __shared__ uint32_t s_pm[3][kLookupVoxels];
   __shared__ uint32_t s_cnt[27];
+  // Out-of-range coordinates (no structure built): every entry -1, so that work already enqueued
+  // on the map by a caller who has not checked its status yet reads only valid entries.
   const int mode = st->mode;
-  if (mode == kModeNone) return;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int plane = t / kLookupVoxels;
@@ -333,7 +362,10 @@ __global__ __launch_bounds__(3 * kLookupVoxels) void map_lookup_kernel(const int
   const int64_t i0 = (int64_t)blockIdx.x * kLookupVoxels;
   const int64_t i = i0 + v;
   uint32_t pm = 0;  // hit bits of this plane's taps, at their tap positions
-  if (i < n) {
+  if (i < n && mode == kModeNone) {
+#pragma unroll
+    for (int q = 0; q < 9; ++q) s_out[v * 27 + plane * 9 + q] = -1;
+  } else if (i < n) {
     const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
     if (mode == kModeGrid) {
       const int32_t* grid = static_cast<const int32_t*>(table);
@@ -391,35 +423,7 @@ __global__ __launch_bounds__(3 * kLookupVoxels) void map_lookup_kernel(const int
     if (lane == 0 && b) atomicAdd(&s_cnt[k], (uint32_t)__popcll(b));
   }
   __syncthreads();
-  if (t < 27 && s_cnt[t] != 0) atomicAdd(&st->tap_counts[blockIdx.x % kTapBanks][t], s_cnt[t]);
-}
-
-// ------------------------------------------------------------------ reset
-// Restores the all-0xFF table area: -1 into every voxel's cell (GRID) or every used slot
-// emptied (HASH, where the probe sequences rule out emptying slots one key at a time).  Block 0
-// also sums the counter banks, final once the lookup has completed, into the map's counts.
-__global__ __launch_bounds__(kThreads) void map_reset_kernel(const int32_t* __restrict__ coords, int64_t n,
-                                                             void* __restrict__ table,
-                                                             const MapStats* __restrict__ st,
-                                                             uint32_t* __restrict__ counts) {
-  if (blockIdx.x == 0 && threadIdx.x < 27) {
-    uint32_t c = 0;
-    for (int b = 0; b < kTapBanks; ++b) c += st->tap_counts[b][threadIdx.x];
-    counts[threadIdx.x] = c;
-  }
-  const int mode = st->mode;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  if (mode == kModeGrid) {
-    int32_t* grid = static_cast<int32_t*>(table);
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
-      const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
-      grid[grid_cell(*st, c.x, c.y, c.z, c.w)] = -1;
-    }
-  } else if (mode == kModeHash) {
-    int4* tab = static_cast<int4*>(table);
-    const int4 ff = make_int4(-1, -1, -1, -1);
-    for (int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x; s < st->slots; s += stride) tab[s] = ff;
-  }
+  if (t < 27 && s_cnt[t] != 0) atomicAdd(&banks[(blockIdx.x % kTapBanks) * 27 + t], s_cnt[t]);
 }
 
 __global__ __launch_bounds__(kThreads) void fill_kernel(int4* __restrict__ p, int64_t n16, int value) {
@@ -445,25 +449,29 @@ size_t map_table_bytes(int64_t n) {
 size_t map_partials_bytes(int64_t n) { return (size_t)map_bounds_blocks(n) * sizeof(BoundsPartial); }
 
 hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, void* table, void* partials,
-                            int32_t* nbr, uint32_t* masks, uint32_t* counts, MapStats* stats,
-                            MapHostFlags* host_flags, hipEvent_t inserted, hipStream_t stream) {
+                            int32_t* cells, int64_t prev_n, int32_t* nbr, uint32_t* masks, uint32_t* banks,
+                            MapStats* stats, MapHostFlags* host_flags, hipEvent_t inserted, hipEvent_t ready,
+                            hipStream_t stream) {
   BoundsPartial* parts = static_cast<BoundsPartial*>(partials);
   const int nb = map_bounds_blocks(n);
+  // Wide enough for the previous build's reset too (at most its hash slots, 2 per row).
+  const int clear_blocks = clamp_blocks((map_hash_slots(prev_n) + 4 * kThreads - 1) / (4 * kThreads), kMaxWideBlocks);
   const int64_t slots = map_hash_slots(n);
   const int64_t budget = map_grid_budget_cells(n);
   // One voxel per insert thread (each CAS is a full round trip) up to kMaxInsertBlocks blocks,
   // then up to four per thread with their CASes in flight together.
   const int insert_blocks = clamp_blocks((n + kThreads - 1) / kThreads, kMaxInsertBlocks);
-  map_bounds_kernel<<<nb, kThreads, 0, stream>>>(coords, n, parts);
-  map_insert_kernel<<<insert_blocks, kThreads, 0, stream>>>(coords, n, parts, nb, budget, slots, mode_request, table,
-                                                            stats, host_flags);
-  hipError_t e = hipEventRecord(inserted, stream);
-  if (e != hipSuccess) return e;
-  map_lookup_kernel<<<(unsigned)((n + kLookupVoxels - 1) / kLookupVoxels), 3 * kLookupVoxels, 0, stream>>>(
-      coords, n, table, nbr, masks, stats);
-  const int64_t reset_items = n > slots ? n : slots;
-  map_reset_kernel<<<clamp_blocks((reset_items + 4 * kThreads - 1) / (4 * kThreads), kMaxWideBlocks), kThreads, 0,
-                     stream>>>(coords, n, table, stats, counts);
+  map_bounds_kernel<<<prev_n > 0 && clear_blocks > nb ? clear_blocks : nb, kThreads, 0, stream>>>(coords, n, nb, parts,
+                                                                                                stats, cells, table);
+  // The events ride on the kernels' own completion (no marker packet between kernels).
+  const BoundsPartial* cparts = parts;
+  hipExtLaunchKernelGGL(map_insert_kernel, dim3(insert_blocks), dim3(kThreads), 0, stream, nullptr, inserted, 0u,
+                        coords, n, cparts, nb, budget, slots, mode_request, table, cells, banks, stats, host_flags);
+  const MapStats* cstats = stats;
+  const void* ctable = table;
+  hipExtLaunchKernelGGL(map_lookup_kernel, dim3((unsigned)((n + kLookupVoxels - 1) / kLookupVoxels)),
+                        dim3(3 * kLookupVoxels), 0, stream, nullptr, ready, 0u, coords, n, ctable, nbr, masks, banks,
+                        cstats);
   return hipGetLastError();
 }
 

@@ -92,7 +92,18 @@ struct MapStats {
   int64_t cells;       // GRID: number of cells
   int64_t slots;       // HASH: number of slots
   int64_t sy, sz, sb;  // GRID strides of y, z and the batch slab (x stride is 1)
-  uint32_t tap_counts[kTapBanks][27];
+  int64_t inserted;     // rows the insert kernel wrote (GRID: their cells are in the cell list)
+};
+
+// Where a build's flags arrive: a 16-byte slot of pinned host memory that the kernels write
+// through its device address, and an event recorded after the insert kernel.  Slots come from a
+// per-device pool (submconv_api.hip) and go back once the map has been checked or freed, so
+// several asynchronous builds can be in flight at once.
+struct FlagSlot {
+  MapHostFlags* host = nullptr;
+  MapHostFlags* dev = nullptr;
+  hipEvent_t inserted = nullptr;  // recorded after the insert kernel
+  hipEvent_t ready = nullptr;     // recorded after the build's last kernel
 };
 
 // Map handle contents.
@@ -101,14 +112,23 @@ struct MapData {
   int mode = kModeHash;
   int64_t n = 0;
   // Pair counts: valid once counts_ready (the build's lookup may still run when it returns; the
-  // counts arrive in dev_counts and are read on first use, see map_counts()).
+  // counts arrive in dev_banks and are read on first use, see map_counts()).
   bool counts_ready = false;
   int64_t pairs = 0;
   int64_t per_tap[27] = {};
   int32_t* nbr = nullptr;     // device [n, 27], input row order
   uint32_t* masks = nullptr;  // device [n]: bit k set when nbr[i, k] >= 0 (same allocation as nbr)
-  uint32_t* dev_counts = nullptr;  // device [27] per-tap pair counts (same allocation as nbr)
-  hipEvent_t ready = nullptr;      // recorded after the build's last kernel
+  uint32_t* dev_banks = nullptr;   // device [kTapBanks][27] per-tap pair counts, summed on the host
+                                   // (same allocation as nbr)
+  hipEvent_t ready = nullptr;      // recorded after the build's last kernel (the slot's event for
+                                   // a built map, the map's own for a derived one)
+  // Coordinate check of the build (range, duplicates): `checked` once its flags have been read
+  // (a synchronous build reads them before it returns, an asynchronous one on first use, see
+  // map_check()); `check` is the result; `slot` is held until the map is freed.
+  bool checked = true;
+  Status check;
+  FlagSlot slot;
+  hipEvent_t check_event = nullptr;  // slot.inserted (synchronous build) or ready (asynchronous)
   // Per-tap pair lists of the per-offset convolution, built on first use: the pairs of tap k
   // (k != 13) are pair_out / pair_in [pair_off[k] .. pair_off[k] + per_tap[k]), output row
   // ascending.  One allocation, pair_out first.
@@ -118,19 +138,23 @@ struct MapData {
 };
 
 // Map build (indice_map.hip).  Enqueues on `stream`; does not synchronise.  `table` holds
-// map_table_bytes(n) and must be all 0xFF bytes on entry (it is again on completion: the build
-// resets what it wrote); `partials` holds map_partials_bytes(n), `stats` one MapStats (device).
-// `host_flags` (device address of pinned host memory, zeroed by the caller) holds the plan's
-// flags and mode and the insert's error flags once `inserted` (recorded after the insert
-// kernel) has completed; the per-tap counts reach `counts` (device [27]) with the last kernel.
+// map_table_bytes(n) and `cells` n int32; `stats` (one MapStats, device) still describes the
+// previous build on this workspace (all zero for none; `prev_n` is its row count, 0 for none), whose cells (GRID) or slots (HASH) the
+// first kernel puts back to all 0xFF bytes before this build inserts, so the table area is all
+// 0xFF on entry to the insert.  `partials` holds map_partials_bytes(n).  `host_flags` (device
+// address of pinned host memory, zeroed by the caller) holds the plan's flags and mode and the
+// insert's error flags once `inserted` (the insert kernel's completion, unless null) has
+// completed; the per-tap counts reach `banks` (device [kTapBanks][27], to be summed) once `ready`
+// (the last kernel's completion) has.  Both events must allow timing.
 int64_t map_hash_slots(int64_t n);
 int64_t map_grid_budget_cells(int64_t n);
 int map_bounds_blocks(int64_t n);
 size_t map_table_bytes(int64_t n);
 size_t map_partials_bytes(int64_t n);
 hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, void* table, void* partials,
-                            int32_t* nbr, uint32_t* masks, uint32_t* counts, MapStats* stats,
-                            MapHostFlags* host_flags, hipEvent_t inserted, hipStream_t stream);
+                            int32_t* cells, int64_t prev_n, int32_t* nbr, uint32_t* masks, uint32_t* banks,
+                            MapStats* stats, MapHostFlags* host_flags, hipEvent_t inserted, hipEvent_t ready,
+                            hipStream_t stream);
 // Fill `bytes` bytes at `p` (16-byte aligned, bytes a multiple of 16) with `value` (each 32-bit
 // word).
 hipError_t launch_fill(void* p, size_t bytes, uint32_t value, hipStream_t stream);
@@ -187,7 +211,11 @@ struct submconv_map {
 };
 
 namespace submconv {
-// Makes map->d.pairs / per_tap valid (waits for the build's last kernel on first use).
+// Waits for an asynchronous build's insert kernel on first use and returns the build's coordinate
+// status (SUBM_OK at once for a checked map).
+Status map_check(submconv_map* map);
+// Makes map->d.pairs / per_tap valid (waits for the build's last kernel on first use); fails with
+// the build's coordinate status.
 Status map_counts(submconv_map* map);
 // Host-side checks of a convolution call (subm_conv3d_forward's rules).
 Status check_conv(submconv_map_t map, int64_t n, int ksize, int cin, int cout, int dtype, const void* feats,

@@ -5,6 +5,7 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -113,64 +114,130 @@ extern "C" const char* subm_last_error(void) { return g_last_error.c_str(); }
 
 namespace {
 
-// Build workspace (hash table or dense grid, bounds partials, statistics): one grow-only device
-// buffer per GPU, held under a mutex for the whole build.  A build ends with a stream
-// synchronisation, so the buffer is idle when the next build takes it; builds on one GPU from
-// several threads are serialised by the mutex.
+// Build workspace (statistics, bounds partials, the cell list, the hash table or dense grid):
+// one grow-only device buffer per GPU, held under a mutex while a build is enqueued; builds on
+// one GPU from several threads are serialised by the mutex.
 struct Workspace {
   std::mutex mu;
   void* ptr = nullptr;
   size_t bytes = 0;
-  // Recorded after the last kernel of the latest build: a build returns once its insert kernel
-  // is done, so the next build's kernels wait for this event (on the device) before they touch
-  // the shared structure.
+  int64_t cells_cap = 0;   // rows the cell list holds
+  size_t table_cap = 0;    // bytes of the table area
+  int64_t prev_n = 0;      // rows of the latest build on it (0: nothing to put back)
+  // The latest build's `ready` event (a pooled event, never destroyed): a build returns before
+  // its last kernel has run, so the next build's kernels wait for it (on the device) before
+  // they touch the shared structure.
   hipEvent_t last = nullptr;
 };
 Workspace g_workspace[kMaxDevices];
 
-// Per-thread, per-device event recorded after the insert kernel; the build waits for it.
-hipEvent_t inserted_event(int dev) {
-  thread_local hipEvent_t ev[kMaxDevices] = {};
-  if (ev[dev] == nullptr && hipEventCreateWithFlags(&ev[dev], hipEventDisableTiming) != hipSuccess) ev[dev] = nullptr;
-  return ev[dev];
+// Pool of flag slots per device: pinned pages of 16-byte slots, each with its event, created on
+// demand with the device current and kept until the process ends.
+struct SlotPool {
+  std::mutex mu;
+  std::vector<FlagSlot> free;
+};
+SlotPool g_slots[kMaxDevices];
+constexpr size_t kSlotPage = 4096;
+
+Status take_flag_slot(int dev, FlagSlot* out) {
+  SlotPool& pool = g_slots[dev];
+  std::lock_guard<std::mutex> lock(pool.mu);
+  if (pool.free.empty()) {
+    void* host = nullptr;
+    void* devp = nullptr;
+    SUBM_HIP_TRY(hipHostMalloc(&host, kSlotPage, hipHostMallocDefault));
+    if (hipHostGetDevicePointer(&devp, host, 0) != hipSuccess) {
+      (void)hipHostFree(host);
+      return make_status(SUBM_ERR_HIP, "hipHostGetDevicePointer of the build flags");
+    }
+    for (size_t i = 0; i < kSlotPage / sizeof(MapHostFlags); ++i) {
+      FlagSlot slot;
+      slot.host = static_cast<MapHostFlags*>(host) + i;
+      slot.dev = static_cast<MapHostFlags*>(devp) + i;
+      pool.free.push_back(slot);
+    }
+  }
+  FlagSlot& top = pool.free.back();
+  // (kernel-completion events of hipExtLaunchKernel: created with timing)
+  if (top.inserted == nullptr) SUBM_HIP_TRY(hipEventCreate(&top.inserted));
+  if (top.ready == nullptr) SUBM_HIP_TRY(hipEventCreate(&top.ready));
+  *out = top;
+  pool.free.pop_back();
+  return Status{};
 }
 
-// Layout: [statistics | bounds partials | table area].  The table area is all 0xFF bytes
-// whenever no build is running (each build resets what it wrote), so a new allocation is filled.
+void give_flag_slot(int dev, FlagSlot& slot) {
+  if (slot.host == nullptr) return;
+  SlotPool& pool = g_slots[dev];
+  std::lock_guard<std::mutex> lock(pool.mu);
+  pool.free.push_back(slot);
+  slot = FlagSlot{};
+}
+
+// The build's coordinate status from its flags (valid once the insert kernel has completed).
+Status read_flags(MapData& d) {
+  const volatile MapHostFlags* host = d.slot.host;
+  const uint32_t flags = host->flags;
+  if (flags & kFlagBatchRange) return make_status(SUBM_ERR_COORD_RANGE, "batch index outside [0, 65534]");
+  if (flags & kFlagExtentRange)
+    return make_status(SUBM_ERR_COORD_RANGE, "extent (max - min) of z, y or x exceeds 65534");
+  if (host->duplicate) return make_status(SUBM_ERR_DUPLICATE_COORD, "two rows share the same (b, z, y, x)");
+  if (host->overflow) return make_status(SUBM_ERR_HIP, "internal error: hash table full");
+  d.mode = host->mode;
+  return Status{};
+}
+
+// Waits for the insert kernel and reads the flags (caller holds the map's mutex or owns the map
+// alone).
+Status check_locked(MapData& d) {
+  if (d.checked) return d.check;
+  DeviceGuard guard(d.device);
+  const hipError_t e = hipEventSynchronize(d.check_event);
+  d.check = e != hipSuccess ? hip_status(e, "indice map build") : read_flags(d);
+  d.checked = true;
+  return d.check;
+}
+
+// Layout: [statistics | bounds partials | cell list | table area].  The table area is all 0xFF
+// bytes whenever no build is inserting (each build's first kernel puts back what the previous
+// one wrote), so a new allocation is filled, and its zeroed statistics say "nothing to put back".
 constexpr size_t kStatsBytes = 4096;
 constexpr size_t kPartialsBytes = 65536;
 static_assert(sizeof(MapStats) <= kStatsBytes, "statistics block");
 
-Status workspace_reserve(Workspace& ws, size_t table_bytes, hipStream_t stream) {
-  const size_t bytes = kStatsBytes + kPartialsBytes + table_bytes;
-  if (ws.bytes >= bytes) return Status{};
+size_t cells_bytes(int64_t cap) { return round_up((size_t)cap * sizeof(int32_t), 256); }
+
+Status workspace_reserve(Workspace& ws, int64_t n, size_t table_bytes, hipStream_t stream) {
+  if (ws.cells_cap >= n && ws.table_cap >= table_bytes) return Status{};
   if (ws.ptr != nullptr) {
-    SUBM_HIP_TRY(hipFree(ws.ptr));
+    SUBM_HIP_TRY(hipFree(ws.ptr));  // waits for the device, so no build still uses it
     ws.ptr = nullptr;
     ws.bytes = 0;
   }
+  const int64_t cap = n > ws.cells_cap ? n : ws.cells_cap;
+  const size_t head = kStatsBytes + kPartialsBytes + cells_bytes(cap);
+  const size_t table = table_bytes > ws.table_cap ? table_bytes : ws.table_cap;
   const size_t grain = size_t(64) << 20;
-  const size_t want = (bytes + grain - 1) / grain * grain;
+  const size_t want = (head + table + grain - 1) / grain * grain;
   SUBM_HIP_TRY(hipMalloc(&ws.ptr, want));
   ws.bytes = want;
-  // Statistics and partials start zeroed (the plan's completion counter lives there); the table
-  // area starts empty.
-  SUBM_HIP_TRY(launch_fill(ws.ptr, kStatsBytes + kPartialsBytes, 0u, stream));
-  SUBM_HIP_TRY(launch_fill(static_cast<unsigned char*>(ws.ptr) + kStatsBytes + kPartialsBytes,
-                           want - kStatsBytes - kPartialsBytes, 0xFFFFFFFFu, stream));
+  ws.cells_cap = cap;
+  ws.table_cap = want - head;
+  ws.prev_n = 0;
+  SUBM_HIP_TRY(launch_fill(ws.ptr, head, 0u, stream));
+  SUBM_HIP_TRY(launch_fill(static_cast<unsigned char*>(ws.ptr) + head, want - head, 0xFFFFFFFFu, stream));
   return Status{};
 }
 
-// The plan's flags and mode and the insert's error flags arrive in the calling thread's pinned
-// block for the device (a thread runs one build at a time): the kernels write them through its
-// device address, so the build needs no copy command.
-static_assert(sizeof(MapHostFlags) <= kPinnedBytes, "host flags fit the pinned block");
+static_assert(sizeof(MapHostFlags) == 16 && kSlotPage % sizeof(MapHostFlags) == 0, "flag slots tile a page");
 
 void release_map(submconv_map* m, hipStream_t stream) {
   if (m->d.ready != nullptr) {
     (void)hipEventSynchronize(m->d.ready);  // the build's own kernels write the map memory
-    (void)hipEventDestroy(m->d.ready);
+    if (m->d.slot.host == nullptr) (void)hipEventDestroy(m->d.ready);  // a derived map's own event
   }
+  give_flag_slot(m->d.device, m->d.slot);
   device_free(m->d.nbr, stream);
   device_free(m->d.pair_out, stream);
   delete m;
@@ -178,8 +245,11 @@ void release_map(submconv_map* m, hipStream_t stream) {
 
 }  // namespace
 
-extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int mode, hipStream_t stream,
-                                          submconv_map_t* out_map) {
+namespace {
+
+// Shared by the synchronous and asynchronous builds; `wait` selects whether the coordinate
+// check happens before returning.
+int build_map(const int32_t* coords, int64_t n, int mode, hipStream_t stream, submconv_map_t* out_map, bool wait) {
   clear_error();
   if (out_map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "out_map is NULL");
   *out_map = nullptr;
@@ -206,87 +276,93 @@ extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int 
     delete m;
     return fail(SUBM_ERR_HIP, "device ordinal out of range");
   }
-  const Pinned pinned = pinned_block(m->d.device);
-  const hipEvent_t inserted = inserted_event(m->d.device);
-  if (pinned.host == nullptr || inserted == nullptr) {
-    delete m;
-    return fail(SUBM_ERR_OUT_OF_MEMORY, "pinned host flags or build event");
-  }
-  volatile MapHostFlags* host = static_cast<volatile MapHostFlags*>(pinned.host);
-
   const size_t table_bytes = round_up(map_table_bytes(n), 256);
   if (map_partials_bytes(n) > kPartialsBytes) {
     delete m;
     return fail(SUBM_ERR_HIP, "internal error: bounds partials exceed their workspace block");
   }
+  Status s = take_flag_slot(m->d.device, &m->d.slot);
+  if (!s.ok()) {
+    delete m;
+    return fail(s);
+  }
+  m->d.checked = false;
+  volatile MapHostFlags* host = m->d.slot.host;
 
   Workspace& ws = g_workspace[m->d.device];
   std::lock_guard<std::mutex> lock(ws.mu);
-  hipError_t e = ws.last == nullptr ? hipEventCreateWithFlags(&ws.last, hipEventDisableTiming)
-                                    : hipStreamWaitEvent(stream, ws.last, 0);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->d.ready, hipEventDisableTiming);
+  // (an event already complete needs no wait packet on the stream)
+  hipError_t e = ws.last == nullptr || hipEventQuery(ws.last) == hipSuccess ? hipSuccess
+                                                                            : hipStreamWaitEvent(stream, ws.last, 0);
   if (e != hipSuccess) {
-    if (m->d.ready != nullptr) (void)hipEventDestroy(m->d.ready);
-    delete m;
+    release_map(m, stream);
     return fail(hip_status(e, "build events"));
   }
   void* nbr = nullptr;
-  Status s = workspace_reserve(ws, table_bytes, stream);
-  // nbr [n, 27], masks [n], counts [27]
-  if (s.ok()) s = device_alloc(&nbr, (size_t)n * 28 * sizeof(int32_t) + 128, stream);
+  s = workspace_reserve(ws, n, table_bytes, stream);
+  // nbr [n, 27], masks [n], counter banks [kTapBanks, 27]
+  if (s.ok()) s = device_alloc(&nbr, (size_t)n * 28 * sizeof(int32_t) + kTapBanks * 27 * sizeof(uint32_t), stream);
   if (!s.ok()) {
     device_free(nbr, stream);
-    (void)hipEventDestroy(m->d.ready);
-    delete m;
+    release_map(m, stream);
     return fail(s);
   }
   unsigned char* base = static_cast<unsigned char*>(ws.ptr);
   MapStats* dstats = reinterpret_cast<MapStats*>(base);
   void* partials = base + kStatsBytes;
-  void* table = base + kStatsBytes + kPartialsBytes;
+  int32_t* cells = reinterpret_cast<int32_t*>(base + kStatsBytes + kPartialsBytes);
+  void* table = base + kStatsBytes + kPartialsBytes + cells_bytes(ws.cells_cap);
 
   m->d.nbr = static_cast<int32_t*>(nbr);
   m->d.masks = reinterpret_cast<uint32_t*>(m->d.nbr + (size_t)n * 27);
-  m->d.dev_counts = m->d.masks + n;
+  m->d.dev_banks = m->d.masks + n;
   host->flags = 0;
   host->mode = kModeNone;
   host->duplicate = 0;
   host->overflow = 0;
-  e = launch_map_build(coords, n, mode, table, partials, m->d.nbr, m->d.masks, m->d.dev_counts, dstats,
-                       static_cast<MapHostFlags*>(pinned.dev), inserted, stream);
-  if (e == hipSuccess) e = hipEventRecord(m->d.ready, stream);
-  if (e == hipSuccess) e = hipEventRecord(ws.last, stream);
-  // (Spinning on a host word that the lookup kernel stores as it starts measured slower than
-  // this event wait.)
-  if (e == hipSuccess) e = hipEventSynchronize(inserted);
+  // An asynchronous build tracks no event on its insert kernel; its check waits for the last
+  // kernel instead.
+  m->d.ready = m->d.slot.ready;
+  m->d.check_event = wait ? m->d.slot.inserted : m->d.ready;
+  e = launch_map_build(coords, n, mode, table, partials, cells, ws.prev_n, m->d.nbr, m->d.masks, m->d.dev_banks,
+                       dstats, m->d.slot.dev, wait ? m->d.slot.inserted : nullptr, m->d.ready, stream);
+  ws.prev_n = n;  // from here on the table holds this build's entries (or the launch failed)
+  if (e == hipSuccess) ws.last = m->d.ready;
   if (e != hipSuccess) {
     (void)hipStreamSynchronize(stream);
     release_map(m, stream);
     return fail(hip_status(e, "indice map build"));
   }
-  const uint32_t flags = host->flags;
-  int code = SUBM_OK;
-  const char* msg = "";
-  if (flags & kFlagBatchRange) {
-    code = SUBM_ERR_COORD_RANGE;
-    msg = "batch index outside [0, 65534]";
-  } else if (flags & kFlagExtentRange) {
-    code = SUBM_ERR_COORD_RANGE;
-    msg = "extent (max - min) of z, y or x exceeds 65534";
-  } else if (host->duplicate) {
-    code = SUBM_ERR_DUPLICATE_COORD;
-    msg = "two rows share the same (b, z, y, x)";
-  } else if (host->overflow) {
-    code = SUBM_ERR_HIP;
-    msg = "internal error: hash table full";
+  if (wait) {
+    // (Spinning on a host word that the lookup kernel stores as it starts measured slower than
+    // this event wait.)
+    s = check_locked(m->d);
+    if (!s.ok()) {
+      release_map(m, stream);
+      return fail(s);
+    }
   }
-  if (code != SUBM_OK) {
-    release_map(m, stream);
-    return fail(code, msg);
-  }
-  m->d.mode = host->mode;
   *out_map = m;
   return SUBM_OK;
+}
+
+}  // namespace
+
+extern "C" int sparse_indice_map_build_ex(const int32_t* coords, int64_t n, int mode, hipStream_t stream,
+                                          submconv_map_t* out_map) {
+  return build_map(coords, n, mode, stream, out_map, true);
+}
+
+extern "C" int sparse_indice_map_build_async(const int32_t* coords, int64_t n, int mode, hipStream_t stream,
+                                             submconv_map_t* out_map) {
+  return build_map(coords, n, mode, stream, out_map, false);
+}
+
+extern "C" int sparse_indice_map_status(submconv_map_t map) {
+  clear_error();
+  if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
+  const Status s = map_check(map);
+  return s.ok() ? SUBM_OK : fail(s);
 }
 
 extern "C" int sparse_indice_map_build(const int32_t* coords, int64_t n, hipStream_t stream,
@@ -298,23 +374,34 @@ extern "C" int sparse_indice_map_mode(submconv_map_t map, int* mode) {
   clear_error();
   if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
   if (mode == nullptr) return fail(SUBM_ERR_INVALID_ARG, "mode is NULL");
+  const Status s = map_check(map);
+  if (!s.ok()) return fail(s);
   *mode = map->d.mode == kModeGrid ? SUBM_MAP_GRID : map->d.mode == kModeSubdivided ? SUBM_MAP_SUBDIVIDED : SUBM_MAP_HASH;
   return SUBM_OK;
 }
 
+Status submconv::map_check(submconv_map* map) {
+  std::lock_guard<std::mutex> lock(map->mu);
+  return check_locked(map->d);
+}
+
 Status submconv::map_counts(submconv_map* map) {
   std::lock_guard<std::mutex> lock(map->mu);
+  const Status cs = check_locked(map->d);
+  if (!cs.ok()) return cs;
   if (map->d.counts_ready) return Status{};
-  uint32_t c[27] = {};
+  uint32_t banks[kTapBanks][27] = {};
   if (map->d.n > 0) {
     DeviceGuard guard(map->d.device);
     if (map->d.ready != nullptr) SUBM_HIP_TRY(hipEventSynchronize(map->d.ready));
-    SUBM_HIP_TRY(hipMemcpy(c, map->d.dev_counts, sizeof(c), hipMemcpyDeviceToHost));
+    SUBM_HIP_TRY(hipMemcpy(banks, map->d.dev_banks, sizeof(banks), hipMemcpyDeviceToHost));
   }
   int64_t total = 0;
   for (int k = 0; k < 27; ++k) {
-    map->d.per_tap[k] = c[k];
-    total += c[k];
+    int64_t c = 0;
+    for (int b = 0; b < kTapBanks; ++b) c += banks[b][k];
+    map->d.per_tap[k] = c;
+    total += c;
   }
   map->d.pairs = total;
   map->d.counts_ready = true;
@@ -356,6 +443,8 @@ extern "C" int sparse_indice_map_copy_nbr(submconv_map_t map, int32_t* nbr, hipS
   if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
   if (map->d.n == 0) return SUBM_OK;
   if (nbr == nullptr) return fail(SUBM_ERR_INVALID_ARG, "nbr is NULL");
+  const Status s = map_check(map);
+  if (!s.ok()) return fail(s);
   hipError_t e = hipMemcpyAsync(nbr, map->d.nbr, (size_t)map->d.n * 27 * sizeof(int32_t), hipMemcpyDeviceToDevice, stream);
   if (e != hipSuccess) return fail(hip_status(e, "copy of nbr"));
   return SUBM_OK;

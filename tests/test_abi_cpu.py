@@ -62,6 +62,18 @@ def test_build_rejects_bad_arguments(lib):
     assert b"mode" in lib.subm_last_error()
 
 
+def test_async_build_rejects_bad_arguments_like_the_synchronous_one(lib):
+    out = ctypes.c_void_p(12345)
+    f = lib.sparse_indice_map_build_async
+    assert f(None, 4, 0, None, None) == INVALID
+    assert f(None, -1, 0, None, ctypes.byref(out)) == INVALID
+    assert out.value is None
+    assert f(None, 5, 0, None, ctypes.byref(out)) == INVALID
+    assert f(ctypes.c_void_p(24), 5, 0, None, ctypes.byref(out)) == INVALID
+    assert f(ctypes.c_void_p(256), 5, 7, None, ctypes.byref(out)) == INVALID
+    assert lib.sparse_indice_map_status(None) == INVALID
+
+
 def test_map_accessors_reject_null(lib):
     assert lib.sparse_indice_map_free(None) == OK
     n = ctypes.c_int64()

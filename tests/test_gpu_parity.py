@@ -434,3 +434,70 @@ def test_persistent_walk_full_size(monkeypatch, key):
     rows = sample_rows(len(coords), count=1024, seed=5)
     ref = oracle.conv3_rulebook(oracle_nbr(key), as64(f), as64(w), as64(b), rows=rows)
     check(y1.cpu()[rows], ref, synth.config(key).dtype, f"persistent {key}")
+
+
+# ----------------------------------------------------------------- asynchronous build
+
+@pytest.mark.parametrize("key", ["2a", "3a"])
+def test_async_build_matches_the_synchronous_build(key):
+    coords = torch.from_numpy(coords_of(key)).to(DEV)
+    f, w, b = cfg_tensors(key, 0)
+    fd, wd, bd = f.to(DEV), w.to(DEV), b.to(DEV)
+    with sc.sparse_indice_map_build(coords) as ms, sc.sparse_indice_map_build(coords, sync=False) as ma:
+        ya = sc.subm_conv3d_forward(ma, fd, wd, bd)  # enqueued before the map's status is known
+        ma.check()
+        ys = sc.subm_conv3d_forward(ms, fd, wd, bd)
+        torch.cuda.synchronize()
+        assert torch.equal(ya, ys)
+        assert np.array_equal(gpu_nbr(ma), oracle_nbr(key))
+        assert ma.pairs == ms.pairs
+        assert ma.mode == ms.mode
+
+
+def test_several_async_builds_in_flight():
+    keys = ["1", "2a", "3a", "1"]
+    maps = [sc.sparse_indice_map_build(torch.from_numpy(coords_of(k)).to(DEV), sync=False) for k in keys]
+    try:
+        for k, m in zip(keys, maps):
+            assert np.array_equal(gpu_nbr(m), oracle_nbr(k)), k
+    finally:
+        for m in maps:
+            m.free()
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_async_build_reports_duplicates_later_and_work_on_it_stays_in_bounds(mode):
+    coords = np.concatenate([coords_of("1"), coords_of("1")[17:18]])
+    m = sc.sparse_indice_map_build_async(torch.from_numpy(coords).to(DEV), mode)
+    try:
+        rng = np.random.default_rng(9)
+        f = torch.from_numpy(rng.standard_normal((len(coords), 64))).to(torch.bfloat16).to(DEV)
+        w = torch.from_numpy(rng.standard_normal((64, 3, 3, 3, 64)) * 0.05).to(torch.bfloat16).to(DEV)
+        sc.subm_conv3d_forward(m, f, w)  # a row of the set for every present neighbour: no fault
+        torch.cuda.synchronize()
+        for call in (m.check, lambda: m.pairs, lambda: gpu_nbr(m),
+                     lambda: sc.subm_conv3d_forward_per_offset(m, f, w)):
+            with pytest.raises(sc.SubmError) as e:
+                call()
+            assert e.value.name == "SUBM_ERR_DUPLICATE_COORD"
+    finally:
+        m.free()
+
+
+@pytest.mark.parametrize("cout", [16, 64])
+def test_async_build_out_of_range_leaves_only_the_bias(cout):
+    coords = np.array([[0, 0, 0, 0], [0, 65535, 0, 0], [0, 1, 0, 0]], dtype=np.int32)
+    m = sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV), sync=False)
+    try:
+        rng = np.random.default_rng(10)
+        f = torch.from_numpy(rng.standard_normal((3, 32))).to(torch.bfloat16).to(DEV)
+        w = torch.from_numpy(rng.standard_normal((cout, 3, 3, 3, 32))).to(torch.bfloat16).to(DEV)
+        b = torch.from_numpy(rng.standard_normal(cout)).to(torch.bfloat16).to(DEV)
+        y = sc.subm_conv3d_forward(m, f, w, b)  # every rulebook entry is -1
+        torch.cuda.synchronize()
+        assert torch.equal(y, b.expand(3, cout))
+        with pytest.raises(sc.SubmError) as e:
+            m.check()
+        assert e.value.name == "SUBM_ERR_COORD_RANGE"
+    finally:
+        m.free()
