@@ -408,8 +408,9 @@ def bench_structure(args):
         items = 8 * n
         sub = sc.sparse_subdivide(coords)
         kern = {
-            "expand_kernel": (lambda: sc.sparse_upsample_forward(sub, feats, out=child_feats),
-                              float(n * ch * s + 8 * n * 4 + 8 * n * ch * s)),
+            # a subdivide's children copy their parent row: each coarse row read once, no index
+            "expand8_kernel": (lambda: sc.sparse_upsample_forward(sub, feats, out=child_feats),
+                               float(n * ch * s + 8 * n * ch * s)),
         }
         cm_holder = []
 

@@ -297,19 +297,33 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
       float acc[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] = MAX ? -__builtin_inff() : 0.f;
-      for (int32_t q = lo; q < hi; ++q) {
-        const int64_t f = seg_rows != nullptr ? seg_rows[q] : q;
-        const int64_t base = f * channels + c0;
-        if constexpr (E > 1) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(fine) + base * (16 / E));
-          const unsigned char* b = reinterpret_cast<const unsigned char*>(&raw);
+      if constexpr (E > 1) {
+        // four members at a time: their row indices, then their words, all in flight together
+        for (int32_t q0 = lo; q0 < hi; q0 += 4) {
+          int64_t f[4];
 #pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float v = load_f<D>(b, e);
-            acc[e] = MAX ? fmaxf(acc[e], v) : acc[e] + v;
+          for (int u = 0; u < 4; ++u) f[u] = q0 + u < hi ? (seg_rows != nullptr ? seg_rows[q0 + u] : q0 + u) : -1;
+          uint4 raw[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            raw[u] = f[u] >= 0 ? *reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(fine) +
+                                                                 (f[u] * channels + c0) * (16 / E))
+                               : make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (f[u] < 0) continue;
+            const unsigned char* b = reinterpret_cast<const unsigned char*>(&raw[u]);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const float v = load_f<D>(b, e);
+              acc[e] = MAX ? fmaxf(acc[e], v) : acc[e] + v;
+            }
           }
-        } else {
-          const float v = load_f<D>(fine, base);
+        }
+      } else {
+        for (int32_t q = lo; q < hi; ++q) {
+          const int64_t f = seg_rows != nullptr ? seg_rows[q] : q;
+          const float v = load_f<D>(fine, f * channels + c0);
           acc[0] = MAX ? fmaxf(acc[0], v) : acc[0] + v;
         }
       }
@@ -340,6 +354,23 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(const W* __restrict__ 
   }
 }
 
+// Upsample of a subdivide: fine rows 8i .. 8i + 7 are all copies of coarse row i, so each coarse
+// word is read once and stored eight times, with no parent index to read.
+template <typename W>
+__global__ __launch_bounds__(kThreads) void expand8_kernel(const W* __restrict__ coarse, W* __restrict__ fine,
+                                                           int64_t n_coarse, int words) {
+  const RowLanes L(words);
+  if (L.r >= L.rpb) return;
+  for (int64_t i = (int64_t)blockIdx.x * L.rpb + L.r; i < n_coarse; i += (int64_t)gridDim.x * L.rpb) {
+    W* dst = fine + i * 8 * words;
+    for (int w = L.w0; w < words; w += L.wstep) {
+      const W v = coarse[i * words + w];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dst[c * words + w] = v;
+    }
+  }
+}
+
 // Blocks for a row-by-word launch over `rows` rows of `words` words.
 int row_grid(int64_t rows, int words) {
   const int rpb = words >= kThreads ? 1 : kThreads / words;
@@ -359,7 +390,7 @@ constexpr int kChildParents = kThreads / 8;
 __global__ __launch_bounds__(kThreads) void child_map_kernel(const int32_t* __restrict__ pnbr, int64_t np,
                                                              int32_t* __restrict__ cnbr, uint32_t* __restrict__ cmask) {
   __shared__ int32_t sp[kChildParents * 27];
-  __shared__ int32_t sc[kThreads * 27];
+  __shared__ __align__(16) int32_t sc[kThreads * 27];
   const int64_t p0 = (int64_t)blockIdx.x * kChildParents;
   const int64_t pcount = min((int64_t)kChildParents, np - p0);
   for (int e = threadIdx.x; e < pcount * 27; e += kThreads) sp[e] = pnbr[p0 * 27 + e];
@@ -382,8 +413,13 @@ __global__ __launch_bounds__(kThreads) void child_map_kernel(const int32_t* __re
     cmask[r] = bits;
   }
   __syncthreads();
-  const int64_t rows = pcount * 8;
-  for (int e = tid; e < rows * 27; e += kThreads) cnbr[p0 * 8 * 27 + e] = sc[e];
+  // The block's rows are one contiguous, 16-byte aligned run (8 rows of 27 int32 per parent, a
+  // multiple of 4 entries): 16-byte stores.  (Computing each 16-byte word from the parent rows
+  // instead of staging the child rows in LDS measured 20 % slower.)
+  const int words = (int)(pcount * 8 * 27 / 4);
+  int4* dst4 = reinterpret_cast<int4*>(cnbr + p0 * 8 * 27);
+  const int4* src4 = reinterpret_cast<const int4*>(sc);
+  for (int e = tid; e < words; e += kThreads) dst4[e] = src4[e];
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -848,7 +884,11 @@ extern "C" int sparse_upsample_forward(sparse_subdivision_t s, int channels, int
   const size_t row = (size_t)channels * (dtype == SUBM_F32 ? 4 : 2);
   const uintptr_t ptrs = reinterpret_cast<uintptr_t>(coarse) | reinterpret_cast<uintptr_t>(fine);
   const int64_t nf = s->d.n_fine;
-  if (row % 16 == 0 && ptrs % 16 == 0) {
+  if (s->d.kind == SUBM_SUBDIVIDE && row % 16 == 0 && ptrs % 16 == 0) {
+    const int w = (int)(row / 16);
+    expand8_kernel<uint4><<<row_grid(s->d.n_coarse, w), kThreads, 0, stream>>>(
+        static_cast<const uint4*>(coarse), static_cast<uint4*>(fine), s->d.n_coarse, w);
+  } else if (row % 16 == 0 && ptrs % 16 == 0) {
     const int w = (int)(row / 16);
     expand_kernel<uint4><<<row_grid(nf, w), kThreads, 0, stream>>>(static_cast<const uint4*>(coarse),
                                                                        static_cast<uint4*>(fine), nf, w, s->d.parent);
