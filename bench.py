@@ -56,6 +56,7 @@ def parse():
                    choices=["conv", "per-offset", "subdivide", "downsample", "groupnorm", "conv-groupnorm"])
     p.add_argument("--conv-reps", type=int, default=200, help="back-to-back launches timed for the roofline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-peaks", action="store_true", help="skip the measured GEMM and copy ceilings")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target duration of the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run 5 plain device copies of MIB MiB (reference for hardware byte counters)")
@@ -86,6 +87,42 @@ def layer_plan(key):
 def source_hash(path):
     with open(path, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()
+
+
+def measured_peaks(dev):
+    """This GPU's measured ceilings, beside the published ones: a large bf16 GEMM (hipBLASLt
+    through torch.matmul, contiguous 2-D operands) and a 1 GiB device-to-device copy."""
+    import torch
+    out = {}
+    m = 8192
+    a = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    out["bf16_gemm_TFLOPs"] = 10 * 2.0 * m ** 3 / (e0.elapsed_time(e1) / 1e3) / 1e12
+    del a, b
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["copy_GBps"] = 10 * 2.0 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def load_traffic(key, kernel_hash):
@@ -223,6 +260,17 @@ def main():
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / args.steps
 
+    # Spread of single steps (outside the timed block): an event on the stream before each step,
+    # so consecutive events bracket one step on the GPU timeline.
+    stream0 = torch.cuda.current_stream(dev)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for i in range(args.steps):
+        marks[i].record(stream0)
+        step()
+    marks[-1].record(stream0)
+    torch.cuda.synchronize()
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+
     if per_offset:
         # The step above builds a new map every time, so each per-offset call also built that
         # map's pair lists (and synchronised once); the kernel timing below reuses one map.
@@ -297,6 +345,14 @@ def main():
         kernel = "subm_conv_generic_kernel"
     roofline.update({"kernel": kernel, "avg_launch_ms": conv_ms, "launches": len(per_layer[dom]),
                      "algorithmic_flop_per_launch": flop_launch, "algorithmic_bytes_per_launch": bytes_launch})
+    peaks = None if args.no_peaks else measured_peaks(dev)
+    if peaks is not None:
+        measured = peaks["bf16_gemm_TFLOPs"] if roofline["bound"] == "mfma" else peaks["copy_GBps"]
+        roofline.update({"peak_measured": measured, "frac_measured": roofline["achieved"] / measured,
+                         "peak_measured_by": "torch.matmul bf16 8192^3" if roofline["bound"] == "mfma"
+                         else "1 GiB device copy (read + write)"})
+    pct = lambda v: {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
+                     "p90": float(np.percentile(v, 90))}
 
     value = flops_per_step / step_s / 1e12
     result = {
@@ -320,7 +376,11 @@ def main():
                       "conv_ms_per_layer": {str(i): float(np.mean(v)) for i, v in per_layer.items()},
                       "conv_tflops_effective": flop_launch / conv_s / 1e12,
                       "voxels_per_s_step": n / step_s,
-                      "voxels_per_s_conv": n / conv_s},
+                      "voxels_per_s_conv": n / conv_s,
+                      "step_ms_spread": pct(step_ms),
+                      "conv_ms_spread": pct(per_layer[dom]),
+                      "map_build_GBps": float(n * (16 + 108 + 4)) / build_s / 1e9,
+                      "measured_peaks": peaks},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
