@@ -501,3 +501,44 @@ def test_async_build_out_of_range_leaves_only_the_bias(cout):
         assert e.value.name == "SUBM_ERR_COORD_RANGE"
     finally:
         m.free()
+
+
+# ----------------------------------------------------------------- tensors past 31-bit offsets
+
+def test_features_past_31_bit_byte_offsets():
+    # Two dense 163^3 boxes with 128 bf16 channels: 2.2 GB of features, past the byte offsets the
+    # fast kernels address, so the library takes its 64-bit-indexed kernel.  The rulebook of a
+    # dense box has a closed form (checked bit for bit on sampled rows); features on the same rows
+    # against the oracle.
+    g, cin, cout = 163, 128, 32
+    zz, yy, xx = np.meshgrid(np.arange(g), np.arange(g), np.arange(g), indexing="ij")
+    one = np.stack([zz.ravel(), yy.ravel(), xx.ravel()], 1)
+    coords = np.concatenate([np.concatenate([np.full((len(one), 1), b), one], 1) for b in range(2)]).astype(np.int32)
+    n = len(coords)
+    assert n * cin * 2 >= 2 ** 31
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(11)
+    f = torch.randn(n, cin, generator=gen, device=DEV).to(torch.bfloat16)
+    rng = np.random.default_rng(12)
+    w = torch.from_numpy(rng.standard_normal((cout, 3, 3, 3, cin)) / np.sqrt(27 * cin)).to(torch.bfloat16)
+    b = torch.from_numpy(rng.standard_normal(cout) * 0.3).to(torch.bfloat16)
+    rows = sample_rows(n, count=1024, seed=13)
+    rows_d = torch.from_numpy(rows).to(DEV)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        y = sc.subm_conv3d_forward(m, f, w.to(DEV), b.to(DEV))
+        nbr_rows = sc.sparse_indice_map_copy_nbr(m)[rows_d].cpu().numpy()
+        torch.cuda.synchronize()
+    bb, z, yv, x = (coords[rows, a].astype(np.int64) for a in range(4))
+    expect = np.full((len(rows), 27), -1, np.int64)
+    for k in range(27):
+        z2, y2, x2 = z + k // 9 - 1, yv + (k // 3) % 3 - 1, x + k % 3 - 1
+        ok = (z2 >= 0) & (z2 < g) & (y2 >= 0) & (y2 < g) & (x2 >= 0) & (x2 < g)
+        expect[ok, k] = ((bb[ok] * g + z2[ok]) * g + y2[ok]) * g + x2[ok]
+    assert np.array_equal(nbr_rows, expect)
+    used = np.unique(expect[expect >= 0])
+    fsub = f[torch.from_numpy(used).to(DEV)].cpu()
+    local = np.where(expect >= 0, np.searchsorted(used, expect), -1)
+    ref = oracle.conv3_rulebook(local, as64(fsub), as64(w), as64(b))
+    check(y[rows_d].cpu(), ref, "bf16", "features past 31-bit offsets")
+    del f, y
+    torch.cuda.empty_cache()
