@@ -59,7 +59,7 @@ struct DeviceGuard {
   }
 };
 
-// Device-side plan and statistics of one map build (copied to the host at its end).
+// Map build constants.
 constexpr int kTapBanks = 16;               // tap hit counters are spread over banks of 27
 constexpr int64_t kGridCellsPerVoxel = 128;       // dense grid allowed up to this many cells per voxel
 constexpr int64_t kGridMaxCells = int64_t(1) << 29;  // ... and at most 2 GiB of int32 cells
@@ -73,8 +73,8 @@ constexpr uint32_t kFlagBatchRange = 2u;
 constexpr uint32_t kFlagProbeOverflow = 4u;
 constexpr uint32_t kFlagExtentRange = 8u;
 
-// Words the plan and insert kernels write straight into pinned host memory; the host reads them
-// once the insert kernel has completed.
+// Words the insert kernel (its plan and its inserts) writes straight into pinned host memory;
+// the host reads them once that kernel has completed.
 struct MapHostFlags {
   uint32_t flags;      // kFlag* range bits of the plan
   int32_t mode;        // kMode* of the plan
@@ -82,6 +82,8 @@ struct MapHostFlags {
   uint32_t overflow;   // 1: the hash probe ran out of slots
 };
 
+// Device-side plan of the latest build on a workspace, published by the insert kernel's block 0
+// for the lookup kernel and for the next build's first kernel (which puts its entries back).
 struct MapStats {
   int32_t mn[4];       // per-column minimum of (b, z, y, x)
   int32_t mx[4];       // per-column maximum
@@ -92,7 +94,7 @@ struct MapStats {
   int64_t cells;       // GRID: number of cells
   int64_t slots;       // HASH: number of slots
   int64_t sy, sz, sb;  // GRID strides of y, z and the batch slab (x stride is 1)
-  int64_t inserted;     // rows the insert kernel wrote (GRID: their cells are in the cell list)
+  int64_t inserted;    // rows the insert kernel wrote (GRID: their cells are in the cell list)
 };
 
 // Where a build's flags arrive: a 16-byte slot of pinned host memory that the kernels write
