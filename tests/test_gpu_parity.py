@@ -542,3 +542,40 @@ def test_features_past_31_bit_byte_offsets():
     check(y[rows_d].cpu(), ref, "bf16", "features past 31-bit offsets")
     del f, y
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------- builds from two threads
+
+def test_builds_from_two_threads_on_two_streams():
+    # The build workspace is shared by every build on the device: builds from two host threads on
+    # two streams must still each see only their own coordinate set, synchronous or not.
+    import threading
+    keys = ("2a", "3a")
+    got = {k: [] for k in keys}
+    errors = []
+
+    def worker(key):
+        try:
+            stream = torch.cuda.Stream(device=DEV)
+            coords = torch.from_numpy(coords_of(key)).to(DEV)
+            torch.cuda.synchronize()
+            for rep in range(6):
+                with torch.cuda.stream(stream):
+                    m = sc.sparse_indice_map_build(coords, stream=stream, sync=rep % 2 == 0)
+                    nbr = sc.sparse_indice_map_copy_nbr(m, stream=stream)
+                    stream.synchronize()
+                    got[key].append(nbr.cpu().numpy())
+                    m.free()
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in keys]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for k in keys:
+        assert len(got[k]) == 6
+        for nbr in got[k]:
+            assert np.array_equal(nbr, oracle_nbr(k)), k
