@@ -1068,22 +1068,32 @@ constexpr int kPersistentBlocks = 256;  // one workgroup per compute unit
 // Orders ordinary LDS accesses against the direct loads, which the compiler does not see.
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-template <DT D, int WM, int FM, int FN, int SL>
-__global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_persistent_kernel(const ConvArgs args) {
+template <DT D, int WM, int FM, int FN, int SL, int LW>
+__global__ __launch_bounds__(64 * (4 + LW), 1) void subm_conv_ws_persistent_kernel(const ConvArgs args) {
   using Sh = MmaShape<WM, FM, FN, SL, 27>;
-  constexpr int WTM = Sh::WTM, WTN = Sh::WTN, BM = Sh::BM, BN = Sh::BN, BNP = Sh::BNP;
+  constexpr int WTM = Sh::WTM, WTN = Sh::WTN, BM = Sh::BM, BN = Sh::BN;
   constexpr int CH = Sh::CH, RPI = Sh::RPI, KSTEPS = Sh::KSTEPS;
-  constexpr int ADMA = Sh::ADMA, BDMA = Sh::BDMA, DMA = Sh::DMA, BUF = Sh::BUF, NS = Sh::NS;
-  constexpr int QROWS = BM / 4;                          // rulebook rows per load wave
-  constexpr int QDMA = (QROWS * 27 * 4 + 1023) / 1024;   // 1 KB direct loads per load wave
+  // LW load waves beside the four compute waves: each loads BM / LW rows of A and its share of
+  // the B rows.  (One wave sustains only so many direct-to-LDS loads: measured with a copy probe,
+  // four waves per CU reach ~37 B/clk, eight ~49 B/clk.)
+  constexpr int NT = 64 * (4 + LW);
+  constexpr int QROWS = BM / LW;                         // A rows (and rulebook rows) per load wave
+  constexpr int ADMA = QROWS / RPI;                      // A loads per load wave per stage
+  constexpr int BDMA = (BN + LW * RPI - 1) / (LW * RPI); // B loads per load wave per stage
+  constexpr int BNP = LW * RPI * BDMA;                   // B rows per stage (rows past BN load zeros)
+  constexpr int DMA = ADMA + BDMA;
+  constexpr int BUF = (BM + BNP) * SL;                   // one ring slot
+  constexpr int QDMA = (QROWS * 27 * 4 + 1023) / 1024;   // 1 KB direct loads of rulebook rows per load wave
+  constexpr int NS_FIT = (160 * 1024 - LW * QDMA * 1024 - 2048) / BUF;
+  constexpr int NS = NS_FIT >= kMaxStages ? kMaxStages : NS_FIT;  // ring depth
+  static_assert(QROWS % RPI == 0, "A rows split into whole load instructions per wave");
   static_assert(NS >= 2, "ring depth");
-  static_assert(4 * QDMA * 1024 <= Sh::NBR, "per-wave rulebook slots fit the rulebook area");
   static_assert((NS - 1) * DMA < 64 && QDMA < 64, "outstanding loads exceed the vmcnt range");
   static_assert((QROWS * 27 * 4) % 16 == 0 && (BM * 27 * 4) % 16 == 0, "rulebook rows in whole 16-byte chunks");
   static_assert(KSTEPS <= 4, "step-ahead schedule covers up to four steps per stage");
 
   __shared__ __align__(16) unsigned char ring[NS * BUF];
-  __shared__ __align__(16) int32_t s_nbr[4 * QDMA * 256];  // one slot of QDMA KB per load wave
+  __shared__ __align__(16) int32_t s_nbr[LW * QDMA * 256];  // one slot of QDMA KB per load wave
   __shared__ __align__(16) float s_bias[BN];
   __shared__ uint32_t s_tmask[kMaxBlockTiles];
 
@@ -1091,7 +1101,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_persistent_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const bool loader = wave >= 4;
-  const int cw = wave & 3;
+  const int cw = loader ? wave - 4 : wave;  // index of the wave within its role
   const int wm = cw % WM;
   const int wn = cw / WM;
   const int cw_u = __builtin_amdgcn_readfirstlane(cw);
@@ -1113,17 +1123,17 @@ __global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_persistent_kernel(
     const int o = o0 + tid;
     s_bias[tid] = (args.bias != nullptr && o < cout) ? to_float<D>(reinterpret_cast<const T*>(args.bias)[o]) : 0.f;
   }
-  for (int k = tid; k < ntiles; k += kWsThreads) s_tmask[k] = 0;
+  for (int k = tid; k < ntiles; k += NT) s_tmask[k] = 0;
   __syncthreads();
   // Tap masks of all tiles: OR of the rows' neighbour masks, eight independent loads in flight.
   // BM is a multiple of 64, so the 64 consecutive rows of a wave's load lie in one tile: OR them
   // across the wave, then one LDS atomic per wave and load.
   static_assert(BM % 64 == 0, "a wave's rows lie in one tile");
-  for (int idx0 = tid; idx0 < ntiles * BM; idx0 += 8 * kWsThreads) {
+  for (int idx0 = tid; idx0 < ntiles * BM; idx0 += 8 * NT) {
     uint32_t m[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int idx = idx0 + u * kWsThreads;
+      const int idx = idx0 + u * NT;
       const int k = idx / BM;
       const int64_t row = (int64_t)tile_of(k < ntiles ? k : 0) * BM + (idx - k * BM);
       const bool ok = idx < ntiles * BM && row < n;
@@ -1133,7 +1143,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_persistent_kernel(
     for (int u = 0; u < 8; ++u) {
       uint32_t v = m[u];
       for (int off = 32; off > 0; off >>= 1) v |= __shfl_xor(v, off, 64);
-      const int k = (idx0 + u * kWsThreads) / BM;
+      const int k = (idx0 + u * NT) / BM;
       if (lane == 0 && v != 0u) atomicOr(&s_tmask[k], v);
     }
   }
@@ -1158,7 +1168,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_persistent_kernel(
     for (int d = 0; d < ADMA; ++d) lane_cb[d] = chunk_bytes(cw * QROWS + RPI * d);
 #pragma unroll
     for (int d = 0; d < BDMA; ++d) {
-      const int g = BM + cw * (BNP / 4) + RPI * d;
+      const int g = BM + cw * (BNP / LW) + RPI * d;
       const int ol = g - BM + lane / CH;
       const int o = o0 + ol;
       lane_cb[ADMA + d] = chunk_bytes(g);
@@ -1236,7 +1246,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_persistent_kernel(
         lds_dma16(rsrc_a, offs[d], lds_offset(base) + (uint32_t)((cw_u * QROWS + RPI * d) * SL));
 #pragma unroll
       for (int d = 0; d < BDMA; ++d)
-        lds_dma16(rsrc_b, offs[ADMA + d], lds_offset(base) + (uint32_t)((BM + cw_u * (BNP / 4) + RPI * d) * SL));
+        lds_dma16(rsrc_b, offs[ADMA + d], lds_offset(base) + (uint32_t)((BM + cw_u * (BNP / LW) + RPI * d) * SL));
     };
 #pragma unroll
     for (int s0 = 0; s0 < NS; ++s0) {
@@ -1386,7 +1396,7 @@ hipError_t launch_mma(const ConvArgs& a0, hipStream_t stream) {
 // Persistent launch: one workgroup per compute unit (a multiple of 8, for the XCD mapping), each
 // walking its tiles.  hipErrorNotSupported when a workgroup would get more than kMaxBlockTiles
 // tiles or the output rows cannot take 8-byte stores (the caller then uses launch_ws).
-template <DT D, int WM, int FM, int FN, int SL>
+template <DT D, int WM, int FM, int FN, int SL, int LW>
 hipError_t launch_ws_persistent(const ConvArgs& a0, hipStream_t stream) {
   using Sh = MmaShape<WM, FM, FN, SL, 27>;
   ConvArgs a = a0;
@@ -1396,7 +1406,7 @@ hipError_t launch_ws_persistent(const ConvArgs& a0, hipStream_t stream) {
   const int per_block = (a.per_xcd + nblk / 8 - 1) / (nblk / 8);
   if (per_block > kMaxBlockTiles || !a.vec_out || a.cout % 8 != 0) return hipErrorNotSupported;
   dim3 grid((unsigned)nblk, (unsigned)((a.cout + Sh::BN - 1) / Sh::BN));
-  subm_conv_ws_persistent_kernel<D, WM, FM, FN, SL><<<grid, kWsThreads, 0, stream>>>(a);
+  subm_conv_ws_persistent_kernel<D, WM, FM, FN, SL, LW><<<grid, 64 * (4 + LW), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -1480,8 +1490,10 @@ hipError_t launch_mma_auto(const ConvArgs& a, hipStream_t stream) {
   const char* forced = std::getenv("SUBMCONV_TILE");
   if (TAPS == 27 && a.cout > 32 && (forced == nullptr || tile_index(forced) < 0) && persistent_enabled()) {
     // the persistent walk of the same tiles the one-tile launch below would use
-    const hipError_t e = a.cout > 64 ? launch_ws_persistent<D, 2, 3, 2, 128>(a, stream)
-                                     : launch_ws_persistent<D, 4, 2, 2, 128>(a, stream);
+    // eight load waves: 2-3 % faster than four on the shell, dense, ellipsoid and subdivided
+    // workloads, same outputs
+    const hipError_t e = a.cout > 64 ? launch_ws_persistent<D, 2, 3, 2, 128, 8>(a, stream)
+                                     : launch_ws_persistent<D, 4, 2, 2, 128, 8>(a, stream);
     if (e != hipErrorNotSupported) return e;
   }
   if (a.cout > 64) {
