@@ -1155,6 +1155,9 @@ __global__ __launch_bounds__(64 * (4 + LW), 1) void subm_conv_ws_persistent_kern
   auto swz_of = [](int row) { return (row / (16 / CH)) % CH; };
 
   if (loader) {
+    // Load waves issue ahead of the compute waves on their SIMD (measured 1-3 % faster; raising
+    // the compute waves instead changes nothing).
+    __builtin_amdgcn_s_setprio(2);
     auto chunk_bytes = [&](int group_row) {
       return (uint32_t)(((lane % CH) ^ swz_of(group_row + lane / CH)) * 16);
     };
