@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -119,6 +120,8 @@ struct MapData {
   int64_t pairs = 0;
   int64_t per_tap[27] = {};
   int32_t* nbr = nullptr;     // device [n, 27], input row order
+  size_t nbr_bytes = 0;       // bytes of the allocation that starts at nbr
+  hipStream_t home = nullptr;  // the stream whose build wrote nbr / masks
   uint32_t* masks = nullptr;  // device [n]: bit k set when nbr[i, k] >= 0 (same allocation as nbr)
   uint32_t* dev_banks = nullptr;   // device [kTapBanks][27] per-tap pair counts, summed on the host
                                    // (same allocation as nbr)
@@ -210,6 +213,7 @@ struct SubdivData {
 struct submconv_map {
   submconv::MapData d;
   std::mutex mu;  // guards the lazy reads of the counts and the lazy build of the pair lists
+  std::atomic<bool> other_streams{false};  // work reading the map was enqueued off d.home
 };
 
 namespace submconv {
@@ -219,6 +223,19 @@ Status map_check(submconv_map* map);
 // Makes map->d.pairs / per_tap valid (waits for the build's last kernel on first use); fails with
 // the build's coordinate status.
 Status map_counts(submconv_map* map);
+// Records that work reading the map's memory is enqueued on `stream` (every entry point that
+// reads a map calls it before enqueuing); a map used only on the stream of its build gives its
+// memory back to the per-device block cache when freed (map_memory_give).
+inline void map_note_use(submconv_map* map, hipStream_t stream) {
+  if (map != nullptr && stream != map->d.home) map->other_streams.store(true, std::memory_order_relaxed);
+}
+// Memory for a map's rulebook on device `dev`: a cached block of a freed map that was built and
+// used only on `stream` when one fits (no allocator call, so nothing is enqueued), else a new
+// stream-ordered allocation.  *got receives the block's size.
+Status map_memory_take(int dev, size_t bytes, hipStream_t stream, void** ptr, size_t* got);
+// Gives a map's rulebook memory back: into the device's cache, tagged with `stream`, when
+// `reusable` (all work on it was on that stream), else back to the pool in stream order.
+void map_memory_give(int dev, void* ptr, size_t bytes, hipStream_t stream, bool reusable);
 // Host-side checks of a convolution call (subm_conv3d_forward's rules).
 Status check_conv(submconv_map_t map, int64_t n, int ksize, int cin, int cout, int dtype, const void* feats,
                   const void* weight, const void* bias, const void* out);

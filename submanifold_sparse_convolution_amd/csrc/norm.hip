@@ -630,6 +630,7 @@ extern "C" int subm_conv3d_forward_group_norm_act(submconv_map_t map, int64_t n,
   if (n == 0) return SUBM_OK;
   st = check_norm_pointers(out, out, item_offsets, gamma, beta, dtype);
   if (!st.ok()) return fail(st);
+  map_note_use(map, stream);
   const MapData* md = map == nullptr ? nullptr : &map->d;
   // Scratch for the fused path (tile partials for the shortest tiles, boundary pieces, statistics).
   const int64_t max_tiles = (n + 191) / 192;

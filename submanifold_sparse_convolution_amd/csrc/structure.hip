@@ -919,6 +919,7 @@ extern "C" int sparse_indice_map_subdivide(submconv_map_t parent_map, sparse_sub
   if (hipGetDevice(&dev) != hipSuccess || dev != s->d.device) return fail(SUBM_ERR_INVALID_ARG, "the handle was built on another device");
   Status cs = map_counts(parent_map);
   if (!cs.ok()) return fail(cs);
+  map_note_use(parent_map, stream);
   submconv_map* m = new (std::nothrow) submconv_map;
   if (m == nullptr) return fail(SUBM_ERR_OUT_OF_MEMORY, "host allocation of the map handle failed");
   const int64_t np = s->d.n_coarse;
@@ -947,12 +948,15 @@ extern "C" int sparse_indice_map_subdivide(submconv_map_t parent_map, sparse_sub
     return SUBM_OK;
   }
   void* nbr = nullptr;
-  Status st = device_alloc(&nbr, (size_t)nc * 28 * sizeof(int32_t), stream);
+  size_t nbr_bytes = 0;
+  Status st = map_memory_take(dev, (size_t)nc * 28 * sizeof(int32_t), stream, &nbr, &nbr_bytes);
   if (!st.ok()) {
     delete m;
     return fail(st);
   }
   m->d.nbr = static_cast<int32_t*>(nbr);
+  m->d.nbr_bytes = nbr_bytes;
+  m->d.home = stream;
   m->d.masks = reinterpret_cast<uint32_t*>(m->d.nbr + (size_t)nc * 27);
   hipError_t e = launch_child_map(parent_map->d.nbr, np, m->d.nbr, m->d.masks, stream);
   // The kernel writes the map's memory after this call returns; freeing the map waits for it.
@@ -961,7 +965,7 @@ extern "C" int sparse_indice_map_subdivide(submconv_map_t parent_map, sparse_sub
   if (e != hipSuccess) {
     (void)hipStreamSynchronize(stream);
     if (m->d.ready != nullptr) (void)hipEventDestroy(m->d.ready);
-    device_free(nbr, stream);
+    map_memory_give(dev, nbr, nbr_bytes, stream, true);
     delete m;
     return fail(hip_status(e, "child map launch"));
   }

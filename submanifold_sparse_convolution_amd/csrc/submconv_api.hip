@@ -232,18 +232,87 @@ Status workspace_reserve(Workspace& ws, int64_t n, size_t table_bytes, hipStream
 
 static_assert(sizeof(MapHostFlags) == 16 && kSlotPage % sizeof(MapHostFlags) == 0, "flag slots tile a page");
 
+// Rulebook blocks of freed maps, per device, for the next build on the same stream.  Returning a
+// block to the stream-ordered pool and allocating it again each enqueue a marker packet (~3 us of
+// idle GPU between two kernels, measured); a cached block costs nothing.  A block is cached only
+// when every use of its map was on the map's own stream, so a later build on that stream writes
+// it after all of them in stream order.  At most kCachedBlocks per device; the oldest goes back
+// to the pool when a new one arrives.
+struct CachedBlock {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  hipStream_t stream = nullptr;
+};
+struct BlockCache {
+  std::mutex mu;
+  std::vector<CachedBlock> blocks;
+};
+BlockCache g_blocks[kMaxDevices];
+constexpr size_t kCachedBlocks = 4;
+
 void release_map(submconv_map* m, hipStream_t stream) {
   if (m->d.ready != nullptr) {
     (void)hipEventSynchronize(m->d.ready);  // the build's own kernels write the map memory
     if (m->d.slot.host == nullptr) (void)hipEventDestroy(m->d.ready);  // a derived map's own event
   }
   give_flag_slot(m->d.device, m->d.slot);
-  device_free(m->d.nbr, stream);
+  map_memory_give(m->d.device, m->d.nbr, m->d.nbr_bytes, m->d.home,
+                  !m->other_streams.load(std::memory_order_relaxed));
   device_free(m->d.pair_out, stream);
   delete m;
 }
 
 }  // namespace
+
+Status submconv::map_memory_take(int dev, size_t bytes, hipStream_t stream, void** ptr, size_t* got) {
+  *ptr = nullptr;
+  *got = 0;
+  if (dev >= 0 && dev < kMaxDevices) {
+    BlockCache& cache = g_blocks[dev];
+    std::lock_guard<std::mutex> lock(cache.mu);
+    int best = -1;
+    for (size_t i = 0; i < cache.blocks.size(); ++i) {
+      const CachedBlock& b = cache.blocks[i];
+      // (at most twice the size asked for, so a small map does not hold a large block)
+      if (b.stream == stream && b.bytes >= bytes && b.bytes / 2 <= bytes &&
+          (best < 0 || b.bytes < cache.blocks[best].bytes))
+        best = (int)i;
+    }
+    if (best >= 0) {
+      *ptr = cache.blocks[best].ptr;
+      *got = cache.blocks[best].bytes;
+      cache.blocks.erase(cache.blocks.begin() + best);
+      return Status{};
+    }
+  }
+  Status s = device_alloc(ptr, bytes, stream);
+  if (s.ok()) *got = bytes;
+  return s;
+}
+
+void submconv::map_memory_give(int dev, void* ptr, size_t bytes, hipStream_t stream, bool reusable) {
+  if (ptr == nullptr) return;
+  if (!reusable || dev < 0 || dev >= kMaxDevices) {
+    device_free(ptr, nullptr);
+    return;
+  }
+  CachedBlock evicted;
+  {
+    BlockCache& cache = g_blocks[dev];
+    std::lock_guard<std::mutex> lock(cache.mu);
+    if (cache.blocks.size() >= kCachedBlocks) {
+      evicted = cache.blocks.front();
+      cache.blocks.erase(cache.blocks.begin());
+    }
+    CachedBlock b;
+    b.ptr = ptr;
+    b.bytes = bytes;
+    b.stream = stream;
+    cache.blocks.push_back(b);
+  }
+  // (the null stream orders the free after the work of every blocking stream)
+  device_free(evicted.ptr, nullptr);
+}
 
 namespace {
 
@@ -299,11 +368,13 @@ int build_map(const int32_t* coords, int64_t n, int mode, hipStream_t stream, su
     return fail(hip_status(e, "build events"));
   }
   void* nbr = nullptr;
+  size_t nbr_bytes = 0;
   s = workspace_reserve(ws, n, table_bytes, stream);
   // nbr [n, 27], masks [n], counter banks [kTapBanks, 27]
-  if (s.ok()) s = device_alloc(&nbr, (size_t)n * 28 * sizeof(int32_t) + kTapBanks * 27 * sizeof(uint32_t), stream);
+  if (s.ok())
+    s = map_memory_take(m->d.device, (size_t)n * 28 * sizeof(int32_t) + kTapBanks * 27 * sizeof(uint32_t), stream,
+                        &nbr, &nbr_bytes);
   if (!s.ok()) {
-    device_free(nbr, stream);
     release_map(m, stream);
     return fail(s);
   }
@@ -314,6 +385,8 @@ int build_map(const int32_t* coords, int64_t n, int mode, hipStream_t stream, su
   void* table = base + kStatsBytes + kPartialsBytes + cells_bytes(ws.cells_cap);
 
   m->d.nbr = static_cast<int32_t*>(nbr);
+  m->d.nbr_bytes = nbr_bytes;
+  m->d.home = stream;
   m->d.masks = reinterpret_cast<uint32_t*>(m->d.nbr + (size_t)n * 27);
   m->d.dev_banks = m->d.masks + n;
   host->flags = 0;
@@ -445,6 +518,7 @@ extern "C" int sparse_indice_map_copy_nbr(submconv_map_t map, int32_t* nbr, hipS
   if (nbr == nullptr) return fail(SUBM_ERR_INVALID_ARG, "nbr is NULL");
   const Status s = map_check(map);
   if (!s.ok()) return fail(s);
+  map_note_use(map, stream);
   hipError_t e = hipMemcpyAsync(nbr, map->d.nbr, (size_t)map->d.n * 27 * sizeof(int32_t), hipMemcpyDeviceToDevice, stream);
   if (e != hipSuccess) return fail(hip_status(e, "copy of nbr"));
   return SUBM_OK;
@@ -484,6 +558,7 @@ extern "C" int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int
   Status s = check_conv(map, n, ksize, cin, cout, dtype, feats, weight, bias, out);
   if (!s.ok()) return fail(s);
   if (n == 0) return SUBM_OK;
+  map_note_use(map, stream);
   hipError_t e = launch_subm_conv(map == nullptr ? nullptr : &map->d, n, ksize, cin, cout, dtype, feats, weight, bias, out, stream);
   if (e != hipSuccess) return fail(hip_status(e, "subm_conv3d_forward launch"));
   return SUBM_OK;
@@ -511,6 +586,7 @@ extern "C" int subm_conv3d_forward_per_offset(submconv_map_t map, int64_t n, int
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(hip_status(e, "hipGetDevice"));
   if (dev != map->d.device) return fail(SUBM_ERR_INVALID_ARG, "the map was built on another device");
+  map_note_use(map, stream);
   {
     Status cs = map_counts(map);
     if (!cs.ok()) return fail(cs);

@@ -579,3 +579,48 @@ def test_builds_from_two_threads_on_two_streams():
         assert len(got[k]) == 6
         for nbr in got[k]:
             assert np.array_equal(nbr, oracle_nbr(k)), k
+
+
+# ----------------------------------------------------------------- freed rulebook memory
+
+def test_freed_rulebook_memory_is_reused_only_in_stream_order():
+    # A freed map's rulebook block is kept for the next build on the same stream.  Build, conv and
+    # free back to back with no host wait (each build may take the block that the previous step's
+    # conv is still reading), over three coordinate sets whose blocks fit each other; every step
+    # must see only its own set.  One map is also read on a second stream, so its block goes back
+    # to the pool instead.
+    base = coords_of("3a")
+    keep = np.arange(len(base)) % 6 != 5
+    sets = {"3a": base, "reversed": np.ascontiguousarray(base[::-1]), "sixth dropped": np.ascontiguousarray(base[keep])}
+    f, w, b = cfg_tensors("3a", 0)
+    f_of = {"3a": f, "reversed": f.flip(0), "sixth dropped": f[torch.from_numpy(keep)]}
+    w, b = w.to(DEV), b.to(DEV)
+    dev_coords, feats, expect_nbr, expect_out = {}, {}, {}, {}
+    for name, c in sets.items():
+        dev_coords[name] = torch.from_numpy(c).to(DEV)
+        feats[name] = f_of[name].contiguous().to(DEV)
+        expect_nbr[name] = oracle.rulebook_sorted(c)
+        with sc.sparse_indice_map_build(dev_coords[name]) as m:
+            assert np.array_equal(gpu_nbr(m), expect_nbr[name]), name
+            expect_out[name] = sc.subm_conv3d_forward(m, feats[name], w, b).cpu()
+    rows = sample_rows(len(base), count=512, seed=2)
+    ref = oracle.conv3_rulebook(expect_nbr["3a"], as64(feats["3a"].cpu()), as64(w.cpu()), as64(b.cpu()), rows=rows)
+    check(expect_out["3a"][rows], ref, "bf16", "fresh map, 3a")
+    side = torch.cuda.Stream(device=DEV)
+    outs, nbrs = [], []
+    names = list(sets) * 4
+    for step, name in enumerate(names):
+        m = sc.sparse_indice_map_build(dev_coords[name], sync=False)
+        outs.append((name, sc.subm_conv3d_forward(m, feats[name], w, b)))
+        if step == 5:
+            side.wait_stream(torch.cuda.current_stream())
+            nbrs.append((name, sc.sparse_indice_map_copy_nbr(m, stream=side)))
+            torch.cuda.current_stream().wait_stream(side)
+        else:
+            nbrs.append((name, sc.sparse_indice_map_copy_nbr(m)))
+        m.check()
+        m.free()
+    torch.cuda.synchronize()
+    for (name, out), (_, nbr) in zip(outs, nbrs):
+        assert np.array_equal(nbr.cpu().numpy(), expect_nbr[name]), name
+        assert torch.equal(out.cpu(), expect_out[name]), name
