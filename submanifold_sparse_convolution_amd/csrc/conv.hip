@@ -1118,6 +1118,21 @@ __global__ __launch_bounds__(64 * (4 + LW), 1) void subm_conv_ws_persistent_kern
     ++ntiles;
   if (ntiles == 0) return;  // whole workgroup: no barrier has run yet
 
+  // Rulebook rows of tile k for this load wave's share of the rows, into its own slot (only this
+  // wave reads it, so its own wait is enough).
+  const i32x4_t rsrc_n = make_rsrc(args.nbr, (uint32_t)(n * 27 * 4));
+  auto issue_rows = [&](int k) {
+    const uint32_t gbase = (uint32_t)(((int64_t)tile_of(k) * BM + cw * QROWS) * 27 * 4);
+#pragma unroll
+    for (int d = 0; d < QDMA; ++d) {
+      const uint32_t blk = (uint32_t)(d * 1024);
+      const uint32_t off = blk + (uint32_t)lane * 16u;
+      lds_dma16(rsrc_n, off < (uint32_t)(QROWS * 27 * 4) ? gbase + off : kOutOfRange,
+                lds_offset(s_nbr) + (uint32_t)(cw_u * QDMA * 1024) + blk);
+    }
+  };
+  // The load waves start on tile 0's rows now, under the tap-mask pass below.
+  if (loader) issue_rows(0);
   using T = typename Elem<D>::T;
   if (tid < BN) {
     const int o = o0 + tid;
@@ -1163,7 +1178,6 @@ __global__ __launch_bounds__(64 * (4 + LW), 1) void subm_conv_ws_persistent_kern
     };
     const i32x4_t rsrc_a = make_rsrc(args.feats, args.feats_bytes);
     const i32x4_t rsrc_b = make_rsrc(args.weight, args.weight_bytes);
-    const i32x4_t rsrc_n = make_rsrc(args.nbr, (uint32_t)(n * 27 * 4));
     int32_t* my_nbr = s_nbr + cw * (QDMA * 256);
     uint32_t lane_cb[DMA], base_b[BDMA];
     bool ok_b[BDMA];
@@ -1179,20 +1193,11 @@ __global__ __launch_bounds__(64 * (4 + LW), 1) void subm_conv_ws_persistent_kern
       base_b[d] = (uint32_t)(ok_b[d] ? o : 0) * 27u * (uint32_t)row_bytes + lane_cb[ADMA + d];
     }
     bool row_ok[ADMA];
-    // Rulebook rows of tile k for this wave's quarter, into this wave's own slot (only this wave
-    // reads it, so its own wait is enough).  At a tile change the wait also drains the ring loads
-    // in flight, which have to land anyway; prefetching the rows one stage earlier, with waits
-    // that leave them in flight, measured 3-6 % slower.
-    auto load_rows = [&](int k) {
+    // At a tile change the wait for the rows also drains the ring loads in flight, which have to
+    // land anyway; prefetching the rows one stage earlier, with waits that leave them in flight,
+    // measured 3-6 % slower.
+    auto rows_landed = [&](int k) {
       const int64_t r0 = (int64_t)tile_of(k) * BM + cw * QROWS;
-      const uint32_t gbase = (uint32_t)(r0 * 27 * 4);
-#pragma unroll
-      for (int d = 0; d < QDMA; ++d) {
-        const uint32_t blk = (uint32_t)(d * 1024);
-        const uint32_t off = blk + (uint32_t)lane * 16u;
-        lds_dma16(rsrc_n, off < (uint32_t)(QROWS * 27 * 4) ? gbase + off : kOutOfRange,
-                  lds_offset(s_nbr) + (uint32_t)(cw_u * QDMA * 1024) + blk);
-      }
 #pragma unroll
       for (int d = 0; d < ADMA; ++d) row_ok[d] = r0 + RPI * d + lane / CH < n;
       wait_vmcnt<0>();
@@ -1205,7 +1210,7 @@ __global__ __launch_bounds__(64 * (4 + LW), 1) void subm_conv_ws_persistent_kern
     bool pvalid = false;
     int32_t raw[ADMA];
     uint32_t offs[DMA];
-    load_rows(0);
+    rows_landed(0);  // (issued before the tap-mask pass)
     auto fetch = [&](int stage_index) {
       pvalid = stage_index < total;
       if (pvalid && iq >= nq && rem == 0u) {  // this tile's stages are done: next tile with taps
@@ -1214,7 +1219,8 @@ __global__ __launch_bounds__(64 * (4 + LW), 1) void subm_conv_ws_persistent_kern
           rem = s_tmask[ck];
         } while (rem == 0u && ck + 1 < ntiles);
         compiler_fence();  // the last rows of the previous tile have been read
-        load_rows(ck);
+        issue_rows(ck);
+        rows_landed(ck);
       }
       const bool adv = pvalid && iq >= nq;
       const int nk = __builtin_ctz(rem | 0x80000000u);
