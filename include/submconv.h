@@ -144,12 +144,12 @@ int sparse_indice_map_mode(submconv_map_t map, int* mode);
  * sparse_indice_map_free -- release a map.  NULL is accepted (returns SUBM_OK).  No work that
  * uses the map may still be in flight on any stream other than the stream of its build, as for
  * freeing any device buffer; work on the build's own stream may still be in flight (it is
- * ordered before whatever reuses the memory).  The rulebook memory of a map that was only ever
- * used on the stream of its build is kept by the library (at most 4 blocks per device, the
- * oldest released first) and reused by a later build of a similar size on that same stream, in
- * stream order, so a build / convolve / free loop enqueues no allocator work; the memory of a
- * map used on several streams goes back to the device's memory pool after the work on the null
- * stream and on every blocking stream.
+ * ordered before whatever reuses the memory), and that stream must still exist.  The rulebook
+ * memory of a map that was only ever used on the stream of its build is kept by the library (at
+ * most 8 blocks per device, until a build takes them or the process ends) and reused by a later
+ * build of a similar size on that same stream, in stream order, so a build / convolve / free
+ * loop enqueues no allocator work; other memory goes back to the device's memory pool in order
+ * after the work on the build's stream.
  */
 int sparse_indice_map_free(submconv_map_t map);
 

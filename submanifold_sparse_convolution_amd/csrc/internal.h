@@ -234,7 +234,8 @@ inline void map_note_use(submconv_map* map, hipStream_t stream) {
 // stream-ordered allocation.  *got receives the block's size.
 Status map_memory_take(int dev, size_t bytes, hipStream_t stream, void** ptr, size_t* got);
 // Gives a map's rulebook memory back: into the device's cache, tagged with `stream`, when
-// `reusable` (all work on it was on that stream), else back to the pool in stream order.
+// `reusable` (all work on it was on that stream) and the cache has room, else back to the pool in
+// order after the work on `stream`.
 void map_memory_give(int dev, void* ptr, size_t bytes, hipStream_t stream, bool reusable);
 // Host-side checks of a convolution call (subm_conv3d_forward's rules).
 Status check_conv(submconv_map_t map, int64_t n, int ksize, int cin, int cout, int dtype, const void* feats,

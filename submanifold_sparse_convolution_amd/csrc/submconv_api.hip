@@ -236,8 +236,11 @@ static_assert(sizeof(MapHostFlags) == 16 && kSlotPage % sizeof(MapHostFlags) == 
 // block to the stream-ordered pool and allocating it again each enqueue a marker packet (~3 us of
 // idle GPU between two kernels, measured); a cached block costs nothing.  A block is cached only
 // when every use of its map was on the map's own stream, so a later build on that stream writes
-// it after all of them in stream order.  At most kCachedBlocks per device; the oldest goes back
-// to the pool when a new one arrives.
+// it after all of them in stream order.  At most kCachedBlocks per device, kept until a build
+// takes them (or the process ends): a block that does not fit goes back to the pool in order
+// after the work on its stream.  Nothing is ever freed on a stream other than the block's own,
+// whose work may still be running (a stream that is not synchronised with the null stream would
+// not order such a free).
 struct CachedBlock {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -248,9 +251,9 @@ struct BlockCache {
   std::vector<CachedBlock> blocks;
 };
 BlockCache g_blocks[kMaxDevices];
-constexpr size_t kCachedBlocks = 4;
+constexpr size_t kCachedBlocks = 8;
 
-void release_map(submconv_map* m, hipStream_t stream) {
+void release_map(submconv_map* m) {
   if (m->d.ready != nullptr) {
     (void)hipEventSynchronize(m->d.ready);  // the build's own kernels write the map memory
     if (m->d.slot.host == nullptr) (void)hipEventDestroy(m->d.ready);  // a derived map's own event
@@ -258,7 +261,7 @@ void release_map(submconv_map* m, hipStream_t stream) {
   give_flag_slot(m->d.device, m->d.slot);
   map_memory_give(m->d.device, m->d.nbr, m->d.nbr_bytes, m->d.home,
                   !m->other_streams.load(std::memory_order_relaxed));
-  device_free(m->d.pair_out, stream);
+  device_free(m->d.pair_out, m->d.home);  // (work on other streams has completed: the free rules)
   delete m;
 }
 
@@ -292,26 +295,19 @@ Status submconv::map_memory_take(int dev, size_t bytes, hipStream_t stream, void
 
 void submconv::map_memory_give(int dev, void* ptr, size_t bytes, hipStream_t stream, bool reusable) {
   if (ptr == nullptr) return;
-  if (!reusable || dev < 0 || dev >= kMaxDevices) {
-    device_free(ptr, nullptr);
-    return;
-  }
-  CachedBlock evicted;
-  {
+  if (reusable && dev >= 0 && dev < kMaxDevices) {
     BlockCache& cache = g_blocks[dev];
     std::lock_guard<std::mutex> lock(cache.mu);
-    if (cache.blocks.size() >= kCachedBlocks) {
-      evicted = cache.blocks.front();
-      cache.blocks.erase(cache.blocks.begin());
+    if (cache.blocks.size() < kCachedBlocks) {
+      CachedBlock b;
+      b.ptr = ptr;
+      b.bytes = bytes;
+      b.stream = stream;
+      cache.blocks.push_back(b);
+      return;
     }
-    CachedBlock b;
-    b.ptr = ptr;
-    b.bytes = bytes;
-    b.stream = stream;
-    cache.blocks.push_back(b);
   }
-  // (the null stream orders the free after the work of every blocking stream)
-  device_free(evicted.ptr, nullptr);
+  device_free(ptr, stream);
 }
 
 namespace {
@@ -364,7 +360,7 @@ int build_map(const int32_t* coords, int64_t n, int mode, hipStream_t stream, su
   hipError_t e = ws.last == nullptr || hipEventQuery(ws.last) == hipSuccess ? hipSuccess
                                                                             : hipStreamWaitEvent(stream, ws.last, 0);
   if (e != hipSuccess) {
-    release_map(m, stream);
+    release_map(m);
     return fail(hip_status(e, "build events"));
   }
   void* nbr = nullptr;
@@ -375,7 +371,7 @@ int build_map(const int32_t* coords, int64_t n, int mode, hipStream_t stream, su
     s = map_memory_take(m->d.device, (size_t)n * 28 * sizeof(int32_t) + kTapBanks * 27 * sizeof(uint32_t), stream,
                         &nbr, &nbr_bytes);
   if (!s.ok()) {
-    release_map(m, stream);
+    release_map(m);
     return fail(s);
   }
   unsigned char* base = static_cast<unsigned char*>(ws.ptr);
@@ -403,7 +399,7 @@ int build_map(const int32_t* coords, int64_t n, int mode, hipStream_t stream, su
   if (e == hipSuccess) ws.last = m->d.ready;
   if (e != hipSuccess) {
     (void)hipStreamSynchronize(stream);
-    release_map(m, stream);
+    release_map(m);
     return fail(hip_status(e, "indice map build"));
   }
   if (wait) {
@@ -411,7 +407,7 @@ int build_map(const int32_t* coords, int64_t n, int mode, hipStream_t stream, su
     // this event wait.)
     s = check_locked(m->d);
     if (!s.ok()) {
-      release_map(m, stream);
+      release_map(m);
       return fail(s);
     }
   }
@@ -485,7 +481,7 @@ extern "C" int sparse_indice_map_free(submconv_map_t map) {
   clear_error();
   if (map == nullptr) return SUBM_OK;
   DeviceGuard guard(map->d.device);
-  release_map(map, nullptr);
+  release_map(map);
   return SUBM_OK;
 }
 
