@@ -27,6 +27,16 @@
 // Block -> tile mapping is XCD-aware: workgroups are dealt to the 8 XCDs round-robin, so
 // block b goes to tile (b % 8) * per_xcd + b / 8 and each XCD walks one contiguous range of
 // rows, whose neighbourhoods then stay in that XCD's L2.
+//
+// The kernels in this file, from the most general to the default fast path:
+//   subm_conv_generic_kernel        the design above: fp32 storage, odd channel counts,
+//                                   misaligned pointers, tensors beyond 31-bit byte offsets
+//   subm_conv_mma_kernel            16-bit storage: 32x32x16 MFMA tiles fed by direct
+//                                   global->LDS loads (no register staging)
+//   subm_conv_ws_kernel             the same with separate load and matrix-core waves
+//   subm_conv_ws_persistent_kernel  the default for k = 3 above 32 output channels: one
+//                                   workgroup per CU walks several row tiles, eight load waves
+//                                   beside four matrix-core waves
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
