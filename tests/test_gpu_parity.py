@@ -624,3 +624,43 @@ def test_freed_rulebook_memory_is_reused_only_in_stream_order():
     for (name, out), (_, nbr) in zip(outs, nbrs):
         assert np.array_equal(nbr.cpu().numpy(), expect_nbr[name]), name
         assert torch.equal(out.cpu(), expect_out[name]), name
+
+
+# ----------------------------------------------------------------- seeded random sweep
+
+def random_case(seed):
+    # A random set (1-3 batch items, a random box with a negative corner, random occupancy), random
+    # channel counts across every dispatch boundary, and a random storage dtype.
+    rng = np.random.default_rng(1000 + seed)
+    batch = int(rng.integers(1, 4))
+    dims = rng.integers(4, 24, size=3)
+    occ = float(rng.uniform(0.02, 0.6))
+    rows = []
+    for b in range(batch):
+        cells = int(np.prod(dims))
+        k = max(1, int(cells * occ))
+        pick = rng.choice(cells, size=k, replace=False)
+        z, y, x = np.unravel_index(pick, dims)
+        rows.append(np.stack([np.full(k, b), z, y, x], axis=1))
+    coords = np.concatenate(rows).astype(np.int32)
+    coords[:, 1:] += rng.integers(-300, 300, size=3).astype(np.int32)
+    coords = coords[rng.permutation(len(coords))]
+    dtype = ["f32", "f16", "bf16"][seed % 3]
+    cin = int(rng.choice([1, 3, 8, 16, 24, 40, 64, 72, 128, 136]))
+    cout = int(rng.choice([1, 5, 16, 17, 32, 33, 48, 64, 65, 96, 128, 136, 256]))
+    f = synth.round_to(rng.standard_normal((len(coords), cin)), dtype)
+    w = synth.round_to(rng.standard_normal((cout, 3, 3, 3, cin)) / np.sqrt(27 * cin), dtype)
+    b = synth.round_to(rng.standard_normal(cout) * 0.3, dtype)
+    return np.ascontiguousarray(coords), f, w, b, dtype
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_sets_and_shapes_match_the_oracle(seed):
+    coords, f, w, b, dtype = random_case(seed)
+    what = f"seed {seed}: n={len(coords)} {dtype} {f.shape[1]}->{w.shape[0]}"
+    print(what, flush=True)
+    nbr = oracle.rulebook(coords)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        assert np.array_equal(gpu_nbr(m), nbr), what
+        out = forward(m, f, w, b)
+    check(out, oracle.conv3_rulebook(nbr, as64(f), as64(w), as64(b)), dtype, what)
