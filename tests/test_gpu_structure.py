@@ -332,3 +332,39 @@ def test_child_map_argument_errors():
         with pytest.raises(sc.SubmError) as e:
             sc.sparse_indice_map_subdivide(pm, s)
         assert e.value.name == "SUBM_ERR_SHAPE_MISMATCH"
+
+
+# ----------------------------------------------------------------- seeded random sweep
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_sets_downsample_subdivide_and_child_map(seed):
+    # Random sets (1-3 items, random boxes with negative corners and odd sizes, random occupancy,
+    # shuffled rows) through downsample (structure, max, mean, cached upsample), subdivide and the
+    # child map, against the oracle.
+    rng = np.random.default_rng(500 + seed)
+    lo = int(rng.integers(-40, 10))
+    c = shuffled(random_sites(600 + seed, int(rng.integers(1, 4)), lo, lo + int(rng.integers(3, 18)),
+                              float(rng.uniform(0.05, 0.9))), seed)
+    dtype = ["f32", "f16", "bf16"][seed % 3]
+    ch = int(rng.choice([1, 3, 8, 64, 96]))
+    print(f"seed {seed}: n={len(c)} {dtype} C={ch}", flush=True)
+    f = values(len(c), ch, dtype, 700 + seed)
+    f64 = f.double().numpy()
+    coarse, want_max, parent = st.downsample(c, f64, "max")
+    _, want_mean, _ = st.downsample(c, f64, "mean")
+    with sc.sparse_downsample_build(dev_coords(c)) as s:
+        assert np.array_equal(host(s.coarse_coords()).numpy(), coarse)
+        assert np.array_equal(host(s.parent()).numpy(), parent)
+        fd = f.to(DEV)
+        got_max = host(sc.sparse_downsample_forward(s, fd, sc.SUBM_POOL_MAX))
+        got_mean = host(sc.sparse_downsample_forward(s, fd, sc.SUBM_POOL_MEAN))
+        assert np.array_equal(got_max.double().numpy(), want_max)
+        assert oracle.normwise_rel_error(got_mean.double().numpy(), want_mean) <= TOL[dtype]
+        up = host(sc.sparse_upsample_forward(s, got_max.to(DEV)))
+        assert torch.equal(up, got_max[torch.from_numpy(parent)])
+    fine, _, fparent = st.subdivide(c)
+    with sc.sparse_indice_map_build(dev_coords(c)) as m, sc.sparse_subdivide(dev_coords(c)) as s:
+        assert np.array_equal(host(s.fine_coords()).numpy(), fine)
+        assert np.array_equal(host(s.parent()).numpy(), fparent)
+        with sc.sparse_indice_map_subdivide(m, s) as cm:
+            assert np.array_equal(host(sc.sparse_indice_map_copy_nbr(cm)).numpy(), oracle.rulebook(fine))
