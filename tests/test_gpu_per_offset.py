@@ -127,3 +127,29 @@ def test_unsupported_shapes_and_dtypes():
         f, w, b = small("bf16", 16, 16, coords)
         with pytest.raises(ValueError):
             sc.subm_conv3d_forward_per_offset(m, f.to(DEV), w[:, :1, :1, :1].contiguous().to(DEV))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_sets_match_the_oracle_and_the_fused_kernel(seed):
+    # Random sets (1-3 items, random boxes with negative corners, random occupancy, shuffled rows)
+    # and channel counts within the per-offset limits (Cin % 8 == 0, Cout % 4 == 0).
+    rng = np.random.default_rng(800 + seed)
+    rows = []
+    for b in range(int(rng.integers(1, 4))):
+        g = int(rng.integers(4, 20))
+        zyx = np.argwhere(rng.random((g, g, g)) < rng.uniform(0.05, 0.8)) + int(rng.integers(-50, 50))
+        rows.append(np.concatenate([np.full((len(zyx), 1), b), zyx], axis=1))
+    coords = np.concatenate(rows).astype(np.int32)
+    coords = np.ascontiguousarray(coords[rng.permutation(len(coords))])
+    dtype = ["f16", "bf16"][seed % 2]
+    cin = int(rng.choice([8, 16, 40, 64, 128]))
+    cout = int(rng.choice([4, 12, 36, 64, 100, 128]))
+    f, w, b = small(dtype, cin, cout, coords, seed=900 + seed, bias=seed % 3 != 0)
+    what = f"seed {seed}: n={len(coords)} {dtype} {cin}->{cout}"
+    out = run(coords, f, w, b)
+    ref = oracle.conv3_rulebook(oracle.rulebook(coords), as64(f), as64(w), None if b is None else as64(b))
+    check(out, ref, dtype, what)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        fused = sc.subm_conv3d_forward(m, f.to(DEV), w.to(DEV), None if b is None else b.to(DEV))
+        torch.cuda.synchronize()
+    check(out, as64(fused), dtype, what + " vs the output-stationary kernel")
