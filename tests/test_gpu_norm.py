@@ -171,3 +171,23 @@ def test_fused_conv_group_norm(seed, sizes, cin, cout, groups, dtype, act, epilo
     ref = conv_norm_oracle(coords, f, w, b, offsets, groups, gamma, beta, act, dtype)
     check(fused.cpu(), ref, dtype, "fused vs oracle")
     check(split.cpu(), ref, dtype, "conv + norm vs oracle")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_item_splits_and_shapes(seed):
+    # Random row counts split into 1-6 items (empty and one-row items included), random channel
+    # and group counts (rows a multiple of 16 bytes, the kernel's layout rule), dtypes, activations
+    # and means far from zero.
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(1, 6000))
+    cuts = np.sort(rng.integers(0, n + 1, size=int(rng.integers(0, 6))))
+    offsets = [0] + [int(v) for v in cuts] + [n]
+    groups = int(rng.choice([1, 2, 4, 8, 32]))
+    c = int(np.lcm(groups, 8)) * int(rng.choice([1, 2, 3, 4, 8]))
+    dtype = ["f32", "f16", "bf16"][seed % 3]
+    act = ["none", "silu", "relu"][(seed // 3) % 3]
+    x, g, b = inputs(n, c, dtype, 400 + seed, shift=float(rng.uniform(-20, 20)))
+    y = run(x.to(DEV), offsets, groups, g.to(DEV), b.to(DEV), act)
+    ref = norm_ref.group_norm_act(x.double().numpy(), offsets, groups, g.double().numpy(), b.double().numpy(),
+                                  1e-5, act)
+    check(y, ref, dtype, f"seed {seed}: n={n} items={len(offsets) - 1} C={c} G={groups} {dtype} {act}")
