@@ -17,5 +17,7 @@ from .submconv_ref import (  # noqa: F401
     conv3_rulebook,
     conv1,
     normwise_rel_error,
+    elementwise_rel_error,
+    componentwise_ratio,
 )
 from . import structure_ref, norm_ref  # noqa: F401,E402

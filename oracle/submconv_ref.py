@@ -197,3 +197,41 @@ def normwise_rel_error(y, ref) -> float:
     if scale == 0.0:
         return float(diff)
     return float(diff / scale)
+
+
+def elementwise_rel_error(y, ref, floor: float = 1e-2) -> float:
+    """max |y - ref| / |ref| over the entries with |ref| >= floor * max |ref| (0 if there are none).
+
+    A diagnostic beside the normwise figure: it sees a wrong small entry that the normwise ratio
+    hides behind the tensor's largest one, while skipping entries so close to zero that only the
+    componentwise ratio below can judge them.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    a = np.abs(ref)
+    keep = a >= floor * a.max()
+    if not keep.any() or a.max() == 0.0:
+        return 0.0
+    return float(np.max(np.abs(y[keep] - ref[keep]) / a[keep]))
+
+
+def componentwise_ratio(y, ref, magnitude) -> float:
+    """max |y - ref| / magnitude, entry by entry.
+
+    ``magnitude`` is the same sum taken over absolute values, |b| + sum |W| |f| (``conv3`` or
+    ``conv3_rulebook`` called on np.abs of the inputs).  Every rounding of a floating-point
+    evaluation of the sum is bounded by a multiple of that magnitude, so the ratio is bounded
+    even where the sum cancels to near zero.  An entry whose magnitude is 0 must be exact (its
+    ratio is infinite otherwise).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    mag = np.asarray(magnitude, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    diff = np.abs(y - ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(mag > 0.0, diff / np.where(mag > 0.0, mag, 1.0), np.where(diff > 0.0, np.inf, 0.0))
+    return float(r.max())

@@ -340,3 +340,53 @@ def test_normwise_error_definition():
     assert oracle.normwise_rel_error([1.0, -4.0], [1.0, -4.0]) == 0.0
     assert oracle.normwise_rel_error([1.5, -4.0], [1.0, -4.0]) == pytest.approx(0.125)
     assert oracle.normwise_rel_error(np.zeros((0, 3)), np.zeros((0, 3))) == 0.0
+
+
+def test_elementwise_error_definition():
+    ref = np.array([10.0, -0.5, 0.05, 0.0])
+    y = np.array([10.5, -0.45, 1.0, 3.0])
+    # floor 1e-2 keeps |ref| >= 0.1: entries 0 and 1 -> max(0.05, 0.1)
+    assert oracle.elementwise_rel_error(y, ref) == pytest.approx(0.1)
+    # floor 1e-3 also keeps 0.05 (|1.0 - 0.05| / 0.05 = 19)
+    assert oracle.elementwise_rel_error(y, ref, floor=1e-3) == pytest.approx(19.0)
+    assert oracle.elementwise_rel_error(np.zeros(3), np.zeros(3)) == 0.0
+
+
+def test_componentwise_ratio_definition_and_float32_bound():
+    assert oracle.componentwise_ratio([1.0, 0.5], [1.0, 0.25], [2.0, 1.0]) == pytest.approx(0.25)
+    assert oracle.componentwise_ratio([0.0, 1.0], [0.0, 1.0], [0.0, 3.0]) == 0.0
+    assert oracle.componentwise_ratio([1e-30, 1.0], [0.0, 1.0], [0.0, 3.0]) == np.inf
+    # A float32 evaluation of the convolution's sums (products and a left-to-right sum, each
+    # rounded to nearest) stays within gamma_K = K u / (1 - K u) of |b| + sum |W||f|, u = 2^-24,
+    # K = 27 cin + 1 terms, entry by entry (the standard error bound of recursive summation);
+    # the same evaluation with one sign of the magnitude flipped breaks the bound somewhere.
+    coords = np.array([[0, z, y, x] for z in range(4) for y in range(4) for x in range(4) if (x + y + z) % 3], np.int32)
+    rng = np.random.default_rng(21)
+    cin, cout = 16, 8
+    f = rng.standard_normal((len(coords), cin))
+    w = rng.standard_normal((cout, 3, 3, 3, cin))
+    b = rng.standard_normal(cout)
+    nbr = oracle.rulebook(coords)
+    ref = oracle.conv3_rulebook(nbr, f, w, b)
+    mag = oracle.conv3_rulebook(nbr, np.abs(f), np.abs(w), np.abs(b))
+    f32, w32 = f.astype(np.float32), w.astype(np.float32).reshape(cout, 27, cin)
+    y = np.empty_like(ref)
+    for i in range(len(coords)):
+        for o in range(cout):
+            acc = np.float32(b[o])
+            for k in range(27):
+                j = nbr[i, k]
+                if j >= 0:
+                    for c in range(cin):
+                        acc = np.float32(acc + np.float32(w32[o, k, c] * f32[j, c]))
+            y[i, o] = acc
+    # the inputs were rounded to float32 too: compare against the sum of the rounded inputs
+    ref32 = oracle.conv3_rulebook(nbr, f32, w32.reshape(cout, 3, 3, 3, cin), b.astype(np.float32))
+    mag32 = oracle.conv3_rulebook(nbr, np.abs(f32), np.abs(w32).reshape(cout, 3, 3, 3, cin), np.abs(b.astype(np.float32)))
+    u = 2.0 ** -24
+    k_terms = 2 * (27 * cin + 1)  # one rounding per product and one per addition
+    gamma = k_terms * u / (1 - k_terms * u)
+    ratio = oracle.componentwise_ratio(y, ref32, mag32)
+    assert 0.0 < ratio <= gamma
+    assert oracle.componentwise_ratio(y, ref32, mag32 * 1e-6) > gamma  # a magnitude far too small fails
+    assert np.all(mag >= np.abs(ref))
