@@ -167,6 +167,18 @@ int sparse_indice_map_info(submconv_map_t map, int64_t* n, int64_t* pairs);
 int sparse_indice_map_offset_counts(submconv_map_t map, int64_t* counts);
 
 /*
+ * sparse_indice_map_plan_state -- *state (host int) = the state of the map's neighbour-pool plan
+ * (see subm_conv3d_forward): SUBM_PLAN_NONE (no eligible convolution has run on the map yet),
+ * SUBM_PLAN_PENDING (enqueued; the host has not seen its overflow flag yet), SUBM_PLAN_READY
+ * (eligible convolutions take the neighbour-pool kernel) or SUBM_PLAN_OVERFLOW (they take the
+ * general kernels).  Never waits: a pending plan whose kernel has completed becomes READY or
+ * OVERFLOW here.  Source: lato.2_mrp_mlx README, header summary (the structure cached per
+ * coordinate set).
+ */
+enum { SUBM_PLAN_NONE = 0, SUBM_PLAN_PENDING = 1, SUBM_PLAN_READY = 2, SUBM_PLAN_OVERFLOW = 3 };
+int sparse_indice_map_plan_state(submconv_map_t map, int* state);
+
+/*
  * sparse_indice_map_copy_nbr -- copy the rulebook into caller memory.
  *   nbr     device int32 [n, 27] in input row order; nbr[i, k] is the input row of the active
  *           voxel at coord_i + offset(k), or -1.  Independent of any internal ordering.
@@ -190,13 +202,27 @@ int sparse_indice_map_copy_nbr(submconv_map_t map, int32_t* nbr, hipStream_t str
  *   bias     device [cout], or NULL for no bias.
  *   out      device [n, cout]; must not be the same pointer as feats (partial overlap is
  *            undefined).  Fully overwritten.
- *   stream   stream on which the kernel is enqueued.  Never synchronises; validation is on the
- *            host only.  n == 0 returns SUBM_OK with no launch.
+ *   stream   stream on which the kernels are enqueued.  Never synchronises; validation is on the
+ *            host only.  n == 0 returns SUBM_OK with no launch.  Work on another stream than the
+ *            map's build is ordered after the build by the library (a stream wait on the build's
+ *            last kernel, unless it has completed).
  * Row i of out is written only from rows of feats that are neighbours of i, so the result does
  * not depend on launch order and is bitwise reproducible run to run (no float atomics).
- * Tuning and tests: the environment variable SUBMCONV_TILE=<name> forces one of the library's
- * tile configurations, and SUBMCONV_PERSISTENT=0 launches one workgroup per row tile instead of
- * one per compute unit walking several tiles (the two agree bit for bit).
+ * Kernels.  k = 3 with 16-bit storage, cout == 128, cin a multiple of 32, 16-byte aligned
+ * feats / weight / out and at least 131,072 rows take the neighbour-pool kernel: the first such
+ * call on a map enqueues the map's plan (cached with the map, freed with it; device memory of
+ * about 0.3 KB per row), and every call enqueues a small kernel that packs the weights into a
+ * library-owned per-(device, stream) buffer (27 x 128 x cin x 2 bytes, kept for later calls on
+ * that stream) before the convolution.  Until the host has seen the plan's overflow flag (a tile
+ * whose neighbours do not fit the kernel's LDS pool, e.g. rows in random order), the call also
+ * enqueues the general kernel behind it, and each of the two does nothing unless the flags on
+ * the device say it should; sparse_indice_map_plan_state reports the plan's state.  Every other
+ * call takes the general kernels.  Both families compute the same sums (results differ by
+ * summation order only, within the storage rounding).
+ * Tuning and tests: the environment variable SUBMCONV_POOL=0 keeps the general kernels,
+ * SUBMCONV_TILE=<name> forces one of their tile configurations (and the general kernels), and
+ * SUBMCONV_PERSISTENT=0 launches one workgroup per row tile instead of one per compute unit
+ * walking several tiles (the two agree bit for bit).
  * Errors: SUBM_ERR_INVALID_ARG, SUBM_ERR_SHAPE_MISMATCH, SUBM_ERR_UNSUPPORTED, SUBM_ERR_HIP.
  * Source: lato.2_mrp_mlx README, header summary and "Correctness"; trellis_sparse_mrp_mlx
  * commit log, "Extracted from lato.2_mrp_mlx" commit (the 128^3 / 128-channel timing).

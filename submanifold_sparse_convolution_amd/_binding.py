@@ -36,6 +36,7 @@ C_FUNCTIONS = (
     "sparse_indice_map_info",
     "sparse_indice_map_offset_counts",
     "sparse_indice_map_copy_nbr",
+    "sparse_indice_map_plan_state",
     "subm_conv3d_forward",
     "subm_conv3d_forward_per_offset",
     "sparse_subdivide",
@@ -92,6 +93,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.sparse_indice_map_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
         lib.sparse_indice_map_offset_counts.argtypes = [vp, ctypes.POINTER(i64)]
         lib.sparse_indice_map_copy_nbr.argtypes = [vp, vp, vp]
+        lib.sparse_indice_map_plan_state.argtypes = [vp, ctypes.POINTER(ci)]
         lib.subm_conv3d_forward.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp]
         lib.subm_conv3d_forward_per_offset.argtypes = [vp, i64, ci, ci, ci, vp, vp, vp, vp, vp]
         lib.sparse_subdivide.argtypes = [vp, i64, vp, ctypes.POINTER(vp)]
@@ -263,6 +265,17 @@ def sparse_indice_map_mode(m: IndiceMap) -> int:
     mode = ctypes.c_int()
     _check(lib, "sparse_indice_map_mode", lib.sparse_indice_map_mode(m.handle, ctypes.byref(mode)))
     return mode.value
+
+
+SUBM_PLAN_NONE, SUBM_PLAN_PENDING, SUBM_PLAN_READY, SUBM_PLAN_OVERFLOW = 0, 1, 2, 3
+
+
+def sparse_indice_map_plan_state(m: IndiceMap) -> int:
+    """State of the map's neighbour-pool plan: SUBM_PLAN_NONE / _PENDING / _READY / _OVERFLOW."""
+    lib = load_library()
+    state = ctypes.c_int()
+    _check(lib, "sparse_indice_map_plan_state", lib.sparse_indice_map_plan_state(m.handle, ctypes.byref(state)))
+    return state.value
 
 
 def sparse_indice_map_free(m: IndiceMap) -> None:

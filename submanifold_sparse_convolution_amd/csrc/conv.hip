@@ -70,7 +70,16 @@ struct ConvArgs {
   float2* gn_part;
   int gn_cpg;
   int gn_groups;
+  // non-null: flags [gate_n]; the kernel does nothing unless one is set (the fallback launched
+  // beside a neighbour-pool convolution whose plan may have overflowed)
+  const uint32_t* gate;
+  int gate_n;
 };
+
+// (every thread of the workgroup calls it)
+__device__ __forceinline__ bool gated_off(const ConvArgs& a) {
+  return a.gate != nullptr && !pool_any_flag(a.gate, a.gate_n);
+}
 
 constexpr int kThreads = 256;
 constexpr int kStageBytes = 256;  // bytes of one row per stage (16 chunks of 16 B)
@@ -786,6 +795,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void subm_conv_ws_kernel(const ConvA
   __shared__ __align__(16) int32_t s_nbr[TAPS == 27 ? Sh::NBR / 4 : 4];
   __shared__ __align__(16) float s_bias[BN];
   __shared__ uint32_t s_mask;
+  if (gated_off(args)) return;  // (whole workgroup: no barrier has run yet)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1106,6 +1116,7 @@ __global__ __launch_bounds__(64 * (4 + LW), 1) void subm_conv_ws_persistent_kern
   __shared__ __align__(16) int32_t s_nbr[LW * QDMA * 256];  // one slot of QDMA KB per load wave
   __shared__ __align__(16) float s_bias[BN];
   __shared__ uint32_t s_tmask[kMaxBlockTiles];
+  if (gated_off(args)) return;  // (whole workgroup: no barrier has run yet)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1611,7 +1622,7 @@ hipError_t launch_subm_conv_gn_partials(const MapData* map, int64_t n, int ksize
 
 hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, int cout, int dtype,
                             const void* feats, const void* weight, const void* bias, void* out,
-                            hipStream_t stream) {
+                            hipStream_t stream, const uint32_t* gate, int gate_n) {
   const int s = dtype == SUBM_F32 ? 4 : 2;
   ConvArgs a{};
   a.feats = feats;
@@ -1635,6 +1646,8 @@ hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, i
   const uint64_t nb = ksize == 3 ? (uint64_t)n * 27u * 4u : 0u;
   a.feats_bytes = (fb < kOffsetLimit && nb < kOffsetLimit) ? (uint32_t)fb : 0u;
   a.weight_bytes = wb < kOffsetLimit ? (uint32_t)wb : 0u;
+  a.gate = gate;
+  a.gate_n = gate_n;
   switch (dtype) {
     case SUBM_F32: return launch_dtype<DT::F32>(a, vec_in, taps, stream);
     case SUBM_F16: return launch_dtype<DT::F16>(a, vec_in, taps, stream);

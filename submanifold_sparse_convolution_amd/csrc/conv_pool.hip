@@ -1,0 +1,689 @@
+// Neighbour-pool submanifold convolution for 128 output channels, 16-bit storage, gfx950.
+//
+//   out[i, o] = bias[o] + sum_{k : nbr[i,k] >= 0} sum_c W[o, k, c] * f[nbr[i,k], c]
+//
+// (lato.2_mrp_mlx README, header summary and "Correctness": KRSC weights, features gathered at
+// coord_i + d.)  The same sum as the kernels of conv.hip, computed in a different order of
+// memory traffic.
+//
+// Design.  A workgroup (four waves, one per SIMD) owns a tile of 16 or 17 row blocks of 32
+// consecutive rows and all 128 output channels; each wave keeps a 128-row x 128-channel block of
+// fp32 accumulators in its AGPRs (the seventeenth block, when there is one, is shared: each wave
+// holds its 32-channel quarter of it in VGPRs).  The rows that the tile's rows reach through the
+// nine taps of one dz (the tile's "sub-pool" for that dz: at most 768 distinct rows on every
+// workload measured, and sorted by row) are gathered ONCE per 32-channel slice into LDS and read
+// by all nine taps, instead of being gathered again for every tap: the tile's rows reach about
+// 3.1 distinct rows each on the 128^3 shell, against 20.9 gathered per row tap by tap.  A plan,
+// built once per map by pool_plan_kernel, lists each sub-pool's rows and, for every (tap, row),
+// the LDS slot of its neighbour (a zero row when it is absent).
+//
+// The reduction runs over steps (slice q of 32 input channels, dz, the nine (dy, dx) taps): per
+// step a wave issues 2 x 17 v_mfma_f32_32x32x16 (weights as operand A from a 6-slot LDS ring of
+// half-steps, neighbour rows as operand B from the sub-pool), one barrier, and its share of the
+// loads that run ahead: the weight half-steps three steps ahead (weights are pre-packed so that a
+// half-step is one contiguous 4 KB block), one tap of the slot table four steps ahead, two
+// direct-to-LDS gathers of the next sub-pool (steps 0..5 of each nine) and, once per sub-pool,
+// one group of row ids.  Every load goes out behind its own MFMA, so the single wave per SIMD
+// does not stall on a run of loads while its matrix core idles.  A finished tile is rounded
+// (one RNE conversion after + bias in fp32) and written through LDS as whole 256-byte rows.
+//
+// LDS (162,112 bytes): two sub-pool buffers of 769 x 64 bytes (slot 768 is a zero row), the
+// weight ring, the slot table of the current tile, three groups of row ids, the bias.
+#include <hip/hip_ext.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <type_traits>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace submconv {
+namespace {
+
+constexpr int kPT = 256;        // threads: four waves, one per SIMD
+constexpr int kSL = 64;         // bytes of a row per slice (32 channels)
+constexpr int kWH = 128 * 32;   // a weight half-step: 128 output channels x 16 input channels
+constexpr int kWS = 6;          // weight half-steps held in LDS
+constexpr int kUcap = 768;      // rows per sub-pool
+
+template <int E>
+struct PoolShape {
+  static constexpr int NBLK = 16 + E;             // row blocks of 32 per tile
+  static constexpr int TAPB = NBLK * 64;          // slot table bytes per tap (u16 per row)
+  static constexpr int TABB = 27 * TAPB;
+  static constexpr int WSLOTS = kUcap / 4;        // pool slots gathered by one wave
+  static constexpr int NJ = kUcap / 64;           // gather loads per wave per sub-pool
+  static constexpr int IDB = kUcap * 4;           // row ids of one dz group
+  static constexpr int RECB = TABB + 3 * IDB;     // plan record of one tile
+  static constexpr int POOLB = (kUcap + 1) * kSL; // one sub-pool buffer, zero slot last
+  static constexpr int O_W = 2 * POOLB;
+  static constexpr int O_TAB = O_W + kWS * kWH;
+  static constexpr int O_IDS = O_TAB + TABB;
+  static constexpr int O_BIAS = O_IDS + 3 * IDB;
+  static constexpr int LDSB = O_BIAS + 128 * 4;
+  static_assert(kUcap % 64 == 0 && WSLOTS % 16 == 0, "whole gather loads per wave");
+  static_assert(LDSB <= 160 * 1024, "LDS");
+  static_assert((TAPB / 4) % 16 == 0 && (IDB / 4) % 16 == 0, "refills in whole 16-byte lanes");
+  static_assert(NJ == 12, "the load schedule assumes 12 gathers per wave per sub-pool");
+  static_assert(RECB % 16 == 0, "records in whole 16-byte chunks");
+};
+
+// Byte offset of pool slot s in a sub-pool buffer, with the 16-byte chunk index XOR-swizzled by
+// (s >> 2) & 3 so that sixteen consecutive slots read by one quarter-wave hit distinct banks.
+__host__ __device__ constexpr uint32_t slot_offset(uint32_t s) { return s * kSL + (((s >> 2) & 3u) << 4); }
+
+// ------------------------------------------------------------------------------------------
+// Plan: one workgroup per tile.  For each dz the distinct rows nbr[i, 9 dz + j] >= 0 of the
+// tile's rows i are marked in a byte array over [lo, hi] (plain stores: many rows mark the same
+// neighbour), turned into a bitmap with prefix counts, and ranked; the record gets the rows (in
+// the order the gather lanes load them) and the slot table (byte offsets of the slots, slot 768 =
+// the zero row for absent neighbours and rows past the tile).  A sub-pool beyond 768 rows or a
+// range beyond 32,768 rows sets the tile's flag (flags[tile] = 1, else 0) and stores 1 into
+// *host_flag (zeroed by the host).  A thread holds whole rows of the tile's rulebook in registers
+// (one round of loads), so no index is divided and no entry is read twice; 40 KB of LDS lets
+// several workgroups share a compute unit.
+constexpr int kMarkBytes = 32768;
+template <int E>
+__global__ __launch_bounds__(kPT, 4) void pool_plan_kernel(const int32_t* __restrict__ nbr, int64_t n, int nb,
+                                                           int ntiles, unsigned char* __restrict__ plan,
+                                                           uint32_t* __restrict__ flags, uint32_t* host_flag) {
+  using P = PoolShape<E>;
+  constexpr int R = P::NBLK * 32;
+  __shared__ __align__(16) unsigned char mark[kMarkBytes];
+  __shared__ uint32_t bitmap[kMarkBytes / 32];
+  __shared__ uint32_t prefix[kMarkBytes / 32];
+  __shared__ int s_red[8];
+  __shared__ uint32_t s_part[kPT / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tile = blockIdx.x;
+  const int blk0 = (int)((int64_t)tile * nb / ntiles);
+  const int blk1 = (int)((int64_t)(tile + 1) * nb / ntiles);
+  const int64_t r0 = (int64_t)blk0 * 32;
+  const int rows = (int)min((int64_t)(blk1 - blk0) * 32, n - r0);
+  const int32_t* tnbr = nbr + r0 * 27;
+  unsigned char* rec = plan + (size_t)tile * P::RECB;
+  uint16_t* tab = reinterpret_cast<uint16_t*>(rec);
+  int32_t* ids = reinterpret_cast<int32_t*>(rec + P::TABB);
+  // this thread's rows tid + 256 u (u < 3 covers R <= 768), all 27 entries, loaded once
+  constexpr int RU = (R + kPT - 1) / kPT;
+  int nb27[RU][27];
+#pragma unroll
+  for (int u = 0; u < RU; ++u) {
+    const int r = tid + kPT * u;
+#pragma unroll
+    for (int k = 0; k < 27; ++k) nb27[u][k] = r < rows ? tnbr[r * 27 + k] : -1;
+  }
+  bool bad = false;
+#pragma unroll
+  for (int dz = 0; dz < 3; ++dz) {
+    // 1. range of the neighbour rows of this dz
+    int lo = INT32_MAX, hi = -1;
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+      for (int j = 0; j < 9; ++j) {
+        const int v = nb27[u][9 * dz + j];
+        if (v >= 0) {
+          lo = min(lo, v);
+          hi = max(hi, v);
+        }
+      }
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = min(lo, __shfl_xor(lo, off, 64));
+      hi = max(hi, __shfl_xor(hi, off, 64));
+    }
+    if (lane == 0) {
+      s_red[wv] = lo;
+      s_red[4 + wv] = hi;
+    }
+    __syncthreads();
+    lo = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
+    hi = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
+    const int64_t range = hi >= lo ? (int64_t)hi - lo + 1 : 0;
+    const bool fits = range <= kMarkBytes;
+    bad |= !fits;
+    const int nw = fits ? (int)((range + 31) / 32) : 0;  // bitmap words
+    // 2. marks of the rows present
+    for (int k = tid; k < nw * 8; k += kPT) reinterpret_cast<uint32_t*>(mark)[k] = 0u;
+    __syncthreads();
+    if (fits) {
+#pragma unroll
+      for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+          const int v = nb27[u][9 * dz + j];
+          if (v >= 0) mark[v - lo] = 1;
+        }
+    }
+    __syncthreads();
+    // 3. bitmap words and their exclusive prefix counts (each thread owns a run of words)
+    const int per = (nw + kPT - 1) / kPT;
+    uint32_t cnt = 0;
+    for (int k = tid * per; k < min(nw, (tid + 1) * per); ++k) {
+      const uint4 x = reinterpret_cast<const uint4*>(mark)[2 * k];
+      const uint4 y = reinterpret_cast<const uint4*>(mark)[2 * k + 1];
+      const uint32_t m8[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+      uint32_t word = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t m = m8[u];  // four mark bytes, 0 or 1 each
+        word |= ((m & 1u) | ((m >> 7) & 2u) | ((m >> 14) & 4u) | ((m >> 21) & 8u)) << (4 * u);
+      }
+      bitmap[k] = word;
+      cnt += __popc(word);
+    }
+    uint32_t incl = cnt;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_part[wv] = incl;
+    __syncthreads();
+    uint32_t base = incl - cnt;
+    for (int k = 0; k < wv; ++k) base += s_part[k];
+    const uint32_t total = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+    for (int k = tid * per; k < min(nw, (tid + 1) * per); ++k) {
+      prefix[k] = base;
+      base += __popc(bitmap[k]);
+    }
+    bad |= total > (uint32_t)kUcap;
+    __syncthreads();
+    // 4. row ids in gather order: slot s is loaded by wave s / 192, load (s % 192) / 16, lane
+    //    group s % 16, and the ids of a lane group are contiguous; unused slots hold -1
+    int32_t* idz = ids + dz * kUcap;
+    for (int k = tid; k < kUcap; k += kPT) {
+      const uint32_t wg = k / P::WSLOTS, rem = k % P::WSLOTS;
+      int v = -1;
+      if ((uint32_t)k < total) {
+        // the k-th set bit: binary search of the word whose prefix count reaches it
+        int a = 0, b = nw - 1;
+        while (a < b) {
+          const int m = (a + b + 1) >> 1;
+          if (prefix[m] <= (uint32_t)k) a = m;
+          else b = m - 1;
+        }
+        uint32_t word = bitmap[a];
+        for (uint32_t c = prefix[a]; c < (uint32_t)k; ++c) word &= word - 1u;
+        v = lo + a * 32 + __builtin_ctz(word);
+      }
+      idz[(wg * 16 + rem % 16) * P::NJ + rem / 16] = v;
+    }
+    // 5. slot table of the nine taps of this dz (rows past the tile read the zero slot)
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int r = tid + kPT * u;
+      if (r >= R) break;
+#pragma unroll
+      for (int j = 0; j < 9; ++j) {
+        const int vj = fits ? nb27[u][9 * dz + j] : -1;
+        uint32_t slot = kUcap;
+        if (vj >= 0) {
+          const uint32_t d = (uint32_t)(vj - lo);
+          const uint32_t rank = prefix[d >> 5] + __popc(bitmap[d >> 5] & ((1u << (d & 31)) - 1u));
+          slot = rank < (uint32_t)kUcap ? rank : (uint32_t)kUcap;
+        }
+        tab[(9 * dz + j) * R + r] = (uint16_t)slot_offset(slot);
+      }
+    }
+    __syncthreads();  // (marks, bitmap and prefix are reused by the next dz)
+  }
+  if (tid == 0) {
+    flags[tile] = bad ? 1u : 0u;
+    if (bad) *reinterpret_cast<volatile uint32_t*>(host_flag) = 1u;
+  }
+}
+
+// Weights KRSC [128, 27, cin] -> packed [cin / 32][27][2][128][2][16 bytes]: half-step (q, t, kk)
+// is one contiguous 4 KB block; unit u of output channel co holds input channels
+// 32 q + 8 (2 kk + (u ^ ((co >> 3) & 1))) .. + 8 (the XOR makes sixteen consecutive channels'
+// fragment reads hit distinct banks).
+__global__ __launch_bounds__(256) void pool_pack_kernel(const uint4* __restrict__ w, int cin, uint4* __restrict__ wpk) {
+  const int64_t total = (int64_t)(cin / 32) * 27 * 2 * 128 * 2;
+  const int row16 = cin / 8;  // 16-byte chunks per (co, tap) row
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t x = i;
+    const int u = (int)(x & 1);
+    x >>= 1;
+    const int co = (int)(x & 127);
+    x >>= 7;
+    const int kk = (int)(x & 1);
+    x >>= 1;
+    const int t = (int)(x % 27);
+    const int q = (int)(x / 27);
+    const int c = 2 * kk + (u ^ ((co >> 3) & 1));
+    wpk[i] = w[((int64_t)co * 27 + t) * row16 + 4 * q + c];
+  }
+}
+
+struct PoolArgs {
+  const void* feats;
+  const void* wpk;
+  const void* bias;
+  void* out;
+  const unsigned char* plan;
+  const uint32_t* gate;  // non-null: per-tile overflow flags [ntiles]; the kernel does nothing when one is set
+  int64_t n;
+  int row_bytes;
+  int qs;       // slices of 32 input channels
+  int ntiles;
+  int nb;       // row blocks of 32
+  int per_wg;   // tiles per workgroup
+  uint32_t feats_bytes;
+  uint32_t wpk_bytes;
+  uint32_t plan_bytes;
+};
+
+template <int V> using IC = std::integral_constant<int, V>;
+
+// acc += a * b with the accumulator in VGPRs (the AGPRs hold the other sixteen blocks).
+template <DT D>
+__device__ __forceinline__ void mfma32_vgpr(f32x16_t& acc, const uint4& a, const uint4& b) {
+  const i32x4_t av = __builtin_bit_cast(i32x4_t, a), bv = __builtin_bit_cast(i32x4_t, b);
+  if constexpr (D == DT::BF16)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(av), "v"(bv));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(av), "v"(bv));
+}
+
+template <DT D, int E>
+__global__ __launch_bounds__(kPT, 1) void pool_conv_kernel(const PoolArgs a) {
+  using P = PoolShape<E>;
+  using T = typename Elem<D>::T;
+  __shared__ __align__(16) unsigned char lds[P::LDSB];
+
+  const int tid = threadIdx.x;
+  if (a.gate != nullptr && pool_any_flag(a.gate, a.ntiles)) return;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lk = lane >> 5;
+  // Workgroups are dealt to the eight XCDs round-robin: virtual block v takes the tiles
+  // [v per_wg, (v + 1) per_wg), so each XCD walks one contiguous range of rows.
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  const int v = (G % 8 == 0) ? (b & 7) * (G >> 3) + (b >> 3) : b;
+  const int tile0 = v * a.per_wg;
+  const int ntl = min(a.per_wg, a.ntiles - tile0);
+  if (ntl <= 0) return;
+  const int Q = a.qs;
+  const int S = 27 * Q;  // steps per tile
+
+  const uint32_t lbase = lds_offset(lds);
+  const i32x4_t rs_f = make_rsrc(a.feats, a.feats_bytes);
+  const i32x4_t rs_w = make_rsrc(a.wpk, a.wpk_bytes);
+  const i32x4_t rs_p = make_rsrc(a.plan, a.plan_bytes);
+
+  if (tid < 128)
+    reinterpret_cast<float*>(lds + P::O_BIAS)[tid] =
+        a.bias != nullptr ? to_float<D>(reinterpret_cast<const T*>(a.bias)[tid]) : 0.f;
+  if (tid < 8)
+    *reinterpret_cast<uint4*>(lds + (tid >> 2) * P::POOLB + kUcap * kSL + (tid & 3) * 16) = make_uint4(0, 0, 0, 0);
+
+  // Per-lane constants.  A gather lane of load j of wave w fills slot w * 192 + 16 j + lane / 4,
+  // 16-byte unit lane % 4, so it fetches chunk (lane % 4) ^ ((slot >> 2) & 3) = (lane % 4) ^ (lane / 16).
+  const uint32_t gchunk = (uint32_t)(((lane & 3) ^ (lane >> 4)) * 16);
+  // Operand A position j of a wave holds output block (w + j) % 4; its fragment is 16 bytes of
+  // row co of the half-step, unit lk ^ ((co >> 3) & 1).
+  uint32_t a_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int co = 32 * ((w + j) & 3) + lr;
+    a_off[j] = (uint32_t)(co * 32 + ((((co >> 3) & 1) ^ lk) << 4));
+  }
+
+  int ids[P::NJ];
+  auto read_ids = [&](int dz) {
+    const uint4* p = reinterpret_cast<const uint4*>(lds + P::O_IDS + dz * P::IDB + (w * 16 + (lane >> 2)) * P::NJ * 4);
+#pragma unroll
+    for (int u = 0; u < P::NJ / 4; ++u) {
+      const uint4 x = p[u];
+      ids[4 * u] = (int)x.x;
+      ids[4 * u + 1] = (int)x.y;
+      ids[4 * u + 2] = (int)x.z;
+      ids[4 * u + 3] = (int)x.w;
+    }
+  };
+  // gather load j of a sub-pool of slice q into pool buffer buf (live = false: reads nothing)
+  auto gather1 = [&](int j, int q, int buf, bool live) {
+    const uint32_t qoff = (uint32_t)(q * kSL) + gchunk;
+    const uint32_t dst = lbase + (uint32_t)(buf * P::POOLB + w * P::WSLOTS * kSL);
+    const uint32_t off = (live && ids[j] >= 0) ? (uint32_t)ids[j] * (uint32_t)a.row_bytes + qoff : kOutOfRange;
+    lds_dma16(rs_f, off, dst + (uint32_t)(j * 16 * kSL));
+  };
+  // weight half-step (step = q * 27 + t, kk) -> half-slot: one contiguous 4 KB block of the packed
+  // weights (loading the 32-byte runs of the KRSC tensor directly measured 19-20 % slower on the
+  // shell and the dense grid, each load touching 32 cache lines instead of 8)
+  auto issue_w = [&](int step, int kk, int hslot) {
+    const uint32_t src = (uint32_t)(2 * step + kk) * kWH + (uint32_t)(w * 1024) + (uint32_t)lane * 16u;
+    lds_dma16(rs_w, src, lbase + P::O_W + (uint32_t)(hslot * kWH + w * 1024));
+  };
+  // slot-table tap t of a tile (tile < 0: nothing to load)
+  auto issue_table = [&](int tile, int t) {
+    const uint32_t off = tile < 0 ? kOutOfRange
+                                  : (uint32_t)tile * P::RECB + (uint32_t)(t * P::TAPB + w * (P::TAPB / 4)) + (uint32_t)lane * 16u;
+    if (lane < P::TAPB / 64) lds_dma16(rs_p, off, lbase + P::O_TAB + (uint32_t)(t * P::TAPB + w * (P::TAPB / 4)));
+  };
+  // row-id group dz of a tile (tile < 0: nothing to load)
+  auto issue_ids = [&](int tile, int dz) {
+    const uint32_t off = tile < 0 ? kOutOfRange
+                                  : (uint32_t)tile * P::RECB + (uint32_t)(P::TABB + dz * P::IDB + w * (P::IDB / 4)) +
+                                        (uint32_t)lane * 16u;
+    if (lane < P::IDB / 64) lds_dma16(rs_p, off, lbase + P::O_IDS + (uint32_t)(dz * P::IDB + w * (P::IDB / 4)));
+  };
+
+  // ---- prologue: the gathers of the first tile's sub-pool 0 go out as soon as this lane's row
+  // ids arrive (straight from the record); slot-table taps 0..3 (the loop loads each tap four
+  // steps ahead), row-id groups 1 and 2 and the first five weight half-steps follow.
+  {
+    const uint4* rid = reinterpret_cast<const uint4*>(a.plan + (size_t)tile0 * P::RECB + P::TABB +
+                                                      (w * 16 + (lane >> 2)) * P::NJ * 4);
+#pragma unroll
+    for (int u = 0; u < P::NJ / 4; ++u) {
+      const uint4 x = rid[u];
+      ids[4 * u] = (int)x.x;
+      ids[4 * u + 1] = (int)x.y;
+      ids[4 * u + 2] = (int)x.z;
+      ids[4 * u + 3] = (int)x.w;
+    }
+#pragma unroll
+    for (int j = 0; j < P::NJ; ++j) gather1(j, 0, 0, true);
+    const uint4* rec = reinterpret_cast<const uint4*>(a.plan + (size_t)tile0 * P::RECB);
+    uint4* dst = reinterpret_cast<uint4*>(lds + P::O_TAB);
+    for (int i = tid; i < 4 * P::TAPB / 16; i += kPT) dst[i] = rec[i];
+    for (int i = tid; i < 2 * P::IDB / 16; i += kPT) dst[(P::TABB + P::IDB) / 16 + i] = rec[(P::TABB + P::IDB) / 16 + i];
+    const uint4* wsrc = reinterpret_cast<const uint4*>(a.wpk);
+    uint4* wdst = reinterpret_cast<uint4*>(lds + P::O_W);
+    for (int i = tid; i < 5 * kWH / 16; i += kPT) wdst[i] = wsrc[i];  // half-steps (0,0) .. (2,0)
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+
+  f32x16_t acc[4][4];
+  f32x16_t accx;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) accx[e] = 0.f;
+
+  constexpr int NB4 = 4 + E;
+  constexpr int NU = 16 + E;  // MFMAs per half-step
+  uint32_t soff[NB4], soff_n[NB4];
+  uint4 fa[2][4], fb[2][NB4];
+
+  auto read_slots = [&](int t, uint32_t* dst) {
+    const uint16_t* tab = reinterpret_cast<const uint16_t*>(lds + P::O_TAB + t * P::TAPB);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = tab[(4 * w + i) * 32 + lr];
+    if constexpr (E) dst[4] = tab[16 * 32 + lr];
+  };
+  auto read_a = [&](auto SET, int hslot, int j) {
+    constexpr int st = decltype(SET)::value;
+    fa[st][j] = *reinterpret_cast<const uint4*>(lds + P::O_W + hslot * kWH + a_off[j]);
+  };
+  auto read_b = [&](auto SET, int kk, int pbuf, const uint32_t* so, int i) {
+    constexpr int st = decltype(SET)::value;
+    const uint32_t cx = (uint32_t)((2 * kk + lk) << 4);
+    fb[st][i] = *reinterpret_cast<const uint4*>(lds + pbuf * P::POOLB + (so[i] ^ cx));
+  };
+  // MFMAs [LO, HI) of one half-step: unit u = 4 i + j (row block i, operand A position j); unit
+  // 16 is the shared extra block with this wave's own output block.
+  auto mfmas = [&](auto SET, auto LO, auto HI) {
+    constexpr int st = decltype(SET)::value;
+    constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
+#pragma unroll
+    for (int u = lo; u < hi; ++u) {
+      if (u < 16) {
+        acc[u >> 2][u & 3] = mfma32<D>(fa[st][u & 3], fb[st][u >> 2], acc[u >> 2][u & 3]);
+      } else if constexpr (E) {
+        mfma32_vgpr<D>(accx, fa[st][0], fb[st][4]);
+      }
+    }
+  };
+
+  void* out = a.out;
+  const float* s_bias = reinterpret_cast<const float*>(lds + P::O_BIAS);
+  (void)s_bias;
+  // Finished tile: + bias, one rounding.  Each 32-row block of a wave goes through a
+  // wave-private LDS region (rows padded to 272 bytes against bank conflicts), so the stores
+  // are whole 256-byte rows, 16 bytes per lane.  `stage` is the LDS byte offset of the four
+  // regions; no load writes there any more.
+  constexpr int kRowPad = 272;
+  auto write_tile = [&](int tile, int stage) {
+    if constexpr (E) asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");  // the last MFMA into accx is done
+    int lanex = lane;  // (opaque: nothing derived from it is kept live across the main loop)
+    asm volatile("" : "+v"(lanex));
+    const int lrx = lanex & 31, lkx = lanex >> 5;
+    const int blk0 = (int)((int64_t)tile * a.nb / a.ntiles);
+    const int blk1 = (int)((int64_t)(tile + 1) * a.nb / a.ntiles);
+    const int64_t r0 = (int64_t)blk0 * 32;
+    const int valid = (int)min((int64_t)(blk1 - blk0) * 32, a.n - r0);  // rows of this tile
+    unsigned char* obase = reinterpret_cast<unsigned char*>(out) + r0 * 256;
+    const unsigned char* bbase = lds + P::O_BIAS + 16 * lkx;
+    unsigned char* wst = lds + stage + w * 32 * kRowPad;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x16_t& c = acc[i][j];
+        const int ob = (w + j) & 3;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          // accumulator element 4 g + e of lane (lr, lk) = output channel 32 ob + 8 g + 4 lk + e
+          const int cb = 32 * ob + 8 * g;
+          const float4 bb = *reinterpret_cast<const float4*>(bbase + cb * 4);
+          *reinterpret_cast<uint2*>(wst + lrx * kRowPad + cb * 2 + 8 * lkx) =
+              pack4<D>(c[4 * g] + bb.x, c[4 * g + 1] + bb.y, c[4 * g + 2] + bb.z, c[4 * g + 3] + bb.w);
+          c[4 * g] = c[4 * g + 1] = c[4 * g + 2] = c[4 * g + 3] = 0.f;
+        }
+      }
+      const int tr0 = (4 * w + i) * 32;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int rr = 4 * k + (lanex >> 4);
+        const uint4 val = *reinterpret_cast<const uint4*>(wst + rr * kRowPad + (lanex & 15) * 16);
+        if (tr0 + rr < valid) *reinterpret_cast<uint4*>(obase + (uint32_t)((tr0 + rr) * 256 + (lanex & 15) * 16)) = val;
+      }
+    }
+    if constexpr (E) {
+      // block 16: this wave holds output block w of it
+      const int trow = 16 * 32 + lrx;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int cb = 32 * w + 8 * g;
+        const float4 bb = *reinterpret_cast<const float4*>(bbase + cb * 4);
+        if (trow < valid)
+          *reinterpret_cast<uint2*>(obase + (uint32_t)(trow * 256 + cb * 2 + 8 * lkx)) =
+              pack4<D>(accx[4 * g] + bb.x, accx[4 * g + 1] + bb.y, accx[4 * g + 2] + bb.z, accx[4 * g + 3] + bb.w);
+        accx[4 * g] = accx[4 * g + 1] = accx[4 * g + 2] = accx[4 * g + 3] = 0.f;
+      }
+    }
+  };
+
+  // step 0's slots and first half-step fragments, the row ids of the gathers of step 0
+  read_slots(0, soff);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) read_a(IC<0>{}, 0, j);
+#pragma unroll
+  for (int i = 0; i < NB4; ++i) read_b(IC<0>{}, 0, 0, soff, i);
+  read_ids(1);
+
+  // One step (q, dz, g) of tile `tile`; `nxt` is the next tile of this workgroup (-1: none),
+  // `sb` = q * 27 + dz * 9, `pbuf` the pool buffer of this sub-pool.
+  auto step = [&](auto GG, int tile, int nxt, int q, int dz, int sb, int pbuf) {
+    constexpr int g = decltype(GG)::value;
+    // (2 s) mod 6 for the weight half-slots: S is a multiple of 3, so it is 2 (g mod 3)
+    constexpr int hs = 2 * (g % 3);
+    // Loads per step, in this order: 2 weight half-steps, 1 slot-table tap, 2 gathers of the
+    // next sub-pool (g <= 5, possibly reading nothing), 1 row-id group (g == 0).  Wait until this
+    // wave's loads of the weight half-steps (s, 1) and (s + 1, 0), the first two of step s - 2,
+    // have landed (vector-memory loads complete in order), then the barrier makes every wave's
+    // share visible and frees the slots the loads below overwrite.
+    constexpr int cnt[9] = {6, 5, 5, 5, 5, 5, 3, 3, 3};
+    constexpr int N = cnt[(g + 7) % 9] - 2 + cnt[(g + 8) % 9];
+    wait_vmcnt<N>();
+    barrier_no_fence();
+    const bool last = q == Q - 1;
+    const int src = last ? nxt : tile;
+    const int t = dz * 9 + g;
+    const int sl = sb + g;
+    const int pbuf1 = g == 8 ? (pbuf ^ 1) : pbuf;
+    const int hs1 = hs + 1, hs2 = hs + 2 == kWS ? 0 : hs + 2;
+    const int nq = dz == 2 ? (last ? 0 : q + 1) : q;  // slice of the next sub-pool
+    const bool glive = !(dz == 2 && last) || nxt >= 0;
+    // ---- first half: MFMAs of (s, 0).  Each MFMA is followed by one LDS read of (s, 1) (the
+    // first nine) or by one load of this step (the next six); scheduling barriers fix the order.
+    // The slots of step s + 1 are read first: the second half needs them.
+    read_slots(t == 26 ? 0 : t + 1, soff_n);
+    auto one = [&](auto SETM, auto U) {
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(SETM, U, IC<decltype(U)::value + 1>{});
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    one(IC<0>{}, IC<0>{}); read_a(IC<1>{}, hs1, 0);
+    one(IC<0>{}, IC<1>{}); read_a(IC<1>{}, hs1, 1);
+    one(IC<0>{}, IC<2>{}); read_a(IC<1>{}, hs1, 2);
+    one(IC<0>{}, IC<3>{}); read_a(IC<1>{}, hs1, 3);
+    one(IC<0>{}, IC<4>{}); read_b(IC<1>{}, 1, pbuf, soff, 0);
+    one(IC<0>{}, IC<5>{}); read_b(IC<1>{}, 1, pbuf, soff, 1);
+    one(IC<0>{}, IC<6>{}); read_b(IC<1>{}, 1, pbuf, soff, 2);
+    one(IC<0>{}, IC<7>{}); read_b(IC<1>{}, 1, pbuf, soff, 3);
+    one(IC<0>{}, IC<8>{}); if constexpr (E) read_b(IC<1>{}, 1, pbuf, soff, 4);
+    // weight half-steps (s + 3, 0) into the half-slot of (s, 0), read last step, and (s + 2, 1)
+    // into the half-slot of (s - 1, 1)
+    one(IC<0>{}, IC<9>{}); issue_w(sl + 3 < S ? sl + 3 : sl + 3 - S, 0, hs);
+    one(IC<0>{}, IC<10>{}); issue_w(sl + 2 < S ? sl + 2 : sl + 2 - S, 1, hs == 0 ? kWS - 1 : hs - 1);
+    // slot-table tap of step s + 4 (the next slice's, or the next tile's in the last slice)
+    one(IC<0>{}, IC<11>{}); issue_table(t >= 23 && last ? nxt : tile, t >= 23 ? t - 23 : t + 4);
+    // gathers of the next sub-pool: (q, dz + 1), (q + 1, 0) or the next tile's (0, 0); its row
+    // ids were read at the end of the previous sub-pool
+    one(IC<0>{}, IC<12>{}); if constexpr (g <= 5) gather1(2 * g, nq, pbuf ^ 1, glive);
+    one(IC<0>{}, IC<13>{}); if constexpr (g <= 5) gather1(2 * g + 1, nq, pbuf ^ 1, glive);
+    one(IC<0>{}, IC<14>{}); if constexpr (g == 0) issue_ids(src, dz);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(IC<0>{}, IC<15>{}, IC<NU>{});
+    // ---- second half: MFMAs of (s, 1), each of the first nine followed by one read of (s + 1, 0)
+    one(IC<1>{}, IC<0>{}); read_a(IC<0>{}, hs2, 0);
+    one(IC<1>{}, IC<1>{}); read_a(IC<0>{}, hs2, 1);
+    one(IC<1>{}, IC<2>{}); read_a(IC<0>{}, hs2, 2);
+    one(IC<1>{}, IC<3>{}); read_a(IC<0>{}, hs2, 3);
+    one(IC<1>{}, IC<4>{}); read_b(IC<0>{}, 0, pbuf1, soff_n, 0);
+    one(IC<1>{}, IC<5>{}); read_b(IC<0>{}, 0, pbuf1, soff_n, 1);
+    one(IC<1>{}, IC<6>{}); read_b(IC<0>{}, 0, pbuf1, soff_n, 2);
+    one(IC<1>{}, IC<7>{}); read_b(IC<0>{}, 0, pbuf1, soff_n, 3);
+    one(IC<1>{}, IC<8>{}); if constexpr (E) read_b(IC<0>{}, 0, pbuf1, soff_n, 4);
+    one(IC<1>{}, IC<9>{}); if constexpr (g == 8) read_ids(dz == 0 ? 2 : dz - 1);  // the next sub-pool's gathers
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(IC<1>{}, IC<10>{}, IC<NU>{});
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NB4; ++i) soff[i] = soff_n[i];
+  };
+
+  int pb = 0;
+  for (int ti = 0; ti < ntl; ++ti) {
+    const int tile = tile0 + ti;
+    const int nxt = ti + 1 < ntl ? tile + 1 : -1;
+    for (int q = 0; q < Q; ++q) {
+      for (int dz = 0; dz < 3; ++dz) {
+        const int sb = q * 27 + dz * 9;
+        step(IC<0>{}, tile, nxt, q, dz, sb, pb);
+        step(IC<1>{}, tile, nxt, q, dz, sb, pb);
+        step(IC<2>{}, tile, nxt, q, dz, sb, pb);
+        step(IC<3>{}, tile, nxt, q, dz, sb, pb);
+        step(IC<4>{}, tile, nxt, q, dz, sb, pb);
+        step(IC<5>{}, tile, nxt, q, dz, sb, pb);
+        step(IC<6>{}, tile, nxt, q, dz, sb, pb);
+        step(IC<7>{}, tile, nxt, q, dz, sb, pb);
+        step(IC<8>{}, tile, nxt, q, dz, sb, pb);
+        pb ^= 1;
+      }
+    }
+    // The buffer of the tile's last sub-pool (pb ^ 1 after the toggle) is free once every wave
+    // has finished reading it; the next tile's sub-pool 0 is in pb.
+    barrier_no_fence();
+    write_tile(tile, (pb ^ 1) * P::POOLB);
+  }
+  wait_vmcnt<0>();  // no direct-to-LDS load may still be in flight when the workgroup ends
+}
+
+}  // namespace
+
+bool pool_tiling(int64_t n, PoolTiling* t) {
+  const int64_t nb = (n + 31) / 32;
+  if (nb < 256 * 16) return false;  // fewer than one full tile per compute unit
+  const int64_t per_cu = (nb + 255) / 256;
+  const int64_t k = (per_cu + 16) / 17;
+  const int64_t T = std::min<int64_t>(256 * k, (nb + 15) / 16);
+  const int64_t recb = (nb + T - 1) / T > 16 ? PoolShape<1>::RECB : PoolShape<0>::RECB;
+  if (T * recb >= (int64_t)0x7FFFF000) return false;  // records addressed with 31-bit offsets
+  if (nb >= ((int64_t)1 << 31) / 32 / 27) return false;  // (row indices of the rulebook are int32)
+  t->nb = (int)nb;
+  t->ntiles = (int)T;
+  t->per_wg = (int)((T + 255) / 256);
+  t->e = (nb + T - 1) / T > 16 ? 1 : 0;
+  return true;
+}
+
+static size_t pool_records_bytes(const PoolTiling& t) {
+  return (size_t)t.ntiles * (size_t)(t.e ? PoolShape<1>::RECB : PoolShape<0>::RECB);
+}
+
+size_t pool_plan_bytes(const PoolTiling& t) { return pool_records_bytes(t) + ((size_t)t.ntiles * 4 + 255) / 256 * 256; }
+
+uint32_t* pool_tile_flags(const PoolTiling& t, void* plan) {
+  return reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(plan) + pool_records_bytes(t));
+}
+
+size_t pool_weight_bytes(int cin) { return (size_t)27 * 128 * (size_t)cin * 2; }
+
+hipError_t launch_pool_plan(const int32_t* nbr, int64_t n, const PoolTiling& t, void* plan, uint32_t* host_flag,
+                            hipEvent_t done, hipStream_t stream) {
+  auto* rec = static_cast<unsigned char*>(plan);
+  uint32_t* flags = pool_tile_flags(t, plan);
+  if (t.e)
+    hipExtLaunchKernelGGL(pool_plan_kernel<1>, dim3((unsigned)t.ntiles), dim3(kPT), 0, stream, nullptr, done, 0u, nbr,
+                          n, t.nb, t.ntiles, rec, flags, host_flag);
+  else
+    hipExtLaunchKernelGGL(pool_plan_kernel<0>, dim3((unsigned)t.ntiles), dim3(kPT), 0, stream, nullptr, done, 0u, nbr,
+                          n, t.nb, t.ntiles, rec, flags, host_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_conv(const PoolTiling& t, const void* plan, const uint32_t* gate, int64_t n, int cin, int dtype,
+                            const void* feats, const void* weight, const void* bias, void* out, void* wpk,
+                            hipStream_t stream) {
+  const size_t wbytes = pool_weight_bytes(cin);
+  const int64_t units = (int64_t)(wbytes / 16);
+  pool_pack_kernel<<<(unsigned)std::min<int64_t>((units + 255) / 256, 1024), 256, 0, stream>>>(
+      static_cast<const uint4*>(weight), cin, static_cast<uint4*>(wpk));
+  PoolArgs a{};
+  a.feats = feats;
+  a.wpk = wpk;
+  a.bias = bias;
+  a.out = out;
+  a.plan = static_cast<const unsigned char*>(plan);
+  a.gate = gate;
+  a.n = n;
+  a.row_bytes = cin * 2;
+  a.qs = cin / 32;
+  a.ntiles = t.ntiles;
+  a.nb = t.nb;
+  a.per_wg = t.per_wg;
+  a.feats_bytes = (uint32_t)((uint64_t)n * (uint64_t)cin * 2);
+  a.wpk_bytes = (uint32_t)wbytes;
+  a.plan_bytes = (uint32_t)pool_records_bytes(t);
+  const dim3 grid((unsigned)((t.ntiles + t.per_wg - 1) / t.per_wg));
+  if (dtype == SUBM_BF16) {
+    if (t.e) pool_conv_kernel<DT::BF16, 1><<<grid, kPT, 0, stream>>>(a);
+    else pool_conv_kernel<DT::BF16, 0><<<grid, kPT, 0, stream>>>(a);
+  } else {
+    if (t.e) pool_conv_kernel<DT::F16, 1><<<grid, kPT, 0, stream>>>(a);
+    else pool_conv_kernel<DT::F16, 0><<<grid, kPT, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace submconv

@@ -135,4 +135,17 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }
 
+// Whether any of flags[0 .. count) is nonzero, the same answer in every thread of the workgroup.
+// Every thread of the workgroup must call it: it synchronises the workgroup.
+__device__ __forceinline__ bool pool_any_flag(const uint32_t* flags, int count) {
+  __shared__ uint32_t s_any;
+  if (threadIdx.x == 0) s_any = 0u;
+  __syncthreads();
+  uint32_t v = 0u;
+  for (int k = threadIdx.x; k < count; k += blockDim.x) v |= flags[k];
+  if (v != 0u) s_any = 1u;  // (every writer stores 1)
+  __syncthreads();
+  return s_any != 0u;
+}
+
 }  // namespace submconv

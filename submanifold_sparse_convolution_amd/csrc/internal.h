@@ -109,6 +109,16 @@ struct FlagSlot {
   hipEvent_t ready = nullptr;     // recorded after the build's last kernel
 };
 
+// Tiling of the neighbour-pool convolution (conv_pool.hip): tile t covers row blocks of 32
+// [t nb / ntiles, (t + 1) nb / ntiles) (16 or 17 blocks; e = 1 when some tile has 17), workgroup
+// v takes tiles [v per_wg, (v + 1) per_wg).
+struct PoolTiling {
+  int nb = 0;
+  int ntiles = 0;
+  int per_wg = 0;
+  int e = 0;
+};
+
 // Map handle contents.
 struct MapData {
   int device = 0;
@@ -140,6 +150,14 @@ struct MapData {
   int32_t* pair_out = nullptr;
   int32_t* pair_in = nullptr;
   int64_t pair_off[27] = {};
+  // Neighbour-pool plan of the 128-channel convolution (conv_pool.hip), built by the first
+  // convolution that takes that path.  pool_state: 0 not built, 1 built but its overflow flag
+  // not read yet, 2 usable, 3 a sub-pool overflowed (that map keeps the conv.hip kernels).
+  int pool_state = 0;
+  PoolTiling pool_tiling;
+  void* pool_plan = nullptr;
+  hipStream_t pool_stream = nullptr;  // the stream the plan kernel ran on
+  FlagSlot pool_slot;  // .host->flags / .dev: the overflow flag; .ready: the plan kernel's completion
 };
 
 // Map build (indice_map.hip).  Enqueues on `stream`; does not synchronise.  `table` holds
@@ -185,10 +203,36 @@ hipError_t launch_subm_conv_gn_partials(const MapData* map, int64_t n, int ksize
                                         const void* feats, const void* weight, const void* bias, void* out,
                                         float2* part, int cpg, int groups, int* tile_rows, hipStream_t stream);
 
-// Convolution launcher (conv.hip).  Arguments already validated by the caller.
+// Convolution launcher (conv.hip).  Arguments already validated by the caller.  gate != null:
+// flags [gate_n]; the launched kernels do nothing unless one of them is set (the fallback of a
+// neighbour-pool launch whose plan may have overflowed; only the 16-bit k = 3 path above 64
+// output channels takes it).
 hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, int cout, int dtype,
                             const void* feats, const void* weight, const void* bias, void* out,
+                            hipStream_t stream, const uint32_t* gate = nullptr, int gate_n = 0);
+
+
+// Neighbour-pool convolution (conv_pool.hip): k = 3, 16-bit storage, cout == 128, cin % 32 == 0.
+// pool_tiling: false when n is too small (fewer than one full tile per compute unit) or the plan
+// would exceed 31-bit offsets.  launch_pool_plan writes the plan of map rows nbr [n, 27] (plan:
+// pool_plan_bytes(t)): the tile records and per-tile overflow flags (pool_tile_flags), and stores
+// 1 into *host_flag (pinned, zeroed by the caller) when a tile's sub-pool does not fit; `done`
+// records its completion.  launch_pool_conv packs the weights into wpk (pool_weight_bytes(cin))
+// and runs the convolution; gate != null: the tile flags, the kernel does nothing if one is set.
+bool pool_tiling(int64_t n, PoolTiling* t);
+size_t pool_plan_bytes(const PoolTiling& t);
+uint32_t* pool_tile_flags(const PoolTiling& t, void* plan);
+size_t pool_weight_bytes(int cin);
+hipError_t launch_pool_plan(const int32_t* nbr, int64_t n, const PoolTiling& t, void* plan, uint32_t* host_flag,
+                            hipEvent_t done, hipStream_t stream);
+hipError_t launch_pool_conv(const PoolTiling& t, const void* plan, const uint32_t* gate, int64_t n, int cin, int dtype,
+                            const void* feats, const void* weight, const void* bias, void* out, void* wpk,
                             hipStream_t stream);
+
+// Per-(device, stream) scratch of at least `bytes`, reused by every call on that stream (work on
+// one stream is ordered, so a later call cannot overwrite it while an earlier one still reads
+// it); grows by a stream-ordered free and allocation (submconv_api.hip).
+Status stream_scratch(int dev, hipStream_t stream, size_t bytes, void** ptr);
 
 }  // namespace submconv
 
@@ -226,8 +270,14 @@ Status map_counts(submconv_map* map);
 // Records that work reading the map's memory is enqueued on `stream` (every entry point that
 // reads a map calls it before enqueuing); a map used only on the stream of its build gives its
 // memory back to the per-device block cache when freed (map_memory_give).
+// Work enqueued on another stream than the build's is also ordered after the build: the stream
+// waits for the build's last kernel unless it has already completed.
 inline void map_note_use(submconv_map* map, hipStream_t stream) {
-  if (map != nullptr && stream != map->d.home) map->other_streams.store(true, std::memory_order_relaxed);
+  if (map != nullptr && stream != map->d.home) {
+    map->other_streams.store(true, std::memory_order_relaxed);
+    if (map->d.ready != nullptr && hipEventQuery(map->d.ready) != hipSuccess)
+      (void)hipStreamWaitEvent(stream, map->d.ready, 0);
+  }
 }
 // Memory for a map's rulebook on device `dev`: a cached block of a freed map that was built and
 // used only on `stream` when one fits (no allocator call, so nothing is enqueued), else a new

@@ -1,6 +1,7 @@
 // C ABI entry points: argument validation, status codes, device memory, the map handle.
 // Every check that does not need the GPU runs before any HIP call, so invalid arguments are
 // rejected identically on a machine without a GPU.
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -259,13 +260,66 @@ void release_map(submconv_map* m) {
     if (m->d.slot.host == nullptr) (void)hipEventDestroy(m->d.ready);  // a derived map's own event
   }
   give_flag_slot(m->d.device, m->d.slot);
+  if (m->d.pool_slot.ready != nullptr) (void)hipEventSynchronize(m->d.pool_slot.ready);  // the plan kernel
+  give_flag_slot(m->d.device, m->d.pool_slot);
   map_memory_give(m->d.device, m->d.nbr, m->d.nbr_bytes, m->d.home,
                   !m->other_streams.load(std::memory_order_relaxed));
   device_free(m->d.pair_out, m->d.home);  // (work on other streams has completed: the free rules)
+  device_free(m->d.pool_plan, m->d.home);
   delete m;
 }
 
 }  // namespace
+
+namespace {
+// Per-(device, stream) scratch buffers (packed weights of the neighbour-pool convolution): at
+// most kScratchStreams per device; the oldest goes back to the pool, in order after the work on
+// its own stream, when a new stream needs one.
+struct ScratchEntry {
+  hipStream_t stream = nullptr;
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+struct ScratchCache {
+  std::mutex mu;
+  std::vector<ScratchEntry> entries;
+};
+ScratchCache g_scratch[kMaxDevices];
+constexpr size_t kScratchStreams = 16;
+}  // namespace
+
+Status submconv::stream_scratch(int dev, hipStream_t stream, size_t bytes, void** ptr) {
+  *ptr = nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return make_status(SUBM_ERR_HIP, "device ordinal out of range");
+  ScratchCache& c = g_scratch[dev];
+  std::lock_guard<std::mutex> lock(c.mu);
+  for (size_t i = 0; i < c.entries.size(); ++i) {
+    ScratchEntry& e = c.entries[i];
+    if (e.stream != stream) continue;
+    if (e.bytes >= bytes) {
+      *ptr = e.ptr;
+      return Status{};
+    }
+    device_free(e.ptr, e.stream);  // in order after this stream's earlier work
+    c.entries.erase(c.entries.begin() + i);
+    break;
+  }
+  if (c.entries.size() >= kScratchStreams) {
+    device_free(c.entries.front().ptr, c.entries.front().stream);
+    c.entries.erase(c.entries.begin());
+  }
+  const size_t want = round_up(bytes, size_t(1) << 20);
+  void* p = nullptr;
+  Status s = device_alloc(&p, want, stream);
+  if (!s.ok()) return s;
+  ScratchEntry e;
+  e.stream = stream;
+  e.ptr = p;
+  e.bytes = want;
+  c.entries.push_back(e);
+  *ptr = p;
+  return Status{};
+}
 
 Status submconv::map_memory_take(int dev, size_t bytes, hipStream_t stream, void** ptr, size_t* got) {
   *ptr = nullptr;
@@ -547,6 +601,71 @@ Status submconv::check_conv(submconv_map_t map, int64_t n, int ksize, int cin, i
   return Status{};
 }
 
+namespace {
+
+// Whether a convolution takes the neighbour-pool kernel (conv_pool.hip): k = 3, 16-bit storage,
+// 128 output channels, cin a multiple of 32, 16-byte aligned tensors, features within 31-bit
+// offsets, enough rows for one full tile per compute unit, and a plan that did not overflow.
+// SUBMCONV_POOL=0 or a forced conv.hip tile (SUBMCONV_TILE) keep the conv.hip kernels.
+bool pool_eligible(const submconv_map* map, int64_t n, int ksize, int cin, int cout, int dtype, const void* feats,
+                   const void* weight, const void* out) {
+  if (map == nullptr || ksize != 3 || cout != 128 || (dtype != SUBM_BF16 && dtype != SUBM_F16)) return false;
+  if (cin < 32 || cin % 32 != 0 || map->d.pool_state == 3) return false;
+  if (((reinterpret_cast<uintptr_t>(feats) | reinterpret_cast<uintptr_t>(weight) | reinterpret_cast<uintptr_t>(out)) &
+       15u) != 0)
+    return false;
+  if ((uint64_t)n * (uint64_t)cin * 2u >= 0x7FFFF000ull) return false;
+  const char* v = std::getenv("SUBMCONV_POOL");
+  if ((v != nullptr && v[0] == '0') || std::getenv("SUBMCONV_TILE") != nullptr) return false;
+  PoolTiling t;
+  return pool_tiling(n, &t);
+}
+
+// Builds the map's plan on first use (enqueued on `stream`; the overflow flag arrives in the
+// plan's pinned word) and reads the flag once the plan kernel has completed.  Returns the
+// map's pool_state (1: built, flag not read yet; 2: usable; 3: overflowed).
+Status pool_prepare(submconv_map* map, hipStream_t stream, int* state) {
+  std::lock_guard<std::mutex> lock(map->mu);
+  MapData& d = map->d;
+  if (d.pool_state == 0) {
+    PoolTiling t;
+    if (!pool_tiling(d.n, &t)) return make_status(SUBM_ERR_HIP, "internal error: no neighbour-pool tiling");
+    Status s = take_flag_slot(d.device, &d.pool_slot);
+    if (!s.ok()) return s;
+    d.pool_slot.host->flags = 0u;
+    s = device_alloc(&d.pool_plan, pool_plan_bytes(t), stream);
+    if (!s.ok()) {
+      give_flag_slot(d.device, d.pool_slot);
+      return s;
+    }
+    const hipError_t e = launch_pool_plan(d.nbr, d.n, t, d.pool_plan, &d.pool_slot.dev->flags, d.pool_slot.ready, stream);
+    if (e != hipSuccess) return hip_status(e, "neighbour-pool plan");
+    d.pool_tiling = t;
+    d.pool_state = 1;
+    d.pool_stream = stream;
+  }
+  if (d.pool_state == 1 && hipEventQuery(d.pool_slot.ready) == hipSuccess)
+    d.pool_state = reinterpret_cast<volatile MapHostFlags*>(d.pool_slot.host)->flags != 0u ? 3 : 2;
+  // work on another stream than the plan's waits for the plan kernel
+  if (d.pool_state == 1 && stream != d.pool_stream) SUBM_HIP_TRY(hipStreamWaitEvent(stream, d.pool_slot.ready, 0));
+  *state = d.pool_state;
+  return Status{};
+}
+
+}  // namespace
+
+extern "C" int sparse_indice_map_plan_state(submconv_map_t map, int* state) {
+  clear_error();
+  if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
+  if (state == nullptr) return fail(SUBM_ERR_INVALID_ARG, "state is NULL");
+  std::lock_guard<std::mutex> lock(map->mu);
+  MapData& d = map->d;
+  if (d.pool_state == 1 && hipEventQuery(d.pool_slot.ready) == hipSuccess)
+    d.pool_state = reinterpret_cast<volatile MapHostFlags*>(d.pool_slot.host)->flags != 0u ? 3 : 2;
+  *state = d.pool_state;
+  return SUBM_OK;
+}
+
 extern "C" int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int cin, int cout, int dtype,
                                    const void* feats, const void* weight, const void* bias, void* out,
                                    hipStream_t stream) {
@@ -555,6 +674,28 @@ extern "C" int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int
   if (!s.ok()) return fail(s);
   if (n == 0) return SUBM_OK;
   map_note_use(map, stream);
+  if (pool_eligible(map, n, ksize, cin, cout, dtype, feats, weight, out)) {
+    // (the plan needs no coordinate check first: every rulebook entry is -1 or a row of the set,
+    // whatever the coordinates were)
+    int state = 0;
+    s = pool_prepare(map, stream, &state);
+    if (!s.ok()) return fail(s);
+    if (state != 3) {
+      void* wpk = nullptr;
+      s = stream_scratch(map->d.device, stream, pool_weight_bytes(cin), &wpk);
+      if (!s.ok()) return fail(s);
+      // state 1: the plan's flags are not known on the host yet, so the conv.hip kernel is launched
+      // behind the pool kernel and each of the two runs only if the tile flags say it should
+      const uint32_t* gate = state == 1 ? pool_tile_flags(map->d.pool_tiling, map->d.pool_plan) : nullptr;
+      hipError_t e = launch_pool_conv(map->d.pool_tiling, map->d.pool_plan, gate, n, cin, dtype, feats, weight, bias, out,
+                                      wpk, stream);
+      if (e == hipSuccess && gate != nullptr)
+        e = launch_subm_conv(&map->d, n, ksize, cin, cout, dtype, feats, weight, bias, out, stream, gate,
+                             map->d.pool_tiling.ntiles);
+      if (e != hipSuccess) return fail(hip_status(e, "subm_conv3d_forward launch"));
+      return SUBM_OK;
+    }
+  }
   hipError_t e = launch_subm_conv(map == nullptr ? nullptr : &map->d, n, ksize, cin, cout, dtype, feats, weight, bias, out, stream);
   if (e != hipSuccess) return fail(hip_status(e, "subm_conv3d_forward launch"));
   return SUBM_OK;

@@ -3,13 +3,14 @@
 Rulebook: bit-exact.  Features: normwise relative error max|y - ref| / max|ref|
 against the float64 oracle on the same rounded inputs, at most 1e-5 for fp32
 storage and 1e-2 for fp16 / bf16 storage (fp32 accumulation, one rounding to
-the storage dtype at the end: the rounding alone contributes up to 2^-9 for
-bf16 and 2^-11 for fp16).
+the storage dtype at the end: the rounding alone contributes up to 2^-8 for
+bf16 and 2^-11 for fp16), plus the componentwise bound and the elementwise
+diagnostic of tests/parity_util.py.
 
-Small configurations are compared in full.  At the full multi-million-voxel
-sizes (the launch configuration the benchmark times) the rulebook is still
-compared in full, and the features on sampled rows (first and last tiles plus
-random rows) that the oracle computes one by one.
+Every row of every configuration is compared with the oracle, the
+multi-million-voxel ones included (the oracle's sums run in row chunks on the
+host's threads); the componentwise bound is taken on sampled rows there (first
+and last tiles plus random rows) and on all rows elsewhere.
 """
 import functools
 
@@ -20,6 +21,7 @@ import torch
 import oracle
 import submanifold_sparse_convolution_amd as sc
 import synth
+from parity_util import check_features
 
 pytestmark = pytest.mark.gpu
 
@@ -134,6 +136,7 @@ def test_config1_tiny_fp32_full():
     with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
         out = forward(m, f, w, b)
     check(out, oracle.conv3(coords, as64(f), as64(w), as64(b)), "f32", "config 1")
+    check_features(out, oracle_nbr("1"), as64(f), as64(w), as64(b), "f32", "config 1")
 
 
 def test_config2_fp16_k3_and_k1_full():
@@ -144,7 +147,7 @@ def test_config2_fp16_k3_and_k1_full():
         out3 = forward(m, f3, w3, b3)
         out1 = forward(m, f1, w1, b1)
     out1_nomap = forward(None, f1, w1, b1)
-    check(out3, oracle.conv3_rulebook(oracle_nbr("2a"), as64(f3), as64(w3), as64(b3)), "f16", "config 2a k3")
+    check_features(out3, oracle_nbr("2a"), as64(f3), as64(w3), as64(b3), "f16", "config 2a k3")
     ref1 = oracle.conv1(as64(f1), as64(w1), as64(b1))
     check(out1, ref1, "f16", "config 2b k1")
     assert torch.equal(out1, out1_nomap)
@@ -155,54 +158,54 @@ def test_config3a_shell_bf16_full():
     f, w, b = cfg_tensors("3a", 0)
     with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
         out = forward(m, f, w, b)
-    check(out, oracle.conv3_rulebook(oracle_nbr("3a"), as64(f), as64(w), as64(b)), "bf16", "config 3a")
+    check_features(out, oracle_nbr("3a"), as64(f), as64(w), as64(b), "bf16", "config 3a")
     # spot-check the sampled-row path against the dictionary oracle as well
     rows = sample_rows(len(coords), count=256)
     check(out[rows], oracle.conv3(coords, as64(f), as64(w), as64(b), rows=rows), "bf16", "config 3a (dict rows)")
 
 
-def test_config3b_dense_bf16_sampled():
+def test_config3b_dense_bf16_full():
     coords = coords_of("3b")
     f, w, b = cfg_tensors("3b", 0)
     with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
         out = forward(m, f, w, b)
-    rows = sample_rows(len(coords))
-    check(out[rows], oracle.conv3_rulebook(oracle_nbr("3b"), as64(f), as64(w), as64(b), rows=rows), "bf16", "config 3b")
+    check_features(out, oracle_nbr("3b"), as64(f), as64(w), as64(b), "bf16", "config 3b",
+                   mag_rows=sample_rows(len(coords)))
 
 
-def test_config4_four_layers_shared_map_sampled():
+@pytest.mark.parametrize("layer", range(4))
+def test_config4_layers_on_a_shared_map_full(layer):
     key = "4"
     c = synth.config(key)
     coords = coords_of(key)
     f = synth.feats_for(c.number, 0, len(coords), c.cin, c.dtype)
-    rows = sample_rows(len(coords))
     fd = f.to(DEV)
     with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
-        for layer in range(c.layers):
-            w = synth.weight_for(c.number, layer, 3, c.cin, c.cout, c.dtype)
-            b = synth.bias_for(c.number, layer, c.cout, c.dtype)
+        for lay in range(layer + 1):  # the earlier layers run on the map first, as in the stack
+            w = synth.weight_for(c.number, lay, 3, c.cin, c.cout, c.dtype)
+            b = synth.bias_for(c.number, lay, c.cout, c.dtype)
             out = sc.subm_conv3d_forward(m, fd, w.to(DEV), b.to(DEV))
-            torch.cuda.synchronize()
-            ref = oracle.conv3_rulebook(oracle_nbr(key), as64(f), as64(w), as64(b), rows=rows)
-            check(out.cpu()[rows], ref, c.dtype, f"config 4 layer {layer}")
+        torch.cuda.synchronize()
+    check_features(out.cpu(), oracle_nbr(key), as64(f), as64(w), as64(b), c.dtype, f"config 4 layer {layer}",
+                   mag_rows=sample_rows(len(coords)))
 
 
-def test_config5_eight_chained_layers_sampled():
+@pytest.mark.parametrize("layer", range(8))
+def test_config5_chained_layers_full(layer):
     key = "5"
     c = synth.config(key)
     coords = coords_of(key)
     x = synth.feats_for(c.number, 0, len(coords), c.cin, c.dtype).to(DEV)
-    rows = sample_rows(len(coords), count=2048)
     with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
-        for layer in range(c.layers):
-            w = synth.weight_for(c.number, layer, 3, c.cin, c.cout, c.dtype)
-            b = synth.bias_for(c.number, layer, c.cout, c.dtype)
-            y = sc.subm_conv3d_forward(m, x, w.to(DEV), b.to(DEV))
-            torch.cuda.synchronize()
-            # The oracle consumes the GPU's stored input of this layer (same rounded values).
-            ref = oracle.conv3_rulebook(oracle_nbr(key), as64(x), as64(w), as64(b), rows=rows)
-            check(y.cpu()[rows], ref, c.dtype, f"config 5 layer {layer}")
-            x = y
+        for lay in range(layer + 1):
+            w = synth.weight_for(c.number, lay, 3, c.cin, c.cout, c.dtype)
+            b = synth.bias_for(c.number, lay, c.cout, c.dtype)
+            x_in = x
+            x = sc.subm_conv3d_forward(m, x_in, w.to(DEV), b.to(DEV))
+        torch.cuda.synchronize()
+    # The oracle consumes the GPU's stored input of this layer (same rounded values).
+    check_features(x.cpu(), oracle_nbr(key), as64(x_in), as64(w), as64(b), c.dtype, f"config 5 layer {layer}",
+                   mag_rows=sample_rows(len(coords), count=2048))
 
 
 # ----------------------------------------------------------------- edge cases
@@ -406,6 +409,7 @@ PERSISTENT_CASES = [("bf16", 128, 128, "2a"), ("f16", 64, 64, "2a"), ("bf16", 96
 @pytest.mark.parametrize("dtype,cin,cout,key", PERSISTENT_CASES)
 def test_persistent_walk_matches_oracle_and_one_tile_launch(monkeypatch, dtype, cin, cout, key):
     monkeypatch.delenv("SUBMCONV_TILE", raising=False)
+    monkeypatch.setenv("SUBMCONV_POOL", "0")
     coords, f, w, b = small_case(dtype, cin, cout, key=key, seed=3)
     outs = {}
     with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
@@ -420,7 +424,9 @@ def test_persistent_walk_matches_oracle_and_one_tile_launch(monkeypatch, dtype, 
 @pytest.mark.parametrize("key", ["3a", "3b", "4"])
 def test_persistent_walk_full_size(monkeypatch, key):
     # 3a: 708 tiles, two or three per workgroup; 3b: 43 per workgroup; 4: the 64-channel tile.
+    # (SUBMCONV_POOL=0: 3a and 3b would take the neighbour-pool kernel otherwise.)
     monkeypatch.delenv("SUBMCONV_TILE", raising=False)
+    monkeypatch.setenv("SUBMCONV_POOL", "0")
     coords = coords_of(key)
     f, w, b = cfg_tensors(key, 0)
     fd, wd, bd = f.to(DEV), w.to(DEV), b.to(DEV)
@@ -663,4 +669,4 @@ def test_random_sets_and_shapes_match_the_oracle(seed):
     with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
         assert np.array_equal(gpu_nbr(m), nbr), what
         out = forward(m, f, w, b)
-    check(out, oracle.conv3_rulebook(nbr, as64(f), as64(w), as64(b)), dtype, what)
+    check_features(out, nbr, as64(f), as64(w), as64(b), dtype, what)

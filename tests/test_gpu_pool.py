@@ -1,0 +1,220 @@
+"""GPU parity of the neighbour-pool convolution (k = 3, 128 output channels, 16-bit storage).
+
+Sets of at least 131,072 rows with cout = 128 and cin a multiple of 32 take the neighbour-pool
+kernel: a plan per map (built by the first such call), packed weights, and while the plan's
+overflow flag is unknown to the host, the general kernel enqueued behind it, each gated by the
+plan's per-tile flags on the device.  Every case here is compared in full with the oracle
+(normwise bar, componentwise bound), and the paths that must agree bit for bit are compared so:
+the first (gated) call with later calls, two maps of one set, streams with and without waits, and
+the overflow fallback with the general kernels.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import submanifold_sparse_convolution_amd as sc
+import synth
+from parity_util import as64, check_features
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TDT = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    sc.load_library()
+
+
+@pytest.fixture(autouse=True)
+def _pool_env(monkeypatch):
+    for var in ("SUBMCONV_POOL", "SUBMCONV_TILE", "SUBMCONV_PERSISTENT"):
+        monkeypatch.delenv(var, raising=False)
+
+
+@functools.lru_cache(maxsize=None)
+def shell():
+    return synth.coords_for("3a")
+
+
+@functools.lru_cache(maxsize=None)
+def rulebook_of(name):
+    return oracle.rulebook_sorted(SETS[name]())
+
+
+def two_shells():
+    c = shell()
+    second = c.copy()
+    second[:, 0] = 1
+    return np.ascontiguousarray(np.concatenate([c, second]))
+
+
+def dense_slab():
+    # 128 x 128 x 8: 131,072 rows, 16 blocks of 32 per tile, each tile four full x lines whose
+    # neighbours at one dz fill the pool exactly (6 lines x 128 = 768 rows).
+    g = np.arange(128)
+    z, y, x = np.meshgrid(np.arange(8), g, g, indexing="ij")
+    return np.ascontiguousarray(np.stack([np.zeros(z.size, np.int64), z.ravel(), y.ravel(), x.ravel()], 1).astype(np.int32))
+
+
+def shuffled_shell():
+    c = shell()
+    return np.ascontiguousarray(c[np.random.default_rng(31).permutation(len(c))])
+
+
+SETS = {"shell": shell, "two shells": two_shells, "dense slab": dense_slab, "shuffled shell": shuffled_shell}
+
+
+def inputs(n, cin, dtype, seed, cout=128):
+    rng = np.random.default_rng(seed)
+    f = synth.round_to(rng.standard_normal((n, cin)), dtype)
+    w = synth.round_to(rng.standard_normal((cout, 3, 3, 3, cin)) / np.sqrt(27 * cin), dtype)
+    b = synth.round_to(rng.standard_normal(cout) * 0.3, dtype)
+    return f, w, b
+
+
+def dev(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+def state(m):
+    return sc.sparse_indice_map_plan_state(m)
+
+
+def test_plan_states_and_the_gated_first_call():
+    coords = shell()
+    f, w, b = synth.feats_for(3, 0, len(coords), 128, "bf16"), synth.weight_for(3, 0, 3, 128, 128, "bf16"), \
+        synth.bias_for(3, 0, 128, "bf16")
+    fd, wd, bd = dev(f, w, b)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        assert state(m) == sc.SUBM_PLAN_NONE
+        y1 = sc.subm_conv3d_forward(m, fd, wd, bd)  # plan enqueued, gated pair
+        assert state(m) in (sc.SUBM_PLAN_PENDING, sc.SUBM_PLAN_READY)
+        torch.cuda.synchronize()
+        assert state(m) == sc.SUBM_PLAN_READY
+        y2 = sc.subm_conv3d_forward(m, fd, wd, bd)  # neighbour-pool kernel alone
+        y3 = sc.subm_conv3d_forward(m, fd, wd, bd)
+        torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y2, y3)
+    check_features(y2, rulebook_of("shell"), as64(f), as64(w), as64(b), "bf16", "shell 128->128 bf16")
+
+
+@pytest.mark.parametrize("dtype,cin", [("bf16", 32), ("bf16", 64), ("bf16", 96), ("bf16", 160), ("bf16", 256),
+                                       ("f16", 128), ("f16", 64)])
+def test_channel_counts_and_dtypes(dtype, cin):
+    coords = shell()
+    f, w, b = inputs(len(coords), cin, dtype, seed=cin)
+    fd, wd, bd = dev(f, w, b)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        y = sc.subm_conv3d_forward(m, fd, wd, bd)
+        torch.cuda.synchronize()
+        assert state(m) == sc.SUBM_PLAN_READY
+    check_features(y, rulebook_of("shell"), as64(f), as64(w), as64(b), dtype, f"shell {cin}->128 {dtype}")
+
+
+@pytest.mark.parametrize("name,cin", [("two shells", 96), ("dense slab", 128), ("dense slab", 32)])
+def test_tilings(name, cin):
+    # two shells: 17-block tiles and two tiles per workgroup, three 32-channel slices;
+    # dense slab: 16-block tiles whose sub-pools are exactly full.
+    coords = SETS[name]()
+    f, w, b = inputs(len(coords), cin, "bf16", seed=7)
+    fd, wd, bd = dev(f, w, b)
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        y = sc.subm_conv3d_forward(m, fd, wd, bd)
+        y2 = sc.subm_conv3d_forward(m, fd, wd, None)
+        torch.cuda.synchronize()
+        assert state(m) == sc.SUBM_PLAN_READY
+    nbr = rulebook_of(name)
+    check_features(y, nbr, as64(f), as64(w), as64(b), "bf16", f"{name} {cin}->128")
+    check_features(y2, nbr, as64(f), as64(w), None, "bf16", f"{name} {cin}->128 no bias")
+
+
+def test_overflow_falls_back_to_the_general_kernels(monkeypatch):
+    # Rows in random order: every tile's neighbours overflow the pool, so the pool kernel must
+    # leave every row to the general kernel, on the first (gated) call and on later ones.
+    coords = shuffled_shell()
+    f, w, b = inputs(len(coords), 128, "bf16", seed=5)
+    fd, wd, bd = dev(f, w, b)
+    cd = torch.from_numpy(coords).to(DEV)
+    with sc.sparse_indice_map_build(cd) as m:
+        y1 = sc.subm_conv3d_forward(m, fd, wd, bd)
+        torch.cuda.synchronize()
+        assert state(m) == sc.SUBM_PLAN_OVERFLOW
+        y2 = sc.subm_conv3d_forward(m, fd, wd, bd)
+        torch.cuda.synchronize()
+    monkeypatch.setenv("SUBMCONV_POOL", "0")
+    with sc.sparse_indice_map_build(cd) as m:
+        y0 = sc.subm_conv3d_forward(m, fd, wd, bd)
+        torch.cuda.synchronize()
+        assert state(m) == sc.SUBM_PLAN_NONE
+    assert torch.equal(y1, y0) and torch.equal(y2, y0)
+    check_features(y1, rulebook_of("shuffled shell"), as64(f), as64(w), as64(b), "bf16", "shuffled shell")
+
+
+def test_streams_without_waits():
+    # Map built on the current stream, convolved at once on two side streams with no
+    # wait_stream: the library orders the side streams after the build and after the plan.
+    coords = shell()
+    f, w, b = inputs(len(coords), 128, "bf16", seed=11)
+    fd, wd, bd = dev(f, w, b)
+    side1, side2 = torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)
+    y1 = torch.empty(len(coords), 128, dtype=torch.bfloat16, device=DEV)
+    y2 = torch.empty_like(y1)
+    torch.cuda.synchronize()
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV), sync=False) as m:
+        sc.subm_conv3d_forward(m, fd, wd, bd, out=y1, stream=side1)  # plan built on side1
+        sc.subm_conv3d_forward(m, fd, wd, bd, out=y2, stream=side2)  # waits for side1's plan
+        torch.cuda.synchronize()
+        y3 = sc.subm_conv3d_forward(m, fd, wd, bd)
+        torch.cuda.synchronize()
+    assert torch.equal(y1, y3) and torch.equal(y2, y3)
+    check_features(y1, rulebook_of("shell"), as64(f), as64(w), as64(b), "bf16", "side stream")
+
+
+def test_two_maps_of_one_set_agree_bitwise():
+    coords = torch.from_numpy(shell()).to(DEV)
+    f, w, b = inputs(len(shell()), 128, "bf16", seed=13)
+    fd, wd, bd = dev(f, w, b)
+    with sc.sparse_indice_map_build(coords) as m1, sc.sparse_indice_map_build(coords) as m2:
+        a = sc.subm_conv3d_forward(m1, fd, wd, bd)
+        c = sc.subm_conv3d_forward(m2, fd, wd, bd)
+        torch.cuda.synchronize()
+    assert torch.equal(a, c)
+
+
+def test_ineligible_calls_keep_the_general_kernels(monkeypatch):
+    coords = shell()
+    n = len(coords)
+    f, w, b = inputs(n, 128, "bf16", seed=17)
+    fd, wd, bd = dev(f, w, b)
+    nbr = rulebook_of("shell")
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        # feats not 16-byte aligned
+        big = torch.empty(n * 128 + 8, dtype=torch.bfloat16, device=DEV)
+        fm = big[1:1 + n * 128].view(n, 128)
+        fm.copy_(fd)
+        y = sc.subm_conv3d_forward(m, fm, wd, bd)
+        torch.cuda.synchronize()
+        assert state(m) == sc.SUBM_PLAN_NONE
+        check_features(y, nbr, as64(f), as64(w), as64(b), "bf16", "misaligned feats")
+        # 64 output channels, fp32 storage, the environment switch
+        y64 = sc.subm_conv3d_forward(m, fd, wd[:64].contiguous(), bd[:64].contiguous())
+        monkeypatch.setenv("SUBMCONV_POOL", "0")
+        y0 = sc.subm_conv3d_forward(m, fd, wd, bd)
+        torch.cuda.synchronize()
+        assert state(m) == sc.SUBM_PLAN_NONE
+    check_features(y64, nbr, as64(f), as64(w)[:64], as64(b)[:64], "bf16", "64 output channels")
+    check_features(y0, nbr, as64(f), as64(w), as64(b), "bf16", "SUBMCONV_POOL=0")
+    small = synth.coords_for("2a")
+    fs, ws, bs = inputs(len(small), 128, "bf16", seed=19)
+    with sc.sparse_indice_map_build(torch.from_numpy(small).to(DEV)) as m:
+        monkeypatch.delenv("SUBMCONV_POOL")
+        ys = sc.subm_conv3d_forward(m, *dev(fs, ws, bs))
+        torch.cuda.synchronize()
+        assert state(m) == sc.SUBM_PLAN_NONE  # fewer rows than one full tile per compute unit
+    check_features(ys, oracle.rulebook_sorted(small), as64(fs), as64(ws), as64(bs), "bf16", "small set")
