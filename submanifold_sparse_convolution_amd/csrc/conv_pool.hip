@@ -74,162 +74,201 @@ struct PoolShape {
 __host__ __device__ constexpr uint32_t slot_offset(uint32_t s) { return s * kSL + (((s >> 2) & 3u) << 4); }
 
 // ------------------------------------------------------------------------------------------
-// Plan: one workgroup per tile.  For each dz the distinct rows nbr[i, 9 dz + j] >= 0 of the
-// tile's rows i are marked in a byte array over [lo, hi] (plain stores: many rows mark the same
-// neighbour), turned into a bitmap with prefix counts, and ranked; the record gets the rows (in
-// the order the gather lanes load them) and the slot table (byte offsets of the slots, slot 768 =
-// the zero row for absent neighbours and rows past the tile).  A sub-pool beyond 768 rows or a
-// range beyond 32,768 rows sets the tile's flag (flags[tile] = 1, else 0) and stores 1 into
-// *host_flag (zeroed by the host).  A thread holds whole rows of the tile's rulebook in registers
-// (one round of loads), so no index is divided and no entry is read twice; 40 KB of LDS lets
-// several workgroups share a compute unit.
-constexpr int kMarkBytes = 32768;
+// Plan: one workgroup of three 256-thread groups per tile, group g handling dz = g.  The tile's
+// rulebook rows are read once with coalesced loads and transposed through LDS, so that a thread
+// holds the nine entries of two adjacent rows in registers.  Per group, the distinct rows
+// nbr[i, 9 dz + j] >= 0 of the tile's rows i are marked in a byte array over [lo, hi] (plain
+// stores: many rows mark the same neighbour), turned into a bitmap with prefix counts, and ranked;
+// the record gets the rows (in the order the gather lanes load them) and the slot table of the
+// nine taps (byte offsets of the slots, slot 768 = the zero row for absent neighbours and rows
+// past the tile).  A sub-pool beyond 768 rows or a range beyond 16,384 rows sets the (tile, dz)
+// flag (flags[3 tile + dz] = 1, else 0) and stores 1 into *host_flag (zeroed by the host).  The
+// marks reuse the staging area; 71 KB of LDS lets two workgroups share a compute unit.  nbr must
+// be 16-byte aligned.
+constexpr int kMarkBytes = 16384;
 template <int E>
-__global__ __launch_bounds__(kPT, 4) void pool_plan_kernel(const int32_t* __restrict__ nbr, int64_t n, int nb,
-                                                           int ntiles, unsigned char* __restrict__ plan,
-                                                           uint32_t* __restrict__ flags, uint32_t* host_flag) {
+struct PlanShape {
+  static constexpr int R = PoolShape<E>::NBLK * 32;
+  static constexpr int STAGEB = R * 27 * 4;
+  static constexpr int MARKB = 3 * kMarkBytes;
+  static constexpr int AREAB = STAGEB > MARKB ? STAGEB : MARKB;
+};
+template <int E>
+__global__ __launch_bounds__(3 * kPT, 2) void pool_plan_kernel(const int32_t* __restrict__ nbr, int64_t n, int nb,
+                                                               int ntiles, unsigned char* __restrict__ plan,
+                                                               uint32_t* __restrict__ flags, uint32_t* host_flag) {
   using P = PoolShape<E>;
   constexpr int R = P::NBLK * 32;
-  __shared__ __align__(16) unsigned char mark[kMarkBytes];
-  __shared__ uint32_t bitmap[kMarkBytes / 32];
-  __shared__ uint32_t prefix[kMarkBytes / 32];
-  __shared__ int s_red[8];
-  __shared__ uint32_t s_part[kPT / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int tile = blockIdx.x;
+  constexpr int NW = kMarkBytes / 32;  // bitmap words per group
+  __shared__ __align__(16) unsigned char area[PlanShape<E>::AREAB];
+  __shared__ uint2 bits[3][NW];  // (bitmap word, exclusive prefix count)
+  __shared__ int s_red[3][8];
+  __shared__ uint32_t s_part[3][4];
+  const int g = threadIdx.x >> 8, tid = threadIdx.x & 255, lane = tid & 63, wv = tid >> 6;
+  const int dz = g;
+  const int tile = (int)blockIdx.x;
   const int blk0 = (int)((int64_t)tile * nb / ntiles);
   const int blk1 = (int)((int64_t)(tile + 1) * nb / ntiles);
   const int64_t r0 = (int64_t)blk0 * 32;
   const int rows = (int)min((int64_t)(blk1 - blk0) * 32, n - r0);
-  const int32_t* tnbr = nbr + r0 * 27;
   unsigned char* rec = plan + (size_t)tile * P::RECB;
-  uint16_t* tab = reinterpret_cast<uint16_t*>(rec);
-  int32_t* ids = reinterpret_cast<int32_t*>(rec + P::TABB);
-  // this thread's rows tid + 256 u (u < 3 covers R <= 768), all 27 entries, loaded once
-  constexpr int RU = (R + kPT - 1) / kPT;
-  int nb27[RU][27];
+  uint32_t* tab2 = reinterpret_cast<uint32_t*>(rec) + 9 * dz * (R / 2);  // slot offsets, two rows per word
+  int32_t* idz = reinterpret_cast<int32_t*>(rec + P::TABB) + dz * kUcap;
+  // 0. the tile's rulebook rows [rows][27], read with coalesced 16-byte loads (a tile starts at a
+  //    multiple of 32 rows, 3,456 bytes) into LDS
+  int32_t* stage = reinterpret_cast<int32_t*>(area);
+  {
+    const int nel = rows * 27;
+    const int4* blk = reinterpret_cast<const int4*>(nbr + r0 * 27);
+    constexpr int NV = (R * 27 / 4 + 3 * kPT - 1) / (3 * kPT);
+    int4 x[NV];
 #pragma unroll
-  for (int u = 0; u < RU; ++u) {
-    const int r = tid + kPT * u;
+    for (int i = 0; i < NV; ++i) {
+      const int v = (int)threadIdx.x + 3 * kPT * i;
+      if (4 * v + 3 < nel) {
+        x[i] = blk[v];
+      } else {
+        const int32_t* e = reinterpret_cast<const int32_t*>(blk) + 4 * v;
+        x[i] = make_int4(4 * v < nel ? e[0] : -1, 4 * v + 1 < nel ? e[1] : -1, 4 * v + 2 < nel ? e[2] : -1,
+                         4 * v + 3 < nel ? e[3] : -1);
+      }
+    }
 #pragma unroll
-    for (int k = 0; k < 27; ++k) nb27[u][k] = r < rows ? tnbr[r * 27 + k] : -1;
+    for (int i = 0; i < NV; ++i) {
+      const int v = (int)threadIdx.x + 3 * kPT * i;
+      if (4 * v < R * 27) reinterpret_cast<int4*>(stage)[v] = x[i];
+    }
   }
-  bool bad = false;
+  __syncthreads();
+  // this thread's rows 2 tid + h + 512 u, the nine entries of its dz
+  constexpr int RU = (R + 2 * kPT - 1) / (2 * kPT);
+  int nb9[RU][2][9];
 #pragma unroll
-  for (int dz = 0; dz < 3; ++dz) {
-    // 1. range of the neighbour rows of this dz
-    int lo = INT32_MAX, hi = -1;
+  for (int u = 0; u < RU; ++u)
 #pragma unroll
-    for (int u = 0; u < RU; ++u)
+    for (int h = 0; h < 2; ++h) {
+      const int r = 2 * tid + h + 2 * kPT * u;
+#pragma unroll
+      for (int j = 0; j < 9; ++j) nb9[u][h][j] = r < rows ? stage[r * 27 + 9 * dz + j] : -1;
+    }
+  // 1. range of the neighbour rows
+  int lo = INT32_MAX, hi = -1;
+#pragma unroll
+  for (int u = 0; u < RU; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int j = 0; j < 9; ++j) {
-        const int v = nb27[u][9 * dz + j];
+        const int v = nb9[u][h][j];
         if (v >= 0) {
           lo = min(lo, v);
           hi = max(hi, v);
         }
       }
-    for (int off = 32; off > 0; off >>= 1) {
-      lo = min(lo, __shfl_xor(lo, off, 64));
-      hi = max(hi, __shfl_xor(hi, off, 64));
-    }
-    if (lane == 0) {
-      s_red[wv] = lo;
-      s_red[4 + wv] = hi;
-    }
-    __syncthreads();
-    lo = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
-    hi = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
-    const int64_t range = hi >= lo ? (int64_t)hi - lo + 1 : 0;
-    const bool fits = range <= kMarkBytes;
-    bad |= !fits;
-    const int nw = fits ? (int)((range + 31) / 32) : 0;  // bitmap words
-    // 2. marks of the rows present
-    for (int k = tid; k < nw * 8; k += kPT) reinterpret_cast<uint32_t*>(mark)[k] = 0u;
-    __syncthreads();
-    if (fits) {
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, __shfl_xor(lo, off, 64));
+    hi = max(hi, __shfl_xor(hi, off, 64));
+  }
+  if (lane == 0) {
+    s_red[g][wv] = lo;
+    s_red[g][4 + wv] = hi;
+  }
+  __syncthreads();  // (also: every group has read the staging area, which the marks reuse)
+  lo = min(min(s_red[g][0], s_red[g][1]), min(s_red[g][2], s_red[g][3]));
+  hi = max(max(s_red[g][4], s_red[g][5]), max(s_red[g][6], s_red[g][7]));
+  const int64_t range = hi >= lo ? (int64_t)hi - lo + 1 : 0;
+  const bool fits = range <= kMarkBytes;
+  bool bad = !fits;
+  const int nw = fits ? (int)((range + 31) / 32) : 0;  // bitmap words
+  unsigned char* mark = area + g * kMarkBytes;
+  // 2. marks of the rows present
+  for (int k = tid; k < nw * 8; k += kPT) reinterpret_cast<uint32_t*>(mark)[k] = 0u;
+  __syncthreads();
+  if (fits) {
 #pragma unroll
-      for (int u = 0; u < RU; ++u)
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int j = 0; j < 9; ++j) {
-          const int v = nb27[u][9 * dz + j];
+          const int v = nb9[u][h][j];
           if (v >= 0) mark[v - lo] = 1;
         }
-    }
-    __syncthreads();
-    // 3. bitmap words and their exclusive prefix counts (each thread owns a run of words)
-    const int per = (nw + kPT - 1) / kPT;
-    uint32_t cnt = 0;
-    for (int k = tid * per; k < min(nw, (tid + 1) * per); ++k) {
-      const uint4 x = reinterpret_cast<const uint4*>(mark)[2 * k];
-      const uint4 y = reinterpret_cast<const uint4*>(mark)[2 * k + 1];
-      const uint32_t m8[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-      uint32_t word = 0;
+  }
+  __syncthreads();
+  // 3. bitmap words and their exclusive prefix counts (each thread owns a run of words)
+  const int per = (nw + kPT - 1) / kPT;
+  const int k0 = min(nw, tid * per), k1 = min(nw, (tid + 1) * per);
+  uint32_t cnt = 0;
+  for (int k = k0; k < k1; ++k) {
+    const uint4 x = reinterpret_cast<const uint4*>(mark)[2 * k];
+    const uint4 y = reinterpret_cast<const uint4*>(mark)[2 * k + 1];
+    const uint32_t m8[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+    uint32_t word = 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t m = m8[u];  // four mark bytes, 0 or 1 each
-        word |= ((m & 1u) | ((m >> 7) & 2u) | ((m >> 14) & 4u) | ((m >> 21) & 8u)) << (4 * u);
-      }
-      bitmap[k] = word;
-      cnt += __popc(word);
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t m = m8[u];  // four mark bytes, 0 or 1 each
+      word |= ((m & 1u) | ((m >> 7) & 2u) | ((m >> 14) & 4u) | ((m >> 21) & 8u)) << (4 * u);
     }
-    uint32_t incl = cnt;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
+    bits[g][k].x = word;
+    cnt += __popc(word);
+  }
+  uint32_t incl = cnt;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_part[g][wv] = incl;
+  __syncthreads();
+  {
+    uint32_t c = incl - cnt;
+    for (int k = 0; k < wv; ++k) c += s_part[g][k];
+    for (int k = k0; k < k1; ++k) {
+      bits[g][k].y = c;
+      c += __popc(bits[g][k].x);
     }
-    if (lane == 63) s_part[wv] = incl;
-    __syncthreads();
-    uint32_t base = incl - cnt;
-    for (int k = 0; k < wv; ++k) base += s_part[k];
-    const uint32_t total = s_part[0] + s_part[1] + s_part[2] + s_part[3];
-    for (int k = tid * per; k < min(nw, (tid + 1) * per); ++k) {
-      prefix[k] = base;
-      base += __popc(bitmap[k]);
+  }
+  const uint32_t total = s_part[g][0] + s_part[g][1] + s_part[g][2] + s_part[g][3];
+  bad |= total > (uint32_t)kUcap;
+  __syncthreads();
+  // 4. rows by rank into LDS (the marks are dead), one bit per lane: a wave takes two words at a
+  //    time; then the ids in gather order: slot c is loaded by wave c / 192, load (c % 192) / 16,
+  //    lane group c % 16, and the ids of a lane group are contiguous; unused slots hold -1
+  int32_t* by_rank = reinterpret_cast<int32_t*>(mark);
+  for (int k = 2 * wv + (lane >> 5); k < nw; k += 8) {
+    const uint2 wp = bits[g][k];
+    const uint32_t bit = lane & 31;
+    if ((wp.x >> bit) & 1u) {
+      const uint32_t c = wp.y + __popc(wp.x & ((1u << bit) - 1u));
+      if (c < (uint32_t)kUcap) by_rank[c] = lo + 32 * k + (int)bit;
     }
-    bad |= total > (uint32_t)kUcap;
-    __syncthreads();
-    // 4. row ids in gather order: slot s is loaded by wave s / 192, load (s % 192) / 16, lane
-    //    group s % 16, and the ids of a lane group are contiguous; unused slots hold -1
-    int32_t* idz = ids + dz * kUcap;
-    for (int k = tid; k < kUcap; k += kPT) {
-      const uint32_t wg = k / P::WSLOTS, rem = k % P::WSLOTS;
-      int v = -1;
-      if ((uint32_t)k < total) {
-        // the k-th set bit: binary search of the word whose prefix count reaches it
-        int a = 0, b = nw - 1;
-        while (a < b) {
-          const int m = (a + b + 1) >> 1;
-          if (prefix[m] <= (uint32_t)k) a = m;
-          else b = m - 1;
-        }
-        uint32_t word = bitmap[a];
-        for (uint32_t c = prefix[a]; c < (uint32_t)k; ++c) word &= word - 1u;
-        v = lo + a * 32 + __builtin_ctz(word);
-      }
-      idz[(wg * 16 + rem % 16) * P::NJ + rem / 16] = v;
+  }
+  __syncthreads();
+  for (int d = tid; d < kUcap; d += kPT) {
+    const int grp = d / P::NJ, j = d - P::NJ * grp;
+    const uint32_t c = (uint32_t)((grp >> 4) * P::WSLOTS + 16 * j + (grp & 15));
+    idz[d] = c < total ? by_rank[c] : -1;
+  }
+  // 5. slot table of the nine taps (rows past the tile read the zero slot)
+  auto slot_of = [&](int vj) -> uint32_t {
+    uint32_t slot = kUcap;
+    if (fits && vj >= 0) {
+      const uint32_t d = (uint32_t)(vj - lo);
+      const uint2 wp = bits[g][d >> 5];
+      const uint32_t rank = wp.y + __popc(wp.x & ((1u << (d & 31)) - 1u));
+      slot = rank < (uint32_t)kUcap ? rank : (uint32_t)kUcap;
     }
-    // 5. slot table of the nine taps of this dz (rows past the tile read the zero slot)
+    return slot_offset(slot);
+  };
 #pragma unroll
-    for (int u = 0; u < RU; ++u) {
-      const int r = tid + kPT * u;
-      if (r >= R) break;
+  for (int u = 0; u < RU; ++u) {
+    const int r = 2 * tid + 2 * kPT * u;
+    if (r >= R) break;
 #pragma unroll
-      for (int j = 0; j < 9; ++j) {
-        const int vj = fits ? nb27[u][9 * dz + j] : -1;
-        uint32_t slot = kUcap;
-        if (vj >= 0) {
-          const uint32_t d = (uint32_t)(vj - lo);
-          const uint32_t rank = prefix[d >> 5] + __popc(bitmap[d >> 5] & ((1u << (d & 31)) - 1u));
-          slot = rank < (uint32_t)kUcap ? rank : (uint32_t)kUcap;
-        }
-        tab[(9 * dz + j) * R + r] = (uint16_t)slot_offset(slot);
-      }
-    }
-    __syncthreads();  // (marks, bitmap and prefix are reused by the next dz)
+    for (int j = 0; j < 9; ++j) tab2[j * (R / 2) + r / 2] = slot_of(nb9[u][0][j]) | (slot_of(nb9[u][1][j]) << 16);
   }
   if (tid == 0) {
-    flags[tile] = bad ? 1u : 0u;
+    flags[3 * tile + dz] = bad ? 1u : 0u;
     if (bad) *reinterpret_cast<volatile uint32_t*>(host_flag) = 1u;
   }
 }
@@ -262,7 +301,7 @@ struct PoolArgs {
   const void* bias;
   void* out;
   const unsigned char* plan;
-  const uint32_t* gate;  // non-null: per-tile overflow flags [ntiles]; the kernel does nothing when one is set
+  const uint32_t* gate;  // non-null: overflow flags [3 ntiles]; the kernel does nothing when one is set
   int64_t n;
   int row_bytes;
   int qs;       // slices of 32 input channels
@@ -293,7 +332,7 @@ __global__ __launch_bounds__(kPT, 1) void pool_conv_kernel(const PoolArgs a) {
   __shared__ __align__(16) unsigned char lds[P::LDSB];
 
   const int tid = threadIdx.x;
-  if (a.gate != nullptr && pool_any_flag(a.gate, a.ntiles)) return;
+  if (a.gate != nullptr && pool_any_flag(a.gate, 3 * a.ntiles)) return;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lk = lane >> 5;
@@ -631,7 +670,11 @@ static size_t pool_records_bytes(const PoolTiling& t) {
   return (size_t)t.ntiles * (size_t)(t.e ? PoolShape<1>::RECB : PoolShape<0>::RECB);
 }
 
-size_t pool_plan_bytes(const PoolTiling& t) { return pool_records_bytes(t) + ((size_t)t.ntiles * 4 + 255) / 256 * 256; }
+int pool_flag_count(const PoolTiling& t) { return 3 * t.ntiles; }
+
+size_t pool_plan_bytes(const PoolTiling& t) {
+  return pool_records_bytes(t) + ((size_t)pool_flag_count(t) * 4 + 255) / 256 * 256;
+}
 
 uint32_t* pool_tile_flags(const PoolTiling& t, void* plan) {
   return reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(plan) + pool_records_bytes(t));
@@ -644,10 +687,10 @@ hipError_t launch_pool_plan(const int32_t* nbr, int64_t n, const PoolTiling& t, 
   auto* rec = static_cast<unsigned char*>(plan);
   uint32_t* flags = pool_tile_flags(t, plan);
   if (t.e)
-    hipExtLaunchKernelGGL(pool_plan_kernel<1>, dim3((unsigned)t.ntiles), dim3(kPT), 0, stream, nullptr, done, 0u, nbr,
+    hipExtLaunchKernelGGL(pool_plan_kernel<1>, dim3((unsigned)t.ntiles), dim3(3 * kPT), 0, stream, nullptr, done, 0u, nbr,
                           n, t.nb, t.ntiles, rec, flags, host_flag);
   else
-    hipExtLaunchKernelGGL(pool_plan_kernel<0>, dim3((unsigned)t.ntiles), dim3(kPT), 0, stream, nullptr, done, 0u, nbr,
+    hipExtLaunchKernelGGL(pool_plan_kernel<0>, dim3((unsigned)t.ntiles), dim3(3 * kPT), 0, stream, nullptr, done, 0u, nbr,
                           n, t.nb, t.ntiles, rec, flags, host_flag);
   return hipGetLastError();
 }

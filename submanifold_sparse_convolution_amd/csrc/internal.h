@@ -215,11 +215,13 @@ hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, i
 // Neighbour-pool convolution (conv_pool.hip): k = 3, 16-bit storage, cout == 128, cin % 32 == 0.
 // pool_tiling: false when n is too small (fewer than one full tile per compute unit) or the plan
 // would exceed 31-bit offsets.  launch_pool_plan writes the plan of map rows nbr [n, 27] (plan:
-// pool_plan_bytes(t)): the tile records and per-tile overflow flags (pool_tile_flags), and stores
-// 1 into *host_flag (pinned, zeroed by the caller) when a tile's sub-pool does not fit; `done`
-// records its completion.  launch_pool_conv packs the weights into wpk (pool_weight_bytes(cin))
-// and runs the convolution; gate != null: the tile flags, the kernel does nothing if one is set.
+// pool_plan_bytes(t)): the tile records and the overflow flags of every (tile, dz)
+// (pool_tile_flags, pool_flag_count(t) of them), and stores 1 into *host_flag (pinned, zeroed by
+// the caller) when a sub-pool does not fit; `done` records its completion.  launch_pool_conv
+// packs the weights into wpk (pool_weight_bytes(cin)) and runs the convolution; gate != null:
+// the flags, the kernel does nothing if one is set.
 bool pool_tiling(int64_t n, PoolTiling* t);
+int pool_flag_count(const PoolTiling& t);
 size_t pool_plan_bytes(const PoolTiling& t);
 uint32_t* pool_tile_flags(const PoolTiling& t, void* plan);
 size_t pool_weight_bytes(int cin);

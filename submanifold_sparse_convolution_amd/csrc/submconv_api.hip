@@ -611,8 +611,8 @@ bool pool_eligible(const submconv_map* map, int64_t n, int ksize, int cin, int c
                    const void* weight, const void* out) {
   if (map == nullptr || ksize != 3 || cout != 128 || (dtype != SUBM_BF16 && dtype != SUBM_F16)) return false;
   if (cin < 32 || cin % 32 != 0 || map->d.pool_state == 3) return false;
-  if (((reinterpret_cast<uintptr_t>(feats) | reinterpret_cast<uintptr_t>(weight) | reinterpret_cast<uintptr_t>(out)) &
-       15u) != 0)
+  if (((reinterpret_cast<uintptr_t>(feats) | reinterpret_cast<uintptr_t>(weight) | reinterpret_cast<uintptr_t>(out) |
+        reinterpret_cast<uintptr_t>(map->d.nbr)) & 15u) != 0)
     return false;
   if ((uint64_t)n * (uint64_t)cin * 2u >= 0x7FFFF000ull) return false;
   const char* v = std::getenv("SUBMCONV_POOL");
@@ -691,7 +691,7 @@ extern "C" int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int
                                       wpk, stream);
       if (e == hipSuccess && gate != nullptr)
         e = launch_subm_conv(&map->d, n, ksize, cin, cout, dtype, feats, weight, bias, out, stream, gate,
-                             map->d.pool_tiling.ntiles);
+                             pool_flag_count(map->d.pool_tiling));
       if (e != hipSuccess) return fail(hip_status(e, "subm_conv3d_forward launch"));
       return SUBM_OK;
     }
