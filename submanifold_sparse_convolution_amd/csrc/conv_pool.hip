@@ -70,8 +70,9 @@ struct PoolShape {
 };
 
 // Byte offset of pool slot s in a sub-pool buffer, with the 16-byte chunk index XOR-swizzled by
-// (s >> 2) & 3 so that sixteen consecutive slots read by one quarter-wave hit distinct banks.
-__host__ __device__ constexpr uint32_t slot_offset(uint32_t s) { return s * kSL + (((s >> 2) & 3u) << 4); }
+// (s >> 1) & 3.  Of the swizzles measured for one operand-B read (32 lanes of slots, one 16-byte
+// chunk each), this one read fastest both for consecutive slots and for runs broken by gaps.
+__host__ __device__ constexpr uint32_t slot_offset(uint32_t s) { return s * kSL + (((s >> 1) & 3u) << 4); }
 
 // ------------------------------------------------------------------------------------------
 // Plan: one workgroup of three 256-thread groups per tile, group g handling dz = g.  The tile's
@@ -273,25 +274,27 @@ __global__ __launch_bounds__(3 * kPT, 2) void pool_plan_kernel(const int32_t* __
   }
 }
 
-// Weights KRSC [128, 27, cin] -> packed [cin / 32][27][2][128][2][16 bytes]: half-step (q, t, kk)
-// is one contiguous 4 KB block; unit u of output channel co holds input channels
-// 32 q + 8 (2 kk + (u ^ ((co >> 3) & 1))) .. + 8 (the XOR makes sixteen consecutive channels'
-// fragment reads hit distinct banks).
+// Weights KRSC [128, 27, cin] -> packed [cin / 32][27][2 kk][4 ob][64 lanes][16 bytes]: half-step
+// (q, t, kk) is one contiguous 4 KB block, and in it the operand-A fragment of output block ob is
+// 1 KB in lane order: lane l = 32 lk + r holds output channel 32 ob + r, input channels
+// 32 q + 8 (2 kk + lk) .. + 8.  Consecutive lanes then read consecutive 16-byte units, the
+// pattern the LDS serves fastest.
 __global__ __launch_bounds__(256) void pool_pack_kernel(const uint4* __restrict__ w, int cin, uint4* __restrict__ wpk) {
   const int64_t total = (int64_t)(cin / 32) * 27 * 2 * 128 * 2;
   const int row16 = cin / 8;  // 16-byte chunks per (co, tap) row
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     int64_t x = i;
-    const int u = (int)(x & 1);
+    const int r = (int)(x & 31);
+    x >>= 5;
+    const int lk = (int)(x & 1);
     x >>= 1;
-    const int co = (int)(x & 127);
-    x >>= 7;
+    const int ob = (int)(x & 3);
+    x >>= 2;
     const int kk = (int)(x & 1);
     x >>= 1;
     const int t = (int)(x % 27);
     const int q = (int)(x / 27);
-    const int c = 2 * kk + (u ^ ((co >> 3) & 1));
-    wpk[i] = w[((int64_t)co * 27 + t) * row16 + 4 * q + c];
+    wpk[i] = w[((int64_t)(32 * ob + r) * 27 + t) * row16 + 4 * q + 2 * kk + lk];
   }
 }
 
@@ -358,16 +361,13 @@ __global__ __launch_bounds__(kPT, 1) void pool_conv_kernel(const PoolArgs a) {
     *reinterpret_cast<uint4*>(lds + (tid >> 2) * P::POOLB + kUcap * kSL + (tid & 3) * 16) = make_uint4(0, 0, 0, 0);
 
   // Per-lane constants.  A gather lane of load j of wave w fills slot w * 192 + 16 j + lane / 4,
-  // 16-byte unit lane % 4, so it fetches chunk (lane % 4) ^ ((slot >> 2) & 3) = (lane % 4) ^ (lane / 16).
-  const uint32_t gchunk = (uint32_t)(((lane & 3) ^ (lane >> 4)) * 16);
-  // Operand A position j of a wave holds output block (w + j) % 4; its fragment is 16 bytes of
-  // row co of the half-step, unit lk ^ ((co >> 3) & 1).
+  // 16-byte unit lane % 4, so it fetches chunk (lane % 4) ^ ((slot >> 1) & 3) = (lane % 4) ^ ((lane / 8) % 4).
+  const uint32_t gchunk = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) * 16);
+  // Operand A position j of a wave holds output block (w + j) % 4; its fragment is the 1 KB run
+  // of that block in the half-step, 16 bytes per lane in lane order.
   uint32_t a_off[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int co = 32 * ((w + j) & 3) + lr;
-    a_off[j] = (uint32_t)(co * 32 + ((((co >> 3) & 1) ^ lk) << 4));
-  }
+  for (int j = 0; j < 4; ++j) a_off[j] = (uint32_t)(((w + j) & 3) * 1024 + lane * 16);
 
   int ids[P::NJ];
   auto read_ids = [&](int dz) {
