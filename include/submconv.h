@@ -232,6 +232,23 @@ int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int cin, int c
                         void* out, hipStream_t stream);
 
 /*
+ * subm_conv3d_forward_noalloc -- subm_conv3d_forward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments, rules, results (bit for bit) and stream semantics, and it calls no hipMalloc, hipFree
+ * or other allocating routine.  Its one scratch buffer (the packed weights of the neighbour-pool
+ * kernel) is a static 1,769,472-byte array in device memory, held by every device the library runs
+ * on until the process ends; a call that would need more (neighbour-pool kernel with cin > 256)
+ * returns SUBM_ERR_UNSUPPORTED.  It never builds the map's neighbour-pool plan (that allocates):
+ * until an allocating call (subm_conv3d_forward) has built it, eligible calls take the general
+ * kernels.  All calls on one device share that array, so calls that overlap in time on one device
+ * (on different streams, or from different threads without ordering) race; calls in stream order
+ * do not.
+ */
+int subm_conv3d_forward_noalloc(submconv_map_t map, int64_t n, int ksize, int cin, int cout, int dtype,
+                                const void* feats, const void* weight, const void* bias, void* out,
+                                hipStream_t stream);
+
+/*
  * subm_conv3d_forward_per_offset -- the same SubMConv3d (ksize 3) as subm_conv3d_forward, computed
  * the per-offset way: for each of the 27 offsets, gather the neighbour rows of that offset,
  * multiply them by that offset's weight slice, and add the products into the output rows.  This

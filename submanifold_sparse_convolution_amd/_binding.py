@@ -38,6 +38,7 @@ C_FUNCTIONS = (
     "sparse_indice_map_copy_nbr",
     "sparse_indice_map_plan_state",
     "subm_conv3d_forward",
+    "subm_conv3d_forward_noalloc",
     "subm_conv3d_forward_per_offset",
     "sparse_subdivide",
     "sparse_downsample_build",
@@ -95,6 +96,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.sparse_indice_map_copy_nbr.argtypes = [vp, vp, vp]
         lib.sparse_indice_map_plan_state.argtypes = [vp, ctypes.POINTER(ci)]
         lib.subm_conv3d_forward.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp]
+        lib.subm_conv3d_forward_noalloc.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp]
         lib.subm_conv3d_forward_per_offset.argtypes = [vp, i64, ci, ci, ci, vp, vp, vp, vp, vp]
         lib.sparse_subdivide.argtypes = [vp, i64, vp, ctypes.POINTER(vp)]
         lib.sparse_downsample_build.argtypes = [vp, i64, vp, ctypes.POINTER(vp)]
@@ -313,7 +315,7 @@ def sparse_indice_map_copy_nbr(m: IndiceMap, out: torch.Tensor | None = None, st
     return out
 
 
-def _conv_args(feats, weight, bias, out):
+def _conv_args(feats, weight, bias, out, need_out=False):
     _device_tensor(feats, "feats")
     _device_tensor(weight, "weight")
     if feats.dim() != 2 or weight.dim() != 5:
@@ -333,6 +335,8 @@ def _conv_args(feats, weight, bias, out):
             raise ValueError("bias must be [Cout] in the feats dtype")
         bias_ptr = bias.data_ptr()
     if out is None:
+        if need_out:
+            raise ValueError("out must be given (this call allocates nothing)")
         out = torch.empty((n, cout), dtype=feats.dtype, device=feats.device)
     _device_tensor(out, "out")
     if out.dtype != feats.dtype or tuple(out.shape) != (n, cout):
@@ -360,35 +364,30 @@ def subm_conv3d_forward(m: IndiceMap | None, feats: torch.Tensor, weight: torch.
                         bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
                         stream=None) -> torch.Tensor:
     """SubMConv3d forward: feats [N, Cin], KRSC weight [Cout, k, k, k, Cin] (k = 3 or 1), bias [Cout]."""
-    _device_tensor(feats, "feats")
-    _device_tensor(weight, "weight")
-    if feats.dim() != 2 or weight.dim() != 5:
-        raise ValueError("feats must be [N, Cin] and weight KRSC [Cout, k, k, k, Cin]")
-    k = weight.shape[1]
-    if weight.shape[2] != k or weight.shape[3] != k:
-        raise ValueError("weight spatial dims must be equal (KRSC [Cout, k, k, k, Cin])")
-    if weight.shape[4] != feats.shape[1]:
-        raise ValueError("weight Cin does not match feats")
-    if feats.dtype not in _DTYPE_CODES or weight.dtype != feats.dtype:
-        raise ValueError("feats and weight must share one of float32 / float16 / bfloat16")
+    k, bias_ptr, out = _conv_args(feats, weight, bias, out)
     n, cin, cout = feats.shape[0], feats.shape[1], weight.shape[0]
-    bias_ptr = None
-    if bias is not None:
-        _device_tensor(bias, "bias")
-        if bias.dtype != feats.dtype or tuple(bias.shape) != (cout,):
-            raise ValueError("bias must be [Cout] in the feats dtype")
-        bias_ptr = bias.data_ptr()
-    if out is None:
-        out = torch.empty((n, cout), dtype=feats.dtype, device=feats.device)
-    _device_tensor(out, "out")
-    if out.dtype != feats.dtype or tuple(out.shape) != (n, cout):
-        raise ValueError("out must be [N, Cout] in the feats dtype")
     lib = load_library()
     handle = None if m is None else m.handle
     with _on_device(feats.device):
         st = lib.subm_conv3d_forward(handle, n, k, cin, cout, _DTYPE_CODES[feats.dtype], feats.data_ptr(),
                                      weight.data_ptr(), bias_ptr, out.data_ptr(), _stream_ptr(stream, feats.device))
     _check(lib, "subm_conv3d_forward", st)
+    return out
+
+
+def subm_conv3d_forward_noalloc(m: IndiceMap | None, feats: torch.Tensor, weight: torch.Tensor,
+                                bias: torch.Tensor | None, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """subm_conv3d_forward with no device allocation (out must be given); see subm_conv3d_forward_noalloc
+    in include/submconv.h."""
+    k, bias_ptr, out = _conv_args(feats, weight, bias, out, need_out=True)
+    n, cin, cout = feats.shape[0], feats.shape[1], weight.shape[0]
+    lib = load_library()
+    handle = None if m is None else m.handle
+    with _on_device(feats.device):
+        st = lib.subm_conv3d_forward_noalloc(handle, n, k, cin, cout, _DTYPE_CODES[feats.dtype], feats.data_ptr(),
+                                             weight.data_ptr(), bias_ptr, out.data_ptr(),
+                                             _stream_ptr(stream, feats.device))
+    _check(lib, "subm_conv3d_forward_noalloc", st)
     return out
 
 

@@ -701,6 +701,77 @@ extern "C" int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int
   return SUBM_OK;
 }
 
+// ---------------------------------------------------------------------------------------------
+// subm_conv3d_forward_noalloc: subm_conv3d_forward without any device allocation.  The one
+// scratch buffer of the convolution (the packed weights of the neighbour-pool kernel) is this
+// file-scope array; each device holds its own copy until the process ends, and its device
+// address is looked up once per device (host code never passes the array's name to a kernel).
+namespace {
+constexpr size_t kNoAllocScratchBytes = (size_t)27 * 128 * 256 * 2;  // packed weights, cin <= 256
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kMaxDevices] = {};
+
+Status noalloc_scratch(int dev, void** ptr) {
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (g_noalloc_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    SUBM_HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (p == nullptr) return make_status(SUBM_ERR_HIP, "hipGetSymbolAddress returned no address for the scratch array");
+    g_noalloc_ptr[dev] = p;
+  }
+  *ptr = g_noalloc_ptr[dev];
+  return Status{};
+}
+}  // namespace
+
+extern "C" int subm_conv3d_forward_noalloc(submconv_map_t map, int64_t n, int ksize, int cin, int cout, int dtype,
+                                           const void* feats, const void* weight, const void* bias, void* out,
+                                           hipStream_t stream) {
+  clear_error();
+  Status s = check_conv(map, n, ksize, cin, cout, dtype, feats, weight, bias, out);
+  if (!s.ok()) return fail(s);
+  if (n == 0) return SUBM_OK;
+  map_note_use(map, stream);
+  if (pool_eligible(map, n, ksize, cin, cout, dtype, feats, weight, out)) {
+    int state = 0;
+    {
+      std::lock_guard<std::mutex> lock(map->mu);
+      MapData& d = map->d;
+      if (d.pool_state == 1 && hipEventQuery(d.pool_slot.ready) == hipSuccess)
+        d.pool_state = reinterpret_cast<volatile MapHostFlags*>(d.pool_slot.host)->flags != 0u ? 3 : 2;
+      if (d.pool_state == 1 && stream != d.pool_stream) {
+        const hipError_t we = hipStreamWaitEvent(stream, d.pool_slot.ready, 0);
+        if (we != hipSuccess) return fail(hip_status(we, "subm_conv3d_forward_noalloc stream wait"));
+      }
+      state = d.pool_state;
+    }
+    // (no plan yet: building one allocates, so the general kernels run instead)
+    if (state == 1 || state == 2) {
+      if (pool_weight_bytes(cin) > kNoAllocScratchBytes)
+        return fail(SUBM_ERR_UNSUPPORTED, "subm_conv3d_forward_noalloc: cin above 256 needs more packed-weight "
+                                          "workspace than its static 1.7 MB");
+      int dev = -1;
+      if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(SUBM_ERR_HIP, "subm_conv3d_forward_noalloc: no current device");
+      void* wpk = nullptr;
+      s = noalloc_scratch(dev, &wpk);
+      if (!s.ok()) return fail(s);
+      const uint32_t* gate = state == 1 ? pool_tile_flags(map->d.pool_tiling, map->d.pool_plan) : nullptr;
+      hipError_t e = launch_pool_conv(map->d.pool_tiling, map->d.pool_plan, gate, n, cin, dtype, feats, weight, bias, out,
+                                      wpk, stream);
+      if (e == hipSuccess && gate != nullptr)
+        e = launch_subm_conv(&map->d, n, ksize, cin, cout, dtype, feats, weight, bias, out, stream, gate,
+                             pool_flag_count(map->d.pool_tiling));
+      if (e != hipSuccess) return fail(hip_status(e, "subm_conv3d_forward_noalloc launch"));
+      return SUBM_OK;
+    }
+  }
+  hipError_t e = launch_subm_conv(map == nullptr ? nullptr : &map->d, n, ksize, cin, cout, dtype, feats, weight, bias, out, stream);
+  if (e != hipSuccess) return fail(hip_status(e, "subm_conv3d_forward_noalloc launch"));
+  return SUBM_OK;
+}
+
 extern "C" int subm_conv3d_forward_per_offset(submconv_map_t map, int64_t n, int cin, int cout, int dtype,
                                               const void* feats, const void* weight, const void* bias, void* out,
                                               hipStream_t stream) {
