@@ -12,9 +12,13 @@ voxels), 128 -> 128 channels, bf16 storage, k = 3.
 
 Printed: one JSON line with the step throughput (effective TFLOP/s =
 2 * pairs * Cin * Cout per layer, summed over layers, divided by the step
-time), the roofline position of the convolution kernel (its average duration
-from HIP events around back-to-back launches on the stream it runs on), and
-the CPU oracle timed on a bounded sample of the same workload.
+time), the roofline position of the convolution call (its average duration
+from HIP events around back-to-back calls on the stream it runs on; on the
+neighbour-pool path a call is the weight packing plus the convolution
+kernel), the same call with cold caches (1 GiB written between calls,
+outside the events), the map build's GPU time from events, and the CPU
+oracle timed on a bounded sample of the same workload in one process per
+host core (at most 16).
 
 --op selects another row of the path, each printed as one JSON line of its own:
 per-offset (the same convolution computed offset by offset: gather -> GEMM ->
@@ -43,7 +47,8 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # dense MFMA, MI355
 PEAK_HBM_GBS = 8000.0
 ELEM = {"bf16": 2, "f16": 2, "f32": 4}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_traffic.json")
-CONV_SOURCE = os.path.join(ROOT, "submanifold_sparse_convolution_amd", "csrc", "conv.hip")
+CSRC = os.path.join(ROOT, "submanifold_sparse_convolution_amd", "csrc")
+MALL_FLUSH_BYTES = 1 << 30  # written between launches for the cold-cache timing (MALL: 256 MB)
 
 
 def parse():
@@ -125,57 +130,88 @@ def measured_peaks(dev):
     return out
 
 
-def load_traffic(key, kernel_hash):
-    """HBM bytes per conv launch from committed rocprofv3 PMC runs, if taken on this kernel source."""
+def load_traffic(key, source, kernel_hash):
+    """HBM bytes per conv call from committed rocprofv3 PMC runs, if taken on this kernel source."""
     try:
         with open(TRAFFIC_FILE) as fh:
             data = json.load(fh)
     except (OSError, ValueError):
         return None
     entry = data.get(key)
-    if not entry or entry.get("conv_source_sha256") != kernel_hash:
+    if not entry or entry.get("kernel_source") != source or entry.get("source_sha256") != kernel_hash:
         return None
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(key, coords, feats, weight, bias, nbr_pairs_per_row, cin, cout, budget_s):
-    """The oracle as it stands, single-threaded, on a row sample sized to ~budget_s seconds."""
+def _oracle_inputs(key, layer, cin, cout):
+    import synth
+    c = synth.config(key)
+    coords = synth.coords_for(key)
+    f = synth.feats_for(c.number, 0, len(coords), cin, c.dtype).double().numpy()
+    w = synth.weight_for(c.number, layer, 3, cin, cout, c.dtype).double().numpy()
+    b = synth.bias_for(c.number, layer, cout, c.dtype).double().numpy()
+    return coords, f, w, b
+
+
+def _oracle_worker(task):
+    """One host process: the oracle on its share of the sampled rows, one thread; returns seconds."""
+    key, layer, cin, cout, rows = task
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    coords, f, w, b = _oracle_inputs(key, layer, cin, cout)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.conv3(coords, f, w, b, rows=rows)
+        return time.perf_counter() - t0
+
+
+def host_cores():
+    """Host cores this process may use, at most 16 (one GPU's share of the host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_baseline(key, layer, coords, nbr_pairs_per_row, cin, cout, budget_s):
+    """The oracle as it stands (dictionary lookup + per-voxel loop, float64) on P host processes,
+    one thread each, each on its share of a random row sample sized to ~budget_s seconds."""
+    import multiprocessing
+
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
 
-    f64 = feats.double().numpy()
-    w64 = weight.double().numpy()
-    b64 = bias.double().numpy()
     n = coords.shape[0]
+    procs = host_cores()
     rng = np.random.default_rng(12345)
+    _, f64, w64, b64 = _oracle_inputs(key, layer, cin, cout)
     with threadpool_limits(limits=1):
-        # Two calibration calls fit cost = fixed (dictionary build) + per_row * rows; then one
-        # timed call sized to the budget.
+        # Two calibration calls fit cost = fixed (dictionary build) + per_row * rows.
         def run(k):
             sel = rng.choice(n, size=min(n, k), replace=False)
             t0 = time.perf_counter()
             oracle.conv3(coords, f64, w64, b64, rows=sel)
             return time.perf_counter() - t0
         t_a, t_b = run(64), run(512)
-        per_row = max((t_b - t_a) / (512 - 64), 1e-7)
-        fixed = max(t_a - 64 * per_row, 0.0)
-        rows_target = int(min(n, max(256, (budget_s - fixed) / per_row)))
-        rows = rng.choice(n, size=rows_target, replace=False)
-        t0 = time.perf_counter()
-        oracle.conv3(coords, f64, w64, b64, rows=rows)
-        elapsed = time.perf_counter() - t0
+    per_row = max((t_b - t_a) / (512 - 64), 1e-7)
+    fixed = max(t_a - 64 * per_row, 0.0)
+    rows_each = int(max(256, (budget_s - fixed) / per_row))
+    rows = rng.choice(n, size=min(n, rows_each * procs), replace=False)
+    chunks = np.array_split(rows, procs)
+    ctx = multiprocessing.get_context("spawn")  # no fork of a process that holds the GPU
+    with ctx.Pool(procs) as pool:
+        secs = pool.map(_oracle_worker, [(key, layer, cin, cout, c) for c in chunks])
+    elapsed = max(secs)
     pairs = int(nbr_pairs_per_row[rows].sum())
     flops = 2.0 * pairs * cin * cout
     return {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": procs,
         "kind": "oracle",
-        "sample": (f"oracle.conv3 (float64 dictionary lookup + per-voxel loop, 1 thread) on {rows_target} random "
-                   f"of {n} output rows of workload {key} ({pairs} pairs), including its dictionary build over "
-                   f"all {n} rows; {elapsed:.2f} s"),
+        "sample": (f"oracle.conv3 (float64 dictionary lookup + per-voxel loop) in {procs} host processes of "
+                   f"1 thread, on {len(rows)} random of {n} output rows of workload {key} ({pairs} pairs), each "
+                   f"process building the dictionary over all {n} rows; slowest process {elapsed:.2f} s"),
     }
 
 
@@ -275,18 +311,25 @@ def main():
         # The step above builds a new map every time, so each per-offset call also built that
         # map's pair lists (and synchronised once); the kernel timing below reuses one map.
         pass
-    # Map build alone (includes its one stream synchronisation).
+    # Map build alone, GPU time: events around the enqueue of each build (no host wait inside).
+    stream0.synchronize()
+    bmarks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    built = []
+    for e0, e1 in bmarks:
+        e0.record(stream0)
+        built.append(sc.sparse_indice_map_build(coords, sync=False))
+        e1.record(stream0)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        sc.sparse_indice_map_build(coords).free()
-    torch.cuda.synchronize()
-    build_s = (time.perf_counter() - t0) / args.steps
+    for m in built:
+        m.check()
+        m.free()
+    build_s = float(np.mean([e0.elapsed_time(e1) for e0, e1 in bmarks])) / 1e3
 
     # Convolution kernel alone: HIP events around each of many back-to-back launches on the
     # stream the library launches on (torch's current stream, passed through the binding).
     stream = torch.cuda.current_stream(dev)
     conv_ms = []
+    flush = torch.empty(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     with sc.sparse_indice_map_build(coords) as m:
         k3 = [(ks, cin, cout, w, b) for ks, cin, cout, w, b, _, _ in layers]
         reps = max(args.conv_reps, len(k3))
@@ -306,6 +349,22 @@ def main():
         torch.cuda.synchronize()
         for r in range(reps):
             per_layer[r % len(k3)].append(evs[r][0].elapsed_time(evs[r][1]))
+        pool_path = (not per_offset and layers[0][0] == 3
+                     and sc.sparse_indice_map_plan_state(m) == sc.SUBM_PLAN_READY and layers[0][2] == 128)
+        # Cold caches: 1 GiB written between launches (outside the events) evicts the layer's
+        # working set from the 256 MB MALL and the L2s.
+        cold = []
+        for r in range(min(reps, 40)):
+            flush.fill_(float(r))
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ks, cin, cout, w, b = k3[0]
+            ev0.record(stream)
+            conv(m, ks, x0_dev if not chained else outs[0], w, b, outs[-1])
+            ev1.record(stream)
+            cold.append((ev0, ev1))
+        torch.cuda.synchronize()
+        cold_ms = [a.elapsed_time(b) for a, b in cold]
+    del flush
     # Dominant kernel: the k = 3 layer (all layers of a workload share shape except 2a's k = 1).
     dom = 0
     conv_ms = float(np.mean(per_layer[dom]))
@@ -319,8 +378,9 @@ def main():
     t_mfma = flop_launch / (PEAK_TFLOPS[cfg.dtype] * 1e12)
     t_hbm = bytes_launch / (PEAK_HBM_GBS * 1e9)
     conv_s = conv_ms / 1e3
-    kernel_hash = source_hash(CONV_SOURCE)
-    traffic = None if per_offset else load_traffic(key, kernel_hash)
+    source = "conv_pool.hip" if pool_path else "conv.hip"
+    kernel_hash = source_hash(os.path.join(CSRC, source))
+    traffic = None if per_offset else load_traffic(key, source, kernel_hash)
     if t_mfma >= t_hbm:
         achieved = flop_launch / conv_s / 1e12
         roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS[cfg.dtype], "unit": "TFLOP/s",
@@ -334,6 +394,9 @@ def main():
     # with whole 16-byte output groups; the single-role one from 17 to 32).
     if per_offset and ks == 3:
         kernel = "offset_gemm_kernel (27 launches, one per offset) + round_out_kernel, per call"
+    elif pool_path:
+        # the neighbour-pool kernel, behind the packing of the call's weights (both in the events)
+        kernel = "pool_pack_kernel + pool_conv_kernel (one call)"
     elif (cfg.dtype in ("bf16", "f16") and cout > 32 and ks == 3 and cout % 8 == 0
           and os.environ.get("SUBMCONV_PERSISTENT", "1")[:1] != "0"):
         kernel = "subm_conv_ws_persistent_kernel"
@@ -343,7 +406,7 @@ def main():
         kernel = "subm_conv_mma_kernel"
     else:
         kernel = "subm_conv_generic_kernel"
-    roofline.update({"kernel": kernel, "avg_launch_ms": conv_ms, "launches": len(per_layer[dom]),
+    roofline.update({"kernel": kernel, "kernel_source": source, "avg_launch_ms": conv_ms, "launches": len(per_layer[dom]),
                      "algorithmic_flop_per_launch": flop_launch, "algorithmic_bytes_per_launch": bytes_launch})
     peaks = None if args.no_peaks else measured_peaks(dev)
     if peaks is not None:
@@ -379,14 +442,15 @@ def main():
                       "voxels_per_s_conv": n / conv_s,
                       "step_ms_spread": pct(step_ms),
                       "conv_ms_spread": pct(per_layer[dom]),
+                      "conv_ms_cold_mall": float(np.mean(cold_ms)),
+                      "conv_ms_cold_mall_spread": pct(cold_ms),
                       "map_build_GBps": float(n * (16 + 108 + 4)) / build_s / 1e9,
                       "measured_peaks": peaks},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        ks, cin, cout, _, _, w_cpu, b_cpu = layers[dom]
-        result["cpu_baseline"] = cpu_baseline(key, coords_np, x0, w_cpu, b_cpu, nbr_rows, cin, cout,
-                                              args.cpu_seconds)
+        ks, cin, cout = layers[dom][0], layers[dom][1], layers[dom][2]
+        result["cpu_baseline"] = cpu_baseline(key, plan[dom][3], coords_np, nbr_rows, cin, cout, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
