@@ -76,7 +76,9 @@ typedef enum {
 } subm_map_mode_t;
 
 #define SUBM_TAPS 27
-#define SUBM_MAX_BATCH 65535       /* b must lie in [0, SUBM_MAX_BATCH) */
+#define SUBM_MAX_BATCH 65535       /* b must lie in [0, SUBM_MAX_BATCH): the hash structure packs b
+                                      into 16 bits and keeps the all-ones key for its empty slots,
+                                      so b = 65535 is the one batch index left out */
 #define SUBM_MAX_EXTENT 65534      /* max - min of each of z, y, x must not exceed this */
 
 /*
@@ -130,6 +132,8 @@ int sparse_indice_map_build_async(const int32_t* coords, int64_t n, int mode, hi
  * SUBM_ERR_HIP).  For a map from sparse_indice_map_build_async the first call waits on the host
  * for the build's kernels (not for work enqueued after them); later calls, and calls on
  * synchronously built or derived maps, return at once.  NULL returns SUBM_ERR_INVALID_ARG.
+ * Source: lato.2_mrp_mlx README, "Correctness" (duplicate and out-of-range coordinates are the
+ * failure modes the reference's checks look for).
  */
 int sparse_indice_map_status(submconv_map_t map);
 
@@ -150,6 +154,12 @@ int sparse_indice_map_mode(submconv_map_t map, int* mode);
  * build of a similar size on that same stream, in stream order, so a build / convolve / free
  * loop enqueues no allocator work; other memory goes back to the device's memory pool in order
  * after the work on the build's stream.
+ * Host wait: free blocks the calling thread until the map's own kernels have completed (the
+ * build's lookup kernel and, if one was built, the neighbour-pool plan kernel: they write memory
+ * of the map that goes back to the pool, and their completion events and pinned flag words are
+ * recycled).  It does not wait for convolutions or copies enqueued on the map.
+ * Source: lato.2_mrp_mlx README, header summary (the indice map is built once per coordinate set
+ * and dropped with it).
  */
 int sparse_indice_map_free(submconv_map_t map);
 
@@ -183,6 +193,8 @@ int sparse_indice_map_plan_state(submconv_map_t map, int* state);
  *   nbr     device int32 [n, 27] in input row order; nbr[i, k] is the input row of the active
  *           voxel at coord_i + offset(k), or -1.  Independent of any internal ordering.
  *   stream  stream on which the copy is enqueued (asynchronous).
+ * Source: lato.2_mrp_mlx README, header summary (the 27-lookup neighbour map per voxel); the
+ * copy exists so that tests can compare the map with the oracle's rulebook bit for bit.
  */
 int sparse_indice_map_copy_nbr(submconv_map_t map, int32_t* nbr, hipStream_t stream);
 
