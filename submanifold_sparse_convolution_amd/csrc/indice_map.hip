@@ -348,7 +348,7 @@ __global__ __launch_bounds__(3 * kLookupVoxels) void map_lookup_kernel(const int
                                                                       uint32_t* __restrict__ masks,
                                                                       uint32_t* __restrict__ banks,
                                                                       const MapStats* __restrict__ st) {
-  __shared__ int32_t s_out[kLookupVoxels * 27];
+  __shared__ __align__(16) int32_t s_out[kLookupVoxels * 27];
   __shared__ uint32_t s_pm[3][kLookupVoxels];
   __shared__ uint32_t s_cnt[27];
   // Out-of-range coordinates (no structure built): every entry -1, so that work already enqueued
@@ -412,8 +412,12 @@ __global__ __launch_bounds__(3 * kLookupVoxels) void map_lookup_kernel(const int
   __syncthreads();
   const int64_t rows = (n - i0) < kLookupVoxels ? (n - i0) : kLookupVoxels;
   const int total = (int)rows * 27;
-  int32_t* dst = nbr + i0 * 27;
-  for (int e = t; e < total; e += 3 * kLookupVoxels) dst[e] = s_out[e];
+  int32_t* dst = nbr + i0 * 27;  // 16-byte aligned: i0 is a multiple of 256
+  for (int e = 4 * t; e < total; e += 4 * 3 * kLookupVoxels) {
+    if (e + 3 < total) *reinterpret_cast<int4*>(dst + e) = *reinterpret_cast<const int4*>(s_out + e);
+    else
+      for (int k = e; k < total; ++k) dst[k] = s_out[k];
+  }
   if (plane == 0 && i < n) masks[i] = s_pm[0][v] | s_pm[1][v] | s_pm[2][v];
   // Per-tap hit counts: one ballot per tap of the plane and wave, LDS adds, 27 global adds per block.
 #pragma unroll
