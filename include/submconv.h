@@ -177,6 +177,25 @@ int sparse_indice_map_info(submconv_map_t map, int64_t* n, int64_t* pairs);
 int sparse_indice_map_offset_counts(submconv_map_t map, int64_t* counts);
 
 /*
+ * subm_release_cached_memory -- free the device memory the library keeps between calls on the
+ * current device, and wait for the device.  Resident until then (per device):
+ *   - the map-build workspace: grown to the largest build so far, never shrunk by itself:
+ *     statistics and partials (~130 KB), 4 bytes per row, and the dense grid (4 bytes per cell of
+ *     the set's bounding box with a one-cell margin, at most 128 cells per row and 2 GiB) or the
+ *     hash table (32 bytes per row), whichever the build sizes for, rounded up to 64 MiB;
+ *   - the rulebook blocks of freed maps kept for reuse on their stream (at most 8 and at most
+ *     1 GiB; a block is 112 bytes per row);
+ *   - the packed-weight buffers of the neighbour-pool kernel, one per stream that ran it (at most
+ *     16; 27 x 128 x cin x 2 bytes, rounded up to 1 MiB).
+ * Live maps keep their own memory (rulebook, plan), freed with them; the static array of
+ * subm_conv3d_forward_noalloc (1,769,472 bytes) stays for the life of the process.  The call
+ * waits for all work on the device (hipDeviceSynchronize) while it holds the library's locks, so
+ * calls from other threads on this device block until it returns.  Later calls allocate again
+ * as needed.
+ */
+int subm_release_cached_memory(void);
+
+/*
  * sparse_indice_map_plan_state -- *state (host int) = the state of the map's neighbour-pool plan
  * (see subm_conv3d_forward): SUBM_PLAN_NONE (no eligible convolution has run on the map yet),
  * SUBM_PLAN_PENDING (enqueued; the host has not seen its overflow flag yet), SUBM_PLAN_READY

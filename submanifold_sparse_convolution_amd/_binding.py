@@ -37,6 +37,7 @@ C_FUNCTIONS = (
     "sparse_indice_map_offset_counts",
     "sparse_indice_map_copy_nbr",
     "sparse_indice_map_plan_state",
+    "subm_release_cached_memory",
     "subm_conv3d_forward",
     "subm_conv3d_forward_noalloc",
     "subm_conv3d_forward_per_offset",
@@ -95,6 +96,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.sparse_indice_map_offset_counts.argtypes = [vp, ctypes.POINTER(i64)]
         lib.sparse_indice_map_copy_nbr.argtypes = [vp, vp, vp]
         lib.sparse_indice_map_plan_state.argtypes = [vp, ctypes.POINTER(ci)]
+        lib.subm_release_cached_memory.argtypes = []
         lib.subm_conv3d_forward.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp]
         lib.subm_conv3d_forward_noalloc.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp]
         lib.subm_conv3d_forward_per_offset.argtypes = [vp, i64, ci, ci, ci, vp, vp, vp, vp, vp]
@@ -270,6 +272,15 @@ def sparse_indice_map_mode(m: IndiceMap) -> int:
 
 
 SUBM_PLAN_NONE, SUBM_PLAN_PENDING, SUBM_PLAN_READY, SUBM_PLAN_OVERFLOW = 0, 1, 2, 3
+
+
+def subm_release_cached_memory(device=None) -> None:
+    """Free the library's cached device memory on `device` (default: torch's current device),
+    after waiting for that device; see subm_release_cached_memory in include/submconv.h."""
+    lib = load_library()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with _on_device(dev):
+        _check(lib, "subm_release_cached_memory", lib.subm_release_cached_memory())
 
 
 def sparse_indice_map_plan_state(m: IndiceMap) -> int:

@@ -253,6 +253,7 @@ struct BlockCache {
 };
 BlockCache g_blocks[kMaxDevices];
 constexpr size_t kCachedBlocks = 8;
+constexpr size_t kCachedBlockBytes = size_t(1) << 30;  // and at most 1 GiB of them per device
 
 void release_map(submconv_map* m) {
   if (m->d.ready != nullptr) {
@@ -352,7 +353,9 @@ void submconv::map_memory_give(int dev, void* ptr, size_t bytes, hipStream_t str
   if (reusable && dev >= 0 && dev < kMaxDevices) {
     BlockCache& cache = g_blocks[dev];
     std::lock_guard<std::mutex> lock(cache.mu);
-    if (cache.blocks.size() < kCachedBlocks) {
+    size_t held = 0;
+    for (const CachedBlock& b : cache.blocks) held += b.bytes;
+    if (cache.blocks.size() < kCachedBlocks && held + bytes <= kCachedBlockBytes) {
       CachedBlock b;
       b.ptr = ptr;
       b.bytes = bytes;
@@ -653,6 +656,38 @@ Status pool_prepare(submconv_map* map, hipStream_t stream, int* state) {
 }
 
 }  // namespace
+
+extern "C" int subm_release_cached_memory(void) {
+  clear_error();
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(SUBM_ERR_HIP, "subm_release_cached_memory: no current device");
+  Workspace& ws = g_workspace[dev];
+  BlockCache& cache = g_blocks[dev];
+  ScratchCache& sc = g_scratch[dev];
+  // hold every cache while the device drains, so that nothing new is enqueued on their memory
+  std::lock_guard<std::mutex> l1(ws.mu);
+  std::lock_guard<std::mutex> l2(cache.mu);
+  std::lock_guard<std::mutex> l3(sc.mu);
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail(hip_status(e, "subm_release_cached_memory"));
+  if (ws.ptr != nullptr) {
+    e = hipFree(ws.ptr);
+    ws.ptr = nullptr;
+    ws.bytes = 0;
+    ws.cells_cap = 0;
+    ws.table_cap = 0;
+    ws.prev_n = 0;
+    if (e != hipSuccess) return fail(hip_status(e, "subm_release_cached_memory workspace"));
+  }
+  for (const CachedBlock& b : cache.blocks) device_free(b.ptr, b.stream);
+  cache.blocks.clear();
+  for (const ScratchEntry& x : sc.entries) device_free(x.ptr, x.stream);
+  sc.entries.clear();
+  e = hipDeviceSynchronize();  // (the stream-ordered frees above)
+  if (e != hipSuccess) return fail(hip_status(e, "subm_release_cached_memory"));
+  return SUBM_OK;
+}
 
 extern "C" int sparse_indice_map_plan_state(submconv_map_t map, int* state) {
   clear_error();

@@ -218,3 +218,24 @@ def test_ineligible_calls_keep_the_general_kernels(monkeypatch):
         torch.cuda.synchronize()
         assert state(m) == sc.SUBM_PLAN_NONE  # fewer rows than one full tile per compute unit
     check_features(ys, oracle.rulebook_sorted(small), as64(fs), as64(ws), as64(bs), "bf16", "small set")
+
+
+def test_release_cached_memory_and_build_again():
+    coords = shell()
+    f, w, b = inputs(len(coords), 128, "bf16", seed=23)
+    fd, wd, bd = dev(f, w, b)
+    cd = torch.from_numpy(coords).to(DEV)
+    with sc.sparse_indice_map_build(cd) as m:
+        y1 = sc.subm_conv3d_forward(m, fd, wd, bd)
+        torch.cuda.synchronize()
+    free_before = torch.cuda.mem_get_info()[0]
+    sc.subm_release_cached_memory()
+    sc.subm_release_cached_memory()  # nothing left to free: a no-op
+    free_after = torch.cuda.mem_get_info()[0]
+    # (the runtime may keep freed blocks for reuse, so only the direction is checked)
+    assert free_after >= free_before
+    with sc.sparse_indice_map_build(cd) as m:  # everything is allocated again on demand
+        y2 = sc.subm_conv3d_forward(m, fd, wd, bd)
+        y3 = sc.subm_conv3d_forward(m, fd, wd, bd)
+        torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y2, y3)
