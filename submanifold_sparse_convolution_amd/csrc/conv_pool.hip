@@ -278,23 +278,26 @@ __global__ __launch_bounds__(3 * kPT, 2) void pool_plan_kernel(const int32_t* __
 // (q, t, kk) is one contiguous 4 KB block, and in it the operand-A fragment of output block ob is
 // 1 KB in lane order: lane l = 32 lk + r holds output channel 32 ob + r, input channels
 // 32 q + 8 (2 kk + lk) .. + 8.  Consecutive lanes then read consecutive 16-byte units, the
-// pattern the LDS serves fastest.
+// pattern the LDS serves fastest.  One workgroup per (ob, t): it reads the 32 channels' rows of tap
+// t (cin * 2 contiguous bytes each, 512 bytes at a time) into LDS and writes, for every 16-byte
+// column c = 4 q + 2 kk + lk, the 32 rows' units as one contiguous 512-byte run.
 __global__ __launch_bounds__(256) void pool_pack_kernel(const uint4* __restrict__ w, int cin, uint4* __restrict__ wpk) {
-  const int64_t total = (int64_t)(cin / 32) * 27 * 2 * 128 * 2;
-  const int row16 = cin / 8;  // 16-byte chunks per (co, tap) row
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    int64_t x = i;
-    const int r = (int)(x & 31);
-    x >>= 5;
-    const int lk = (int)(x & 1);
-    x >>= 1;
-    const int ob = (int)(x & 3);
-    x >>= 2;
-    const int kk = (int)(x & 1);
-    x >>= 1;
-    const int t = (int)(x % 27);
-    const int q = (int)(x / 27);
-    wpk[i] = w[((int64_t)(32 * ob + r) * 27 + t) * row16 + 4 * q + 2 * kk + lk];
+  __shared__ uint4 s_rows[32 * 33];  // [r][c - c0], rows padded by one unit against bank conflicts
+  const int ob = (int)blockIdx.x / 27, t = (int)blockIdx.x % 27;
+  const int row16 = cin / 8;  // 16-byte units per (co, tap) row
+  for (int c0 = 0; c0 < row16; c0 += 32) {
+    const int nc = min(32, row16 - c0);
+    for (int i = threadIdx.x; i < 32 * nc; i += blockDim.x) {
+      const int r = i / nc, c = i - r * nc;
+      s_rows[r * 33 + c] = w[((int64_t)(32 * ob + r) * 27 + t) * row16 + c0 + c];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 32 * nc; i += blockDim.x) {
+      const int c = c0 + (i >> 5), r = i & 31;
+      const int q = c >> 2, kk = (c >> 1) & 1, lk = c & 1;
+      wpk[((((int64_t)(q * 27 + t) * 2 + kk) * 4 + ob) * 2 + lk) * 32 + r] = s_rows[r * 33 + (i >> 5)];
+    }
+    __syncthreads();
   }
 }
 
@@ -699,9 +702,7 @@ hipError_t launch_pool_conv(const PoolTiling& t, const void* plan, const uint32_
                             const void* feats, const void* weight, const void* bias, void* out, void* wpk,
                             hipStream_t stream) {
   const size_t wbytes = pool_weight_bytes(cin);
-  const int64_t units = (int64_t)(wbytes / 16);
-  pool_pack_kernel<<<(unsigned)std::min<int64_t>((units + 255) / 256, 1024), 256, 0, stream>>>(
-      static_cast<const uint4*>(weight), cin, static_cast<uint4*>(wpk));
+  pool_pack_kernel<<<4 * 27, 256, 0, stream>>>(static_cast<const uint4*>(weight), cin, static_cast<uint4*>(wpk));
   PoolArgs a{};
   a.feats = feats;
   a.wpk = wpk;
