@@ -105,7 +105,7 @@ def test_plan_states_and_the_gated_first_call():
 
 
 @pytest.mark.parametrize("dtype,cin", [("bf16", 32), ("bf16", 64), ("bf16", 96), ("bf16", 160), ("bf16", 256),
-                                       ("f16", 128), ("f16", 64)])
+                                       ("bf16", 288), ("bf16", 512), ("f16", 128), ("f16", 64)])
 def test_channel_counts_and_dtypes(dtype, cin):
     coords = shell()
     f, w, b = inputs(len(coords), cin, dtype, seed=cin)
