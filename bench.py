@@ -192,9 +192,16 @@ def cpu_baseline(key, layer, coords, nbr_pairs_per_row, cin, cout, budget_s):
             t0 = time.perf_counter()
             oracle.conv3(coords, f64, w64, b64, rows=sel)
             return time.perf_counter() - t0
-        t_a, t_b = run(64), run(512)
-    per_row = max((t_b - t_a) / (512 - 64), 1e-7)
-    fixed = max(t_a - 64 * per_row, 0.0)
+        ka, kb = min(n, 256), min(n, 2048)
+        t_a, t_b = run(ka), run(kb)
+    if kb > ka:
+        per_row = max((t_b - t_a) / (kb - ka), 1e-7)
+        fixed = max(t_a - ka * per_row, 0.0)
+    else:  # (a set of at most 256 rows: one call covers it)
+        per_row, fixed = t_b / kb, 0.0
+    # one core on the whole layer, from the same fit: the dictionary build plus every row
+    layer_one_core_s = fixed + n * per_row
+    layer_flops = 2.0 * float(nbr_pairs_per_row.sum()) * cin * cout
     rows_each = int(max(256, (budget_s - fixed) / per_row))
     rows = rng.choice(n, size=min(n, rows_each * procs), replace=False)
     chunks = np.array_split(rows, procs)
@@ -212,6 +219,13 @@ def cpu_baseline(key, layer, coords, nbr_pairs_per_row, cin, cout, budget_s):
         "sample": (f"oracle.conv3 (float64 dictionary lookup + per-voxel loop) in {procs} host processes of "
                    f"1 thread, on {len(rows)} random of {n} output rows of workload {key} ({pairs} pairs), each "
                    f"process building the dictionary over all {n} rows; slowest process {elapsed:.2f} s"),
+        "single_core": {
+            "value": layer_flops / layer_one_core_s / 1e12,
+            "unit": "TFLOP/s",
+            "layer_s": layer_one_core_s,
+            "fit": (f"one process of 1 thread on {ka} and {kb} random rows: dictionary build {fixed:.3f} s + "
+                    f"{per_row * 1e6:.1f} us per row, extrapolated to all {n} rows"),
+        },
     }
 
 

@@ -120,10 +120,12 @@ def test_child_map_drives_the_convolution_bit_exactly():
 
 
 def test_subdivide_three_rounds_full_size():
-    """Config-5 structure at full size: three subdivisions of the 64^3 shell (5.1 M children),
-    each child map derived from its parent map, checked by properties that hold at any size:
-    the doubled parent of every child, and every rulebook entry's coordinate difference."""
-    coords = dev_coords(synth.coords_for("2a"))
+    """Three subdivisions of the 64^3 shell and torus (22,406 -> 11,471,872 children), each child
+    map derived from its parent map, checked by properties that hold at any size (the doubled
+    parent of every child, every rulebook entry's coordinate difference, symmetry) and, at the
+    last level, in full against the oracle: its subdivided coordinates and their rulebook."""
+    base = synth.coords_for("2a")
+    coords = dev_coords(base)
     pm = sc.sparse_indice_map_build(coords)
     for level in range(3):
         s = sc.sparse_subdivide(coords)
@@ -147,10 +149,18 @@ def test_subdivide_three_rounds_full_size():
             assert torch.equal(nbr[j[hit], 26 - k], rows[hit])
         assert int((nbr >= 0).sum()) == cm.pairs
         if level == 2:
-            # the last level against the hashing build on the same 5.1 M coordinates
+            # the last level against the hashing build on the same 11.5 M coordinates
             with sc.sparse_indice_map_build(fine) as bm:
                 assert torch.equal(sc.sparse_indice_map_copy_nbr(bm).long(), nbr)
                 assert sc.sparse_indice_map_offset_counts(bm) == sc.sparse_indice_map_offset_counts(cm)
+            # and against the oracle: three rounds of its subdivision of the base set, then its
+            # rulebook of the 11.5 M children (bit for bit, coordinates and rulebook)
+            want = base
+            for _ in range(3):
+                want, _, _ = oracle.structure_ref.subdivide(want)
+            assert np.array_equal(fine.cpu().numpy(), want)
+            assert np.array_equal(nbr.int().cpu().numpy(), oracle.rulebook_sorted(want))
+            print("  level 3 equals the oracle's subdivision and rulebook", flush=True)
         torch.cuda.synchronize()
         print(f"  level {level + 1}: {s.n_fine} children, {cm.pairs} pairs", flush=True)
         pm.free()
