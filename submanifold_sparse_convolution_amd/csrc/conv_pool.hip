@@ -6,25 +6,26 @@
 // coord_i + d.)  The same sum as the kernels of conv.hip, computed in a different order of
 // memory traffic.
 //
-// Design.  A workgroup (four waves, one per SIMD) owns a tile of 16 or 17 row blocks of 32
-// consecutive rows and all 128 output channels; each wave keeps a 128-row x 128-channel block of
-// fp32 accumulators in its AGPRs (the seventeenth block, when there is one, is shared: each wave
-// holds its 32-channel quarter of it in VGPRs).  The rows that the tile's rows reach through the
-// nine taps of one dz (the tile's "sub-pool" for that dz: at most 768 distinct rows on every
-// workload measured, and sorted by row) are gathered ONCE per 32-channel slice into LDS and read
-// by all nine taps, instead of being gathered again for every tap: the tile's rows reach about
-// 3.1 distinct rows each on the 128^3 shell, against 20.9 gathered per row tap by tap.  A plan,
-// built once per map by pool_plan_kernel, lists each sub-pool's rows and, for every (tap, row),
-// the LDS slot of its neighbour (a zero row when it is absent).
+// Design.  A workgroup (eight waves, two per SIMD) owns a tile of 16 or 17 row blocks of 32
+// consecutive rows and all 128 output channels; each wave keeps a 64-row x 128-channel block of
+// fp32 accumulators (two row blocks x four output blocks; the seventeenth row block, when there is
+// one, is shared by waves 0..3, each holding its 32-channel quarter).  The rows that the tile's
+// rows reach through the nine taps of one dz (the tile's "sub-pool" for that dz: at most 768
+// distinct rows on every workload measured, and sorted by row) are gathered ONCE per 32-channel
+// slice into LDS and read by all nine taps, instead of being gathered again for every tap: the
+// tile's rows reach about 3.1 distinct rows each on the 128^3 shell, against 20.9 gathered per
+// row tap by tap.  A plan, built once per map by pool_plan_kernel, lists each sub-pool's rows and,
+// for every (tap, row), the LDS slot of its neighbour (a zero row when it is absent).
 //
 // The reduction runs over steps (slice q of 32 input channels, dz, the nine (dy, dx) taps): per
-// step a wave issues 2 x 17 v_mfma_f32_32x32x16 (weights as operand A from a 6-slot LDS ring of
-// half-steps, neighbour rows as operand B from the sub-pool), one barrier, and its share of the
-// loads that run ahead: the weight half-steps three steps ahead (weights are pre-packed so that a
-// half-step is one contiguous 4 KB block), one tap of the slot table four steps ahead, two
-// direct-to-LDS gathers of the next sub-pool (steps 0..5 of each nine) and, once per sub-pool,
-// one group of row ids.  Every load goes out behind its own MFMA, so the single wave per SIMD
-// does not stall on a run of loads while its matrix core idles.  A finished tile is rounded
+// step a wave issues 2 x 8 (or 9) v_mfma_f32_32x32x16 (weights as operand A from a 6-slot LDS
+// ring of half-steps, neighbour rows as operand B from the sub-pool), one barrier, and its share
+// of the loads that run ahead: a quarter of a weight half-step three steps ahead (weights are
+// pre-packed so that a half-step is one contiguous 4 KB block), a quarter of one slot-table tap
+// four steps ahead (waves 0..3), one direct-to-LDS gather of the next sub-pool (steps 0..5 of each
+// nine) and, once per sub-pool, an eighth of one group of row ids.  With two waves per SIMD one
+// wave's MFMAs cover the other's waits for LDS reads (measured 1.6 % faster on the shell and 3 %
+// on the dense grid than one wave per SIMD holding twice the rows).  A finished tile is rounded
 // (one RNE conversion after + bias in fp32) and written through LDS as whole 256-byte rows.
 //
 // LDS (162,112 bytes): two sub-pool buffers of 769 x 64 bytes (slot 768 is a zero row), the
@@ -41,7 +42,8 @@
 namespace submconv {
 namespace {
 
-constexpr int kPT = 256;        // threads: four waves, one per SIMD
+constexpr int kPT = 256;        // threads of one plan group (the plan kernel runs three)
+constexpr int kCT = 512;        // threads of the convolution: eight waves, two per SIMD
 constexpr int kSL = 64;         // bytes of a row per slice (32 channels)
 constexpr int kWH = 128 * 32;   // a weight half-step: 128 output channels x 16 input channels
 constexpr int kWS = 6;          // weight half-steps held in LDS
@@ -52,8 +54,8 @@ struct PoolShape {
   static constexpr int NBLK = 16 + E;             // row blocks of 32 per tile
   static constexpr int TAPB = NBLK * 64;          // slot table bytes per tap (u16 per row)
   static constexpr int TABB = 27 * TAPB;
-  static constexpr int WSLOTS = kUcap / 4;        // pool slots gathered by one wave
-  static constexpr int NJ = kUcap / 64;           // gather loads per wave per sub-pool
+  static constexpr int WSLOTS = kUcap / 8;        // pool slots gathered by one wave (of eight)
+  static constexpr int NJ = kUcap / 128;          // gather loads per wave per sub-pool
   static constexpr int IDB = kUcap * 4;           // row ids of one dz group
   static constexpr int RECB = TABB + 3 * IDB;     // plan record of one tile
   static constexpr int POOLB = (kUcap + 1) * kSL; // one sub-pool buffer, zero slot last
@@ -64,8 +66,8 @@ struct PoolShape {
   static constexpr int LDSB = O_BIAS + 128 * 4;
   static_assert(kUcap % 64 == 0 && WSLOTS % 16 == 0, "whole gather loads per wave");
   static_assert(LDSB <= 160 * 1024, "LDS");
-  static_assert((TAPB / 4) % 16 == 0 && (IDB / 4) % 16 == 0, "refills in whole 16-byte lanes");
-  static_assert(NJ == 12, "the load schedule assumes 12 gathers per wave per sub-pool");
+  static_assert((TAPB / 4) % 16 == 0 && (IDB / 8) % 16 == 0, "refills in whole 16-byte lanes");
+  static_assert(NJ == 6, "the load schedule assumes 6 gathers per wave per sub-pool");
   static_assert(RECB % 16 == 0, "records in whole 16-byte chunks");
 };
 
@@ -321,7 +323,9 @@ struct PoolArgs {
 
 template <int V> using IC = std::integral_constant<int, V>;
 
-// acc += a * b with the accumulator in VGPRs (the AGPRs hold the other sixteen blocks).
+// acc += a * b for the shared seventeenth block, as inline assembly with the accumulator in
+// VGPRs: measured ~2 % faster on the shell than the builtin, whose scheduling and hazard waits
+// around this ninth, conditional MFMA cost more than the explicit wait before the final write.
 template <DT D>
 __device__ __forceinline__ void mfma32_vgpr(f32x16_t& acc, const uint4& a, const uint4& b) {
   const i32x4_t av = __builtin_bit_cast(i32x4_t, a), bv = __builtin_bit_cast(i32x4_t, b);
@@ -332,7 +336,7 @@ __device__ __forceinline__ void mfma32_vgpr(f32x16_t& acc, const uint4& a, const
 }
 
 template <DT D, int E>
-__global__ __launch_bounds__(kPT, 1) void pool_conv_kernel(const PoolArgs a) {
+__global__ __launch_bounds__(kCT, 1) void pool_conv_kernel(const PoolArgs a) {
   using P = PoolShape<E>;
   using T = typename Elem<D>::T;
   __shared__ __align__(16) unsigned char lds[P::LDSB];
@@ -341,6 +345,11 @@ __global__ __launch_bounds__(kPT, 1) void pool_conv_kernel(const PoolArgs a) {
   if (a.gate != nullptr && pool_any_flag(a.gate, 3 * a.ntiles)) return;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Waves w and w + 4 share a SIMD.  wq: the wave's quarter of a weight half-step (its 1 KB share
+  // of the loads) and the rotation of its operand-A reads; waves 0..3 also load the slot table and
+  // hold the shared seventeenth row block.
+  const int wq = w & 3;
+  const bool lo4 = w < 4;
   const int lr = lane & 31, lk = lane >> 5;
   // Workgroups are dealt to the eight XCDs round-robin: virtual block v takes the tiles
   // [v per_wg, (v + 1) per_wg), so each XCD walks one contiguous range of rows.
@@ -363,27 +372,26 @@ __global__ __launch_bounds__(kPT, 1) void pool_conv_kernel(const PoolArgs a) {
   if (tid < 8)
     *reinterpret_cast<uint4*>(lds + (tid >> 2) * P::POOLB + kUcap * kSL + (tid & 3) * 16) = make_uint4(0, 0, 0, 0);
 
-  // Per-lane constants.  A gather lane of load j of wave w fills slot w * 192 + 16 j + lane / 4,
+  // Per-lane constants.  A gather lane of load j of wave w fills slot w * 96 + 16 j + lane / 4,
   // 16-byte unit lane % 4, so it fetches chunk (lane % 4) ^ ((slot >> 1) & 3) = (lane % 4) ^ ((lane / 8) % 4).
   const uint32_t gchunk = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) * 16);
-  // Operand A position j of a wave holds output block (w + j) % 4; its fragment is the 1 KB run
+  // Operand A position j of a wave holds output block (wq + j) % 4; its fragment is the 1 KB run
   // of that block in the half-step, 16 bytes per lane in lane order.
   uint32_t a_off[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) a_off[j] = (uint32_t)(((w + j) & 3) * 1024 + lane * 16);
+  for (int j = 0; j < 4; ++j) a_off[j] = (uint32_t)(((wq + j) & 3) * 1024 + lane * 16);
 
   int ids[P::NJ];
-  auto read_ids = [&](int dz) {
-    const uint4* p = reinterpret_cast<const uint4*>(lds + P::O_IDS + dz * P::IDB + (w * 16 + (lane >> 2)) * P::NJ * 4);
+  auto load_ids = [&](const unsigned char* base) {
+    const uint2* p = reinterpret_cast<const uint2*>(base + (w * 16 + (lane >> 2)) * P::NJ * 4);
 #pragma unroll
-    for (int u = 0; u < P::NJ / 4; ++u) {
-      const uint4 x = p[u];
-      ids[4 * u] = (int)x.x;
-      ids[4 * u + 1] = (int)x.y;
-      ids[4 * u + 2] = (int)x.z;
-      ids[4 * u + 3] = (int)x.w;
+    for (int u = 0; u < P::NJ / 2; ++u) {
+      const uint2 x = p[u];
+      ids[2 * u] = (int)x.x;
+      ids[2 * u + 1] = (int)x.y;
     }
   };
+  auto read_ids = [&](int dz) { load_ids(lds + P::O_IDS + dz * P::IDB); };
   // gather load j of a sub-pool of slice q into pool buffer buf (live = false: reads nothing)
   auto gather1 = [&](int j, int q, int buf, bool live) {
     const uint32_t qoff = (uint32_t)(q * kSL) + gchunk;
@@ -391,58 +399,50 @@ __global__ __launch_bounds__(kPT, 1) void pool_conv_kernel(const PoolArgs a) {
     const uint32_t off = (live && ids[j] >= 0) ? (uint32_t)ids[j] * (uint32_t)a.row_bytes + qoff : kOutOfRange;
     lds_dma16(rs_f, off, dst + (uint32_t)(j * 16 * kSL));
   };
-  // weight half-step (step = q * 27 + t, kk) -> half-slot: one contiguous 4 KB block of the packed
-  // weights (loading the 32-byte runs of the KRSC tensor directly measured 19-20 % slower on the
-  // shell and the dense grid, each load touching 32 cache lines instead of 8)
+  // this wave's quarter of weight half-step (step = q * 27 + t, kk) -> half-slot: the packed
+  // weights make a half-step one contiguous 4 KB block
   auto issue_w = [&](int step, int kk, int hslot) {
-    const uint32_t src = (uint32_t)(2 * step + kk) * kWH + (uint32_t)(w * 1024) + (uint32_t)lane * 16u;
-    lds_dma16(rs_w, src, lbase + P::O_W + (uint32_t)(hslot * kWH + w * 1024));
+    const uint32_t src = (uint32_t)(2 * step + kk) * kWH + (uint32_t)(wq * 1024) + (uint32_t)lane * 16u;
+    lds_dma16(rs_w, src, lbase + P::O_W + (uint32_t)(hslot * kWH + wq * 1024));
   };
-  // slot-table tap t of a tile (tile < 0: nothing to load)
+  // slot-table tap t of a tile (tile < 0: nothing to load); waves 0..3
   auto issue_table = [&](int tile, int t) {
     const uint32_t off = tile < 0 ? kOutOfRange
-                                  : (uint32_t)tile * P::RECB + (uint32_t)(t * P::TAPB + w * (P::TAPB / 4)) + (uint32_t)lane * 16u;
-    if (lane < P::TAPB / 64) lds_dma16(rs_p, off, lbase + P::O_TAB + (uint32_t)(t * P::TAPB + w * (P::TAPB / 4)));
+                                  : (uint32_t)tile * P::RECB + (uint32_t)(t * P::TAPB + wq * (P::TAPB / 4)) + (uint32_t)lane * 16u;
+    if (lane < P::TAPB / 64) lds_dma16(rs_p, off, lbase + P::O_TAB + (uint32_t)(t * P::TAPB + wq * (P::TAPB / 4)));
   };
-  // row-id group dz of a tile (tile < 0: nothing to load)
+  // row-id group dz of a tile (tile < 0: nothing to load); every wave loads an eighth
   auto issue_ids = [&](int tile, int dz) {
     const uint32_t off = tile < 0 ? kOutOfRange
-                                  : (uint32_t)tile * P::RECB + (uint32_t)(P::TABB + dz * P::IDB + w * (P::IDB / 4)) +
+                                  : (uint32_t)tile * P::RECB + (uint32_t)(P::TABB + dz * P::IDB + w * (P::IDB / 8)) +
                                         (uint32_t)lane * 16u;
-    if (lane < P::IDB / 64) lds_dma16(rs_p, off, lbase + P::O_IDS + (uint32_t)(dz * P::IDB + w * (P::IDB / 4)));
+    if (lane < P::IDB / 128) lds_dma16(rs_p, off, lbase + P::O_IDS + (uint32_t)(dz * P::IDB + w * (P::IDB / 8)));
   };
 
   // ---- prologue: the gathers of the first tile's sub-pool 0 go out as soon as this lane's row
   // ids arrive (straight from the record); slot-table taps 0..3 (the loop loads each tap four
   // steps ahead), row-id groups 1 and 2 and the first five weight half-steps follow.
   {
-    const uint4* rid = reinterpret_cast<const uint4*>(a.plan + (size_t)tile0 * P::RECB + P::TABB +
-                                                      (w * 16 + (lane >> 2)) * P::NJ * 4);
-#pragma unroll
-    for (int u = 0; u < P::NJ / 4; ++u) {
-      const uint4 x = rid[u];
-      ids[4 * u] = (int)x.x;
-      ids[4 * u + 1] = (int)x.y;
-      ids[4 * u + 2] = (int)x.z;
-      ids[4 * u + 3] = (int)x.w;
-    }
+    load_ids(a.plan + (size_t)tile0 * P::RECB + P::TABB);
 #pragma unroll
     for (int j = 0; j < P::NJ; ++j) gather1(j, 0, 0, true);
     const uint4* rec = reinterpret_cast<const uint4*>(a.plan + (size_t)tile0 * P::RECB);
     uint4* dst = reinterpret_cast<uint4*>(lds + P::O_TAB);
-    for (int i = tid; i < 4 * P::TAPB / 16; i += kPT) dst[i] = rec[i];
-    for (int i = tid; i < 2 * P::IDB / 16; i += kPT) dst[(P::TABB + P::IDB) / 16 + i] = rec[(P::TABB + P::IDB) / 16 + i];
+    for (int i = tid; i < 4 * P::TAPB / 16; i += kCT) dst[i] = rec[i];
+    for (int i = tid; i < 2 * P::IDB / 16; i += kCT) dst[(P::TABB + P::IDB) / 16 + i] = rec[(P::TABB + P::IDB) / 16 + i];
     const uint4* wsrc = reinterpret_cast<const uint4*>(a.wpk);
     uint4* wdst = reinterpret_cast<uint4*>(lds + P::O_W);
-    for (int i = tid; i < 5 * kWH / 16; i += kPT) wdst[i] = wsrc[i];  // half-steps (0,0) .. (2,0)
+    for (int i = tid; i < 5 * kWH / 16; i += kCT) wdst[i] = wsrc[i];  // half-steps (0,0) .. (2,0)
     wait_vmcnt<0>();
     __syncthreads();
   }
 
-  f32x16_t acc[4][4];
+  // Accumulators: row blocks 2 w and 2 w + 1 of the tile, all four output blocks; waves
+  // 0..3 also hold output block w of the seventeenth row block, when there is one (VGPRs).
+  f32x16_t acc[2][4];
   f32x16_t accx;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -450,16 +450,16 @@ __global__ __launch_bounds__(kPT, 1) void pool_conv_kernel(const PoolArgs a) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) accx[e] = 0.f;
 
-  constexpr int NB4 = 4 + E;
-  constexpr int NU = 16 + E;  // MFMAs per half-step
-  uint32_t soff[NB4], soff_n[NB4];
-  uint4 fa[2][4], fb[2][NB4];
+  constexpr int NB = 2 + E;  // operand-B fragments per half-step (the third: waves 0..3)
+  constexpr int NU = 8 + E;  // MFMA units per half-step (unit 8: waves 0..3)
+  uint32_t soff[NB], soff_n[NB];
+  uint4 fa[2][4], fb[2][NB];
 
   auto read_slots = [&](int t, uint32_t* dst) {
     const uint16_t* tab = reinterpret_cast<const uint16_t*>(lds + P::O_TAB + t * P::TAPB);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = tab[(4 * w + i) * 32 + lr];
-    if constexpr (E) dst[4] = tab[16 * 32 + lr];
+    for (int i = 0; i < 2; ++i) dst[i] = tab[(2 * w + i) * 32 + lr];
+    if constexpr (E) dst[2] = tab[16 * 32 + lr];
   };
   auto read_a = [&](auto SET, int hslot, int j) {
     constexpr int st = decltype(SET)::value;
@@ -470,28 +470,26 @@ __global__ __launch_bounds__(kPT, 1) void pool_conv_kernel(const PoolArgs a) {
     const uint32_t cx = (uint32_t)((2 * kk + lk) << 4);
     fb[st][i] = *reinterpret_cast<const uint4*>(lds + pbuf * P::POOLB + (so[i] ^ cx));
   };
-  // MFMAs [LO, HI) of one half-step: unit u = 4 i + j (row block i, operand A position j); unit
-  // 16 is the shared extra block with this wave's own output block.
+  // MFMAs [LO, HI) of one half-step: unit u = 4 i + j (row block 2 w + i, operand A position j);
+  // unit 8 is the shared block with this wave's own output block (waves 0..3).
   auto mfmas = [&](auto SET, auto LO, auto HI) {
     constexpr int st = decltype(SET)::value;
     constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
 #pragma unroll
     for (int u = lo; u < hi; ++u) {
-      if (u < 16) {
+      if (u < 8) {
         acc[u >> 2][u & 3] = mfma32<D>(fa[st][u & 3], fb[st][u >> 2], acc[u >> 2][u & 3]);
       } else if constexpr (E) {
-        mfma32_vgpr<D>(accx, fa[st][0], fb[st][4]);
+        if (lo4) mfma32_vgpr<D>(accx, fa[st][0], fb[st][2]);
       }
     }
   };
 
   void* out = a.out;
-  const float* s_bias = reinterpret_cast<const float*>(lds + P::O_BIAS);
-  (void)s_bias;
   // Finished tile: + bias, one rounding.  Each 32-row block of a wave goes through a
-  // wave-private LDS region (rows padded to 272 bytes against bank conflicts), so the stores
-  // are whole 256-byte rows, 16 bytes per lane.  `stage` is the LDS byte offset of the four
-  // regions; no load writes there any more.
+  // wave-private LDS region, 16 rows at a time (rows padded to 272 bytes against bank
+  // conflicts), so the stores are whole 256-byte rows, 16 bytes per lane.  `stage` is the LDS
+  // byte offset of the eight regions; no load writes there any more.
   constexpr int kRowPad = 272;
   auto write_tile = [&](int tile, int stage) {
     if constexpr (E) asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");  // the last MFMA into accx is done
@@ -504,42 +502,53 @@ __global__ __launch_bounds__(kPT, 1) void pool_conv_kernel(const PoolArgs a) {
     const int valid = (int)min((int64_t)(blk1 - blk0) * 32, a.n - r0);  // rows of this tile
     unsigned char* obase = reinterpret_cast<unsigned char*>(out) + r0 * 256;
     const unsigned char* bbase = lds + P::O_BIAS + 16 * lkx;
-    unsigned char* wst = lds + stage + w * 32 * kRowPad;
+    unsigned char* wst = lds + stage + w * 16 * kRowPad;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
+      const int tr0 = (2 * w + i) * 32;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x16_t& c = acc[i][j];
-        const int ob = (w + j) & 3;
+      for (int h = 0; h < 2; ++h) {
+        if ((lrx >> 4) == h) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          // accumulator element 4 g + e of lane (lr, lk) = output channel 32 ob + 8 g + 4 lk + e
-          const int cb = 32 * ob + 8 * g;
-          const float4 bb = *reinterpret_cast<const float4*>(bbase + cb * 4);
-          *reinterpret_cast<uint2*>(wst + lrx * kRowPad + cb * 2 + 8 * lkx) =
-              pack4<D>(c[4 * g] + bb.x, c[4 * g + 1] + bb.y, c[4 * g + 2] + bb.z, c[4 * g + 3] + bb.w);
-          c[4 * g] = c[4 * g + 1] = c[4 * g + 2] = c[4 * g + 3] = 0.f;
+          for (int j = 0; j < 4; ++j) {
+            f32x16_t& c = acc[i][j];
+            const int ob = (wq + j) & 3;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              // accumulator element 4 g + e of lane (lr, lk) = output channel 32 ob + 8 g + 4 lk + e
+              const int cb = 32 * ob + 8 * g;
+              const float4 bb = *reinterpret_cast<const float4*>(bbase + cb * 4);
+              *reinterpret_cast<uint2*>(wst + (lrx - 16 * h) * kRowPad + cb * 2 + 8 * lkx) =
+                  pack4<D>(c[4 * g] + bb.x, c[4 * g + 1] + bb.y, c[4 * g + 2] + bb.z, c[4 * g + 3] + bb.w);
+            }
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int rr = 4 * k + (lanex >> 4);
+          const uint4 val = *reinterpret_cast<const uint4*>(wst + rr * kRowPad + (lanex & 15) * 16);
+          const int row = tr0 + 16 * h + rr;
+          if (row < valid) *reinterpret_cast<uint4*>(obase + (uint32_t)(row * 256 + (lanex & 15) * 16)) = val;
         }
       }
-      const int tr0 = (4 * w + i) * 32;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int rr = 4 * k + (lanex >> 4);
-        const uint4 val = *reinterpret_cast<const uint4*>(wst + rr * kRowPad + (lanex & 15) * 16);
-        if (tr0 + rr < valid) *reinterpret_cast<uint4*>(obase + (uint32_t)((tr0 + rr) * 256 + (lanex & 15) * 16)) = val;
-      }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     }
     if constexpr (E) {
-      // block 16: this wave holds output block w of it
-      const int trow = 16 * 32 + lrx;
+      if (lo4) {
+        // block 16: this wave holds output block w of it
+        const int trow = 16 * 32 + lrx;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int cb = 32 * w + 8 * g;
-        const float4 bb = *reinterpret_cast<const float4*>(bbase + cb * 4);
-        if (trow < valid)
-          *reinterpret_cast<uint2*>(obase + (uint32_t)(trow * 256 + cb * 2 + 8 * lkx)) =
-              pack4<D>(accx[4 * g] + bb.x, accx[4 * g + 1] + bb.y, accx[4 * g + 2] + bb.z, accx[4 * g + 3] + bb.w);
-        accx[4 * g] = accx[4 * g + 1] = accx[4 * g + 2] = accx[4 * g + 3] = 0.f;
+        for (int g = 0; g < 4; ++g) {
+          const int cb = 32 * w + 8 * g;
+          const float4 bb = *reinterpret_cast<const float4*>(bbase + cb * 4);
+          if (trow < valid)
+            *reinterpret_cast<uint2*>(obase + (uint32_t)(trow * 256 + cb * 2 + 8 * lkx)) =
+                pack4<D>(accx[4 * g] + bb.x, accx[4 * g + 1] + bb.y, accx[4 * g + 2] + bb.z, accx[4 * g + 3] + bb.w);
+          accx[4 * g] = accx[4 * g + 1] = accx[4 * g + 2] = accx[4 * g + 3] = 0.f;
+        }
       }
     }
   };
@@ -549,7 +558,10 @@ __global__ __launch_bounds__(kPT, 1) void pool_conv_kernel(const PoolArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) read_a(IC<0>{}, 0, j);
 #pragma unroll
-  for (int i = 0; i < NB4; ++i) read_b(IC<0>{}, 0, 0, soff, i);
+  for (int i = 0; i < 2; ++i) read_b(IC<0>{}, 0, 0, soff, i);
+  if constexpr (E) {
+    if (lo4) read_b(IC<0>{}, 0, 0, soff, 2);
+  }
   read_ids(1);
 
   // One step (q, dz, g) of tile `tile`; `nxt` is the next tile of this workgroup (-1: none),
@@ -558,14 +570,18 @@ __global__ __launch_bounds__(kPT, 1) void pool_conv_kernel(const PoolArgs a) {
     constexpr int g = decltype(GG)::value;
     // (2 s) mod 6 for the weight half-slots: S is a multiple of 3, so it is 2 (g mod 3)
     constexpr int hs = 2 * (g % 3);
-    // Loads per step, in this order: 2 weight half-steps, 1 slot-table tap, 2 gathers of the
-    // next sub-pool (g <= 5, possibly reading nothing), 1 row-id group (g == 0).  Wait until this
-    // wave's loads of the weight half-steps (s, 1) and (s + 1, 0), the first two of step s - 2,
-    // have landed (vector-memory loads complete in order), then the barrier makes every wave's
-    // share visible and frees the slots the loads below overwrite.
-    constexpr int cnt[9] = {6, 5, 5, 5, 5, 5, 3, 3, 3};
-    constexpr int N = cnt[(g + 7) % 9] - 2 + cnt[(g + 8) % 9];
-    wait_vmcnt<N>();
+    // Loads per step and wave, in this order: 1 weight quarter (waves 0..3: (s + 3, 0); waves
+    // 4..7: (s + 2, 1)), 1 slot-table tap (waves 0..3), 1 gather of the next sub-pool (g <= 5,
+    // possibly reading nothing), 1 row-id group (g == 0).  Wait until this wave's weight quarter
+    // of step s - 2 ((s + 1, 0) or (s, 1)) has landed (vector-memory loads complete in order); the
+    // barrier then makes every wave's share visible and frees the slots the loads below overwrite.
+    constexpr int g2 = (g + 7) % 9, g1 = (g + 8) % 9;
+    constexpr int after2 = (g2 <= 5 ? 1 : 0) + (g2 == 0 ? 1 : 0);  // step s - 2, after its weight load
+    constexpr int all1 = 1 + (g1 <= 5 ? 1 : 0) + (g1 == 0 ? 1 : 0);  // step s - 1, all of it
+    if (lo4)
+      wait_vmcnt<after2 + 1 + all1 + 1>();
+    else
+      wait_vmcnt<after2 + all1>();
     barrier_no_fence();
     const bool last = q == Q - 1;
     const int src = last ? nxt : tile;
@@ -575,53 +591,50 @@ __global__ __launch_bounds__(kPT, 1) void pool_conv_kernel(const PoolArgs a) {
     const int hs1 = hs + 1, hs2 = hs + 2 == kWS ? 0 : hs + 2;
     const int nq = dz == 2 ? (last ? 0 : q + 1) : q;  // slice of the next sub-pool
     const bool glive = !(dz == 2 && last) || nxt >= 0;
-    // ---- first half: MFMAs of (s, 0).  Each MFMA is followed by one LDS read of (s, 1) (the
-    // first nine) or by one load of this step (the next six); scheduling barriers fix the order.
-    // The slots of step s + 1 are read first: the second half needs them.
+    // ---- first half: MFMAs of (s, 0), written one per LDS read of (s, 1) or load of this step.
+    // With two waves per SIMD the compiler's own schedule of this stream measured 2-3 % faster
+    // than pinning that order with scheduling barriers.  The slots of step s + 1 are read first:
+    // the second half needs them.
     read_slots(t == 26 ? 0 : t + 1, soff_n);
-    auto one = [&](auto SETM, auto U) {
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(SETM, U, IC<decltype(U)::value + 1>{});
-      __builtin_amdgcn_sched_barrier(0);
-    };
+    auto one = [&](auto SETM, auto U) { mfmas(SETM, U, IC<decltype(U)::value + 1>{}); };
     one(IC<0>{}, IC<0>{}); read_a(IC<1>{}, hs1, 0);
     one(IC<0>{}, IC<1>{}); read_a(IC<1>{}, hs1, 1);
     one(IC<0>{}, IC<2>{}); read_a(IC<1>{}, hs1, 2);
     one(IC<0>{}, IC<3>{}); read_a(IC<1>{}, hs1, 3);
     one(IC<0>{}, IC<4>{}); read_b(IC<1>{}, 1, pbuf, soff, 0);
     one(IC<0>{}, IC<5>{}); read_b(IC<1>{}, 1, pbuf, soff, 1);
-    one(IC<0>{}, IC<6>{}); read_b(IC<1>{}, 1, pbuf, soff, 2);
-    one(IC<0>{}, IC<7>{}); read_b(IC<1>{}, 1, pbuf, soff, 3);
-    one(IC<0>{}, IC<8>{}); if constexpr (E) read_b(IC<1>{}, 1, pbuf, soff, 4);
-    // weight half-steps (s + 3, 0) into the half-slot of (s, 0), read last step, and (s + 2, 1)
+    if constexpr (E) {
+      if (lo4) read_b(IC<1>{}, 1, pbuf, soff, 2);
+    }
+    // weight quarters: (s + 3, 0) into the half-slot of (s, 0), read last step, or (s + 2, 1)
     // into the half-slot of (s - 1, 1)
-    one(IC<0>{}, IC<9>{}); issue_w(sl + 3 < S ? sl + 3 : sl + 3 - S, 0, hs);
-    one(IC<0>{}, IC<10>{}); issue_w(sl + 2 < S ? sl + 2 : sl + 2 - S, 1, hs == 0 ? kWS - 1 : hs - 1);
-    // slot-table tap of step s + 4 (the next slice's, or the next tile's in the last slice)
-    one(IC<0>{}, IC<11>{}); issue_table(t >= 23 && last ? nxt : tile, t >= 23 ? t - 23 : t + 4);
-    // gathers of the next sub-pool: (q, dz + 1), (q + 1, 0) or the next tile's (0, 0); its row
+    one(IC<0>{}, IC<6>{});
+    if (lo4)
+      issue_w(sl + 3 < S ? sl + 3 : sl + 3 - S, 0, hs);
+    else
+      issue_w(sl + 2 < S ? sl + 2 : sl + 2 - S, 1, hs == 0 ? kWS - 1 : hs - 1);
+    // slot-table tap of step s + 4 (the next slice's, or the next tile's in the last slice); the
+    // gather of the next sub-pool: (q, dz + 1), (q + 1, 0) or the next tile's (0, 0), whose row
     // ids were read at the end of the previous sub-pool
-    one(IC<0>{}, IC<12>{}); if constexpr (g <= 5) gather1(2 * g, nq, pbuf ^ 1, glive);
-    one(IC<0>{}, IC<13>{}); if constexpr (g <= 5) gather1(2 * g + 1, nq, pbuf ^ 1, glive);
-    one(IC<0>{}, IC<14>{}); if constexpr (g == 0) issue_ids(src, dz);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(IC<0>{}, IC<15>{}, IC<NU>{});
-    // ---- second half: MFMAs of (s, 1), each of the first nine followed by one read of (s + 1, 0)
+    one(IC<0>{}, IC<7>{});
+    if (lo4) issue_table(t >= 23 && last ? nxt : tile, t >= 23 ? t - 23 : t + 4);
+    if constexpr (g <= 5) gather1(g, nq, pbuf ^ 1, glive);
+    mfmas(IC<0>{}, IC<8>{}, IC<NU>{});
+    if constexpr (g == 0) issue_ids(src, dz);
+    // ---- second half: MFMAs of (s, 1), the first six followed by one read of (s + 1, 0)
     one(IC<1>{}, IC<0>{}); read_a(IC<0>{}, hs2, 0);
     one(IC<1>{}, IC<1>{}); read_a(IC<0>{}, hs2, 1);
     one(IC<1>{}, IC<2>{}); read_a(IC<0>{}, hs2, 2);
     one(IC<1>{}, IC<3>{}); read_a(IC<0>{}, hs2, 3);
     one(IC<1>{}, IC<4>{}); read_b(IC<0>{}, 0, pbuf1, soff_n, 0);
     one(IC<1>{}, IC<5>{}); read_b(IC<0>{}, 0, pbuf1, soff_n, 1);
-    one(IC<1>{}, IC<6>{}); read_b(IC<0>{}, 0, pbuf1, soff_n, 2);
-    one(IC<1>{}, IC<7>{}); read_b(IC<0>{}, 0, pbuf1, soff_n, 3);
-    one(IC<1>{}, IC<8>{}); if constexpr (E) read_b(IC<0>{}, 0, pbuf1, soff_n, 4);
-    one(IC<1>{}, IC<9>{}); if constexpr (g == 8) read_ids(dz == 0 ? 2 : dz - 1);  // the next sub-pool's gathers
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(IC<1>{}, IC<10>{}, IC<NU>{});
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (E) {
+      if (lo4) read_b(IC<0>{}, 0, pbuf1, soff_n, 2);
+    }
+    one(IC<1>{}, IC<6>{}); if constexpr (g == 8) read_ids(dz == 0 ? 2 : dz - 1);  // the next sub-pool's gathers
+    mfmas(IC<1>{}, IC<7>{}, IC<NU>{});
 #pragma unroll
-    for (int i = 0; i < NB4; ++i) soff[i] = soff_n[i];
+    for (int i = 0; i < NB; ++i) soff[i] = soff_n[i];
   };
 
   int pb = 0;
@@ -721,11 +734,11 @@ hipError_t launch_pool_conv(const PoolTiling& t, const void* plan, const uint32_
   a.plan_bytes = (uint32_t)pool_records_bytes(t);
   const dim3 grid((unsigned)((t.ntiles + t.per_wg - 1) / t.per_wg));
   if (dtype == SUBM_BF16) {
-    if (t.e) pool_conv_kernel<DT::BF16, 1><<<grid, kPT, 0, stream>>>(a);
-    else pool_conv_kernel<DT::BF16, 0><<<grid, kPT, 0, stream>>>(a);
+    if (t.e) pool_conv_kernel<DT::BF16, 1><<<grid, kCT, 0, stream>>>(a);
+    else pool_conv_kernel<DT::BF16, 0><<<grid, kCT, 0, stream>>>(a);
   } else {
-    if (t.e) pool_conv_kernel<DT::F16, 1><<<grid, kPT, 0, stream>>>(a);
-    else pool_conv_kernel<DT::F16, 0><<<grid, kPT, 0, stream>>>(a);
+    if (t.e) pool_conv_kernel<DT::F16, 1><<<grid, kCT, 0, stream>>>(a);
+    else pool_conv_kernel<DT::F16, 0><<<grid, kCT, 0, stream>>>(a);
   }
   return hipGetLastError();
 }
