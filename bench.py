@@ -155,19 +155,20 @@ def _oracle_inputs(key, layer, cin, cout):
 
 def _oracle_worker(task):
     """One host process: the oracle on its share of the sampled rows, one thread.  Returns the
-    seconds of that call and of a one-row call just before it (its dictionary build, under the
-    same load from the other processes)."""
+    seconds of that call and of a one-row call after it (its dictionary build, under the same load
+    from the other processes); a first one-row call warms the process up untimed."""
     key, layer, cin, cout, rows = task
     from threadpoolctl import threadpool_limits
 
     import oracle
     coords, f, w, b = _oracle_inputs(key, layer, cin, cout)
     with threadpool_limits(limits=1):
+        oracle.conv3(coords, f, w, b, rows=rows[:1])  # (first call of the process: not timed)
         t0 = time.perf_counter()
-        oracle.conv3(coords, f, w, b, rows=rows[:1])
-        t1 = time.perf_counter()
         oracle.conv3(coords, f, w, b, rows=rows)
-        return time.perf_counter() - t1, t1 - t0
+        t1 = time.perf_counter()
+        oracle.conv3(coords, f, w, b, rows=rows[:1])
+        return t1 - t0, time.perf_counter() - t1
 
 
 def host_cores():
