@@ -91,9 +91,9 @@ typedef enum {
  *   out_map  host pointer; receives the new handle.  Set to NULL first, left NULL on error.
  * The map stores nbr[n, 27] (int32, row = ORIGINAL input row of the neighbour, -1 if absent),
  * the total pair count (entries >= 0, centre included) and the per-tap pair counts.
- * The call waits on the host until the build's insert kernel has run, to report the duplicate /
- * range errors; the rest of the build (the lookup) is still running on `stream` when it returns,
- * and the pair counts are read on first use.
+ * The call waits on the host until the build's kernels have run, to report the duplicate /
+ * range errors (the duplicate check of the dense-grid structure is part of its neighbour
+ * lookup); the pair counts are read on first use.
  * Errors: SUBM_ERR_INVALID_ARG, SUBM_ERR_DUPLICATE_COORD, SUBM_ERR_COORD_RANGE,
  *         SUBM_ERR_OUT_OF_MEMORY, SUBM_ERR_HIP.
  * Source: lato.2_mrp_mlx README, header summary (indice map with 27 lookups per voxel,
@@ -180,9 +180,9 @@ int sparse_indice_map_offset_counts(submconv_map_t map, int64_t* counts);
  * subm_release_cached_memory -- free the device memory the library keeps between calls on the
  * current device, and wait for the device.  Resident until then (per device):
  *   - the map-build workspace: grown to the largest build so far, never shrunk by itself:
- *     statistics and partials (~130 KB), 4 bytes per row, and the dense grid (4 bytes per cell of
- *     the set's bounding box with a one-cell margin, at most 128 cells per row and 2 GiB) or the
- *     hash table (32 bytes per row), whichever the build sizes for, rounded up to 64 MiB;
+ *     statistics and partials (~70 KB), the hash table area (32 bytes per row) and the dense
+ *     grid area (4 bytes per cell of the set's bounding box with a one-cell margin, at most 128
+ *     cells per row and 2 GiB), both sized for the largest build so far, rounded up to 64 MiB;
  *   - the rulebook blocks of freed maps kept for reuse on their stream (at most 8 and at most
  *     1 GiB; a block is 112 bytes per row);
  *   - the packed-weight buffers of the neighbour-pool kernel, one per stream that ran it (at most

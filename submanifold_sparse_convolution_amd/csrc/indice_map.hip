@@ -17,32 +17,37 @@
 //         axis' extent (max - min) is at most 65534, which the build enforces.
 //
 // The structure is chosen on the device from the set's bounds, so the whole build needs at most
-// one host synchronisation, taken as soon as the insert kernel has finished: by then it has
-// written the plan's range flags and its own error flags straight into pinned host memory, and
-// the lookup kernel goes on running while the caller enqueues its convolutions (an asynchronous
-// build skips even that wait).  No structure is ever cleared in full: the table area is all
-// 0xFF bytes whenever no build is inserting (an empty cell is -1 and an empty slot is key ~0,
-// row -1); each build records the cells it wrote, and the next build's first kernel puts
-// exactly those back.
+// one host synchronisation (a synchronous build waits for the last kernel, which has then written
+// the range and duplicate flags straight into pinned host memory; an asynchronous build skips even
+// that wait).  Neither structure is ever cleared in full.  The grid and the hash table have areas
+// of their own.  A grid cell holds tag + row, where the tag is a 32-bit base that advances by n
+// with every build on the workspace: a cell counts as occupied only when cell - tag < n (unsigned),
+// so every entry of an earlier build reads as empty with no reset at all; the host refills the
+// grid with 0xFF bytes once, when the tags would pass 2^32 - 1.  The hash table area is all 0xFF
+// bytes whenever no build is inserting, and the next build's first kernel puts a hash build's
+// slots back.
 //
 // Kernels, all on the caller's stream:
-//   map_bounds_kernel   puts back the previous build's cells (GRID: from its cell list) or slots
-//                       (HASH: all of its table), then per-block min/max of (b, z, y, x) ->
-//                       partials (at most 256)
+//   map_bounds_kernel   puts back the previous build's slots if it was a hash build, then
+//                       per-block min/max of (b, z, y, x) -> partials (at most 256), eight rows
+//                       per thread in flight
 //   map_insert_kernel   every block first reduces the partials itself and so derives the same
 //                       plan (range checks, structure, strides) with no second launch and no
 //                       signalling between blocks (that needs a device-scope fence, which writes
 //                       back the whole L2 of each XCD); block 0 publishes it (and the range flags
-//                       and mode to the host) and zeroes the map's counters.  Then GRID: CAS the
-//                       row into its cell and record the cell, up to four voxels per thread in
-//                       flight; HASH: CAS the key into the table.  A cell or key already taken by
-//                       another row raises the duplicate flag in host memory (a plain store of a
-//                       constant, so concurrent writers agree).
+//                       and mode to the host) and zeroes the map's counters.  Then GRID: a plain
+//                       store of tag + row into each row's cell; HASH: CAS the key into the table
+//                       (a key already taken raises the duplicate flag in host memory).
 //   map_lookup_kernel   three threads per voxel, one per dz plane: 9 loads (GRID) or 9 probe
 //                       sequences (HASH) each, all in flight; the block's rows are staged in LDS
 //                       and written as one contiguous run of nbr; per-row 27-bit hit mask; hits
 //                       counted per tap with wave ballots and added to one of 16 counter banks of
-//                       the map, summed on the host when first needed
+//                       the map, summed on the host when first needed.  GRID: a row whose own cell
+//                       holds another row shares its coordinates with that row (the later store
+//                       won), which raises the duplicate flag.
+// The insert and lookup blocks are dealt out so that each of the eight XCDs (the hardware hands
+// workgroups to them round-robin) takes one contiguous range of rows: the cells a row's
+// neighbours share then meet in one L2.
 #include <hip/hip_ext.h>
 
 #include "internal.h"
@@ -100,33 +105,48 @@ __device__ __forceinline__ int wave_max(int v) {
   return v;
 }
 
+// Logical block of hardware block b of g: the blocks of XCD b mod 8 take one contiguous range.
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t g) {
+  const int64_t q = g / 8, r = g % 8, x = b % 8;
+  return x * q + (x < r ? x : r) + b / 8;
+}
+
 // ------------------------------------------------------------------ bounds
 __global__ __launch_bounds__(kThreads) void map_bounds_kernel(const int32_t* __restrict__ coords, int64_t n,
                                                               int nparts, BoundsPartial* __restrict__ partials,
                                                               const MapStats* __restrict__ prev,
-                                                              const int32_t* __restrict__ cells,
-                                                              void* __restrict__ table) {
-  // The previous build's entries back to empty (its lookup has finished: stream order).
+                                                              void* __restrict__ hash_table) {
+  // A previous hash build's slots back to empty (its lookup has finished: stream order).  Grid
+  // entries need nothing: their tags tell them apart.
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (prev->mode == kModeGrid) {
-    int32_t* grid = static_cast<int32_t*>(table);
-    for (int64_t i = t0; i < prev->inserted; i += stride) grid[cells[i]] = -1;
-  } else if (prev->mode == kModeHash) {
-    int4* tab = static_cast<int4*>(table);
+  if (prev->mode == kModeHash) {
+    int4* tab = static_cast<int4*>(hash_table);
     const int4 ff = make_int4(-1, -1, -1, -1);
     for (int64_t i = t0; i < prev->slots; i += stride) tab[i] = ff;
   }
-  // Bounds: the first nparts blocks (the grid may be wider for a large previous build).
+  // Bounds: the first nparts blocks (the grid may be wider for a large previous build), eight
+  // rows per thread in flight.
   if ((int)blockIdx.x >= nparts) return;
   int mn[4] = {INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX};
   int mx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)nparts * kThreads) {
-    const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
-    mn[0] = min(mn[0], c.x); mx[0] = max(mx[0], c.x);
-    mn[1] = min(mn[1], c.y); mx[1] = max(mx[1], c.y);
-    mn[2] = min(mn[2], c.z); mx[2] = max(mx[2], c.z);
-    mn[3] = min(mn[3], c.w); mx[3] = max(mx[3], c.w);
+  constexpr int kBatch = 8;
+  const int64_t pstride = (int64_t)nparts * kThreads;
+  for (int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; i0 < n; i0 += kBatch * pstride) {
+    int4 c[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t i = i0 + u * pstride;
+      // (rows past the end repeat row i0, which changes no minimum or maximum)
+      c[u] = *reinterpret_cast<const int4*>(coords + 4 * (i < n ? i : i0));
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      mn[0] = min(mn[0], c[u].x); mx[0] = max(mx[0], c[u].x);
+      mn[1] = min(mn[1], c[u].y); mx[1] = max(mx[1], c[u].y);
+      mn[2] = min(mn[2], c[u].z); mx[2] = max(mx[2], c[u].z);
+      mn[3] = min(mn[3], c[u].w); mx[3] = max(mx[3], c[u].w);
+    }
   }
   __shared__ int smn[kThreads / 64][4];
   __shared__ int smx[kThreads / 64][4];
@@ -241,8 +261,8 @@ __device__ __forceinline__ int64_t grid_cell(const MapStats& p, int b, int z, in
 __global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __restrict__ coords, int64_t n,
                                                               const BoundsPartial* __restrict__ partials, int nparts,
                                                               int64_t grid_budget_cells, int64_t slots,
-                                                              int mode_request, void* __restrict__ table,
-                                                              int32_t* __restrict__ cells,
+                                                              int mode_request, void* __restrict__ hash_table,
+                                                              int32_t* __restrict__ grid, uint32_t tag,
                                                               uint32_t* __restrict__ banks,
                                                               MapStats* __restrict__ st,
                                                               MapHostFlags* __restrict__ host) {
@@ -268,38 +288,34 @@ __global__ __launch_bounds__(kThreads) void map_insert_kernel(const int32_t* __r
       st->sy = plan.sy;
       st->sz = plan.sz;
       st->sb = plan.sb;
-      st->inserted = n;
     }
     for (int k = t; k < kTapBanks * 27; k += kThreads) banks[k] = 0;
   }
   if (plan.mode == kModeNone) return;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
   bool dup = false, overflow = false;
   if (plan.mode == kModeGrid) {
-    int32_t* grid = static_cast<int32_t*>(table);
-    for (int64_t i0 = (int64_t)blockIdx.x * kThreads + t; i0 < n; i0 += 4 * stride) {
-      // up to four voxels, their compare-and-swaps in flight together
-      int64_t cell[4];
+    // One contiguous run of rows per block, four rows per thread in flight; a plain store each
+    // (two rows on one cell: the lookup sees it).
+    const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+    const int64_t beg = xcd_block(blockIdx.x, gridDim.x) * per;
+    const int64_t end = beg + per < n ? beg + per : n;
+    for (int64_t i0 = beg + t; i0 < end; i0 += 4 * kThreads) {
+      int4 c[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int64_t i = i0 + u * stride;
-        cell[u] = -1;
-        if (i < n) {
-          const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
-          cell[u] = grid_cell(plan.mn, plan.sb, plan.sz, plan.sy, c.x, c.y, c.z, c.w);
-        }
+        const int64_t i = i0 + u * kThreads;
+        c[u] = *reinterpret_cast<const int4*>(coords + 4 * (i < end ? i : i0));
       }
-      int32_t prev[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) prev[u] = cell[u] >= 0 ? atomicCAS(&grid[cell[u]], -1, (int32_t)(i0 + u * stride)) : -1;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        dup |= prev[u] != -1;
-        if (cell[u] >= 0) cells[i0 + u * stride] = (int32_t)cell[u];  // grid cells < 2^29
+        const int64_t i = i0 + u * kThreads;
+        if (i < end) grid[grid_cell(plan.mn, plan.sb, plan.sz, plan.sy, c[u].x, c[u].y, c[u].z, c[u].w)] =
+            (int32_t)(tag + (uint32_t)i);
       }
     }
   } else {
-    Slot* tab = static_cast<Slot*>(table);
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    Slot* tab = static_cast<Slot*>(hash_table);
     for (int64_t i = (int64_t)blockIdx.x * kThreads + t; i < n; i += stride) {
       const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
       const unsigned long long key = pack_key(c.x, c.y, c.z, c.w);
@@ -343,11 +359,13 @@ __device__ __forceinline__ int32_t probe_rest(const Slot* __restrict__ tab, unsi
 }
 
 __global__ __launch_bounds__(3 * kLookupVoxels) void map_lookup_kernel(const int32_t* __restrict__ coords, int64_t n,
-                                                                      const void* __restrict__ table,
+                                                                      const void* __restrict__ hash_table,
+                                                                      const int32_t* __restrict__ grid, uint32_t tag,
                                                                       int32_t* __restrict__ nbr,
                                                                       uint32_t* __restrict__ masks,
                                                                       uint32_t* __restrict__ banks,
-                                                                      const MapStats* __restrict__ st) {
+                                                                      const MapStats* __restrict__ st,
+                                                                      MapHostFlags* __restrict__ host) {
   __shared__ __align__(16) int32_t s_out[kLookupVoxels * 27];
   __shared__ uint32_t s_pm[3][kLookupVoxels];
   __shared__ uint32_t s_cnt[27];
@@ -359,7 +377,7 @@ __global__ __launch_bounds__(3 * kLookupVoxels) void map_lookup_kernel(const int
   const int plane = t / kLookupVoxels;
   const int v = t - plane * kLookupVoxels;
   if (t < 27) s_cnt[t] = 0;
-  const int64_t i0 = (int64_t)blockIdx.x * kLookupVoxels;
+  const int64_t i0 = xcd_block(blockIdx.x, gridDim.x) * kLookupVoxels;
   const int64_t i = i0 + v;
   uint32_t pm = 0;  // hit bits of this plane's taps, at their tap positions
   if (i < n && mode == kModeNone) {
@@ -368,7 +386,6 @@ __global__ __launch_bounds__(3 * kLookupVoxels) void map_lookup_kernel(const int
   } else if (i < n) {
     const int4 c = *reinterpret_cast<const int4*>(coords + 4 * i);
     if (mode == kModeGrid) {
-      const int32_t* grid = static_cast<const int32_t*>(table);
       const int64_t sy = st->sy, sz = st->sz;
       const int64_t base = grid_cell(*st, c.x, c.y, c.z, c.w) + (plane - 1) * sz;
       int32_t val[9];
@@ -377,11 +394,16 @@ __global__ __launch_bounds__(3 * kLookupVoxels) void map_lookup_kernel(const int
 #pragma unroll
       for (int q = 0; q < 9; ++q) {
         const int k = plane * 9 + q;
-        s_out[v * 27 + k] = val[q];
-        pm |= (val[q] >= 0 ? 1u : 0u) << k;
+        // an entry of this build is tag + row; anything else (empty, or an earlier build's) is absent
+        const uint32_t r = (uint32_t)val[q] - tag;
+        const int32_t row = r < (uint32_t)n ? (int32_t)r : -1;
+        s_out[v * 27 + k] = row;
+        pm |= (row >= 0 ? 1u : 0u) << k;
       }
+      // The row's own cell holds another row when both have the same coordinates.
+      if (plane == 1 && (uint32_t)val[4] - tag != (uint32_t)i) host->duplicate = 1u;
     } else {
-      const Slot* tab = static_cast<const Slot*>(table);
+      const Slot* tab = static_cast<const Slot*>(hash_table);
       const unsigned long long slots = (unsigned long long)st->slots;
       unsigned long long key[9], home[9];
       Slot e[9];
@@ -445,16 +467,13 @@ int64_t map_grid_budget_cells(int64_t n) {
   return c < 4096 ? 4096 : (c > kGridMaxCells ? kGridMaxCells : c);
 }
 int map_bounds_blocks(int64_t n) { return clamp_blocks((n + 4 * kThreads - 1) / (4 * kThreads), kMaxBoundsBlocks); }
-size_t map_table_bytes(int64_t n) {
-  const size_t hash = (size_t)map_hash_slots(n) * sizeof(Slot);
-  const size_t grid = (size_t)map_grid_budget_cells(n) * sizeof(int32_t);
-  return hash > grid ? hash : grid;
-}
+size_t map_hash_bytes(int64_t n) { return (size_t)map_hash_slots(n) * sizeof(Slot); }
+size_t map_grid_bytes(int64_t n) { return (size_t)map_grid_budget_cells(n) * sizeof(int32_t); }
 size_t map_partials_bytes(int64_t n) { return (size_t)map_bounds_blocks(n) * sizeof(BoundsPartial); }
 
-hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, void* table, void* partials,
-                            int32_t* cells, int64_t prev_n, int32_t* nbr, uint32_t* masks, uint32_t* banks,
-                            MapStats* stats, MapHostFlags* host_flags, hipEvent_t inserted, hipEvent_t ready,
+hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, void* hash_table, int32_t* grid,
+                            uint32_t tag, void* partials, int64_t prev_n, int32_t* nbr, uint32_t* masks,
+                            uint32_t* banks, MapStats* stats, MapHostFlags* host_flags, hipEvent_t ready,
                             hipStream_t stream) {
   BoundsPartial* parts = static_cast<BoundsPartial*>(partials);
   const int nb = map_bounds_blocks(n);
@@ -462,20 +481,21 @@ hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, 
   const int clear_blocks = clamp_blocks((map_hash_slots(prev_n) + 4 * kThreads - 1) / (4 * kThreads), kMaxWideBlocks);
   const int64_t slots = map_hash_slots(n);
   const int64_t budget = map_grid_budget_cells(n);
-  // One voxel per insert thread (each CAS is a full round trip) up to kMaxInsertBlocks blocks,
-  // then up to four per thread with their CASes in flight together.
+  // One voxel per insert thread up to kMaxInsertBlocks blocks (each hash CAS is a full round
+  // trip), then more per thread.
   const int insert_blocks = clamp_blocks((n + kThreads - 1) / kThreads, kMaxInsertBlocks);
-  map_bounds_kernel<<<prev_n > 0 && clear_blocks > nb ? clear_blocks : nb, kThreads, 0, stream>>>(coords, n, nb, parts,
-                                                                                                stats, cells, table);
-  // The events ride on the kernels' own completion (no marker packet between kernels).
-  const BoundsPartial* cparts = parts;
-  hipExtLaunchKernelGGL(map_insert_kernel, dim3(insert_blocks), dim3(kThreads), 0, stream, nullptr, inserted, 0u,
-                        coords, n, cparts, nb, budget, slots, mode_request, table, cells, banks, stats, host_flags);
   const MapStats* cstats = stats;
-  const void* ctable = table;
+  map_bounds_kernel<<<prev_n > 0 && clear_blocks > nb ? clear_blocks : nb, kThreads, 0, stream>>>(coords, n, nb, parts,
+                                                                                                cstats, hash_table);
+  const BoundsPartial* cparts = parts;
+  map_insert_kernel<<<insert_blocks, kThreads, 0, stream>>>(coords, n, cparts, nb, budget, slots, mode_request,
+                                                            hash_table, grid, tag, banks, stats, host_flags);
+  // The event rides on the kernel's own completion (no marker packet between kernels).
+  const void* chash = hash_table;
+  const int32_t* cgrid = grid;
   hipExtLaunchKernelGGL(map_lookup_kernel, dim3((unsigned)((n + kLookupVoxels - 1) / kLookupVoxels)),
-                        dim3(3 * kLookupVoxels), 0, stream, nullptr, ready, 0u, coords, n, ctable, nbr, masks, banks,
-                        cstats);
+                        dim3(3 * kLookupVoxels), 0, stream, nullptr, ready, 0u, coords, n, chash, cgrid, tag, nbr,
+                        masks, banks, cstats, host_flags);
   return hipGetLastError();
 }
 

@@ -74,8 +74,9 @@ constexpr uint32_t kFlagBatchRange = 2u;
 constexpr uint32_t kFlagProbeOverflow = 4u;
 constexpr uint32_t kFlagExtentRange = 8u;
 
-// Words the insert kernel (its plan and its inserts) writes straight into pinned host memory;
-// the host reads them once that kernel has completed.
+// Words the build's kernels (the insert kernel's plan and hash inserts, the lookup kernel's grid
+// duplicate check) write straight into pinned host memory; the host reads them once the lookup
+// kernel has completed.
 struct MapHostFlags {
   uint32_t flags;      // kFlag* range bits of the plan
   int32_t mode;        // kMode* of the plan
@@ -84,7 +85,8 @@ struct MapHostFlags {
 };
 
 // Device-side plan of the latest build on a workspace, published by the insert kernel's block 0
-// for the lookup kernel and for the next build's first kernel (which puts its entries back).
+// for the lookup kernel and for the next build's first kernel (which puts a hash build's slots
+// back).
 struct MapStats {
   int32_t mn[4];       // per-column minimum of (b, z, y, x)
   int32_t mx[4];       // per-column maximum
@@ -95,17 +97,15 @@ struct MapStats {
   int64_t cells;       // GRID: number of cells
   int64_t slots;       // HASH: number of slots
   int64_t sy, sz, sb;  // GRID strides of y, z and the batch slab (x stride is 1)
-  int64_t inserted;    // rows the insert kernel wrote (GRID: their cells are in the cell list)
 };
 
 // Where a build's flags arrive: a 16-byte slot of pinned host memory that the kernels write
-// through its device address, and an event recorded after the insert kernel.  Slots come from a
+// through its device address, and an event recorded after the build's last kernel.  Slots come from a
 // per-device pool (submconv_api.hip) and go back once the map has been checked or freed, so
 // several asynchronous builds can be in flight at once.
 struct FlagSlot {
   MapHostFlags* host = nullptr;
   MapHostFlags* dev = nullptr;
-  hipEvent_t inserted = nullptr;  // recorded after the insert kernel
   hipEvent_t ready = nullptr;     // recorded after the build's last kernel
 };
 
@@ -143,7 +143,7 @@ struct MapData {
   bool checked = true;
   Status check;
   FlagSlot slot;
-  hipEvent_t check_event = nullptr;  // slot.inserted (synchronous build) or ready (asynchronous)
+  hipEvent_t check_event = nullptr;  // the event whose completion makes the flags valid
   // Per-tap pair lists of the per-offset convolution, built on first use: the pairs of tap k
   // (k != 13) are pair_out / pair_in [pair_off[k] .. pair_off[k] + per_tap[k]), output row
   // ascending.  One allocation, pair_out first.
@@ -160,23 +160,25 @@ struct MapData {
   FlagSlot pool_slot;  // .host->flags / .dev: the overflow flag; .ready: the plan kernel's completion
 };
 
-// Map build (indice_map.hip).  Enqueues on `stream`; does not synchronise.  `table` holds
-// map_table_bytes(n) and `cells` n int32; `stats` (one MapStats, device) still describes the
-// previous build on this workspace (all zero for none; `prev_n` is its row count, 0 for none), whose cells (GRID) or slots (HASH) the
-// first kernel puts back to all 0xFF bytes before this build inserts, so the table area is all
-// 0xFF on entry to the insert.  `partials` holds map_partials_bytes(n).  `host_flags` (device
-// address of pinned host memory, zeroed by the caller) holds the plan's flags and mode and the
-// insert's error flags once `inserted` (the insert kernel's completion, unless null) has
-// completed; the per-tap counts reach `banks` (device [kTapBanks][27], to be summed) once `ready`
-// (the last kernel's completion) has.  Both events must allow timing.
+// Map build (indice_map.hip).  Enqueues on `stream`; does not synchronise.  `hash_table` holds
+// map_hash_bytes(n) and is all 0xFF bytes except for the slots of the previous build on this
+// workspace if that was a hash build (the first kernel puts those back); `grid` holds
+// map_grid_bytes(n) int32 cells, each either 0xFFFFFFFF or tag' + row of an earlier build with
+// tag' + its n <= `tag`, and tag + n <= 2^32 - 1.  `stats` (one MapStats, device) still describes the
+// previous build on this workspace (all zero for none; `prev_n` is its row count, 0 for none).
+// `partials` holds map_partials_bytes(n).  `host_flags` (device address of pinned host memory,
+// zeroed by the caller) holds the plan's flags and mode and the duplicate / overflow flags, and
+// the per-tap counts reach `banks` (device [kTapBanks][27], to be summed), once `ready` (the
+// lookup kernel's completion; it must allow timing) has completed.
 int64_t map_hash_slots(int64_t n);
 int64_t map_grid_budget_cells(int64_t n);
 int map_bounds_blocks(int64_t n);
-size_t map_table_bytes(int64_t n);
+size_t map_hash_bytes(int64_t n);
+size_t map_grid_bytes(int64_t n);
 size_t map_partials_bytes(int64_t n);
-hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, void* table, void* partials,
-                            int32_t* cells, int64_t prev_n, int32_t* nbr, uint32_t* masks, uint32_t* banks,
-                            MapStats* stats, MapHostFlags* host_flags, hipEvent_t inserted, hipEvent_t ready,
+hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, void* hash_table, int32_t* grid,
+                            uint32_t tag, void* partials, int64_t prev_n, int32_t* nbr, uint32_t* masks,
+                            uint32_t* banks, MapStats* stats, MapHostFlags* host_flags, hipEvent_t ready,
                             hipStream_t stream);
 // Fill `bytes` bytes at `p` (16-byte aligned, bytes a multiple of 16) with `value` (each 32-bit
 // word).

@@ -115,16 +115,17 @@ extern "C" const char* subm_last_error(void) { return g_last_error.c_str(); }
 
 namespace {
 
-// Build workspace (statistics, bounds partials, the cell list, the hash table or dense grid):
-// one grow-only device buffer per GPU, held under a mutex while a build is enqueued; builds on
-// one GPU from several threads are serialised by the mutex.
+// Build workspace (statistics, bounds partials, the hash table area, the dense grid area): one
+// grow-only device buffer per GPU, held under a mutex while a build is enqueued; builds on one GPU
+// from several threads are serialised by the mutex.
 struct Workspace {
   std::mutex mu;
   void* ptr = nullptr;
   size_t bytes = 0;
-  int64_t cells_cap = 0;   // rows the cell list holds
-  size_t table_cap = 0;    // bytes of the table area
+  size_t hash_cap = 0;     // bytes of the hash table area
+  size_t grid_cap = 0;     // bytes of the grid area
   int64_t prev_n = 0;      // rows of the latest build on it (0: nothing to put back)
+  uint32_t tag = 0;        // grid tag of the next build: every grid cell is all-ones or below it
   // The latest build's `ready` event (a pooled event, never destroyed): a build returns before
   // its last kernel has run, so the next build's kernels wait for it (on the device) before
   // they touch the shared structure.
@@ -161,7 +162,6 @@ Status take_flag_slot(int dev, FlagSlot* out) {
   }
   FlagSlot& top = pool.free.back();
   // (kernel-completion events of hipExtLaunchKernel: created with timing)
-  if (top.inserted == nullptr) SUBM_HIP_TRY(hipEventCreate(&top.inserted));
   if (top.ready == nullptr) SUBM_HIP_TRY(hipEventCreate(&top.ready));
   *out = top;
   pool.free.pop_back();
@@ -176,7 +176,7 @@ void give_flag_slot(int dev, FlagSlot& slot) {
   slot = FlagSlot{};
 }
 
-// The build's coordinate status from its flags (valid once the insert kernel has completed).
+// The build's coordinate status from its flags (valid once the lookup kernel has completed).
 Status read_flags(MapData& d) {
   const volatile MapHostFlags* host = d.slot.host;
   const uint32_t flags = host->flags;
@@ -189,8 +189,8 @@ Status read_flags(MapData& d) {
   return Status{};
 }
 
-// Waits for the insert kernel and reads the flags (caller holds the map's mutex or owns the map
-// alone).
+// Waits for the build's last kernel and reads the flags (caller holds the map's mutex or owns the
+// map alone).
 Status check_locked(MapData& d) {
   if (d.checked) return d.check;
   DeviceGuard guard(d.device);
@@ -200,35 +200,45 @@ Status check_locked(MapData& d) {
   return d.check;
 }
 
-// Layout: [statistics | bounds partials | cell list | table area].  The table area is all 0xFF
-// bytes whenever no build is inserting (each build's first kernel puts back what the previous
-// one wrote), so a new allocation is filled, and its zeroed statistics say "nothing to put back".
+// Layout: [statistics | bounds partials | hash table area | grid area].  A new allocation has
+// zeroed statistics (they say "nothing to put back"), both table areas all 0xFF bytes and tag 0.
 constexpr size_t kStatsBytes = 4096;
 constexpr size_t kPartialsBytes = 65536;
 static_assert(sizeof(MapStats) <= kStatsBytes, "statistics block");
 
-size_t cells_bytes(int64_t cap) { return round_up((size_t)cap * sizeof(int32_t), 256); }
-
-Status workspace_reserve(Workspace& ws, int64_t n, size_t table_bytes, hipStream_t stream) {
-  if (ws.cells_cap >= n && ws.table_cap >= table_bytes) return Status{};
+Status workspace_reserve(Workspace& ws, size_t hash_bytes, size_t grid_bytes, hipStream_t stream) {
+  if (ws.hash_cap >= hash_bytes && ws.grid_cap >= grid_bytes) return Status{};
   if (ws.ptr != nullptr) {
     SUBM_HIP_TRY(hipFree(ws.ptr));  // waits for the device, so no build still uses it
     ws.ptr = nullptr;
     ws.bytes = 0;
   }
-  const int64_t cap = n > ws.cells_cap ? n : ws.cells_cap;
-  const size_t head = kStatsBytes + kPartialsBytes + cells_bytes(cap);
-  const size_t table = table_bytes > ws.table_cap ? table_bytes : ws.table_cap;
+  const size_t head = kStatsBytes + kPartialsBytes;
+  const size_t hash = hash_bytes > ws.hash_cap ? hash_bytes : ws.hash_cap;
+  const size_t grid = grid_bytes > ws.grid_cap ? grid_bytes : ws.grid_cap;
   const size_t grain = size_t(64) << 20;
-  const size_t want = (head + table + grain - 1) / grain * grain;
+  const size_t want = (head + hash + grid + grain - 1) / grain * grain;
   SUBM_HIP_TRY(hipMalloc(&ws.ptr, want));
   ws.bytes = want;
-  ws.cells_cap = cap;
-  ws.table_cap = want - head;
+  ws.hash_cap = hash;
+  ws.grid_cap = want - head - hash;
   ws.prev_n = 0;
+  ws.tag = 0;
   SUBM_HIP_TRY(launch_fill(ws.ptr, head, 0u, stream));
   SUBM_HIP_TRY(launch_fill(static_cast<unsigned char*>(ws.ptr) + head, want - head, 0xFFFFFFFFu, stream));
   return Status{};
+}
+
+// Largest tag + n a grid build may reach before the grid area is refilled (2^32 - 1, so that an
+// all-ones cell is never an entry); SUBMCONV_GRID_TAG_LIMIT lowers it, so that tests reach the
+// refill with small sets.
+uint64_t grid_tag_limit() {
+  const char* v = std::getenv("SUBMCONV_GRID_TAG_LIMIT");
+  if (v != nullptr && *v != '\0') {
+    const unsigned long long x = std::strtoull(v, nullptr, 10);
+    if (x > 0 && x < 0xFFFFFFFFull) return x;
+  }
+  return 0xFFFFFFFFull;
 }
 
 static_assert(sizeof(MapHostFlags) == 16 && kSlotPage % sizeof(MapHostFlags) == 0, "flag slots tile a page");
@@ -398,7 +408,8 @@ int build_map(const int32_t* coords, int64_t n, int mode, hipStream_t stream, su
     delete m;
     return fail(SUBM_ERR_HIP, "device ordinal out of range");
   }
-  const size_t table_bytes = round_up(map_table_bytes(n), 256);
+  const size_t hash_bytes = round_up(map_hash_bytes(n), 256);
+  const size_t grid_bytes = round_up(map_grid_bytes(n), 256);
   if (map_partials_bytes(n) > kPartialsBytes) {
     delete m;
     return fail(SUBM_ERR_HIP, "internal error: bounds partials exceed their workspace block");
@@ -422,7 +433,14 @@ int build_map(const int32_t* coords, int64_t n, int mode, hipStream_t stream, su
   }
   void* nbr = nullptr;
   size_t nbr_bytes = 0;
-  s = workspace_reserve(ws, n, table_bytes, stream);
+  s = workspace_reserve(ws, hash_bytes, grid_bytes, stream);
+  if (s.ok() && (uint64_t)ws.tag + (uint64_t)n > grid_tag_limit()) {
+    // The grid's tags would run out: back to all-ones (once per ~2^32 / n builds).
+    const hipError_t fe = launch_fill(static_cast<unsigned char*>(ws.ptr) + kStatsBytes + kPartialsBytes + ws.hash_cap,
+                                      ws.grid_cap, 0xFFFFFFFFu, stream);
+    if (fe != hipSuccess) s = hip_status(fe, "grid refill");
+    ws.tag = 0;
+  }
   // nbr [n, 27], masks [n], counter banks [kTapBanks, 27]
   if (s.ok())
     s = map_memory_take(m->d.device, (size_t)n * 28 * sizeof(int32_t) + kTapBanks * 27 * sizeof(uint32_t), stream,
@@ -434,8 +452,8 @@ int build_map(const int32_t* coords, int64_t n, int mode, hipStream_t stream, su
   unsigned char* base = static_cast<unsigned char*>(ws.ptr);
   MapStats* dstats = reinterpret_cast<MapStats*>(base);
   void* partials = base + kStatsBytes;
-  int32_t* cells = reinterpret_cast<int32_t*>(base + kStatsBytes + kPartialsBytes);
-  void* table = base + kStatsBytes + kPartialsBytes + cells_bytes(ws.cells_cap);
+  void* hash_table = base + kStatsBytes + kPartialsBytes;
+  int32_t* grid = reinterpret_cast<int32_t*>(base + kStatsBytes + kPartialsBytes + ws.hash_cap);
 
   m->d.nbr = static_cast<int32_t*>(nbr);
   m->d.nbr_bytes = nbr_bytes;
@@ -446,13 +464,12 @@ int build_map(const int32_t* coords, int64_t n, int mode, hipStream_t stream, su
   host->mode = kModeNone;
   host->duplicate = 0;
   host->overflow = 0;
-  // An asynchronous build tracks no event on its insert kernel; its check waits for the last
-  // kernel instead.
   m->d.ready = m->d.slot.ready;
-  m->d.check_event = wait ? m->d.slot.inserted : m->d.ready;
-  e = launch_map_build(coords, n, mode, table, partials, cells, ws.prev_n, m->d.nbr, m->d.masks, m->d.dev_banks,
-                       dstats, m->d.slot.dev, wait ? m->d.slot.inserted : nullptr, m->d.ready, stream);
-  ws.prev_n = n;  // from here on the table holds this build's entries (or the launch failed)
+  m->d.check_event = m->d.ready;
+  e = launch_map_build(coords, n, mode, hash_table, grid, ws.tag, partials, ws.prev_n, m->d.nbr, m->d.masks,
+                       m->d.dev_banks, dstats, m->d.slot.dev, m->d.ready, stream);
+  ws.prev_n = n;  // from here on the tables hold this build's entries (or the launch failed)
+  ws.tag += (uint32_t)n;
   if (e == hipSuccess) ws.last = m->d.ready;
   if (e != hipSuccess) {
     (void)hipStreamSynchronize(stream);
@@ -675,9 +692,10 @@ extern "C" int subm_release_cached_memory(void) {
     e = hipFree(ws.ptr);
     ws.ptr = nullptr;
     ws.bytes = 0;
-    ws.cells_cap = 0;
-    ws.table_cap = 0;
+    ws.hash_cap = 0;
+    ws.grid_cap = 0;
     ws.prev_n = 0;
+    ws.tag = 0;
     if (e != hipSuccess) return fail(hip_status(e, "subm_release_cached_memory workspace"));
   }
   for (const CachedBlock& b : cache.blocks) device_free(b.ptr, b.stream);

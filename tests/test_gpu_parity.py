@@ -351,6 +351,33 @@ def test_duplicates_rejected(mode):
     assert e.value.name == "SUBM_ERR_DUPLICATE_COORD"
 
 
+@pytest.mark.parametrize("limit", [None, "3000"])
+def test_grid_entries_of_earlier_builds_read_as_absent(monkeypatch, limit):
+    # Grid cells keep the entries of earlier builds (told apart by their tags), and the hash table
+    # has an area of its own: a subset of a set built after the full set must not see the removed
+    # rows, in either structure order; with a tag limit below the set sizes every build refills
+    # the grid first.
+    if limit is not None:
+        monkeypatch.setenv("SUBMCONV_GRID_TAG_LIMIT", limit)
+    full = coords_of("2a")
+    rng = np.random.default_rng(7)
+    seq = [("grid", full), ("grid", full[rng.random(len(full)) < 0.5]), ("hash", full),
+           ("grid", full[::3]), ("hash", full[1::2]), ("grid", full[rng.permutation(len(full))]),
+           ("grid", full[rng.random(len(full)) < 0.1]), ("grid", coords_of("1"))]
+    for step, (mode, c) in enumerate(seq):
+        c = np.ascontiguousarray(c)
+        req = {"hash": sc.SUBM_MAP_HASH, "grid": sc.SUBM_MAP_GRID}[mode]
+        with sc.sparse_indice_map_build_ex(torch.from_numpy(c).to(DEV), req) as m:
+            assert m.mode == req
+            want = oracle.rulebook_sorted(c)
+            assert np.array_equal(gpu_nbr(m), want), f"step {step} ({mode}, {len(c)} rows)"
+            assert m.pairs == int((want >= 0).sum())
+    dup = np.concatenate([full[::3], full[3:4]])
+    with pytest.raises(sc.SubmError) as e:
+        sc.sparse_indice_map_build_ex(torch.from_numpy(dup).to(DEV), sc.SUBM_MAP_GRID)
+    assert e.value.name == "SUBM_ERR_DUPLICATE_COORD"
+
+
 def test_shape_mismatch_and_alias_rejected():
     coords, f, w, b = small_case("bf16", 16, 16)
     with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
