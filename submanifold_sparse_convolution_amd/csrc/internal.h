@@ -184,6 +184,20 @@ hipError_t launch_map_build(const int32_t* coords, int64_t n, int mode_request, 
 // word).
 hipError_t launch_fill(void* p, size_t bytes, uint32_t value, hipStream_t stream);
 
+// Prefix sum of n int32 (sort_scan.hip): out[i] = in[0] + ... + in[i] (inclusive) or the sum
+// before i (exclusive); out may equal in; both 16-byte aligned.  scratch: scan_scratch_bytes(n).
+size_t scan_scratch_bytes(int64_t n);
+hipError_t launch_scan(const int32_t* in, int32_t* out, int64_t n, bool exclusive, void* scratch, hipStream_t stream);
+// Stable LSD radix sort of n (key, value) pairs by key bits [0, bits), digits of at most 9 bits
+// (as few passes as that allows), ping-pong
+// between (keys, vals) and (keys_alt, vals_alt): *result_in_alt says which pair holds the sorted
+// result (the other is overwritten).  scratch: radix_sort_scratch_bytes(n).  K: uint32_t or
+// uint64_t.
+size_t radix_sort_scratch_bytes(int64_t n);
+template <typename K>
+hipError_t launch_radix_sort_pairs(K* keys, int32_t* vals, K* keys_alt, int32_t* vals_alt, int64_t n, int bits,
+                                   void* scratch, hipStream_t stream, bool* result_in_alt);
+
 // Child map of a subdivide (structure.hip): nbr [8 np, 27] and masks [8 np] from the parent
 // rulebook [np, 27].
 hipError_t launch_child_map(const int32_t* parent_nbr, int64_t np, int32_t* nbr, uint32_t* masks,

@@ -3,16 +3,13 @@
 // sparse_structure.h, which also states what each one computes and where the pages fix it.
 //
 // All of it is memory-bound integer and copy work, so the kernels are plain one-thread-per-item
-// launches with coalesced 16-byte rows; the only library routines are rocPRIM's radix sort and
-// inclusive scan (the downsample's distinct cells in ascending order, and the masked upsample's
-// child positions).
+// launches with coalesced 16-byte rows; the downsample's distinct cells in ascending order and the
+// masked upsample's child positions come from the radix sort and prefix sum of sort_scan.hip.
 #include <cstring>
 #include <algorithm>
 #include <climits>
 #include <mutex>
 #include <new>
-
-#include <rocprim/rocprim.hpp>
 
 #include "internal.h"
 #include "sparse_structure.h"
@@ -495,11 +492,7 @@ Status downsample_sort(const int32_t* coords, int64_t n, const KeyPack& kp, int 
   // scratch: keys in / out, rows in / out, head flags, cell ids, sort and scan temporaries
   const size_t kb = align256((size_t)n * sizeof(K));
   const size_t rb = align256((size_t)n * 4);
-  size_t sort_tmp = 0, scan_tmp = 0;
-  SUBM_HIP_TRY(rocprim::radix_sort_pairs(nullptr, sort_tmp, (const K*)nullptr, (K*)nullptr, (const int32_t*)nullptr,
-                                         (int32_t*)nullptr, (unsigned int)n, 0, bits, stream));
-  SUBM_HIP_TRY(rocprim::inclusive_scan(nullptr, scan_tmp, (const int32_t*)nullptr, (int32_t*)nullptr,
-                                       (unsigned int)n, rocprim::plus<int32_t>(), stream));
+  const size_t sort_tmp = radix_sort_scratch_bytes(n), scan_tmp = scan_scratch_bytes(n);
   const size_t tmp = align256(sort_tmp > scan_tmp ? sort_tmp : scan_tmp);
   Scratch scratch(stream);
   Status s = device_alloc(&scratch.p, 2 * kb + 4 * rb + tmp, stream);
@@ -516,13 +509,13 @@ Status downsample_sort(const int32_t* coords, int64_t n, const KeyPack& kp, int 
   const int g = grid_for(n, 4);
   cell_key_kernel<K><<<g, kThreads, 0, stream>>>(reinterpret_cast<const int4*>(coords), n, kp, keys_in, rows_in);
   SUBM_HIP_TRY(hipGetLastError());
-  size_t t1 = tmp;
-  SUBM_HIP_TRY(rocprim::radix_sort_pairs(tmp_p, t1, keys_in, keys_out, rows_in, rows_out, (unsigned int)n, 0, bits,
-                                         stream));
-  cell_head_kernel<K><<<g, kThreads, 0, stream>>>(keys_out, n, head);
+  bool in_alt = false;
+  SUBM_HIP_TRY(launch_radix_sort_pairs<K>(keys_in, rows_in, keys_out, rows_out, n, bits, tmp_p, stream, &in_alt));
+  const K* keys_sorted = in_alt ? keys_out : keys_in;
+  const int32_t* rows_sorted = in_alt ? rows_out : rows_in;
+  cell_head_kernel<K><<<g, kThreads, 0, stream>>>(keys_sorted, n, head);
   SUBM_HIP_TRY(hipGetLastError());
-  size_t t2 = tmp;
-  SUBM_HIP_TRY(rocprim::inclusive_scan(tmp_p, t2, head, cid, (unsigned int)n, rocprim::plus<int32_t>(), stream));
+  SUBM_HIP_TRY(launch_scan(head, cid, n, false, tmp_p, stream));
   int32_t* host_count = static_cast<int32_t*>(pin.host);
   SUBM_HIP_TRY(hipMemcpyAsync(host_count, cid + (n - 1), sizeof(int32_t), hipMemcpyDeviceToHost, stream));
   SUBM_HIP_TRY(hipStreamSynchronize(stream));
@@ -530,7 +523,7 @@ Status downsample_sort(const int32_t* coords, int64_t n, const KeyPack& kp, int 
   s = alloc_subdiv(d, true, stream);
   if (!s.ok()) return s;
   SUBM_HIP_TRY(hipMemcpyAsync(d.fine, coords, (size_t)n * 16, hipMemcpyDeviceToDevice, stream));
-  cell_emit_kernel<K><<<g, kThreads, 0, stream>>>(keys_out, rows_out, cid, n, kp, reinterpret_cast<int4*>(d.coarse),
+  cell_emit_kernel<K><<<g, kThreads, 0, stream>>>(keys_sorted, rows_sorted, cid, n, kp, reinterpret_cast<int4*>(d.coarse),
                                                   d.parent, d.seg_off, d.seg_rows);
   SUBM_HIP_TRY(hipGetLastError());
   return Status{};
@@ -663,13 +656,7 @@ extern "C" int sparse_upsample_masked_build(const int32_t* coords, const uint8_t
     return fail(SUBM_ERR_OUT_OF_MEMORY, "pinned host block");
   }
   // scratch: range, counts, inclusive scan, scan temporaries
-  size_t scan_tmp = 0;
-  hipError_t e = rocprim::inclusive_scan(nullptr, scan_tmp, (const int32_t*)nullptr, (int32_t*)nullptr,
-                                         (unsigned int)n, rocprim::plus<int32_t>(), stream);
-  if (e != hipSuccess) {
-    delete h;
-    return fail(hip_status(e, "scan size"));
-  }
+  const size_t scan_tmp = scan_scratch_bytes(n);
   const size_t cb = align256((size_t)n * 4);
   Scratch scratch(stream);
   const size_t rb = align256(kRangeScratch);
@@ -686,13 +673,12 @@ extern "C" int sparse_upsample_masked_build(const int32_t* coords, const uint8_t
   CoordRange* host_range = static_cast<CoordRange*>(pin.host);
   int32_t* host_total = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(pin.host) + 64);
 
-  e = enqueue_range(coords, n, dev_range, host_range, stream);
+  hipError_t e = enqueue_range(coords, n, dev_range, host_range, stream);
   if (e == hipSuccess) {
     mask_count_kernel<<<grid_for(n, 4), kThreads, 0, stream>>>(mask, n, count);
     e = hipGetLastError();
   }
-  size_t t = align256(scan_tmp);
-  if (e == hipSuccess) e = rocprim::inclusive_scan(tmp_p, t, count, incl, (unsigned int)n, rocprim::plus<int32_t>(), stream);
+  if (e == hipSuccess) e = launch_scan(count, incl, n, false, tmp_p, stream);
   if (e == hipSuccess) e = hipMemcpyAsync(host_total, incl + (n - 1), sizeof(int32_t), hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) {

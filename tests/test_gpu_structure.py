@@ -3,7 +3,8 @@ through the C ABI against the CPU oracle.
 
 Coordinates, parent indices and rulebooks are compared bit for bit; max pooling and every
 feature copy are exact, so they are compared bit for bit too; mean pooling sums in float32 and
-rounds once, so it is held to the normwise bar of the convolution (1e-5 fp32, 1e-2 fp16 / bf16).
+rounds once, so it is held to the normwise bar of the convolution (1e-5 fp32, 1e-2 fp16 / bf16),
+and one test pins its float32 summation order (ascending fine row within a cell) bit for bit.
 Multi-million-voxel sets are checked through properties that hold at any size.
 """
 import numpy as np
@@ -238,6 +239,65 @@ def test_downsample_undoes_subdivide_on_device():
             for mode in (sc.SUBM_POOL_MAX, sc.SUBM_POOL_MEAN):
                 pooled = host(sc.sparse_downsample_forward(d, ff, mode))
                 assert torch.equal(pooled, f.cpu()[torch.from_numpy(order)])
+
+
+def clustered_sites(seed, cells, span):
+    """Shuffled fine rows of `cells` random coarse cells (b in [0, 3), z, y, x in [-span, span)),
+    each with 1..8 distinct children."""
+    rng = np.random.default_rng(seed)
+    cc = np.unique(np.concatenate([rng.integers(0, 3, (cells, 1)), rng.integers(-span, span, (cells, 3))], axis=1),
+                   axis=0)
+    kids = rng.random((len(cc), 8)) < rng.random((len(cc), 1))
+    kids[np.arange(len(cc)), rng.integers(0, 8, len(cc))] = True
+    ci, s = np.nonzero(kids)
+    off = np.stack([(s >> 2) & 1, (s >> 1) & 1, s & 1], axis=1)
+    fine = np.concatenate([cc[ci, :1], 2 * cc[ci, 1:] + off], axis=1).astype(np.int32)
+    return shuffled(fine, seed + 1)
+
+
+@pytest.mark.parametrize("span", [40, 3000])  # 23- and 41-bit cell keys: 3 and 5 sort passes
+def test_downsample_mean_sums_members_in_ascending_row_order(span):
+    # The members of a cell are summed in float32 in ascending fine-row order.  Values spread over
+    # 2^-10 .. 2^30 with random signs make each float32 sum depend on that order, so the mean pins
+    # that the sort of the cells keeps equal keys in input order (rows shuffled, ~100 k of them,
+    # so equal keys meet across many 4096-row sort tiles).
+    c = clustered_sites(40 + span, 25000, span)
+    n = len(c)
+    rng = np.random.default_rng(span)
+    f = (rng.choice([-1.0, 1.0], (n, 8)) * rng.random((n, 8)) * 2.0 ** rng.integers(-10, 31, (n, 8))).astype(np.float32)
+    coarse, _, parent = st.downsample(c)
+    order = np.lexsort((np.arange(n), parent))  # members of each cell in ascending row order
+    first = np.searchsorted(parent[order], np.arange(len(coarse)))
+    cnt = np.bincount(parent, minlength=len(coarse))
+    acc = f[order[first]].copy()
+    for k in range(1, 8):
+        has = cnt > k
+        acc[has] = (acc[has] + f[order[first[has] + k]]).astype(np.float32)
+    want = (acc / cnt[:, None].astype(np.float32)).astype(np.float32)
+    with sc.sparse_downsample_build(dev_coords(c)) as s:
+        assert np.array_equal(host(s.coarse_coords()).numpy(), coarse)
+        assert np.array_equal(host(s.parent()).numpy(), parent)
+        got = host(sc.sparse_downsample_forward(s, torch.from_numpy(f).to(DEV), sc.SUBM_POOL_MEAN)).numpy()
+    print(f"  n={n} cells={len(coarse)} max members={cnt.max()}", flush=True)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_downsample_undoes_subdivide_at_20m_rows():
+    # 20.4 M children of the config-5 set: the sort's per-tile digit counts (256 x 4,981 tiles)
+    # take the multi-workgroup prefix sum; the cells must come back as the parent set, in order.
+    c = synth.coords_for("5")
+    order = np.lexsort(c.T[::-1])  # the set is parent-major, not in (b, z, y, x) order
+    rank = np.empty(len(c), dtype=np.int64)
+    rank[order] = np.arange(len(c))
+    coords = dev_coords(c)
+    with sc.sparse_subdivide(coords) as s:
+        fine = s.fine_coords()
+        with sc.sparse_downsample_build(fine) as d:
+            assert d.n_coarse == len(c)
+            assert torch.equal(d.coarse_coords(), dev_coords(c[order]))
+            assert torch.equal(d.parent().long(), torch.from_numpy(rank).to(DEV)[s.parent().long()])
+            torch.cuda.synchronize()
+            print(f"  {s.n_fine} children -> {d.n_coarse} cells", flush=True)
 
 
 def test_downsample_full_size_properties():
