@@ -12,11 +12,12 @@ voxels), 128 -> 128 channels, bf16 storage, k = 3.
 
 Printed: one JSON line with the step throughput (effective TFLOP/s =
 2 * pairs * Cin * Cout per layer, summed over layers, divided by the step
-time), the roofline position of the convolution call (its average duration
-from HIP events around back-to-back calls on the stream it runs on; on the
-neighbour-pool path a call is the weight packing plus the convolution
-kernel), the same call with cold caches (1 GiB written between calls,
-outside the events), the map build's GPU time from events, and the CPU
+time), the roofline position of the convolution kernel (its average duration
+over back-to-back calls, from a pair of HIP events bound to the kernel's own
+dispatch through subm_timing_events; the whole call, which on the
+neighbour-pool path also packs the weights, is reported beside it), the same
+kernel with cold caches (1 GiB written between calls), the map build's GPU time
+from events, and the CPU
 oracle timed on a bounded sample of the same workload in one process per
 host core (at most 16).
 
@@ -350,8 +351,8 @@ def main():
         m.free()
     build_s = float(np.mean([e0.elapsed_time(e1) for e0, e1 in bmarks])) / 1e3
 
-    # Convolution kernel alone: HIP events around each of many back-to-back launches on the
-    # stream the library launches on (torch's current stream, passed through the binding).
+    # Convolution kernel alone over many back-to-back calls on the stream the library launches
+    # on (torch's current stream, passed through the binding).
     stream = torch.cuda.current_stream(dev)
     conv_ms = []
     flush = torch.empty(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
@@ -363,17 +364,27 @@ def main():
             ks, cin, cout, w, b = k3[r % len(k3)]
             conv(m, ks, x0_dev if not chained else outs[0], w, b, outs[-1])
         torch.cuda.synchronize()
+        # the kernel's own start and completion (subm_timing_events binds a pair of events to the
+        # next convolution kernel's dispatch), beside the whole call between two stream events
+        kevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for ka, kb in kevs:  # (torch creates an event on its first record)
+            ka.record(stream)
+            kb.record(stream)
+        torch.cuda.synchronize()
         per_layer = {i: [] for i in range(len(k3))}
+        per_layer_call = {i: [] for i in range(len(k3))}
         for r in range(reps):
             i = r % len(k3)
             ks, cin, cout, w, b = k3[i]
             src = x0_dev if not chained else outs[0]
             evs[r][0].record(stream)
+            sc.subm_timing_events(*kevs[r])
             conv(m, ks, src, w, b, outs[-1])
             evs[r][1].record(stream)
         torch.cuda.synchronize()
         for r in range(reps):
-            per_layer[r % len(k3)].append(evs[r][0].elapsed_time(evs[r][1]))
+            per_layer[r % len(k3)].append(kevs[r][0].elapsed_time(kevs[r][1]))
+            per_layer_call[r % len(k3)].append(evs[r][0].elapsed_time(evs[r][1]))
         pool_path = (not per_offset and layers[0][0] == 3
                      and sc.sparse_indice_map_plan_state(m) == sc.SUBM_PLAN_READY and layers[0][2] == 128)
         # Cold caches: 1 GiB written between launches (outside the events) evicts the layer's
@@ -381,18 +392,17 @@ def main():
         cold = []
         for r in range(min(reps, 40)):
             flush.fill_(float(r))
-            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             ks, cin, cout, w, b = k3[0]
-            ev0.record(stream)
+            sc.subm_timing_events(*kevs[r])
             conv(m, ks, x0_dev if not chained else outs[0], w, b, outs[-1])
-            ev1.record(stream)
-            cold.append((ev0, ev1))
+            cold.append(kevs[r])
         torch.cuda.synchronize()
         cold_ms = [a.elapsed_time(b) for a, b in cold]
     del flush
     # Dominant kernel: the k = 3 layer (all layers of a workload share shape except 2a's k = 1).
     dom = 0
     conv_ms = float(np.mean(per_layer[dom]))
+    call_ms = float(np.mean(per_layer_call[dom]))
     ks, cin, cout = layers[dom][0], layers[dom][1], layers[dom][2]
     s = ELEM[cfg.dtype]
     p_layer = pairs if ks == 3 else n
@@ -420,8 +430,8 @@ def main():
     if per_offset and ks == 3:
         kernel = "offset_gemm_kernel (27 launches, one per offset) + round_out_kernel, per call"
     elif pool_path:
-        # the neighbour-pool kernel, behind the packing of the call's weights (both in the events)
-        kernel = "pool_pack_kernel + pool_conv_kernel (one call)"
+        # the neighbour-pool kernel (the call also packs its weights first: avg_call_ms)
+        kernel = "pool_conv_kernel"
     elif (cfg.dtype in ("bf16", "f16") and cout > 32 and ks == 3 and cout % 8 == 0
           and os.environ.get("SUBMCONV_PERSISTENT", "1")[:1] != "0"):
         kernel = "subm_conv_ws_persistent_kernel"
@@ -431,7 +441,8 @@ def main():
         kernel = "subm_conv_mma_kernel"
     else:
         kernel = "subm_conv_generic_kernel"
-    roofline.update({"kernel": kernel, "kernel_source": source, "avg_launch_ms": conv_ms, "launches": len(per_layer[dom]),
+    roofline.update({"kernel": kernel, "kernel_source": source, "avg_launch_ms": conv_ms, "avg_call_ms": call_ms,
+                     "launches": len(per_layer[dom]),
                      "algorithmic_flop_per_launch": flop_launch, "algorithmic_bytes_per_launch": bytes_launch})
     peaks = None if args.no_peaks else measured_peaks(dev)
     if peaks is not None:

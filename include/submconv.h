@@ -302,6 +302,18 @@ int subm_conv3d_forward_per_offset(submconv_map_t map, int64_t n, int cin, int c
                                    const void* feats, const void* weight, const void* bias, void* out,
                                    hipStream_t stream);
 
+/*
+ * subm_timing_events -- measurement hook: the next convolution kernel that this thread launches
+ * (through subm_conv3d_forward or any other entry point that convolves) records `start` when it
+ * begins and `stop` when it completes.  Both events are bound to that kernel's own dispatch (no
+ * marker packet joins the stream), so hipEventElapsedTime(start, stop) is the kernel's duration:
+ * on the neighbour-pool path the pool kernel alone, without the weight packing launched before
+ * it.  Events must be created with timing on the device of that call; NULL, NULL cancels a
+ * pending request.  Only the next kernel takes the request.  Always returns SUBM_OK.
+ * Source: none of the pages; it serves the roofline measurement of the convolution kernel.
+ */
+int subm_timing_events(hipEvent_t start, hipEvent_t stop);
+
 /* Static string naming a status code ("SUBM_OK", ...); "unknown status" otherwise. */
 const char* subm_status_string(int status);
 

@@ -38,6 +38,7 @@ C_FUNCTIONS = (
     "sparse_indice_map_copy_nbr",
     "sparse_indice_map_plan_state",
     "subm_release_cached_memory",
+    "subm_timing_events",
     "subm_conv3d_forward",
     "subm_conv3d_forward_noalloc",
     "subm_conv3d_forward_per_offset",
@@ -97,6 +98,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.sparse_indice_map_copy_nbr.argtypes = [vp, vp, vp]
         lib.sparse_indice_map_plan_state.argtypes = [vp, ctypes.POINTER(ci)]
         lib.subm_release_cached_memory.argtypes = []
+        lib.subm_timing_events.argtypes = [vp, vp]
         lib.subm_conv3d_forward.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp]
         lib.subm_conv3d_forward_noalloc.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp]
         lib.subm_conv3d_forward_per_offset.argtypes = [vp, i64, ci, ci, ci, vp, vp, vp, vp, vp]
@@ -281,6 +283,15 @@ def subm_release_cached_memory(device=None) -> None:
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     with _on_device(dev):
         _check(lib, "subm_release_cached_memory", lib.subm_release_cached_memory())
+
+
+def subm_timing_events(start, stop) -> None:
+    """Bind two timing events (torch.cuda.Event, already recorded once so that they exist) to the
+    next convolution kernel this thread launches: start.elapsed_time(stop) is then that kernel's
+    own duration.  None, None cancels.  See subm_timing_events in include/submconv.h."""
+    lib = load_library()
+    h = lambda e: None if e is None else ctypes.c_void_p(e.cuda_event)
+    _check(lib, "subm_timing_events", lib.subm_timing_events(h(start), h(stop)))
 
 
 def sparse_indice_map_plan_state(m: IndiceMap) -> int:

@@ -1408,7 +1408,7 @@ hipError_t launch_ws(const ConvArgs& a0, hipStream_t stream) {
   a.tiles_m = (int)((a.n + Sh::BM - 1) / Sh::BM);
   a.per_xcd = (a.tiles_m + 7) / 8;
   dim3 grid((unsigned)(8 * a.per_xcd), (unsigned)((a.cout + Sh::BN - 1) / Sh::BN));
-  subm_conv_ws_kernel<D, WM, FM, FN, SL, TAPS, KP, STATS><<<grid, kWsThreads, 0, stream>>>(a);
+  launch_kernel_timed(subm_conv_ws_kernel<D, WM, FM, FN, SL, TAPS, KP, STATS>, grid, dim3(kWsThreads), stream, a);
   return hipGetLastError();
 }
 
@@ -1419,7 +1419,7 @@ hipError_t launch_mma(const ConvArgs& a0, hipStream_t stream) {
   a.tiles_m = (int)((a.n + Sh::BM - 1) / Sh::BM);
   a.per_xcd = (a.tiles_m + 7) / 8;
   dim3 grid((unsigned)(8 * a.per_xcd), (unsigned)((a.cout + Sh::BN - 1) / Sh::BN));
-  subm_conv_mma_kernel<D, WM, FM, FN, SL, TAPS><<<grid, kThreads, 0, stream>>>(a);
+  launch_kernel_timed(subm_conv_mma_kernel<D, WM, FM, FN, SL, TAPS>, grid, dim3(kThreads), stream, a);
   return hipGetLastError();
 }
 
@@ -1436,7 +1436,7 @@ hipError_t launch_ws_persistent(const ConvArgs& a0, hipStream_t stream) {
   const int per_block = (a.per_xcd + nblk / 8 - 1) / (nblk / 8);
   if (per_block > kMaxBlockTiles || !a.vec_out || a.cout % 8 != 0) return hipErrorNotSupported;
   dim3 grid((unsigned)nblk, (unsigned)((a.cout + Sh::BN - 1) / Sh::BN));
-  subm_conv_ws_persistent_kernel<D, WM, FM, FN, SL, LW><<<grid, 64 * (4 + LW), 0, stream>>>(a);
+  launch_kernel_timed(subm_conv_ws_persistent_kernel<D, WM, FM, FN, SL, LW>, grid, dim3(64 * (4 + LW)), stream, a);
   return hipGetLastError();
 }
 
@@ -1549,7 +1549,7 @@ hipError_t launch_tile(const ConvArgs& a0, hipStream_t stream) {
   a.tiles_m = (int)((a.n + BM - 1) / BM);
   a.per_xcd = (a.tiles_m + 7) / 8;
   dim3 grid((unsigned)(8 * a.per_xcd), (unsigned)((a.cout + BN - 1) / BN));
-  subm_conv_generic_kernel<D, BM, BN, WM, VEC, TAPS><<<grid, kThreads, 0, stream>>>(a);
+  launch_kernel_timed(subm_conv_generic_kernel<D, BM, BN, WM, VEC, TAPS>, grid, dim3(kThreads), stream, a);
   return hipGetLastError();
 }
 

@@ -734,11 +734,11 @@ hipError_t launch_pool_conv(const PoolTiling& t, const void* plan, const uint32_
   a.plan_bytes = (uint32_t)pool_records_bytes(t);
   const dim3 grid((unsigned)((t.ntiles + t.per_wg - 1) / t.per_wg));
   if (dtype == SUBM_BF16) {
-    if (t.e) pool_conv_kernel<DT::BF16, 1><<<grid, kCT, 0, stream>>>(a);
-    else pool_conv_kernel<DT::BF16, 0><<<grid, kCT, 0, stream>>>(a);
+    if (t.e) launch_kernel_timed(pool_conv_kernel<DT::BF16, 1>, grid, dim3(kCT), stream, a);
+    else launch_kernel_timed(pool_conv_kernel<DT::BF16, 0>, grid, dim3(kCT), stream, a);
   } else {
-    if (t.e) pool_conv_kernel<DT::F16, 1><<<grid, kCT, 0, stream>>>(a);
-    else pool_conv_kernel<DT::F16, 0><<<grid, kCT, 0, stream>>>(a);
+    if (t.e) launch_kernel_timed(pool_conv_kernel<DT::F16, 1>, grid, dim3(kCT), stream, a);
+    else launch_kernel_timed(pool_conv_kernel<DT::F16, 0>, grid, dim3(kCT), stream, a);
   }
   return hipGetLastError();
 }

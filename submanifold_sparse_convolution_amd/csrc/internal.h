@@ -1,6 +1,7 @@
 // Internal declarations shared by the host entry points and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -59,6 +60,22 @@ struct DeviceGuard {
     if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
   }
 };
+
+// Measurement hook (subm_timing_events): the events that this thread's next convolution kernel
+// records (its own start and completion, bound to its dispatch); take_timing_events() returns
+// them and clears the request.
+struct TimingEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+TimingEvents take_timing_events();
+// Launches kernel(a) on `stream`, binding a pending timing request to it.
+template <typename F, typename A>
+inline void launch_kernel_timed(F kernel, dim3 grid, dim3 block, hipStream_t stream, const A& a) {
+  const TimingEvents te = take_timing_events();
+  if (te.start == nullptr && te.stop == nullptr) kernel<<<grid, block, 0, stream>>>(a);
+  else hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, te.start, te.stop, 0u, a);
+}
 
 // Map build constants.
 constexpr int kTapBanks = 16;               // tap hit counters are spread over banks of 27

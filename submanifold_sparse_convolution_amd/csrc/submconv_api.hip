@@ -113,6 +113,24 @@ extern "C" const char* subm_status_string(int status) {
 
 extern "C" const char* subm_last_error(void) { return g_last_error.c_str(); }
 
+namespace submconv {
+namespace {
+thread_local TimingEvents g_timing;
+}  // namespace
+TimingEvents take_timing_events() {
+  const TimingEvents t = g_timing;
+  g_timing = TimingEvents{};
+  return t;
+}
+}  // namespace submconv
+
+extern "C" int subm_timing_events(hipEvent_t start, hipEvent_t stop) {
+  submconv::clear_error();
+  submconv::g_timing.start = start;
+  submconv::g_timing.stop = stop;
+  return SUBM_OK;
+}
+
 namespace {
 
 // Build workspace (statistics, bounds partials, the hash table area, the dense grid area): one
