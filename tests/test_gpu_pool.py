@@ -239,3 +239,48 @@ def test_release_cached_memory_and_build_again():
         y3 = sc.subm_conv3d_forward(m, fd, wd, bd)
         torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(y2, y3)
+
+
+def test_timing_events_bind_to_the_convolution_kernel_only():
+    # subm_timing_events: the next convolution kernel records the pair (its own start and end), the
+    # call's weight packing before it does not; the request is taken once; None, None cancels.
+    c = shell()
+    n = len(c)
+    f = synth.feats_for(3, 0, n, 128, "bf16").to(DEV)
+    w = synth.weight_for(3, 0, 3, 128, 128, "bf16").to(DEV)
+    b = synth.bias_for(3, 0, 128, "bf16").to(DEV)
+    stream = torch.cuda.current_stream()
+    with sc.sparse_indice_map_build(torch.from_numpy(c).to(DEV)) as m:
+        ref = sc.subm_conv3d_forward(m, f, w, b)
+        torch.cuda.synchronize()
+        assert sc.sparse_indice_map_plan_state(m) == sc.SUBM_PLAN_READY
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for e in ev:  # (torch creates an event on its first record)
+            e.record(stream)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        sc.subm_timing_events(ev[0], ev[1])
+        out = sc.subm_conv3d_forward(m, f, w, b)
+        c1.record(stream)
+        # taken once: the second call leaves the pair as it was
+        sc.subm_conv3d_forward(m, f, w, b)
+        torch.cuda.synchronize()
+        kernel_ms, call_ms = ev[0].elapsed_time(ev[1]), c0.elapsed_time(c1)
+        print(f"  kernel {kernel_ms * 1e3:.1f} us, call {call_ms * 1e3:.1f} us", flush=True)
+        assert 0.0 < kernel_ms < call_ms
+        assert torch.equal(out, ref)
+        # a cancelled request binds nothing: the pair keeps its earlier (dummy) records
+        t_before = ev[2].elapsed_time(ev[3])
+        sc.subm_timing_events(ev[2], ev[3])
+        sc.subm_timing_events(None, None)
+        sc.subm_conv3d_forward(m, f, w, b)
+        torch.cuda.synchronize()
+        assert ev[2].elapsed_time(ev[3]) == t_before
+    # the general kernels take the request too (k = 1, no map)
+    x = synth.feats_for(3, 1, 4096, 64, "bf16").to(DEV)
+    w1 = synth.weight_for(3, 1, 1, 64, 64, "bf16").to(DEV)
+    sc.subm_timing_events(ev[4], ev[5])
+    sc.subm_conv3d_forward(None, x, w1)
+    torch.cuda.synchronize()
+    assert ev[4].elapsed_time(ev[5]) > 0.0
