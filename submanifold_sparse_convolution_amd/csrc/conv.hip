@@ -1498,11 +1498,21 @@ hipError_t launch_tile_index(int t, const ConvArgs& a, hipStream_t stream) {
 // tiles over the 256 compute units.
 constexpr int kComputeUnits = 256;
 constexpr bool persistent_enabled_default = true;
-// SUBMCONV_PERSISTENT=0 selects the one-tile-per-workgroup launch (timing and tests).
+// SUBMCONV_PERSISTENT=0 selects the one-tile-per-workgroup launch, =1 the persistent walk even for
+// the small sets that otherwise take a smaller one-tile launch (timing and tests).
 inline bool persistent_enabled() {
   const char* v = std::getenv("SUBMCONV_PERSISTENT");
   return v == nullptr ? persistent_enabled_default : v[0] != '0';
 }
+inline bool persistent_forced() {
+  const char* v = std::getenv("SUBMCONV_PERSISTENT");
+  return v != nullptr && v[0] == '1';
+}
+// Sets of at most this many rows with 33..64 output channels fill at most half the CUs with
+// 256-row tiles: a smaller one-tile launch spreads them wider (64^3 shell and torus, 22,406 rows:
+// k = 3 17.2 us with 192-row tiles against 20.4 us for the persistent walk; k = 1 5.0 us with
+// 128-row tiles against 6.3 us).
+constexpr int64_t kSmallSetRows = 32768;
 inline int64_t launch_rounds(int64_t n, int cout, int bm, int bn) {
   const int64_t tiles = (n + bm - 1) / bm * ((cout + bn - 1) / bn);
   return (tiles + kComputeUnits - 1) / kComputeUnits;
@@ -1518,7 +1528,8 @@ template <DT D, int TAPS>
 hipError_t launch_mma_auto(const ConvArgs& a, hipStream_t stream) {
   int best;
   const char* forced = std::getenv("SUBMCONV_TILE");
-  if (TAPS == 27 && a.cout > 32 && (forced == nullptr || tile_index(forced) < 0) && persistent_enabled()) {
+  const bool small64 = a.cout > 32 && a.cout <= 64 && a.n <= kSmallSetRows && !persistent_forced();
+  if (TAPS == 27 && a.cout > 32 && !small64 && (forced == nullptr || tile_index(forced) < 0) && persistent_enabled()) {
     // the persistent walk of the same tiles the one-tile launch below would use
     // eight load waves: 2-3 % faster than four on the shell, dense, ellipsoid and subdivided
     // workloads, same outputs
@@ -1526,7 +1537,9 @@ hipError_t launch_mma_auto(const ConvArgs& a, hipStream_t stream) {
                                      : launch_ws_persistent<D, 4, 2, 2, 128, 8>(a, stream);
     if (e != hipErrorNotSupported) return e;
   }
-  if (a.cout > 64) {
+  if (small64) {
+    best = tile_index(TAPS == 27 ? "ws192c64s128k" : "r128c64s64");
+  } else if (a.cout > 64) {
     best = tile_index("ws192c128s128k");
   } else if (a.cout > 32) {
     best = tile_index("ws256c64s128k");
