@@ -97,7 +97,8 @@ def source_hash(path):
 
 def measured_peaks(dev):
     """This GPU's measured ceilings, beside the published ones: a large bf16 GEMM (hipBLASLt
-    through torch.matmul, contiguous 2-D operands) and a 1 GiB device-to-device copy."""
+    through torch.matmul, contiguous 2-D operands), a 1 GiB device-to-device copy, and the
+    library's loop of register-operand bf16 MFMAs with the clock it ran at."""
     import torch
     out = {}
     m = 8192
@@ -127,6 +128,20 @@ def measured_peaks(dev):
     torch.cuda.synchronize()
     out["copy_GBps"] = 10 * 2.0 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
     del src, dst
+    # The matrix cores alone: back-to-back bf16 MFMAs on register operands, one workgroup per CU,
+    # and the shader clock they ran at (s_memtime against the 100 MHz s_memrealtime).
+    import submanifold_sparse_convolution_amd as sc
+    blocks, iters = 256, 40000
+    sc.subm_mfma_rate(iters // 10, blocks)  # warm
+    torch.cuda.synchronize()
+    e0.record()
+    _, clocks = sc.subm_mfma_rate(iters, blocks)
+    e1.record()
+    torch.cuda.synchronize()
+    flop = blocks * 4 * iters * 8 * 32768.0
+    out["mfma_loop_TFLOPs"] = flop / (e0.elapsed_time(e1) / 1e3) / 1e12
+    c = clocks.view(-1, 2).double().cpu()
+    out["mfma_loop_clock_GHz"] = float(c[:, 0].sum() / c[:, 1].sum() * 0.1)
     torch.cuda.empty_cache()
     return out
 
@@ -450,6 +465,10 @@ def main():
         roofline.update({"peak_measured": measured, "frac_measured": roofline["achieved"] / measured,
                          "peak_measured_by": "torch.matmul bf16 8192^3" if roofline["bound"] == "mfma"
                          else "1 GiB device copy (read + write)"})
+        if roofline["bound"] == "mfma":
+            roofline.update({"mfma_loop_TFLOPs": peaks["mfma_loop_TFLOPs"],
+                             "frac_of_mfma_loop": roofline["achieved"] / peaks["mfma_loop_TFLOPs"],
+                             "mfma_loop_clock_GHz": peaks["mfma_loop_clock_GHz"]})
     pct = lambda v: {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
                      "p90": float(np.percentile(v, 90))}
 

@@ -314,6 +314,19 @@ int subm_conv3d_forward_per_offset(submconv_map_t map, int64_t n, int cin, int c
  */
 int subm_timing_events(hipEvent_t start, hipEvent_t stop);
 
+/*
+ * subm_mfma_rate -- measurement: the matrix-core rate of this GPU at the clock it holds under
+ * that load.  Launches `blocks` workgroups of 256 threads (four waves); every wave issues
+ * iters x 8 back-to-back v_mfma_f32_32x32x16_bf16 on register operands (32,768 FLOP each) with
+ * no memory traffic in the loop.  sink: device float [blocks * 256] (each thread's folded
+ * accumulators, written so that no work is dropped); clocks: device uint64 [2 * blocks]: per
+ * workgroup the s_memtime (shader clock) and s_memrealtime (100 MHz) spans of its loop.  The
+ * caller times the launch on `stream` (e.g. with events).  Errors: SUBM_ERR_INVALID_ARG (iters < 1,
+ * blocks outside [1, 65535], a NULL pointer), SUBM_ERR_HIP.
+ * Source: none of the pages; it gives the measured ceiling beside the published 2.5 PFLOP/s.
+ */
+int subm_mfma_rate(int64_t iters, int blocks, float* sink, uint64_t* clocks, hipStream_t stream);
+
 /* Static string naming a status code ("SUBM_OK", ...); "unknown status" otherwise. */
 const char* subm_status_string(int status);
 

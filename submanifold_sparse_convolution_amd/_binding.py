@@ -39,6 +39,7 @@ C_FUNCTIONS = (
     "sparse_indice_map_plan_state",
     "subm_release_cached_memory",
     "subm_timing_events",
+    "subm_mfma_rate",
     "subm_conv3d_forward",
     "subm_conv3d_forward_noalloc",
     "subm_conv3d_forward_per_offset",
@@ -99,6 +100,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.sparse_indice_map_plan_state.argtypes = [vp, ctypes.POINTER(ci)]
         lib.subm_release_cached_memory.argtypes = []
         lib.subm_timing_events.argtypes = [vp, vp]
+        lib.subm_mfma_rate.argtypes = [i64, ci, vp, vp, vp]
         lib.subm_conv3d_forward.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp]
         lib.subm_conv3d_forward_noalloc.argtypes = [vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp]
         lib.subm_conv3d_forward_per_offset.argtypes = [vp, i64, ci, ci, ci, vp, vp, vp, vp, vp]
@@ -292,6 +294,22 @@ def subm_timing_events(start, stop) -> None:
     lib = load_library()
     h = lambda e: None if e is None else ctypes.c_void_p(e.cuda_event)
     _check(lib, "subm_timing_events", lib.subm_timing_events(h(start), h(stop)))
+
+
+def subm_mfma_rate(iters: int, blocks: int, device=None, stream=None):
+    """Launch the matrix-core rate loop (see subm_mfma_rate in include/submconv.h) on `stream`
+    (default: torch's current stream).  Returns (sink, clocks) device tensors; the caller times
+    the launch.  FLOP = blocks * 4 waves * iters * 8 * 32768."""
+    lib = load_library()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    clocks = torch.empty(2 * blocks, dtype=torch.int64, device=dev)
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    with _on_device(dev):
+        _check(lib, "subm_mfma_rate", lib.subm_mfma_rate(int(iters), int(blocks), ctypes.c_void_p(sink.data_ptr()),
+                                                           ctypes.c_void_p(clocks.data_ptr()),
+                                                           ctypes.c_void_p(s.cuda_stream)))
+    return sink, clocks
 
 
 def sparse_indice_map_plan_state(m: IndiceMap) -> int:
