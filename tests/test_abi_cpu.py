@@ -195,3 +195,15 @@ def test_fused_conv_norm_rejects_bad_arguments(lib):
     assert f(items=0) == INVALID
     assert f(o=256) == INVALID  # aliases feats
     assert f(n=0, x=None, w=None, o=None, off=None) == OK
+
+
+def test_measurement_entry_points_validate_on_the_host(lib):
+    # subm_timing_events only records the request; subm_mfma_rate rejects bad sizes and pointers
+    # before it launches anything
+    assert lib.subm_timing_events(None, None) == OK
+    p = ctypes.c_void_p(256)
+    assert lib.subm_mfma_rate(0, 4, p, p, None) == INVALID
+    assert lib.subm_mfma_rate(10, 0, p, p, None) == INVALID
+    assert lib.subm_mfma_rate(10, 65536, p, p, None) == INVALID
+    assert lib.subm_mfma_rate(10, 4, None, p, None) == INVALID
+    assert b"NULL" in lib.subm_last_error()

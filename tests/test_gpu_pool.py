@@ -284,3 +284,22 @@ def test_timing_events_bind_to_the_convolution_kernel_only():
     sc.subm_conv3d_forward(None, x, w1)
     torch.cuda.synchronize()
     assert ev[4].elapsed_time(ev[5]) > 0.0
+
+
+def test_mfma_rate_probe_reports_work_and_clock():
+    # the matrix-core loop of the bench's measured ceiling: finite folded sums, positive clock
+    # spans, a rate below the published 2.5 PFLOP/s and above a tenth of it
+    blocks, iters = 256, 4000
+    sc.subm_mfma_rate(100, blocks)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    sink, clocks = sc.subm_mfma_rate(iters, blocks)
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = blocks * 4 * iters * 8 * 32768.0 / (e0.elapsed_time(e1) / 1e3) / 1e12
+    c = clocks.view(-1, 2).double().cpu()
+    ghz = float(c[:, 0].sum() / c[:, 1].sum() * 0.1)
+    print(f"  MFMA loop {tflops:.0f} TFLOP/s at {ghz:.2f} GHz", flush=True)
+    assert bool(torch.isfinite(sink).all())
+    assert bool((c > 0).all())
+    assert 250.0 < tflops < 2600.0 and 0.5 < ghz < 3.0
