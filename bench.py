@@ -393,13 +393,15 @@ def main():
             ks, cin, cout, w, b = k3[i]
             src = x0_dev if not chained else outs[0]
             evs[r][0].record(stream)
-            sc.subm_timing_events(*kevs[r])
+            if not per_offset:  # (the per-offset design is 27 + 1 launches per call: timed per call)
+                sc.subm_timing_events(*kevs[r])
             conv(m, ks, src, w, b, outs[-1])
             evs[r][1].record(stream)
         torch.cuda.synchronize()
         for r in range(reps):
-            per_layer[r % len(k3)].append(kevs[r][0].elapsed_time(kevs[r][1]))
-            per_layer_call[r % len(k3)].append(evs[r][0].elapsed_time(evs[r][1]))
+            call = evs[r][0].elapsed_time(evs[r][1])
+            per_layer[r % len(k3)].append(call if per_offset else kevs[r][0].elapsed_time(kevs[r][1]))
+            per_layer_call[r % len(k3)].append(call)
         pool_path = (not per_offset and layers[0][0] == 3
                      and sc.sparse_indice_map_plan_state(m) == sc.SUBM_PLAN_READY and layers[0][2] == 128)
         # Cold caches: 1 GiB written between launches (outside the events) evicts the layer's
@@ -408,9 +410,14 @@ def main():
         for r in range(min(reps, 40)):
             flush.fill_(float(r))
             ks, cin, cout, w, b = k3[0]
-            sc.subm_timing_events(*kevs[r])
+            if per_offset:
+                evs[r][0].record(stream)
+            else:
+                sc.subm_timing_events(*kevs[r])
             conv(m, ks, x0_dev if not chained else outs[0], w, b, outs[-1])
-            cold.append(kevs[r])
+            if per_offset:
+                evs[r][1].record(stream)
+            cold.append(evs[r] if per_offset else kevs[r])
         torch.cuda.synchronize()
         cold_ms = [a.elapsed_time(b) for a, b in cold]
     del flush
