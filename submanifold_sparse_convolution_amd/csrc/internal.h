@@ -173,6 +173,7 @@ struct MapData {
   int pool_state = 0;
   PoolTiling pool_tiling;
   void* pool_plan = nullptr;
+  size_t pool_plan_bytes = 0;  // bytes of the block that starts at pool_plan
   hipStream_t pool_stream = nullptr;  // the stream the plan kernel ran on
   FlagSlot pool_slot;  // .host->flags / .dev: the overflow flag; .ready: the plan kernel's completion
 };

@@ -261,7 +261,8 @@ uint64_t grid_tag_limit() {
 
 static_assert(sizeof(MapHostFlags) == 16 && kSlotPage % sizeof(MapHostFlags) == 0, "flag slots tile a page");
 
-// Rulebook blocks of freed maps, per device, for the next build on the same stream.  Returning a
+// Rulebook (and neighbour-pool plan) blocks of freed maps, per device, for the next build (plan)
+// on the same stream.  Returning a
 // block to the stream-ordered pool and allocating it again each enqueue a marker packet (~3 us of
 // idle GPU between two kernels, measured); a cached block costs nothing.  A block is cached only
 // when every use of its map was on the map's own stream, so a later build on that stream writes
@@ -294,7 +295,9 @@ void release_map(submconv_map* m) {
   map_memory_give(m->d.device, m->d.nbr, m->d.nbr_bytes, m->d.home,
                   !m->other_streams.load(std::memory_order_relaxed));
   device_free(m->d.pair_out, m->d.home);  // (work on other streams has completed: the free rules)
-  device_free(m->d.pool_plan, m->d.home);
+  // the plan block goes to the cache when the plan and every use of the map ran on the map's stream
+  map_memory_give(m->d.device, m->d.pool_plan, m->d.pool_plan_bytes, m->d.home,
+                  !m->other_streams.load(std::memory_order_relaxed) && m->d.pool_stream == m->d.home);
   delete m;
 }
 
@@ -671,7 +674,9 @@ Status pool_prepare(submconv_map* map, hipStream_t stream, int* state) {
     Status s = take_flag_slot(d.device, &d.pool_slot);
     if (!s.ok()) return s;
     d.pool_slot.host->flags = 0u;
-    s = device_alloc(&d.pool_plan, pool_plan_bytes(t), stream);
+    // (a block of a freed map's plan on this stream when one fits: no allocator packet between the
+    // build's kernels and the plan kernel)
+    s = map_memory_take(d.device, pool_plan_bytes(t), stream, &d.pool_plan, &d.pool_plan_bytes);
     if (!s.ok()) {
       give_flag_slot(d.device, d.pool_slot);
       return s;
