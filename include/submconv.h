@@ -208,6 +208,20 @@ enum { SUBM_PLAN_NONE = 0, SUBM_PLAN_PENDING = 1, SUBM_PLAN_READY = 2, SUBM_PLAN
 int sparse_indice_map_plan_state(submconv_map_t map, int* state);
 
 /*
+ * sparse_indice_map_row_order_state -- *state (host int) = the state of the map's sparse-row
+ * order: SUBM_ORDER_NONE (not enqueued), SUBM_ORDER_ON (built: 27-tap convolutions on the
+ * matrix-core walk visit rows with similar neighbour masks together) or SUBM_ORDER_OFF (enqueued,
+ * but the map's rows average more than 9 of 27 neighbours, so the input order is kept).  The
+ * second 16-bit 27-tap convolution with more than 32 output channels on a map of at least 65,536
+ * rows, on the map's own stream, enqueues the order there (SUBMCONV_ROW_ORDER=0 disables it); the
+ * outputs are the same bits either way (a skipped tap is one whose neighbour is absent, which adds
+ * exact zeros).  Waits for the order's kernels when it is enqueued.  Source: lato.2_mrp_mlx
+ * README, header summary (the neighbour sum over present offsets only).
+ */
+enum { SUBM_ORDER_NONE = 0, SUBM_ORDER_ON = 1, SUBM_ORDER_OFF = 2 };
+int sparse_indice_map_row_order_state(submconv_map_t map, int* state);
+
+/*
  * sparse_indice_map_copy_nbr -- copy the rulebook into caller memory.
  *   nbr     device int32 [n, 27] in input row order; nbr[i, k] is the input row of the active
  *           voxel at coord_i + offset(k), or -1.  Independent of any internal ordering.

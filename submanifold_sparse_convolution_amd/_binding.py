@@ -37,6 +37,7 @@ C_FUNCTIONS = (
     "sparse_indice_map_offset_counts",
     "sparse_indice_map_copy_nbr",
     "sparse_indice_map_plan_state",
+    "sparse_indice_map_row_order_state",
     "subm_release_cached_memory",
     "subm_timing_events",
     "subm_mfma_rate",
@@ -98,6 +99,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.sparse_indice_map_offset_counts.argtypes = [vp, ctypes.POINTER(i64)]
         lib.sparse_indice_map_copy_nbr.argtypes = [vp, vp, vp]
         lib.sparse_indice_map_plan_state.argtypes = [vp, ctypes.POINTER(ci)]
+        lib.sparse_indice_map_row_order_state.argtypes = [vp, ctypes.POINTER(ci)]
         lib.subm_release_cached_memory.argtypes = []
         lib.subm_timing_events.argtypes = [vp, vp]
         lib.subm_mfma_rate.argtypes = [i64, ci, vp, vp, vp]
@@ -276,6 +278,7 @@ def sparse_indice_map_mode(m: IndiceMap) -> int:
 
 
 SUBM_PLAN_NONE, SUBM_PLAN_PENDING, SUBM_PLAN_READY, SUBM_PLAN_OVERFLOW = 0, 1, 2, 3
+SUBM_ORDER_NONE, SUBM_ORDER_ON, SUBM_ORDER_OFF = 0, 1, 2
 
 
 def subm_release_cached_memory(device=None) -> None:
@@ -310,6 +313,15 @@ def subm_mfma_rate(iters: int, blocks: int, device=None, stream=None):
                                                            ctypes.c_void_p(clocks.data_ptr()),
                                                            ctypes.c_void_p(s.cuda_stream)))
     return sink, clocks
+
+
+def sparse_indice_map_row_order_state(m: IndiceMap) -> int:
+    """State of the map's sparse-row order: SUBM_ORDER_NONE / _ON / _OFF (waits for its kernels)."""
+    lib = load_library()
+    state = ctypes.c_int()
+    _check(lib, "sparse_indice_map_row_order_state",
+           lib.sparse_indice_map_row_order_state(m.handle, ctypes.byref(state)))
+    return state.value
 
 
 def sparse_indice_map_plan_state(m: IndiceMap) -> int:

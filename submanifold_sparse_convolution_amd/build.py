@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsubmconv.so")
 SOURCES = ["submconv_api.hip", "indice_map.hip", "conv.hip", "conv_pool.hip", "conv_offsets.hip", "structure.hip",
-           "norm.hip", "sort_scan.hip", "peak.hip"]
+           "norm.hip", "sort_scan.hip", "row_order.hip", "peak.hip"]
 
 ARCH = "gfx950"
 COMMON = [

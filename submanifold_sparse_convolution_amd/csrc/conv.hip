@@ -74,6 +74,13 @@ struct ConvArgs {
   // beside a neighbour-pool convolution whose plan may have overflowed)
   const uint32_t* gate;
   int gate_n;
+  // Row order of a sparse map (read by the persistent 27-tap walk only; null elsewhere): when
+  // *order_gate is set, walk position j is input row order_rows[j], with rulebook row
+  // order_nbr[j] and mask order_masks[j].
+  const uint32_t* order_gate;
+  const int32_t* order_rows;
+  const int32_t* order_nbr;
+  const uint32_t* order_masks;
 };
 
 // (every thread of the workgroup calls it)
@@ -1117,6 +1124,12 @@ __global__ __launch_bounds__(64 * (4 + LW), 1) void subm_conv_ws_persistent_kern
   __shared__ __align__(16) float s_bias[BN];
   __shared__ uint32_t s_tmask[kMaxBlockTiles];
   if (gated_off(args)) return;  // (whole workgroup: no barrier has run yet)
+  // The walk's row order: the input order, or the map's sparse-row order when its gate is set
+  // (same outputs: a row's taps are added in the same order, and only absent ones are skipped).
+  const bool ordered = args.order_gate != nullptr && *args.order_gate != 0u;
+  const int32_t* const nbr_w = ordered ? args.order_nbr : args.nbr;
+  const uint32_t* const masks_w = ordered ? args.order_masks : args.masks;
+  const int32_t* const rows_w = ordered ? args.order_rows : nullptr;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1141,7 +1154,7 @@ __global__ __launch_bounds__(64 * (4 + LW), 1) void subm_conv_ws_persistent_kern
 
   // Rulebook rows of tile k for this load wave's share of the rows, into its own slot (only this
   // wave reads it, so its own wait is enough).
-  const i32x4_t rsrc_n = make_rsrc(args.nbr, (uint32_t)(n * 27 * 4));
+  const i32x4_t rsrc_n = make_rsrc(nbr_w, (uint32_t)(n * 27 * 4));
   auto issue_rows = [&](int k) {
     const uint32_t gbase = (uint32_t)(((int64_t)tile_of(k) * BM + cw * QROWS) * 27 * 4);
 #pragma unroll
@@ -1173,7 +1186,7 @@ __global__ __launch_bounds__(64 * (4 + LW), 1) void subm_conv_ws_persistent_kern
       const int k = idx / BM;
       const int64_t row = (int64_t)tile_of(k < ntiles ? k : 0) * BM + (idx - k * BM);
       const bool ok = idx < ntiles * BM && row < n;
-      m[u] = ok ? args.masks[row] : 0u;
+      m[u] = ok ? masks_w[row] : 0u;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -1350,6 +1363,7 @@ __global__ __launch_bounds__(64 * (4 + LW), 1) void subm_conv_ws_persistent_kern
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int64_t row = row0 + wm * WTM + i * 32 + lrow;
+        const int64_t orow = (rows_w != nullptr && row < n) ? (int64_t)rows_w[row] : row;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -1357,7 +1371,7 @@ __global__ __launch_bounds__(64 * (4 + LW), 1) void subm_conv_ws_persistent_kern
             const int c = wn * WTN + j * 32 + 8 * g + 4 * lk;
             const float4 bb = *reinterpret_cast<const float4*>(s_bias + c);
             if (row < n && o0 + c < cout)
-              *reinterpret_cast<uint2*>(out + row * cout + o0 + c) =
+              *reinterpret_cast<uint2*>(out + orow * cout + o0 + c) =
                   pack4<D>(acc[i][j][4 * g] + bb.x, acc[i][j][4 * g + 1] + bb.y, acc[i][j][4 * g + 2] + bb.z,
                            acc[i][j][4 * g + 3] + bb.w);
             acc[i][j][4 * g] = acc[i][j][4 * g + 1] = acc[i][j][4 * g + 2] = acc[i][j][4 * g + 3] = 0.f;
@@ -1661,6 +1675,13 @@ hipError_t launch_subm_conv(const MapData* map, int64_t n, int ksize, int cin, i
   a.weight_bytes = wb < kOffsetLimit ? (uint32_t)wb : 0u;
   a.gate = gate;
   a.gate_n = gate_n;
+  if (ksize == 3 && map->order_block != nullptr && stream == map->order_stream) {
+    const OrderView v = order_view(map->order_block, map->n);
+    a.order_gate = v.gate;
+    a.order_rows = v.rows;
+    a.order_nbr = v.nbr;
+    a.order_masks = v.masks;
+  }
   switch (dtype) {
     case SUBM_F32: return launch_dtype<DT::F32>(a, vec_in, taps, stream);
     case SUBM_F16: return launch_dtype<DT::F16>(a, vec_in, taps, stream);

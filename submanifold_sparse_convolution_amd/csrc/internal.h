@@ -176,6 +176,11 @@ struct MapData {
   size_t pool_plan_bytes = 0;  // bytes of the block that starts at pool_plan
   hipStream_t pool_stream = nullptr;  // the stream the plan kernel ran on
   FlagSlot pool_slot;  // .host->flags / .dev: the overflow flag; .ready: the plan kernel's completion
+  // Row order of the persistent 27-tap convolution (row_order.hip), enqueued by the map's second
+  // convolution on that path when the set is large enough; used by the calls on order_stream.
+  int order_calls = 0;
+  void* order_block = nullptr;
+  hipStream_t order_stream = nullptr;
 };
 
 // Map build (indice_map.hip).  Enqueues on `stream`; does not synchronise.  `hash_table` holds
@@ -204,8 +209,11 @@ hipError_t launch_fill(void* p, size_t bytes, uint32_t value, hipStream_t stream
 
 // Prefix sum of n int32 (sort_scan.hip): out[i] = in[0] + ... + in[i] (inclusive) or the sum
 // before i (exclusive); out may equal in; both 16-byte aligned.  scratch: scan_scratch_bytes(n).
+// A non-null `gate` makes every kernel of the call return at once when *gate is zero (the same
+// for the sort below).
 size_t scan_scratch_bytes(int64_t n);
-hipError_t launch_scan(const int32_t* in, int32_t* out, int64_t n, bool exclusive, void* scratch, hipStream_t stream);
+hipError_t launch_scan(const int32_t* in, int32_t* out, int64_t n, bool exclusive, void* scratch, hipStream_t stream,
+                       const uint32_t* gate = nullptr);
 // Stable LSD radix sort of n (key, value) pairs by key bits [0, bits), digits of at most 9 bits
 // (as few passes as that allows), ping-pong
 // between (keys, vals) and (keys_alt, vals_alt): *result_in_alt says which pair holds the sorted
@@ -214,7 +222,24 @@ hipError_t launch_scan(const int32_t* in, int32_t* out, int64_t n, bool exclusiv
 size_t radix_sort_scratch_bytes(int64_t n);
 template <typename K>
 hipError_t launch_radix_sort_pairs(K* keys, int32_t* vals, K* keys_alt, int32_t* vals_alt, int64_t n, int bits,
-                                   void* scratch, hipStream_t stream, bool* result_in_alt);
+                                   void* scratch, hipStream_t stream, bool* result_in_alt,
+                                   const uint32_t* gate = nullptr);
+
+// Row order of a sparse map (row_order.hip).  The block (order_block_bytes(n)) holds the gate
+// (device flag: 1 when the order was built, 0 when the map is too dense for it to pay), the input
+// row at each position, and the rulebook rows and masks in that order.
+struct OrderView {
+  uint32_t* gate;
+  int32_t* rows;
+  int32_t* nbr;
+  uint32_t* masks;
+};
+OrderView order_view(void* block, int64_t n);
+size_t order_block_bytes(int64_t n);
+size_t order_scratch_bytes(int64_t n);
+// Enqueues the gate, the sort and the permuted copy (reads d->nbr, d->masks, d->dev_banks).
+hipError_t launch_row_order(const MapData* d, void* block, void* scratch, hipStream_t stream);
+constexpr int64_t kOrderMinRows = 65536;  // smaller sets keep the input order
 
 // Child map of a subdivide (structure.hip): nbr [8 np, 27] and masks [8 np] from the parent
 // rulebook [np, 27].

@@ -82,9 +82,14 @@ __device__ __forceinline__ void load16(const int32_t* p, int64_t base, int64_t n
   }
 }
 
+// Every kernel below returns at once when `gate` is non-null and *gate is zero (work enqueued
+// ahead of a condition that only the device knows).
+__device__ __forceinline__ bool gated(const uint32_t* gate) { return gate != nullptr && *gate == 0u; }
+
 __global__ __launch_bounds__(kST) void scan_tile_sums_kernel(const int32_t* __restrict__ in, int64_t n,
-                                                              int32_t* __restrict__ sums) {
+                                                              int32_t* __restrict__ sums, const uint32_t* gate) {
   __shared__ int s_w[kST / 64];
+  if (gated(gate)) return;
   int v[kPer];
   load16(in, (int64_t)blockIdx.x * kTile + (int64_t)threadIdx.x * kPer, n, v);
   int s = 0;
@@ -96,8 +101,9 @@ __global__ __launch_bounds__(kST) void scan_tile_sums_kernel(const int32_t* __re
 }
 
 // In place: sums[t] becomes the sum of sums[0 .. t).
-__global__ __launch_bounds__(kTop) void scan_sums_kernel(int32_t* __restrict__ sums, int64_t p) {
+__global__ __launch_bounds__(kTop) void scan_sums_kernel(int32_t* __restrict__ sums, int64_t p, const uint32_t* gate) {
   __shared__ int s_w[kTop / 64];
+  if (gated(gate)) return;
   const int64_t per = (p + kTop - 1) / kTop;
   const int64_t b = (int64_t)threadIdx.x * per;
   const int64_t e = b + per < p ? b + per : p;
@@ -114,8 +120,10 @@ __global__ __launch_bounds__(kTop) void scan_sums_kernel(int32_t* __restrict__ s
 
 // out may be in (each thread reads its own values before it writes them).
 __global__ __launch_bounds__(kST) void scan_apply_kernel(const int32_t* in, int32_t* out, int64_t n,
-                                                          const int32_t* __restrict__ sums, int exclusive) {
+                                                          const int32_t* __restrict__ sums, int exclusive,
+                                                          const uint32_t* gate) {
   __shared__ int s_w[kST / 64];
+  if (gated(gate)) return;
   const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)threadIdx.x * kPer;
   int v[kPer];
   load16(in, base, n, v);
@@ -157,8 +165,10 @@ __device__ __forceinline__ unsigned long long match_digit(uint32_t d, bool valid
 // counts[d * tiles + tile] for the 2^rb digits of key bits [shift, shift + rb).
 template <typename K>
 __global__ __launch_bounds__(kST) void radix_count_kernel(const K* __restrict__ keys, int64_t n, int shift, int rb,
-                                                           int64_t tiles, int32_t* __restrict__ counts) {
+                                                           int64_t tiles, int32_t* __restrict__ counts,
+                                                           const uint32_t* gate) {
   __shared__ int32_t h[kMaxBuckets];
+  if (gated(gate)) return;
   const int t = threadIdx.x, lane = t & 63;
   const uint32_t mask = (1u << rb) - 1u;
   h[t] = 0;
@@ -188,9 +198,11 @@ __global__ __launch_bounds__(kST) void radix_scatter_kernel(const K* __restrict_
                                                              const int32_t* __restrict__ vals_in,
                                                              K* __restrict__ keys_out, int32_t* __restrict__ vals_out,
                                                              int64_t n, int shift, int rb, int64_t tiles,
-                                                             const int32_t* __restrict__ offsets) {
+                                                             const int32_t* __restrict__ offsets,
+                                                             const uint32_t* gate) {
   __shared__ int32_t s_run[kMaxBuckets];          // next output position of each digit in this tile
   __shared__ int32_t s_wc[kST / 64][kMaxBuckets];  // per-wave digit counts of the current round
+  if (gated(gate)) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const uint32_t mask = (1u << rb) - 1u;
   const int64_t base = (int64_t)blockIdx.x * kTile;
@@ -250,14 +262,15 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 size_t scan_scratch_bytes(int64_t n) { return align256((size_t)tiles_of(n) * sizeof(int32_t)); }
 
-hipError_t launch_scan(const int32_t* in, int32_t* out, int64_t n, bool exclusive, void* scratch, hipStream_t stream) {
+hipError_t launch_scan(const int32_t* in, int32_t* out, int64_t n, bool exclusive, void* scratch, hipStream_t stream,
+                       const uint32_t* gate) {
   if (n <= 0) return hipSuccess;
   const int64_t p = tiles_of(n);
   int32_t* sums = static_cast<int32_t*>(scratch);
-  scan_tile_sums_kernel<<<(unsigned)p, kST, 0, stream>>>(in, n, sums);
-  scan_sums_kernel<<<1, kTop, 0, stream>>>(sums, p);
+  scan_tile_sums_kernel<<<(unsigned)p, kST, 0, stream>>>(in, n, sums, gate);
+  scan_sums_kernel<<<1, kTop, 0, stream>>>(sums, p, gate);
   const int32_t* csums = sums;
-  scan_apply_kernel<<<(unsigned)p, kST, 0, stream>>>(in, out, n, csums, exclusive ? 1 : 0);
+  scan_apply_kernel<<<(unsigned)p, kST, 0, stream>>>(in, out, n, csums, exclusive ? 1 : 0, gate);
   return hipGetLastError();
 }
 
@@ -268,7 +281,7 @@ size_t radix_sort_scratch_bytes(int64_t n) {
 
 template <typename K>
 hipError_t launch_radix_sort_pairs(K* keys, int32_t* vals, K* keys_alt, int32_t* vals_alt, int64_t n, int bits,
-                                   void* scratch, hipStream_t stream, bool* result_in_alt) {
+                                   void* scratch, hipStream_t stream, bool* result_in_alt, const uint32_t* gate) {
   *result_in_alt = false;
   if (n <= 0 || bits <= 0) return hipSuccess;
   const int64_t tiles = tiles_of(n);
@@ -283,12 +296,12 @@ hipError_t launch_radix_sort_pairs(K* keys, int32_t* vals, K* keys_alt, int32_t*
   for (int p = 0, shift = 0; p < passes; ++p) {
     const int rb = (bits - shift + (passes - p) - 1) / (passes - p);
     const K* ckin = kin;
-    radix_count_kernel<K><<<(unsigned)tiles, kST, 0, stream>>>(ckin, n, shift, rb, tiles, counts);
-    hipError_t e = launch_scan(counts, counts, (int64_t(1) << rb) * tiles, true, scan_tmp, stream);
+    radix_count_kernel<K><<<(unsigned)tiles, kST, 0, stream>>>(ckin, n, shift, rb, tiles, counts, gate);
+    hipError_t e = launch_scan(counts, counts, (int64_t(1) << rb) * tiles, true, scan_tmp, stream, gate);
     if (e != hipSuccess) return e;
     const int32_t* cvin = vin;
     const int32_t* coff = counts;
-    radix_scatter_kernel<K><<<(unsigned)tiles, kST, 0, stream>>>(ckin, cvin, kout, vout, n, shift, rb, tiles, coff);
+    radix_scatter_kernel<K><<<(unsigned)tiles, kST, 0, stream>>>(ckin, cvin, kout, vout, n, shift, rb, tiles, coff, gate);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     std::swap(kin, kout);
@@ -300,8 +313,8 @@ hipError_t launch_radix_sort_pairs(K* keys, int32_t* vals, K* keys_alt, int32_t*
 }
 
 template hipError_t launch_radix_sort_pairs<uint32_t>(uint32_t*, int32_t*, uint32_t*, int32_t*, int64_t, int, void*,
-                                                      hipStream_t, bool*);
+                                                      hipStream_t, bool*, const uint32_t*);
 template hipError_t launch_radix_sort_pairs<uint64_t>(uint64_t*, int32_t*, uint64_t*, int32_t*, int64_t, int, void*,
-                                                      hipStream_t, bool*);
+                                                      hipStream_t, bool*, const uint32_t*);
 
 }  // namespace submconv

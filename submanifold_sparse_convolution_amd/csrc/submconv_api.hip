@@ -298,6 +298,7 @@ void release_map(submconv_map* m) {
   // the plan block goes to the cache when the plan and every use of the map ran on the map's stream
   map_memory_give(m->d.device, m->d.pool_plan, m->d.pool_plan_bytes, m->d.home,
                   !m->other_streams.load(std::memory_order_relaxed) && m->d.pool_stream == m->d.home);
+  device_free(m->d.order_block, m->d.order_stream);  // (in order after the calls that used it)
   delete m;
 }
 
@@ -742,6 +743,33 @@ extern "C" int sparse_indice_map_plan_state(submconv_map_t map, int* state) {
   return SUBM_OK;
 }
 
+extern "C" int sparse_indice_map_row_order_state(submconv_map_t map, int* state) {
+  clear_error();
+  if (map == nullptr) return fail(SUBM_ERR_INVALID_ARG, "map is NULL");
+  if (state == nullptr) return fail(SUBM_ERR_INVALID_ARG, "state is NULL");
+  std::lock_guard<std::mutex> lock(map->mu);
+  const MapData& d = map->d;
+  if (d.order_block == nullptr) {
+    *state = SUBM_ORDER_NONE;
+    return SUBM_OK;
+  }
+  uint32_t gate = 0;
+  hipError_t e = hipMemcpyAsync(&gate, order_view(d.order_block, d.n).gate, sizeof(gate), hipMemcpyDeviceToHost,
+                                d.order_stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(d.order_stream);
+  if (e != hipSuccess) return fail(hip_status(e, "row order gate read"));
+  *state = gate != 0u ? SUBM_ORDER_ON : SUBM_ORDER_OFF;
+  return SUBM_OK;
+}
+
+namespace {
+// SUBMCONV_ROW_ORDER=0 keeps every map in its input row order (timing and tests).
+bool row_order_enabled() {
+  const char* v = std::getenv("SUBMCONV_ROW_ORDER");
+  return v == nullptr || v[0] != '0';
+}
+}  // namespace
+
 extern "C" int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int cin, int cout, int dtype,
                                    const void* feats, const void* weight, const void* bias, void* out,
                                    hipStream_t stream) {
@@ -771,6 +799,30 @@ extern "C" int subm_conv3d_forward(submconv_map_t map, int64_t n, int ksize, int
       if (e != hipSuccess) return fail(hip_status(e, "subm_conv3d_forward launch"));
       return SUBM_OK;
     }
+  }
+  // A large map's second convolution on the matrix-core walk enqueues its sparse-row order (built
+  // only where rows have few neighbours, decided on the device; row_order.hip).
+  std::unique_lock<std::mutex> order_lock;
+  if (map != nullptr) order_lock = std::unique_lock<std::mutex>(map->mu);
+  if (ksize == 3 && n >= kOrderMinRows && dtype != SUBM_F32 && cout > 32 && map->d.order_block == nullptr &&
+      stream == map->d.home && !map->other_streams.load(std::memory_order_relaxed) && row_order_enabled() &&
+      ++map->d.order_calls == 2) {
+    void* blk = nullptr;
+    void* scr = nullptr;
+    hipError_t e = hipMallocAsync(&blk, order_block_bytes(n), stream);
+    if (e != hipSuccess) return fail(hip_status(e, "row order allocation"));
+    s = stream_scratch(map->d.device, stream, order_scratch_bytes(n), &scr);
+    if (!s.ok()) {
+      device_free(blk, stream);
+      return fail(s);
+    }
+    e = launch_row_order(&map->d, blk, scr, stream);
+    if (e != hipSuccess) {
+      device_free(blk, stream);
+      return fail(hip_status(e, "row order launch"));
+    }
+    map->d.order_block = blk;
+    map->d.order_stream = stream;
   }
   hipError_t e = launch_subm_conv(map == nullptr ? nullptr : &map->d, n, ksize, cin, cout, dtype, feats, weight, bias, out, stream);
   if (e != hipSuccess) return fail(hip_status(e, "subm_conv3d_forward launch"));

@@ -697,3 +697,57 @@ def test_random_sets_and_shapes_match_the_oracle(seed):
         assert np.array_equal(gpu_nbr(m), nbr), what
         out = forward(m, f, w, b)
     check_features(out, nbr, as64(f), as64(w), as64(b), dtype, what)
+
+
+# ----------------------------------------------------------------- sparse-row order of a reused map
+
+def _order_case(coords, cin, cout, dtype, seed):
+    rng = np.random.default_rng(seed)
+    n = len(coords)
+    f = synth.round_to(rng.standard_normal((n, cin)), dtype)
+    w = synth.round_to(rng.standard_normal((cout, 3, 3, 3, cin)) / np.sqrt(27 * cin), dtype)
+    b = synth.round_to(rng.standard_normal(cout) * 0.3, dtype)
+    return f, w, b
+
+
+def _calls_on_one_map(coords, f, w, b, calls):
+    outs, states = [], []
+    with sc.sparse_indice_map_build(torch.from_numpy(coords).to(DEV)) as m:
+        for _ in range(calls):
+            outs.append(sc.subm_conv3d_forward(m, to_dev(f), to_dev(w), to_dev(b)))
+            torch.cuda.synchronize()
+            states.append(sc.sparse_indice_map_row_order_state(m))
+    return [o.cpu() for o in outs], states
+
+
+@pytest.mark.parametrize("dtype,cin,cout", [("bf16", 64, 64), ("f16", 64, 96), ("bf16", 128, 64)])
+def test_sparse_row_order_same_bits_as_input_order(monkeypatch, dtype, cin, cout):
+    # 300,001 rows of the subdivided 512^3 boxes (about 6.7 of 27 neighbours per row): five sort
+    # segments of 65,536 rows, the last one partial, and a partial last tile.
+    coords = np.ascontiguousarray(coords_of("5")[:300_001])
+    f, w, b = _order_case(coords, cin, cout, dtype, seed=11)
+    monkeypatch.setenv("SUBMCONV_ROW_ORDER", "0")
+    ref, st0 = _calls_on_one_map(coords, f, w, b, 2)
+    assert st0 == [sc.SUBM_ORDER_NONE, sc.SUBM_ORDER_NONE]
+    monkeypatch.delenv("SUBMCONV_ROW_ORDER")
+    outs, st = _calls_on_one_map(coords, f, w, b, 3)
+    print(f"  order states {st}", flush=True)
+    assert st == [sc.SUBM_ORDER_NONE, sc.SUBM_ORDER_ON, sc.SUBM_ORDER_ON]
+    for o in outs:  # a skipped tap is an absent neighbour: the same bits as the input order
+        assert torch.equal(o.view(torch.int16), ref[0].view(torch.int16))
+    check_features(outs[2], oracle.rulebook_sorted(coords), as64(f), as64(w), as64(b), dtype,
+                   f"ordered {dtype} {cin}->{cout}", mag_rows=sample_rows(len(coords), count=2048))
+
+
+def test_sparse_row_order_off_on_dense_maps():
+    # 64^3 solid box: 25.4 neighbours per row on average, so the device gate keeps the input order.
+    z, y, x = np.nonzero(synth.dense_box(64))
+    coords = np.stack([np.zeros_like(z), z, y, x], axis=1).astype(np.int32)
+    f, w, b = _order_case(coords, 64, 64, "bf16", seed=12)
+    outs, st = _calls_on_one_map(coords, f, w, b, 3)
+    assert st == [sc.SUBM_ORDER_NONE, sc.SUBM_ORDER_OFF, sc.SUBM_ORDER_OFF]
+    assert torch.equal(outs[1].view(torch.int16), outs[0].view(torch.int16))
+    assert torch.equal(outs[2].view(torch.int16), outs[0].view(torch.int16))
+    rows = sample_rows(len(coords), count=1024)
+    check_features(outs[2][rows], oracle.rulebook_sorted(coords), as64(f), as64(w), as64(b), "bf16",
+                   "dense, input order", rows=rows)
